@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the prefix-tree two-phase attention on one MI355X.
+
+One step = one ca_attend (chunk-first, sequence-first and merge kernels) over
+the whole batch, with the chunk table already uploaded and Q resident in HBM.
+Before each timed step a 1 GiB scratch buffer is rewritten (outside the
+timing events) so neither the 256 MB Infinity Cache nor the L2s hold KV: the
+figures are cold-cache HBM figures.  Warm (back-to-back) figures are reported
+alongside, labelled.
+
+Prints one JSON line:
+  value        attended KV tokens/s (sum of sequence lengths / step time)
+  roofline     the dominant kernel's unique-KV bytes / its own average
+               duration, against the 8 TB/s HBM peak
+  comparator   the same step on the unshared paged layout (every sequence
+               keeps its own copy of every chunk; no chunk-first phase)
+  cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "attended KV tokens/s per decode step; unique-KV HBM GB/s vs 8 TB/s peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: 32 seq, 1024+512)")
+    ap.add_argument("--no-comparator", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="only warmup + timed steps of the main path (for rocprofv3 runs)")
+    return ap.parse_args()
+
+
+class Flusher:
+    """Rewrites a 1 GiB buffer: evicts KV from the Infinity Cache and L2s."""
+
+    def __init__(self, torch):
+        self.buf = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+        self.buf.zero_()
+
+    def __call__(self):
+        self.buf.add_(1)
+
+
+def time_steps(torch, fn, steps, flush=None):
+    """Per-step event times (ms) of fn() on the current stream."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        if flush is not None:
+            flush()
+        ev[i][0].record()
+        fn()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def time_phases(torch, ca, q, out, steps, flush):
+    """Per-kernel event times (ms): chunk-first, sequence-first, merge."""
+    from decode_attention_prefix_tree_amd import _capi
+    phases = (_capi.CA_PHASE_CHUNK_FIRST, _capi.CA_PHASE_SEQUENCE_FIRST, _capi.CA_PHASE_MERGE)
+    ca.prepare()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush()
+        ev[i][0].record()
+        for j, ph in enumerate(phases):
+            ca.attend_phase(ph, q, out)
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    t = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)] for i in range(steps)])
+    return t
+
+
+def cpu_baseline(wl, seconds_target):
+    """fp64 oracle on a bounded sample of rows, threads over sequences."""
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import attention as A
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    workers = len(os.sched_getaffinity(0))
+    rows = list(range(wl.n_seq))
+
+    def one(i):
+        k, v = wl.seq_kv(i)
+        return A.attend_sequence(wl.q[i], k, v)
+
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    try:
+        # size the sample: time one row, then take enough rows for ~seconds_target
+        t0 = time.perf_counter()
+        one(0)
+        t1 = time.perf_counter() - t0
+        n = int(max(1, min(len(rows), seconds_target / max(t1, 1e-4))))
+        n = max(min(n, len(rows)), min(workers, len(rows)))
+        sample = rows[:n]
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            t0 = time.perf_counter()
+            list(ex.map(one, sample))
+            dt = time.perf_counter() - t0
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    toks = int(sum(wl.seq_len(i) for i in sample))
+    used = min(workers, len(sample))
+    return {"value": toks / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{len(sample)} of {wl.n_seq} sequences ({toks} attended tokens, all {wl.heads} heads), "
+                      f"fp64 numpy, {used} threads over sequences, BLAS 1 thread, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(heads shard across GPUs with no exchange; only the one-GPU share is run here)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from decode_attention_prefix_tree_amd import ChunkAttention, load_workload, slots_needed
+    from workloads import CONFIG_NAMES, make_config
+
+    torch.cuda.set_device(0)
+    log(f"building workload {args.config}")
+    wl = make_config(args.config)
+    ca = ChunkAttention(wl.heads, slots_needed(wl) + 8, device="cuda:0")
+    load_workload(ca, wl)
+    q = torch.from_numpy(wl.q).cuda()
+    out = torch.empty_like(q)
+    ca.ensure_workspace()
+    st = ca.stats()
+    torch.cuda.synchronize()
+    flush = Flusher(torch)
+
+    def step():
+        ca.attend(q, out)
+
+    log("warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} cold steps")
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    cold = time_steps(torch, step, args.steps, flush)
+    wall = time.perf_counter() - wall0
+    if args.profile_only:
+        log(f"cold mean {cold.mean()*1e3:.1f} us")
+        return
+
+    log("timing warm steps")
+    warm = time_steps(torch, step, args.steps)
+    log("timing phases")
+    ph = time_phases(torch, ca, q, out, args.steps, flush)
+
+    unique_b = st["unique_kv_bytes"]
+    per_tok = 4 * wl.heads * wl.head_dim
+    shared_b = st["shared_tokens"] * per_tok
+    private_b = st["private_tokens"] * per_tok
+    t_mean = float(cold.mean()) * 1e-3
+    value = st["attended_tokens"] / t_mean
+
+    # dominant kernel by measured time
+    names = ["chunk_first", "sequence_first", "merge"]
+    algo = [shared_b, private_b, 0]
+    dom = int(np.argmax(ph.mean(axis=0)))
+    dom_t = float(ph[:, dom].mean()) * 1e-3
+    roof = {"kernel": names[dom], "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
+            "achieved": algo[dom] / dom_t / 1e9 if algo[dom] else None,
+            "traffic": None,
+            "bytes_per_launch": algo[dom], "avg_launch_us": dom_t * 1e6}
+    roof["frac"] = roof["achieved"] / HBM_PEAK_GBPS if roof["achieved"] else None
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_mean * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": CONFIG_NAMES[args.config], "n_seq": wl.n_seq, "heads": wl.heads,
+                   "head_dim": wl.head_dim, "chunk": wl.chunk, "cache": "cold (1 GiB rewrite before each step)"},
+        "unique_kv_gbps": unique_b / t_mean / 1e9,
+        "hbm_frac_unique": unique_b / t_mean / 1e9 / HBM_PEAK_GBPS,
+        "queries_per_s": wl.n_seq / t_mean,
+        "step_us": {"mean": t_mean * 1e6, "p10": float(np.percentile(cold, 10)) * 1e3,
+                    "p50": float(np.median(cold)) * 1e3, "p90": float(np.percentile(cold, 90)) * 1e3},
+        "warm_step_us": {"mean": float(warm.mean()) * 1e3, "p50": float(np.median(warm)) * 1e3,
+                         "unique_kv_gbps": unique_b / (float(warm.mean()) * 1e-3) / 1e9},
+        "phase_us": {n: float(ph[:, j].mean()) * 1e3 for j, n in enumerate(names)},
+        "tokens": {"attended": st["attended_tokens"], "unique": st["unique_tokens"],
+                   "shared": st["shared_tokens"], "private": st["private_tokens"]},
+        "timed_wall_s": wall,
+        "roofline": roof,
+    }
+
+    if not args.no_comparator:
+        log("comparator: unshared paged layout")
+        cmp_ca = ChunkAttention(wl.heads, slots_needed(wl, share=False) + 8, device="cuda:0", share=False)
+        load_workload(cmp_ca, wl)
+        cmp_ca.ensure_workspace()
+        out2 = torch.empty_like(q)
+
+        def cstep():
+            cmp_ca.attend(q, out2)
+
+        for _ in range(args.warmup):
+            cstep()
+        cc = time_steps(torch, cstep, args.steps, flush)
+        tc = float(cc.mean()) * 1e-3
+        cst = cmp_ca.stats()
+        result["comparator"] = {
+            "kind": "unshared paged decode (own HIP kernel, 64-token blocks per sequence)",
+            "ms_per_step": tc * 1e3, "attended_tokens_per_s": cst["attended_tokens"] / tc,
+            "attended_kv_gbps": cst["attended_kv_bytes"] / tc / 1e9, "speedup": tc / t_mean}
+        del cmp_ca
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+"""Python binding of the C-ABI library: argument marshalling only.
+
+PyTorch provides device memory (the chunk pool, the workspace, q/out) and the
+current stream; every step of the decode path runs in the library's HIP
+kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import _capi
+from ._capi import CaError, check, load
+
+HEAD_DIM = 128
+CHUNK = 64
+
+
+def slot_bytes(heads: int, head_dim: int = HEAD_DIM, chunk: int = CHUNK) -> int:
+    return int(load().ca_slot_bytes(heads, head_dim, chunk))
+
+
+def _tokens(tokens) -> np.ndarray:
+    t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+    return t
+
+
+def _ptr_i32(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+class ChunkAttention:
+    """Prefix-tree KV cache plus the two-phase decode-step attention.
+
+    heads: head count; capacity_slots: pool size in 64-token chunk slots.
+    device: a torch device for the pool, or None for a host-only context
+    (tree and tables only; attend is unavailable).  share=False builds the
+    unshared paged layout (every sequence keeps its own chunks).
+    """
+
+    def __init__(self, heads: int, capacity_slots: int, device="cuda", share: bool = True,
+                 head_dim: int = HEAD_DIM, chunk_size: int = CHUNK):
+        self.lib = load()
+        self.heads, self.head_dim, self.chunk = heads, head_dim, chunk_size
+        ctx = ctypes.c_void_p()
+        flags = 0 if share else _capi.CA_CREATE_UNSHARED
+        rc = self.lib.ca_create_ex(heads, head_dim, chunk_size, flags, ctypes.byref(ctx))
+        if rc != 0:
+            raise CaError(rc, "ca_create_ex failed")
+        self.ctx = ctx
+        self.device = device
+        self.pool = None
+        self.ws = None
+        self._n_live = 0
+        if device is None:
+            check(self.ctx, self.lib.ca_attach_pool(self.ctx, None, capacity_slots))
+        else:
+            import torch
+            nbytes = capacity_slots * slot_bytes(heads, head_dim, chunk_size)
+            self.pool = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            check(self.ctx, self.lib.ca_attach_pool(self.ctx, ctypes.c_void_p(self.pool.data_ptr()),
+                                                   capacity_slots))
+
+    # -- lifetime -------------------------------------------------------------
+    def close(self):
+        if getattr(self, "ctx", None):
+            self.lib.ca_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- helpers --------------------------------------------------------------
+    def _stream(self, stream=None):
+        if self.device is None:
+            return None
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream(self.pool.device)
+        return ctypes.c_void_p(s.cuda_stream)
+
+    def _kv(self, k, v, n: int):
+        if self.device is None:
+            if k is not None or v is not None:
+                raise ValueError("a host-only context takes no K/V")
+            return None, None
+        import torch
+        for name, x in (("k", k), ("v", v)):
+            if not isinstance(x, torch.Tensor) or x.dtype != torch.float16 or not x.is_cuda:
+                raise TypeError(f"{name} must be a float16 CUDA tensor")
+            if tuple(x.shape) != (n, self.heads, self.head_dim) or not x.is_contiguous():
+                raise ValueError(f"{name} must be contiguous [{n}, {self.heads}, {self.head_dim}]")
+        return ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr())
+
+    # -- tree -----------------------------------------------------------------
+    def insert(self, seq_id: int, tokens, k=None, v=None, stream=None) -> int:
+        t = _tokens(tokens)
+        kp, vp = self._kv(k, v, len(t)) if len(t) else (None, None)
+        matched = ctypes.c_int32(0)
+        check(self.ctx, self.lib.ca_insert(self.ctx, seq_id, _ptr_i32(t), len(t), kp, vp, self._stream(stream),
+                                           ctypes.byref(matched)))
+        self._n_live += 1
+        return matched.value
+
+    def append(self, seq_id: int, tokens, k=None, v=None, stream=None) -> None:
+        t = _tokens(tokens)
+        kp, vp = self._kv(k, v, len(t)) if len(t) else (None, None)
+        check(self.ctx, self.lib.ca_append(self.ctx, seq_id, _ptr_i32(t), len(t), kp, vp, self._stream(stream)))
+
+    def remove(self, seq_id: int) -> None:
+        check(self.ctx, self.lib.ca_remove(self.ctx, seq_id))
+        self._n_live -= 1
+
+    def sequences(self) -> List[int]:
+        n = check(self.ctx, self.lib.ca_list_sequences(self.ctx, None, 0))
+        buf = (ctypes.c_int64 * max(n, 1))()
+        check(self.ctx, self.lib.ca_list_sequences(self.ctx, buf, n))
+        return [int(buf[i]) for i in range(n)]
+
+    def set_option(self, option: int, value: int) -> None:
+        check(self.ctx, self.lib.ca_set_option(self.ctx, option, value))
+
+    def export_table(self) -> Tuple[np.ndarray, List[int]]:
+        nr, ns = ctypes.c_int(0), ctypes.c_int(0)
+        check(self.ctx, self.lib.ca_export_table(self.ctx, None, 0, None, 0, ctypes.byref(nr), ctypes.byref(ns)))
+        rows = np.zeros((max(nr.value, 1), 7), np.int32)
+        order = np.zeros(max(ns.value, 1), np.int64)
+        check(self.ctx, self.lib.ca_export_table(
+            self.ctx, rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), nr.value,
+            order.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ns.value, ctypes.byref(nr), ctypes.byref(ns)))
+        return rows[: nr.value], [int(x) for x in order[: ns.value]]
+
+    def stats(self) -> Dict[str, float]:
+        s = _capi.ca_stats_t()
+        check(self.ctx, self.lib.ca_stats(self.ctx, ctypes.byref(s)))
+        return {name: getattr(s, name) for name, _ in s._fields_}
+
+    def workspace_bytes(self) -> int:
+        n = ctypes.c_size_t(0)
+        check(self.ctx, self.lib.ca_workspace_bytes(self.ctx, ctypes.byref(n)))
+        return int(n.value)
+
+    # -- step -----------------------------------------------------------------
+    def ensure_workspace(self) -> None:
+        import torch
+        need = self.workspace_bytes()
+        if self.ws is None or self.ws.numel() < need:
+            self.ws = torch.empty(max(need + need // 4, 4096), dtype=torch.uint8, device=self.pool.device)
+            check(self.ctx, self.lib.ca_attach_workspace(self.ctx, ctypes.c_void_p(self.ws.data_ptr()),
+                                                         self.ws.numel()))
+
+    def _qo(self, q, out):
+        import torch
+        shape = (self._n_live, self.heads, self.head_dim)
+        if not isinstance(q, torch.Tensor) or q.dtype != torch.float16 or not q.is_cuda:
+            raise TypeError("q must be a float16 CUDA tensor")
+        if tuple(q.shape) != shape or not q.is_contiguous():
+            raise ValueError(f"q must be contiguous {list(shape)} (rows in ascending seq id)")
+        if out is None:
+            out = torch.empty_like(q)
+        elif tuple(out.shape) != shape or out.dtype != torch.float16 or not out.is_contiguous():
+            raise ValueError("out must match q")
+        return q, out
+
+    def attend(self, q, out=None, stream=None):
+        """out[r] = softmax(q[r] K_r^T / sqrt(d)) V_r for the r-th live sequence."""
+        if self.device is None:
+            raise CaError(-9, "host-only context")
+        q, out = self._qo(q, out)
+        self.ensure_workspace()
+        check(self.ctx, self.lib.ca_attend(self.ctx, ctypes.c_void_p(q.data_ptr()),
+                                           ctypes.c_void_p(out.data_ptr()), self._stream(stream)))
+        return out
+
+    def prepare(self, stream=None) -> None:
+        self.ensure_workspace()
+        check(self.ctx, self.lib.ca_prepare(self.ctx, self._stream(stream)))
+
+    def attend_phase(self, phase: int, q, out, stream=None) -> None:
+        check(self.ctx, self.lib.ca_attend_phase(self.ctx, phase, ctypes.c_void_p(q.data_ptr()),
+                                                 ctypes.c_void_p(out.data_ptr()), self._stream(stream)))
+
+
+def load_workload(ca: ChunkAttention, wl, device="cuda", stream=None) -> None:
+    """Insert every sequence of a seeded workload (ids 0..N-1) with its K/V."""
+    import torch
+    for i in range(wl.n_seq):
+        k, v = wl.seq_kv(i)
+        kt = torch.from_numpy(np.ascontiguousarray(k)).to(device)
+        vt = torch.from_numpy(np.ascontiguousarray(v)).to(device)
+        ca.insert(i, wl.seq_tokens(i), kt, vt, stream=stream)
+
+
+def slots_needed(wl, chunk: int = CHUNK, share: bool = True) -> int:
+    """Upper bound of the slots a workload occupies (splits included)."""
+    if not share:
+        return int(sum((int(n) + chunk - 1) // chunk for n in wl.lengths()))
+    segs = getattr(wl, "segments", None)
+    if segs is not None and all(s.length % chunk == 0 for p in wl.paths for s in
+                                (segs[j] for j in p[:-1])):
+        # segment boundaries on chunk boundaries: one chunk run per segment
+        used = sorted({j for p in wl.paths for j in p})
+        return int(sum((segs[j].length + chunk - 1) // chunk for j in used))
+    # every sequence at most adds its own chunks plus one split
+    return int(sum((int(n) + chunk - 1) // chunk + 1 for n in wl.lengths()))

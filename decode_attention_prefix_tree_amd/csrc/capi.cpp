@@ -1,0 +1,433 @@
+// extern "C" boundary of the library.  Every entry point catches everything,
+// stores a message and returns a status code (declared in include/chunkattn.h).
+#include <hip/hip_runtime_api.h>
+
+#include <chrono>
+#include <cmath>
+#include <cstring>
+#include <exception>
+#include <string>
+
+#include "../../include/chunkattn.h"
+#include "kernels.h"
+#include "manager.h"
+
+using chunkattn::Error;
+
+struct ca_ctx {
+  int heads = 0, head_dim = 0, chunk = 0, flags = 0;
+  chunkattn::Manager mgr;
+  void* pool = nullptr;
+  bool pool_attached = false;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  int cf_group = 4, sf_group = 8;
+
+  // plan cache: rebuilt after the tree changes, uploaded when stale
+  chunkattn::Plan plan;
+  bool plan_valid = false;
+  uint64_t version = 1, uploaded_version = 0;
+  void* uploaded_ws = nullptr;
+  size_t off_cf = 0, off_sf = 0, off_refs = 0, off_qrow = 0, off_seqparts = 0, off_partlist = 0;
+  size_t table_bytes = 0, off_part_o = 0, off_part_ms = 0, total_bytes = 0;
+  int64_t rebuilds = 0;
+  double last_rebuild_ms = 0.0;
+
+  // pinned staging for the table upload; the event marks when the last copy
+  // out of it has finished so it can be rewritten
+  void* stage = nullptr;
+  size_t stage_bytes = 0;
+  hipEvent_t stage_done = nullptr;
+  bool stage_pending = false;
+
+  std::string err;
+
+  ca_ctx(int H, int D, int C, int f) : heads(H), head_dim(D), chunk(C), flags(f),
+                                       mgr(C, (f & CA_CREATE_UNSHARED) == 0) {}
+  ~ca_ctx() {
+    if (stage_done) {
+      if (stage_pending) (void)hipEventSynchronize(stage_done);
+      (void)hipEventDestroy(stage_done);
+    }
+    if (stage) (void)hipHostFree(stage);
+  }
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int fail(ca_ctx* c, int code, const std::string& msg) {
+  if (c) c->err = msg;
+  return code;
+}
+
+void hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) throw Error(CA_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+void touch(ca_ctx* c) {
+  c->plan_valid = false;
+  c->version += 1;
+}
+
+void ensure_plan(ca_ctx* c) {
+  if (c->plan_valid) return;
+  auto t0 = std::chrono::steady_clock::now();
+  c->mgr.build_plan(c->cf_group, c->sf_group, &c->plan);
+  const chunkattn::Plan& p = c->plan;
+  size_t off = 0;
+  c->off_cf = off;
+  off = align_up(off + p.cf_units.size() * sizeof(chunkattn::CfUnit));
+  c->off_sf = off;
+  off = align_up(off + p.sf_tasks.size() * sizeof(chunkattn::SfTask));
+  c->off_refs = off;
+  off = align_up(off + p.chunk_refs.size() * sizeof(int32_t));
+  c->off_qrow = off;
+  off = align_up(off + p.dfs_qrow.size() * sizeof(int32_t));
+  c->off_seqparts = off;
+  off = align_up(off + p.seq_parts.size() * sizeof(int32_t));
+  c->off_partlist = off;
+  off = align_up(off + p.part_list.size() * sizeof(int32_t));
+  c->table_bytes = off;
+  c->off_part_o = off;
+  off = align_up(off + static_cast<size_t>(p.n_parts) * c->heads * c->head_dim * sizeof(float));
+  c->off_part_ms = off;
+  off = align_up(off + static_cast<size_t>(p.n_parts) * c->heads * 2 * sizeof(float));
+  c->total_bytes = off;
+  c->plan_valid = true;
+  c->rebuilds += 1;
+  c->last_rebuild_ms =
+      std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+}
+
+template <typename T>
+void put(char* base, size_t off, const std::vector<T>& v) {
+  if (!v.empty()) std::memcpy(base + off, v.data(), v.size() * sizeof(T));
+}
+
+void upload(ca_ctx* c, void* stream) {
+  if (c->uploaded_version == c->version && c->uploaded_ws == c->ws) return;
+  if (c->stage_pending) {
+    hip_check(hipEventSynchronize(c->stage_done), "hipEventSynchronize");
+    c->stage_pending = false;
+  }
+  if (c->stage_bytes < c->table_bytes) {
+    if (c->stage) hip_check(hipHostFree(c->stage), "hipHostFree");
+    c->stage = nullptr;
+    size_t want = align_up(c->table_bytes * 2);
+    hip_check(hipHostMalloc(&c->stage, want, hipHostMallocDefault), "hipHostMalloc");
+    c->stage_bytes = want;
+  }
+  if (!c->stage_done) hip_check(hipEventCreateWithFlags(&c->stage_done, hipEventDisableTiming), "hipEventCreate");
+  char* s = static_cast<char*>(c->stage);
+  const chunkattn::Plan& p = c->plan;
+  std::memset(s, 0, c->table_bytes);
+  put(s, c->off_cf, p.cf_units);
+  put(s, c->off_sf, p.sf_tasks);
+  put(s, c->off_refs, p.chunk_refs);
+  put(s, c->off_qrow, p.dfs_qrow);
+  put(s, c->off_seqparts, p.seq_parts);
+  put(s, c->off_partlist, p.part_list);
+  hip_check(hipMemcpyAsync(c->ws, c->stage, c->table_bytes, hipMemcpyHostToDevice,
+                           static_cast<hipStream_t>(stream)),
+            "hipMemcpyAsync(table)");
+  hip_check(hipEventRecord(c->stage_done, static_cast<hipStream_t>(stream)), "hipEventRecord");
+  c->stage_pending = true;
+  c->uploaded_version = c->version;
+  c->uploaded_ws = c->ws;
+}
+
+chunkattn::StepArgs step_args(ca_ctx* c, const void* q, void* out) {
+  char* w = static_cast<char*>(c->ws);
+  const chunkattn::Plan& p = c->plan;
+  chunkattn::StepArgs a{};
+  a.pool = c->pool;
+  a.q = q;
+  a.out = out;
+  a.cf_units = reinterpret_cast<const int32_t*>(w + c->off_cf);
+  a.sf_tasks = reinterpret_cast<const int32_t*>(w + c->off_sf);
+  a.chunk_refs = reinterpret_cast<const int32_t*>(w + c->off_refs);
+  a.dfs_qrow = reinterpret_cast<const int32_t*>(w + c->off_qrow);
+  a.seq_parts = reinterpret_cast<const int32_t*>(w + c->off_seqparts);
+  a.part_list = reinterpret_cast<const int32_t*>(w + c->off_partlist);
+  a.part_o = reinterpret_cast<float*>(w + c->off_part_o);
+  a.part_ms = reinterpret_cast<float*>(w + c->off_part_ms);
+  a.heads = c->heads;
+  a.n_cf_units = static_cast<int>(p.cf_units.size());
+  a.n_sf_tasks = static_cast<int>(p.sf_tasks.size());
+  a.n_seq = static_cast<int>(p.dfs_seq.size());
+  a.scale_log2e = static_cast<float>((1.0 / std::sqrt(static_cast<double>(c->head_dim))) * 1.4426950408889634);
+  return a;
+}
+
+void check_step(ca_ctx* c, const void* q, void* out) {
+  if (!c->pool_attached || c->pool == nullptr) throw Error(CA_E_NO_POOL, "no device pool attached");
+  if (c->mgr.live() == 0) throw Error(CA_E_EMPTY, "no live sequence");
+  if (q == nullptr || out == nullptr) throw Error(CA_E_INVALID_ARG, "q and out must be device pointers");
+  ensure_plan(c);
+  if (c->ws == nullptr || c->ws_bytes < c->total_bytes)
+    throw Error(CA_E_WORKSPACE, "workspace of " + std::to_string(c->total_bytes) + " bytes needed, " +
+                                    std::to_string(c->ws_bytes) + " attached");
+  // int32 indexing limits of the kernels
+  if (static_cast<int64_t>(c->plan.cf_units.size()) * c->heads > INT32_MAX ||
+      static_cast<int64_t>(c->plan.sf_tasks.size()) * c->heads > INT32_MAX ||
+      static_cast<int64_t>(c->plan.dfs_seq.size()) * c->heads > INT32_MAX)
+    throw Error(CA_E_UNSUPPORTED, "step too large for one launch");
+}
+
+void launch(int e, const char* what) {
+  if (e != 0) throw Error(CA_E_HIP, std::string(what) + ": " + hipGetErrorString(static_cast<hipError_t>(e)));
+}
+
+void run_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* k, const void* v, void* stream) {
+  chunkattn::KvOpBatch batch{};
+  int n = 0;
+  for (size_t i = 0; i < ops.size(); ++i) {
+    const chunkattn::KvOp& o = ops[i];
+    batch.ops[n++] = chunkattn::KvOpDev{o.dst_slot, o.dst_key0, o.n_rows, o.src_row0,
+                                        o.src_slot, o.from_pool, o.zero_rest, 0};
+    if (n == chunkattn::kOpsPerLaunch || i + 1 == ops.size()) {
+      launch(chunkattn::launch_kv_write(c->pool, c->heads, batch, n, k, v, stream), "kv_write");
+      n = 0;
+    }
+  }
+}
+
+#define CA_GUARD(ctx, ...)                                                    \
+  do {                                                                         \
+    if ((ctx) == nullptr) return CA_E_INVALID_ARG;                             \
+    try {                                                                      \
+      (ctx)->err.clear();                                                      \
+      __VA_ARGS__                                                              \
+    } catch (const Error& e) {                                                 \
+      return fail((ctx), e.code, e.what());                                    \
+    } catch (const std::bad_alloc&) {                                          \
+      return fail((ctx), CA_E_INTERNAL, "host out of memory");                 \
+    } catch (const std::exception& e) {                                        \
+      return fail((ctx), CA_E_INTERNAL, e.what());                             \
+    } catch (...) {                                                            \
+      return fail((ctx), CA_E_INTERNAL, "unknown error");                      \
+    }                                                                          \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t ca_slot_bytes(int heads, int head_dim, int chunk_size) {
+  if (heads <= 0 || head_dim <= 0 || chunk_size <= 0) return 0;
+  return static_cast<size_t>(4) * heads * chunk_size * head_dim;
+}
+
+int ca_create_ex(int heads, int head_dim, int chunk_size, int flags, ca_ctx** out) {
+  if (out == nullptr) return CA_E_INVALID_ARG;
+  *out = nullptr;
+  if (heads < 1) return CA_E_INVALID_ARG;
+  if (head_dim != chunkattn::kHeadDim || chunk_size != chunkattn::kChunk) return CA_E_UNSUPPORTED;
+  if (flags & ~CA_CREATE_UNSHARED) return CA_E_UNSUPPORTED;
+  try {
+    *out = new ca_ctx(heads, head_dim, chunk_size, flags);
+  } catch (...) {
+    return CA_E_INTERNAL;
+  }
+  return CA_OK;
+}
+
+int ca_create(int heads, int head_dim, int chunk_size, ca_ctx** out) {
+  return ca_create_ex(heads, head_dim, chunk_size, 0, out);
+}
+
+void ca_destroy(ca_ctx* ctx) { delete ctx; }
+
+int ca_attach_pool(ca_ctx* ctx, void* dev, int64_t capacity_slots) {
+  CA_GUARD(ctx, {
+    if (capacity_slots < 0) throw Error(CA_E_INVALID_ARG, "negative capacity");
+    if (dev != nullptr && (reinterpret_cast<uintptr_t>(dev) % kAlign) != 0)
+      throw Error(CA_E_INVALID_ARG, "pool must be 256-byte aligned");
+    ctx->mgr.set_capacity(capacity_slots);
+    ctx->pool = dev;
+    ctx->pool_attached = true;
+    touch(ctx);
+    return CA_OK;
+  });
+}
+
+int ca_workspace_bytes(ca_ctx* ctx, size_t* out) {
+  CA_GUARD(ctx, {
+    if (out == nullptr) throw Error(CA_E_INVALID_ARG, "out is NULL");
+    ensure_plan(ctx);
+    *out = ctx->total_bytes;
+    return CA_OK;
+  });
+}
+
+int ca_attach_workspace(ca_ctx* ctx, void* dev, size_t bytes) {
+  CA_GUARD(ctx, {
+    if (dev != nullptr && (reinterpret_cast<uintptr_t>(dev) % kAlign) != 0)
+      throw Error(CA_E_INVALID_ARG, "workspace must be 256-byte aligned");
+    ctx->ws = dev;
+    ctx->ws_bytes = dev ? bytes : 0;
+    return CA_OK;
+  });
+}
+
+int ca_set_option(ca_ctx* ctx, int option, int value) {
+  CA_GUARD(ctx, {
+    if (option == CA_OPT_CF_CHUNKS_PER_TASK) {
+      if (value < 1 || value > 64) throw Error(CA_E_INVALID_ARG, "chunk-first group must be 1..64");
+      ctx->cf_group = value;
+    } else if (option == CA_OPT_SF_CHUNKS_PER_TASK) {
+      if (value < 1 || value > 256) throw Error(CA_E_INVALID_ARG, "sequence-first group must be 1..256");
+      ctx->sf_group = value;
+    } else {
+      throw Error(CA_E_UNSUPPORTED, "unknown option");
+    }
+    touch(ctx);
+    return CA_OK;
+  });
+}
+
+int ca_insert(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n, const void* k_dev,
+              const void* v_dev, void* stream, int32_t* n_matched) {
+  CA_GUARD(ctx, {
+    if (!ctx->pool_attached) throw Error(CA_E_NO_POOL, "attach a pool (or a NULL pool) first");
+    if (n < 1 || tokens == nullptr) throw Error(CA_E_INVALID_ARG, "insert needs n >= 1 host tokens");
+    const bool device = ctx->pool != nullptr;
+    if (device && (k_dev == nullptr || v_dev == nullptr))
+      throw Error(CA_E_INVALID_ARG, "k_dev and v_dev are required when a device pool is attached");
+    std::vector<chunkattn::KvOp> ops;
+    int32_t matched = ctx->mgr.insert(seq_id, tokens, n, &ops);
+    touch(ctx);
+    if (n_matched) *n_matched = matched;
+    if (device) run_kv_ops(ctx, ops, k_dev, v_dev, stream);
+    return CA_OK;
+  });
+}
+
+int ca_append(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n, const void* k_dev,
+              const void* v_dev, void* stream) {
+  CA_GUARD(ctx, {
+    if (!ctx->pool_attached) throw Error(CA_E_NO_POOL, "attach a pool (or a NULL pool) first");
+    if (n < 1 || tokens == nullptr) throw Error(CA_E_INVALID_ARG, "append needs n >= 1 host tokens");
+    const bool device = ctx->pool != nullptr;
+    if (device && (k_dev == nullptr || v_dev == nullptr))
+      throw Error(CA_E_INVALID_ARG, "k_dev and v_dev are required when a device pool is attached");
+    std::vector<chunkattn::KvOp> ops;
+    ctx->mgr.append(seq_id, tokens, n, &ops);
+    touch(ctx);
+    if (device) run_kv_ops(ctx, ops, k_dev, v_dev, stream);
+    return CA_OK;
+  });
+}
+
+int ca_remove(ca_ctx* ctx, int64_t seq_id) {
+  CA_GUARD(ctx, {
+    ctx->mgr.remove(seq_id);
+    touch(ctx);
+    return CA_OK;
+  });
+}
+
+int ca_prepare(ca_ctx* ctx, void* stream) {
+  CA_GUARD(ctx, {
+    if (!ctx->pool_attached || ctx->pool == nullptr) throw Error(CA_E_NO_POOL, "no device pool attached");
+    if (ctx->mgr.live() == 0) throw Error(CA_E_EMPTY, "no live sequence");
+    ensure_plan(ctx);
+    if (ctx->ws == nullptr || ctx->ws_bytes < ctx->total_bytes)
+      throw Error(CA_E_WORKSPACE, "workspace too small");
+    upload(ctx, stream);
+    return CA_OK;
+  });
+}
+
+int ca_attend_phase(ca_ctx* ctx, int phase, const void* q_dev, void* out_dev, void* stream) {
+  CA_GUARD(ctx, {
+    check_step(ctx, q_dev, out_dev);
+    upload(ctx, stream);
+    chunkattn::StepArgs a = step_args(ctx, q_dev, out_dev);
+    if (phase == CA_PHASE_CHUNK_FIRST)
+      launch(chunkattn::launch_chunk_first(a, stream), "chunk_first");
+    else if (phase == CA_PHASE_SEQUENCE_FIRST)
+      launch(chunkattn::launch_sequence_first(a, stream), "sequence_first");
+    else if (phase == CA_PHASE_MERGE)
+      launch(chunkattn::launch_merge(a, stream), "merge");
+    else
+      throw Error(CA_E_INVALID_ARG, "unknown phase");
+    return CA_OK;
+  });
+}
+
+int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream) {
+  CA_GUARD(ctx, {
+    check_step(ctx, q_dev, out_dev);
+    upload(ctx, stream);
+    chunkattn::StepArgs a = step_args(ctx, q_dev, out_dev);
+    launch(chunkattn::launch_chunk_first(a, stream), "chunk_first");
+    launch(chunkattn::launch_sequence_first(a, stream), "sequence_first");
+    launch(chunkattn::launch_merge(a, stream), "merge");
+    return CA_OK;
+  });
+}
+
+int ca_list_sequences(ca_ctx* ctx, int64_t* ids, int cap) {
+  CA_GUARD(ctx, {
+    std::vector<int64_t> s = ctx->mgr.sequences();
+    if (ids != nullptr)
+      for (int i = 0; i < cap && i < static_cast<int>(s.size()); ++i) ids[i] = s[i];
+    return static_cast<int>(s.size());
+  });
+}
+
+int ca_export_table(ca_ctx* ctx, int32_t* rows, int cap_rows, int64_t* dfs_seq_order, int cap_seqs,
+                    int* n_rows, int* n_seqs) {
+  CA_GUARD(ctx, {
+    ensure_plan(ctx);
+    const chunkattn::Plan& p = ctx->plan;
+    const int nr = static_cast<int>(p.rows.size() / 7), ns = static_cast<int>(p.dfs_seq.size());
+    if (n_rows) *n_rows = nr;
+    if (n_seqs) *n_seqs = ns;
+    if ((rows == nullptr && cap_rows == 0) && (dfs_seq_order == nullptr && cap_seqs == 0)) return CA_OK;
+    if (cap_rows < nr || cap_seqs < ns || (nr > 0 && rows == nullptr) || (ns > 0 && dfs_seq_order == nullptr))
+      throw Error(CA_E_INVALID_ARG, "output capacity too small");
+    if (nr) std::memcpy(rows, p.rows.data(), p.rows.size() * sizeof(int32_t));
+    if (ns) std::memcpy(dfs_seq_order, p.dfs_seq.data(), p.dfs_seq.size() * sizeof(int64_t));
+    return CA_OK;
+  });
+}
+
+int ca_stats(ca_ctx* ctx, ca_stats_t* out) {
+  CA_GUARD(ctx, {
+    if (out == nullptr) throw Error(CA_E_INVALID_ARG, "out is NULL");
+    ensure_plan(ctx);
+    const chunkattn::Plan& p = ctx->plan;
+    ca_stats_t s{};
+    s.live_sequences = static_cast<int64_t>(ctx->mgr.live());
+    s.chunks = ctx->mgr.nodes();
+    s.shared_chunks = p.shared_chunks;
+    s.unique_tokens = p.unique_tokens;
+    s.attended_tokens = p.attended_tokens;
+    s.capacity_slots = ctx->mgr.capacity();
+    s.free_slots = ctx->mgr.free_slots();
+    s.table_rebuilds = ctx->rebuilds;
+    s.last_rebuild_ms = ctx->last_rebuild_ms;
+    s.cf_tasks = p.cf_tasks;
+    s.cf_units = static_cast<int64_t>(p.cf_units.size());
+    s.sf_tasks = static_cast<int64_t>(p.sf_tasks.size());
+    s.partials = p.n_parts;
+    s.cf_chunk_reads = p.cf_chunk_reads;
+    s.sf_chunk_reads = p.sf_chunk_reads;
+    const int64_t per_tok = 4LL * ctx->heads * ctx->head_dim;
+    s.unique_kv_bytes = p.unique_tokens * per_tok;
+    s.attended_kv_bytes = p.attended_tokens * per_tok;
+    s.shared_tokens = p.shared_tokens;
+    s.private_tokens = p.unique_tokens - p.shared_tokens;
+    *out = s;
+    return CA_OK;
+  });
+}
+
+const char* ca_last_error(ca_ctx* ctx) { return ctx ? ctx->err.c_str() : "NULL context"; }
+
+}  // extern "C"

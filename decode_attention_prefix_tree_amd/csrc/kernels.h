@@ -1,0 +1,48 @@
+// Host-callable launchers of the gfx950 kernels.  Plain types only, so the
+// C-ABI layer and the manager never see HIP device code.
+#pragma once
+
+#include <cstdint>
+
+namespace chunkattn {
+
+constexpr int kHeadDim = 128;
+constexpr int kChunk = 64;
+constexpr int kOpsPerLaunch = 32;
+
+struct KvOpDev {
+  int32_t dst_slot, dst_key0, n_rows, src_row0, src_slot, from_pool, zero_rest, pad;
+};
+
+struct KvOpBatch {
+  KvOpDev ops[kOpsPerLaunch];
+};
+
+// Arguments of one decode step.  All pointers are device addresses.
+struct StepArgs {
+  const void* pool;            // fp16 slots: [slot][head][K|V][64 x 128 tile]
+  const void* q;               // fp16 [n_live][H][128], ascending seq id
+  void* out;                   // fp16 [n_live][H][128]
+  const int32_t* cf_units;     // 8 ints per unit (CfUnit)
+  const int32_t* sf_tasks;     // 4 ints per task (SfTask)
+  const int32_t* chunk_refs;   // (slot, n_valid) pairs
+  const int32_t* dfs_qrow;     // caller row per DFS position
+  const int32_t* seq_parts;    // (first, count) per DFS position
+  const int32_t* part_list;    // partial ids
+  float* part_o;               // [n_parts][H][128]
+  float* part_ms;              // [n_parts][H][2]: running max (log2 units), sum
+  int heads;
+  int n_cf_units;
+  int n_sf_tasks;
+  int n_seq;
+  float scale_log2e;           // (1/sqrt(128)) * log2(e)
+};
+
+// Each returns a hipError_t value (0 = success) from the launch.
+int launch_kv_write(void* pool, int heads, const KvOpBatch& batch, int n_ops, const void* k_src,
+                    const void* v_src, void* stream);
+int launch_chunk_first(const StepArgs& a, void* stream);
+int launch_sequence_first(const StepArgs& a, void* stream);
+int launch_merge(const StepArgs& a, void* stream);
+
+}  // namespace chunkattn

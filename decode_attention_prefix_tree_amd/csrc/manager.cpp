@@ -1,0 +1,334 @@
+// Prefix-tree chunk manager and DFS plan builder (host only).  The readings it
+// implements are listed in manager.h.
+#include "manager.h"
+
+#include <algorithm>
+#include <functional>
+
+namespace chunkattn {
+
+namespace {
+constexpr int kInvalidArg = -1;
+constexpr int kNoCapacity = -3;
+constexpr int kDupSeq = -4;
+constexpr int kUnknownSeq = -5;
+constexpr int kState = -10;
+}  // namespace
+
+Manager::Manager(int chunk, bool share) : C_(chunk), share_(share) {
+  nodes_.emplace_back();  // root: no tokens, no slot
+  nodes_[0].alive = true;
+}
+
+void Manager::set_capacity(int64_t capacity) {
+  if (!end_.empty()) throw Error(kState, "pool can only change while no sequence is live");
+  if (capacity < 0 || capacity > INT32_MAX) throw Error(kInvalidArg, "capacity out of range");
+  capacity_ = capacity;
+  free_ = decltype(free_)();
+  std::vector<int32_t> all(static_cast<size_t>(capacity));
+  for (int32_t i = 0; i < capacity; ++i) all[i] = i;
+  free_ = decltype(free_)(std::greater<int32_t>(), std::move(all));
+}
+
+int32_t Manager::alloc_slot() {
+  int32_t s = free_.top();
+  free_.pop();
+  return s;
+}
+
+int32_t Manager::new_node(int32_t parent, int32_t start) {
+  int32_t idx;
+  if (!free_nodes_.empty()) {
+    idx = free_nodes_.back();
+    free_nodes_.pop_back();
+    nodes_[idx] = Node();
+  } else {
+    idx = static_cast<int32_t>(nodes_.size());
+    nodes_.emplace_back();
+  }
+  Node& n = nodes_[idx];
+  n.id = next_id_++;
+  n.parent = parent;
+  n.slot = alloc_slot();
+  n.start = start;
+  n.alive = true;
+  ++n_nodes_;
+  return idx;
+}
+
+void Manager::free_node(int32_t idx) {
+  Node& n = nodes_[idx];
+  free_.push(n.slot);
+  n.alive = false;
+  n.tokens.clear();
+  n.children.clear();
+  n.ended.clear();
+  free_nodes_.push_back(idx);
+  --n_nodes_;
+}
+
+int32_t Manager::insert(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops) {
+  if (n < 1 || tokens == nullptr) throw Error(kInvalidArg, "insert needs at least one token");
+  if (end_.count(seq)) throw Error(kDupSeq, "sequence id already live");
+
+  // Walk from the root without touching anything.
+  int32_t cur = 0, pos = 0, split_node = -1, split_at = 0;
+  while (share_ && pos < n) {
+    int32_t next = -1;
+    for (int32_t c : nodes_[cur].children) {
+      if (nodes_[c].tokens[0] == tokens[pos]) { next = c; break; }
+    }
+    if (next < 0) break;
+    const std::vector<int32_t>& t = nodes_[next].tokens;
+    int32_t lim = std::min<int32_t>(static_cast<int32_t>(t.size()), n - pos), k = 0;
+    while (k < lim && t[k] == tokens[pos + k]) ++k;
+    pos += k;
+    if (k < static_cast<int32_t>(t.size())) { split_node = next; split_at = k; break; }
+    cur = next;
+  }
+  const int64_t need = (split_node >= 0 ? 1 : 0) + chunks_for(n - pos, C_);
+  if (need > free_slots())
+    throw Error(kNoCapacity, "need " + std::to_string(need) + " chunk slots, " +
+                                 std::to_string(free_slots()) + " free");
+  const int32_t matched = pos;
+
+  if (split_node >= 0) {
+    int32_t tail = new_node(split_node, nodes_[split_node].start + split_at);
+    Node& head = nodes_[split_node];
+    Node& t = nodes_[tail];
+    t.tokens.assign(head.tokens.begin() + split_at, head.tokens.end());
+    head.tokens.resize(split_at);
+    t.children.swap(head.children);
+    for (int32_t c : t.children) nodes_[c].parent = tail;
+    head.children.push_back(tail);
+    t.ended.swap(head.ended);
+    for (int64_t s : t.ended) end_[s] = tail;
+    t.ref = head.ref;
+    if (ops)
+      ops->push_back(KvOp{t.slot, 0, static_cast<int32_t>(t.tokens.size()), split_at, head.slot, 1, 1});
+    cur = split_node;
+  }
+  while (pos < n) {
+    int32_t take = std::min<int32_t>(C_, n - pos);
+    int32_t idx = new_node(cur, pos);
+    Node& nd = nodes_[idx];
+    nd.tokens.assign(tokens + pos, tokens + pos + take);
+    nodes_[cur].children.push_back(idx);
+    if (ops) ops->push_back(KvOp{nd.slot, 0, take, pos, -1, 0, 1});
+    cur = idx;
+    pos += take;
+  }
+  nodes_[cur].ended.push_back(seq);
+  end_[seq] = cur;
+  len_[seq] = n;
+  for (int32_t x = cur; x != 0; x = nodes_[x].parent) nodes_[x].ref += 1;
+  return matched;
+}
+
+void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops) {
+  auto it = end_.find(seq);
+  if (it == end_.end()) throw Error(kUnknownSeq, "sequence id not live");
+  if (n < 1 || tokens == nullptr) throw Error(kInvalidArg, "append needs at least one token");
+  int32_t e = it->second;
+  const int32_t fill = static_cast<int32_t>(nodes_[e].tokens.size());
+  const int32_t room = nodes_[e].ref == 1 ? C_ - fill : 0;
+  const int32_t take = std::min(room, n);
+  const int64_t need = chunks_for(n - take, C_);
+  if (need > free_slots())
+    throw Error(kNoCapacity, "need " + std::to_string(need) + " chunk slots, " +
+                                 std::to_string(free_slots()) + " free");
+  if (take > 0) {
+    Node& nd = nodes_[e];
+    nd.tokens.insert(nd.tokens.end(), tokens, tokens + take);
+    if (ops) ops->push_back(KvOp{nd.slot, fill, take, 0, -1, 0, 0});
+  }
+  len_[seq] += n;
+  if (take == n) return;
+  std::vector<int64_t>& ended = nodes_[e].ended;
+  ended.erase(std::find(ended.begin(), ended.end(), seq));
+  int32_t cur = e, i = take;
+  int32_t pos = nodes_[e].start + static_cast<int32_t>(nodes_[e].tokens.size());
+  while (i < n) {
+    int32_t piece = std::min<int32_t>(C_, n - i);
+    int32_t idx = new_node(cur, pos);
+    Node& nd = nodes_[idx];
+    nd.tokens.assign(tokens + i, tokens + i + piece);
+    nd.ref = 1;
+    nodes_[cur].children.push_back(idx);
+    if (ops) ops->push_back(KvOp{nd.slot, 0, piece, i, -1, 0, 1});
+    cur = idx;
+    pos += piece;
+    i += piece;
+  }
+  nodes_[cur].ended.push_back(seq);
+  end_[seq] = cur;
+}
+
+void Manager::remove(int64_t seq) {
+  auto it = end_.find(seq);
+  if (it == end_.end()) throw Error(kUnknownSeq, "sequence id not live");
+  int32_t e = it->second;
+  end_.erase(it);
+  len_.erase(seq);
+  std::vector<int64_t>& ended = nodes_[e].ended;
+  ended.erase(std::find(ended.begin(), ended.end(), seq));
+  for (int32_t x = e; x != 0;) {
+    int32_t p = nodes_[x].parent;
+    if (--nodes_[x].ref == 0) {
+      std::vector<int32_t>& sib = nodes_[p].children;
+      sib.erase(std::find(sib.begin(), sib.end(), x));
+      free_node(x);
+    }
+    x = p;
+  }
+}
+
+std::vector<int64_t> Manager::sequences() const {
+  std::vector<int64_t> out;
+  out.reserve(end_.size());
+  for (const auto& kv : end_) out.push_back(kv.first);
+  return out;
+}
+
+int32_t Manager::seq_len(int64_t seq) const {
+  auto it = len_.find(seq);
+  if (it == len_.end()) throw Error(kUnknownSeq, "sequence id not live");
+  return it->second;
+}
+
+void Manager::build_plan(int cf_group, int sf_group, Plan* plan) const {
+  Plan& P = *plan;
+  P = Plan();
+
+  // Caller row of each sequence: rank in ascending id order.
+  std::map<int64_t, int32_t> qrow;
+  {
+    int32_t r = 0;
+    for (const auto& kv : end_) qrow[kv.first] = r++;
+  }
+
+  // Pass 1: DFS pre-order -> canonical rows, DFS order, row of each node,
+  // the row where each DFS position's sequence ends.
+  std::vector<int32_t> row_node;          // node index of each row
+  std::vector<int32_t> end_row;           // per DFS position
+  struct Frame { int32_t node, parent_row; bool closing; int32_t row; };
+  std::vector<Frame> stack;
+  const auto& rc = nodes_[0].children;
+  for (auto it = rc.rbegin(); it != rc.rend(); ++it) stack.push_back({*it, -1, false, -1});
+  while (!stack.empty()) {
+    Frame f = stack.back();
+    stack.pop_back();
+    if (f.closing) {
+      P.rows[static_cast<size_t>(f.row) * 7 + 5] = static_cast<int32_t>(P.dfs_seq.size());
+      continue;
+    }
+    const Node& nd = nodes_[f.node];
+    int32_t r = static_cast<int32_t>(row_node.size());
+    row_node.push_back(f.node);
+    P.rows.insert(P.rows.end(), {nd.id, f.parent_row, nd.start, static_cast<int32_t>(nd.tokens.size()),
+                                 static_cast<int32_t>(P.dfs_seq.size()), -1, nd.slot});
+    for (int64_t s : nd.ended) {
+      P.dfs_seq.push_back(s);
+      P.dfs_qrow.push_back(qrow.at(s));
+      end_row.push_back(r);
+    }
+    stack.push_back({f.node, f.parent_row, true, r});
+    for (auto it = nd.children.rbegin(); it != nd.children.rend(); ++it) stack.push_back({*it, r, false, -1});
+  }
+  const int32_t n_rows = static_cast<int32_t>(row_node.size());
+  const int32_t n_seq = static_cast<int32_t>(P.dfs_seq.size());
+  auto R = [&](int32_t r, int c) { return P.rows[static_cast<size_t>(r) * 7 + c]; };
+
+  // Pass 2: runs of shared chunks (range >= 2).  A child with the same range
+  // as its parent continues the parent's run (a chain: one child, nobody
+  // ends at the parent); a run holds at most cf_group chunks.
+  std::vector<int32_t> task_of_row(n_rows, -1);
+  struct Task { int32_t b, e, chunk_begin, n_chunks, last_row, part_base; };
+  std::vector<Task> tasks;
+  for (int32_t r = 0; r < n_rows; ++r) {
+    int32_t b = R(r, 4), e = R(r, 5), p = R(r, 1);
+    P.unique_tokens += R(r, 3);
+    P.attended_tokens += static_cast<int64_t>(R(r, 3)) * (e - b);
+    if (e - b < 2) continue;
+    ++P.shared_chunks;
+    P.shared_tokens += R(r, 3);
+    int32_t t = p >= 0 ? task_of_row[p] : -1;
+    if (t >= 0 && tasks[t].b == b && tasks[t].e == e && tasks[t].last_row == p && tasks[t].n_chunks < cf_group) {
+      tasks[t].n_chunks += 1;
+      tasks[t].last_row = r;
+    } else {
+      t = static_cast<int32_t>(tasks.size());
+      tasks.push_back({b, e, -1, 1, r, 0});
+    }
+    task_of_row[r] = t;
+  }
+  // chunk refs of each run, in row order
+  {
+    std::vector<std::vector<int32_t>> task_rows(tasks.size());
+    for (int32_t r = 0; r < n_rows; ++r)
+      if (task_of_row[r] >= 0) task_rows[task_of_row[r]].push_back(r);
+    int32_t parts = 0;
+    for (size_t t = 0; t < tasks.size(); ++t) {
+      tasks[t].chunk_begin = static_cast<int32_t>(P.chunk_refs.size() / 2);
+      for (int32_t r : task_rows[t]) {
+        P.chunk_refs.push_back(R(r, 6));
+        P.chunk_refs.push_back(R(r, 3));
+      }
+      tasks[t].part_base = parts;
+      parts += tasks[t].e - tasks[t].b;
+      P.cf_chunk_reads += tasks[t].n_chunks * ((tasks[t].e - tasks[t].b + 31) / 32);
+      for (int32_t rb = 0; rb * 32 < tasks[t].e - tasks[t].b; ++rb) {
+        CfUnit u{};
+        u.chunk_begin = tasks[t].chunk_begin;
+        u.n_chunks = tasks[t].n_chunks;
+        u.row_begin = tasks[t].b + rb * 32;
+        u.n_rows = std::min(32, tasks[t].e - tasks[t].b - rb * 32);
+        u.part_base = tasks[t].part_base + rb * 32;
+        P.cf_units.push_back(u);
+      }
+    }
+    P.n_parts = parts;
+    P.cf_tasks = static_cast<int64_t>(tasks.size());
+  }
+
+  // Pass 3: per sequence, the shared runs on its path (root first) and its
+  // private chunks cut into sequence-first tasks.
+  P.seq_parts.assign(static_cast<size_t>(n_seq) * 2, 0);
+  std::vector<int32_t> path;
+  for (int32_t i = 0; i < n_seq; ++i) {
+    path.clear();
+    for (int32_t r = end_row[i]; r >= 0; r = R(r, 1)) path.push_back(r);
+    std::reverse(path.begin(), path.end());
+    int32_t first = static_cast<int32_t>(P.part_list.size());
+    int32_t last_task = -1;
+    std::vector<int32_t> priv;
+    for (int32_t r : path) {
+      int32_t t = task_of_row[r];
+      if (t >= 0) {
+        if (t != last_task) P.part_list.push_back(tasks[t].part_base + (i - tasks[t].b));
+        last_task = t;
+      } else {
+        priv.push_back(r);
+      }
+    }
+    for (size_t j = 0; j < priv.size(); j += static_cast<size_t>(sf_group)) {
+      size_t stop = std::min(priv.size(), j + static_cast<size_t>(sf_group));
+      SfTask st{};
+      st.chunk_begin = static_cast<int32_t>(P.chunk_refs.size() / 2);
+      st.n_chunks = static_cast<int32_t>(stop - j);
+      st.dfs_pos = i;
+      st.part_id = P.n_parts++;
+      for (size_t q = j; q < stop; ++q) {
+        P.chunk_refs.push_back(R(priv[q], 6));
+        P.chunk_refs.push_back(R(priv[q], 3));
+      }
+      P.sf_chunk_reads += st.n_chunks;
+      P.sf_tasks.push_back(st);
+      P.part_list.push_back(st.part_id);
+    }
+    P.seq_parts[2 * i] = first;
+    P.seq_parts[2 * i + 1] = static_cast<int32_t>(P.part_list.size()) - first;
+  }
+}
+
+}  // namespace chunkattn

@@ -1,0 +1,147 @@
+// Host-side prefix-tree chunk manager: the trie of chunk nodes, the slot
+// allocator, and the DFS flattening into the per-step work plan.
+//
+// Prefix-aware KV cache (paperlayer.ai summary of arXiv 2402.15220v4, section
+// 3.1 and Figure 1; explainer 0h-n0.github.io/posts/paper-2402-15220,
+// "Prefix-Aware KV Cache" and "dynamic prefix detection"): K/V are cut into
+// chunks that are the nodes of a prefix tree; a path from the root is a token
+// prefix and each live sequence is one path; a shared prefix is stored once;
+// references are counted and an unreferenced chunk returns its slot.
+//
+// Readings for what the pages leave open (each one decides a bit of the
+// exported table):
+//  * a node holds at most C tokens; new paths are cut into full chunks;
+//  * a divergence inside a node splits it -- the head keeps its slot, the tail
+//    gets a new slot, becomes the only child, and inherits the node's
+//    children and the sequences that ended in it;
+//  * children stay in creation order; matching takes the first child whose
+//    first token is the next token;
+//  * sequences that end at a node precede its children in DFS order, in
+//    arrival order;
+//  * append writes in place only into a private (one reference) chunk that is
+//    not full, otherwise grows new private chunks; appends never deduplicate;
+//  * slots: lowest free index first; a split's tail slot before new tokens'
+//    slots, which follow token order;
+//  * a failing call changes nothing.
+#pragma once
+
+#include <cstdint>
+#include <functional>
+#include <map>
+#include <queue>
+#include <stdexcept>
+#include <string>
+#include <vector>
+
+namespace chunkattn {
+
+// Status codes mirror the CA_E_* values of the C header.
+struct Error : std::runtime_error {
+  int code;
+  Error(int c, const std::string& m) : std::runtime_error(m), code(c) {}
+};
+
+// A device-side copy the host asks for after a tree mutation.  Either rows
+// from the caller's K/V ([row][head][dim], fp16) or rows of another slot are
+// written to key positions [dst_key0, dst_key0 + n_rows) of dst_slot; with
+// zero_rest the other keys of the slot are cleared.
+struct KvOp {
+  int32_t dst_slot;
+  int32_t dst_key0;
+  int32_t n_rows;
+  int32_t src_row0;   // caller row (from_pool == 0) or source key (from_pool == 1)
+  int32_t src_slot;   // only for from_pool
+  int32_t from_pool;
+  int32_t zero_rest;
+};
+
+// Per-step work plan built from the DFS order.  All ids are int32 so the
+// arrays go to the device as they are.
+struct CfUnit {        // chunk-first: one 32-row block of one run of shared chunks
+  int32_t chunk_begin; // into chunk_refs (pairs)
+  int32_t n_chunks;
+  int32_t row_begin;   // DFS position of the block's first row
+  int32_t n_rows;      // 1..32
+  int32_t part_base;   // partial id of the block's first row
+  int32_t pad[3];
+};
+struct SfTask {        // sequence-first: some private chunks of one sequence
+  int32_t chunk_begin;
+  int32_t n_chunks;
+  int32_t dfs_pos;
+  int32_t part_id;
+};
+
+struct Plan {
+  std::vector<int32_t> rows;        // canonical table, 7 ints per row
+  std::vector<int64_t> dfs_seq;     // seq ids in DFS order
+  std::vector<int32_t> dfs_qrow;    // caller row of each DFS position
+  std::vector<CfUnit> cf_units;
+  int64_t cf_tasks = 0;
+  std::vector<SfTask> sf_tasks;
+  std::vector<int32_t> chunk_refs;  // (slot, n_valid) pairs
+  std::vector<int32_t> seq_parts;   // (first, count) into part_list, per DFS position
+  std::vector<int32_t> part_list;   // partial ids, per sequence in merge order
+  int32_t n_parts = 0;
+  int64_t cf_chunk_reads = 0;       // per head
+  int64_t sf_chunk_reads = 0;       // per head
+  int64_t shared_chunks = 0;
+  int64_t shared_tokens = 0;
+  int64_t unique_tokens = 0;
+  int64_t attended_tokens = 0;
+};
+
+class Manager {
+ public:
+  Manager(int chunk, bool share);
+
+  void set_capacity(int64_t capacity);   // only while empty
+  int64_t capacity() const { return capacity_; }
+  int64_t free_slots() const { return static_cast<int64_t>(free_.size()); }
+  int chunk() const { return C_; }
+  size_t live() const { return end_.size(); }
+  int64_t nodes() const { return n_nodes_; }
+
+  // Mutations return the device copies they need (possibly none).
+  int32_t insert(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops);
+  void append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops);
+  void remove(int64_t seq);
+
+  std::vector<int64_t> sequences() const;  // ascending
+  int32_t seq_len(int64_t seq) const;
+
+  // Build the canonical table and the work plan.  cf_group / sf_group: chunks
+  // per chunk-first task and per sequence-first task.
+  void build_plan(int cf_group, int sf_group, Plan* plan) const;
+
+ private:
+  struct Node {
+    int32_t id = -1;
+    int32_t parent = -1;   // index into nodes_
+    int32_t slot = -1;
+    int32_t start = 0;     // position of the first token in the sequence
+    int32_t ref = 0;       // live sequences through or ending at this node
+    bool alive = false;
+    std::vector<int32_t> tokens;
+    std::vector<int32_t> children;  // indices, creation order
+    std::vector<int64_t> ended;     // sequences ending here, arrival order
+  };
+
+  int32_t new_node(int32_t parent, int32_t start);
+  void free_node(int32_t idx);
+  int32_t alloc_slot();
+  static int64_t chunks_for(int64_t n, int C) { return (n + C - 1) / C; }
+
+  int C_;
+  bool share_;
+  int64_t capacity_ = 0;
+  int32_t next_id_ = 0;
+  int64_t n_nodes_ = 0;
+  std::vector<Node> nodes_;                 // nodes_[0] is the root
+  std::vector<int32_t> free_nodes_;         // reusable indices in nodes_
+  std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_;
+  std::map<int64_t, int32_t> end_;          // seq -> node index where it ends
+  std::map<int64_t, int32_t> len_;          // seq -> length
+};
+
+}  // namespace chunkattn

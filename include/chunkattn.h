@@ -1,0 +1,200 @@
+/*
+ * chunkattn.h -- C ABI of the MI355X (gfx950) ChunkAttention decode step.
+ *
+ * The library keeps the KV cache of a batch of sequences as fixed-size chunks
+ * in a prefix tree, so a prefix shared by several sequences is stored once
+ * (prefix-aware KV cache: paperlayer.ai summary of arXiv 2402.15220v4,
+ * section 3.1 and Figure 1; explainer 0h-n0.github.io/posts/paper-2402-15220,
+ * "Prefix-Aware KV Cache").  One decode step (one query token per live
+ * sequence, summary section 2.2) runs as a two-phase partition (summary,
+ * section 3.2 and Figure 2): a chunk-first phase over chunks shared by two or
+ * more sequences, a sequence-first phase over each sequence's private chunks,
+ * and a log-sum-exp merge of the partial results (explainer, output
+ * combination formula).  The result equals softmax(q K^T / sqrt(d)) V over
+ * each sequence's stored tokens, up to rounding.
+ *
+ * Conventions
+ *  - Every call returns an int status: CA_OK (0) or a negative CA_E_* code.
+ *    ca_last_error() then holds a message; it stays valid until the next call
+ *    on the same context.  No C++ exception crosses this boundary.
+ *  - Device pointers are raw HIP device addresses; the library never allocates
+ *    device memory and never frees caller memory.  Streams are hipStream_t
+ *    passed as void* (NULL = the null stream).  Device work is enqueued on
+ *    the caller's stream only and is asynchronous: errors inside kernels
+ *    surface through the stream.  Host-side tables are built on the calling
+ *    thread.
+ *  - A context is not thread-safe.  Calls that enqueue device work on
+ *    different streams must be ordered by the caller.
+ *  - Element types: K, V, Q and the output are IEEE binary16 (fp16); the
+ *    kernels accumulate in fp32.  Token ids are int32.
+ *  - v1 supports head_dim 128 and chunk_size 64 (the tuned settings named in
+ *    the summary's section 7 and the chunk size of its Table 3); any head
+ *    count >= 1.
+ */
+#ifndef CHUNKATTN_H
+#define CHUNKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  CA_OK = 0,
+  CA_E_INVALID_ARG = -1,  /* bad pointer, size or shape */
+  CA_E_UNSUPPORTED = -2,  /* head_dim / chunk_size / flag not supported */
+  CA_E_NO_CAPACITY = -3,  /* not enough free chunk slots in the pool */
+  CA_E_DUP_SEQ = -4,      /* seq_id already live */
+  CA_E_UNKNOWN_SEQ = -5,  /* seq_id not live */
+  CA_E_EMPTY = -6,        /* attend with no live sequence */
+  CA_E_WORKSPACE = -7,    /* workspace missing or smaller than ca_workspace_bytes */
+  CA_E_HIP = -8,          /* a HIP runtime call failed; message has its text */
+  CA_E_NO_POOL = -9,      /* device work requested on a context without a pool */
+  CA_E_STATE = -10,       /* call not allowed in the current state */
+  CA_E_INTERNAL = -11
+};
+
+/* ca_create_ex flags. */
+enum {
+  /* Never match an existing prefix: every sequence gets its own chunks, so
+   * every chunk is private and a step runs the sequence-first phase over each
+   * sequence's whole block list.  This is the unshared paged layout used as
+   * the comparator (PagedAttention-style block tables; summary section 4.1). */
+  CA_CREATE_UNSHARED = 1
+};
+
+/* ca_set_option keys. */
+enum {
+  CA_OPT_CF_CHUNKS_PER_TASK = 1, /* chunks of one shared run per chunk-first task (1..64), default 4 */
+  CA_OPT_SF_CHUNKS_PER_TASK = 2  /* private chunks per sequence-first task (1..256), default 8 */
+};
+
+/* ca_attend_phase phases (the three kernels of one step, in order). */
+enum {
+  CA_PHASE_CHUNK_FIRST = 1,
+  CA_PHASE_SEQUENCE_FIRST = 2,
+  CA_PHASE_MERGE = 3
+};
+
+typedef struct ca_ctx ca_ctx;
+
+typedef struct ca_stats_t {
+  int64_t live_sequences;
+  int64_t chunks;            /* tree nodes = occupied slots */
+  int64_t shared_chunks;     /* chunks referenced by >= 2 sequences */
+  int64_t unique_tokens;     /* tokens stored once (sum of chunk fills) */
+  int64_t attended_tokens;   /* sum over live sequences of their length */
+  int64_t capacity_slots;
+  int64_t free_slots;
+  int64_t table_rebuilds;    /* host rebuilds of the chunk table */
+  double last_rebuild_ms;    /* host time of the last rebuild */
+  int64_t cf_tasks;          /* chunk-first tasks (runs of shared chunks) */
+  int64_t cf_units;          /* chunk-first work units (task x 32-row block) */
+  int64_t sf_tasks;          /* sequence-first tasks */
+  int64_t partials;          /* partial results per head */
+  int64_t cf_chunk_reads;    /* chunk tiles read per head by the chunk-first phase */
+  int64_t sf_chunk_reads;    /* chunk tiles read per head by the sequence-first phase */
+  int64_t unique_kv_bytes;   /* unique_tokens * 4 * heads * head_dim */
+  int64_t attended_kv_bytes; /* attended_tokens * 4 * heads * head_dim */
+  int64_t shared_tokens;     /* tokens held in chunks with >= 2 references */
+  int64_t private_tokens;    /* tokens held in chunks with one reference */
+} ca_stats_t;
+
+/* Bytes of one chunk slot: K and V, all heads, fp16 = 4 * heads * chunk_size
+ * * head_dim.  Returns 0 for non-positive arguments. */
+size_t ca_slot_bytes(int heads, int head_dim, int chunk_size);
+
+/* Create a context.  heads >= 1; head_dim must be 128 and chunk_size 64
+ * (else CA_E_UNSUPPORTED).  Scale is 1/sqrt(head_dim) computed in fp32.
+ * *out receives the context; the caller owns it and frees it with
+ * ca_destroy. */
+int ca_create(int heads, int head_dim, int chunk_size, ca_ctx** out);
+int ca_create_ex(int heads, int head_dim, int chunk_size, int flags, ca_ctx** out);
+void ca_destroy(ca_ctx* ctx);
+
+/* Lend the context a device pool of capacity_slots slots, each
+ * ca_slot_bytes() long, 256-byte aligned.  Layout inside the pool:
+ * slot-major, then head, then K tile and V tile of 64 x 128 fp16 each (tile
+ * element order is private to the library).  dev may be NULL: the context
+ * then manages the tree and tables on the host only and every call that
+ * needs the device returns CA_E_NO_POOL.  Allowed only while no sequence is
+ * live (CA_E_STATE otherwise).  The caller keeps the memory alive and owns it. */
+int ca_attach_pool(ca_ctx* ctx, void* dev, int64_t capacity_slots);
+
+/* Device workspace needed by ca_attend for the current tree: the chunk table
+ * and the partial results.  Changes after insert/append/remove. */
+int ca_workspace_bytes(ca_ctx* ctx, size_t* out);
+
+/* Lend a device workspace (256-byte aligned).  The caller owns it; it must
+ * stay alive while enqueued steps use it. */
+int ca_attach_workspace(ca_ctx* ctx, void* dev, size_t bytes);
+
+/* Tuning knobs (CA_OPT_*).  Takes effect at the next table rebuild. */
+int ca_set_option(ca_ctx* ctx, int option, int value);
+
+/* Add a sequence (prefix detection at arrival: summary section 3.1; explainer
+ * "dynamic prefix detection").  tokens: n >= 1 host int32 ids.  k_dev, v_dev:
+ * fp16 [n][heads][head_dim] device tensors holding the keys/values of the
+ * whole sequence; only the rows after the longest stored prefix are copied,
+ * stream-ordered on `stream`, so the caller keeps them alive until the stream
+ * passes this call.  A divergence inside a stored chunk splits that chunk.
+ * *n_matched (may be NULL) receives the number of leading tokens already
+ * stored.  Errors: CA_E_DUP_SEQ, CA_E_INVALID_ARG (n < 1, NULL pointers),
+ * CA_E_NO_CAPACITY.  A failed call changes nothing. */
+int ca_insert(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n,
+              const void* k_dev, const void* v_dev, void* stream, int32_t* n_matched);
+
+/* Append n >= 1 decoded tokens to a live sequence (summary section 3.1:
+ * decoding appends to leaf chunks or grows new chunks).  Writes into the
+ * sequence's last chunk only if that chunk is private and not full, else
+ * grows new private chunks.  k_dev, v_dev: fp16 [n][heads][head_dim].
+ * Errors: CA_E_UNKNOWN_SEQ, CA_E_INVALID_ARG, CA_E_NO_CAPACITY. */
+int ca_append(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n,
+              const void* k_dev, const void* v_dev, void* stream);
+
+/* Remove a finished sequence: every chunk on its path loses one reference and
+ * chunks left without references return their slots (explainer, "dynamic
+ * prefix detection").  Pure host bookkeeping; steps already enqueued still
+ * see the old data, but slots freed here may be overwritten by the next
+ * insert/append, so order those after the enqueued steps.
+ * Error: CA_E_UNKNOWN_SEQ. */
+int ca_remove(ca_ctx* ctx, int64_t seq_id);
+
+/* One decode step.  q_dev: fp16 [n_live][heads][head_dim]; out_dev: fp16
+ * [n_live][heads][head_dim]; row r belongs to the r-th live sequence in
+ * ascending seq_id order (ca_list_sequences).  Uploads the chunk table if the
+ * tree changed since the last upload, then enqueues the chunk-first,
+ * sequence-first and merge kernels on `stream`.  No host synchronisation.
+ * Errors: CA_E_EMPTY, CA_E_WORKSPACE, CA_E_NO_POOL, CA_E_HIP. */
+int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream);
+
+/* The same step split into its parts, for measuring each kernel: call
+ * ca_prepare once (uploads the table if needed), then ca_attend_phase with
+ * CA_PHASE_CHUNK_FIRST, CA_PHASE_SEQUENCE_FIRST and CA_PHASE_MERGE in that
+ * order on one stream.  Same arguments and errors as ca_attend. */
+int ca_prepare(ca_ctx* ctx, void* stream);
+int ca_attend_phase(ca_ctx* ctx, int phase, const void* q_dev, void* out_dev, void* stream);
+
+/* Live sequence ids in ascending order (the row order of q and out).  Writes
+ * min(count, cap) ids and returns the count (>= 0) or an error code. */
+int ca_list_sequences(ca_ctx* ctx, int64_t* ids, int cap);
+
+/* The chunk table in DFS pre-order: 7 int32 per row (node_id, parent_row,
+ * token_start, n_tokens, seq_begin, seq_end, slot), parent_row -1 under the
+ * root, [seq_begin, seq_end) the node's contiguous range in the DFS order of
+ * sequences, which is written to dfs_seq_order.  Sizes go to *n_rows and
+ * *n_seqs; nothing is written if a capacity is too small (CA_E_INVALID_ARG).
+ * Pointers may be NULL with capacity 0 to query sizes. */
+int ca_export_table(ca_ctx* ctx, int32_t* rows, int cap_rows, int64_t* dfs_seq_order,
+                    int cap_seqs, int* n_rows, int* n_seqs);
+
+int ca_stats(ca_ctx* ctx, ca_stats_t* out);
+const char* ca_last_error(ca_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CHUNKATTN_H */

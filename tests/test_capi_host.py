@@ -1,0 +1,205 @@
+"""The C-ABI library on the CPU: it loads, exports what the header declares,
+and its host-side tree and chunk table match the hand-worked golden cases and
+the independent Python model bit for bit.  No device work is done here: the
+contexts have no device pool."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from decode_attention_prefix_tree_amd import CaError, ChunkAttention, _capi
+from oracle.tree_model import PrefixTreeModel, TreeError
+from tests.golden_cases import load_cases
+from workloads import make_config
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _capi.load()
+    names = _capi.header_symbols()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_capi._SIGS), "binding and header disagree"
+
+
+def test_create_rejects_unsupported_shapes():
+    lib = _capi.load()
+    ctx = ctypes.c_void_p()
+    assert lib.ca_create(8, 64, 64, ctypes.byref(ctx)) == -2
+    assert lib.ca_create(8, 128, 32, ctypes.byref(ctx)) == -2
+    assert lib.ca_create(0, 128, 64, ctypes.byref(ctx)) == -1
+    assert lib.ca_create_ex(8, 128, 64, 0x100, ctypes.byref(ctx)) == -2
+    assert lib.ca_slot_bytes(32, 128, 64) == 4 * 32 * 64 * 128
+
+
+def _apply(ca, op):
+    try:
+        if op.kind == "insert":
+            return str(ca.insert(op.seq, op.tokens))
+        if op.kind == "append":
+            ca.append(op.seq, op.tokens)
+        else:
+            ca.remove(op.seq)
+        return None
+    except CaError as e:
+        return e.name
+
+
+def model_and_lib_agree(m, ca):
+    rows, order = m.table()
+    got_rows, got_order = ca.export_table()
+    assert [tuple(int(x) for x in r) for r in got_rows] == rows
+    assert got_order == order
+    st = ca.stats()
+    assert st["unique_tokens"] == sum(r[3] for r in rows)
+    assert st["chunks"] == len(rows)
+    assert st["free_slots"] == m.free_slots()
+    assert ca.sequences() == m.sequences()
+
+
+@pytest.mark.parametrize("case", load_cases(), ids=lambda c: c.name)
+def test_golden_scripts_lib_equals_model_at_chunk64(case):
+    m = PrefixTreeModel(64, case.capacity, case.share)
+    ca = ChunkAttention(2, case.capacity, device=None, share=case.share)
+    for op in case.ops:
+        if op.kind == "table":
+            model_and_lib_agree(m, ca)
+            continue
+        before = ca.export_table()
+        got = _apply(ca, op)
+        try:
+            if op.kind == "insert":
+                want = str(m.insert(op.seq, op.tokens))
+            elif op.kind == "append":
+                m.append(op.seq, op.tokens)
+                want = None
+            else:
+                m.remove(op.seq)
+                want = None
+        except TreeError as e:
+            want = e.code
+            after = ca.export_table()
+            assert np.array_equal(before[0], after[0]) and before[1] == after[1]
+        assert got == want
+        model_and_lib_agree(m, ca)
+
+
+def expand(tokens, rep):
+    return [t for t in tokens for _ in range(rep)]
+
+
+@pytest.mark.parametrize("case", [c for c in load_cases()], ids=lambda c: c.name)
+def test_golden_tables_at_chunk64_by_token_expansion(case):
+    """Repeating every token 64/C times turns a chunk-C golden case into a
+    chunk-64 case with the same tree shape, so the hand-worked rows carry
+    over with token_start and n_tokens scaled (splits in the golden cases
+    fall on token boundaries, which stay chunk-relative after expansion)."""
+    rep = 64 // case.chunk
+    if 64 % case.chunk:
+        pytest.skip("chunk does not divide 64")
+    ca = ChunkAttention(2, case.capacity, device=None, share=case.share)
+    for op in case.ops:
+        if op.kind == "table":
+            rows, order = ca.export_table()
+            want = [(r[0], r[1], r[2] * rep, r[3] * rep, r[4], r[5], r[6]) for r in op.rows]
+            assert [tuple(int(x) for x in r) for r in rows] == want
+            assert order == op.order
+            continue
+        got = _apply(ca, type(op)(op.kind, op.seq, expand(op.tokens, rep), op.expect))
+        if op.kind == "insert" and op.expect is not None and op.expect.lstrip("-").isdigit():
+            assert got == str(int(op.expect) * rep)
+        else:
+            assert got == op.expect
+
+
+def test_random_ops_bit_exact_against_model():
+    rng = np.random.default_rng(1234)
+    for trial in range(25):
+        cap = int(rng.integers(5, 60))
+        share = bool(rng.random() < 0.85)
+        m = PrefixTreeModel(64, cap, share)
+        ca = ChunkAttention(4, cap, device=None, share=share)
+        ids = []
+        for step in range(80):
+            r = rng.random()
+            # tokens from a small alphabet in runs, so prefixes collide often and
+            # divergences land inside chunks
+            def toks(n):
+                base = rng.integers(0, 3, size=max(1, n // 16))
+                return list(np.repeat(base, 16)[:n] if n >= 16 else rng.integers(0, 3, size=n))
+            if r < 0.45 or not ids:
+                sid = int(rng.integers(0, 1000))
+                t = toks(int(rng.integers(1, 300)))
+                op = ("insert", sid, t)
+            elif r < 0.75:
+                op = ("append", int(rng.choice(ids)), toks(int(rng.integers(1, 100))))
+            elif r < 0.95:
+                op = ("remove", int(rng.choice(ids)), [])
+            else:
+                op = ("remove", 5000, [])  # unknown
+            kind, sid, t = op
+            try:
+                getattr(m, kind)(sid, t) if kind != "remove" else m.remove(sid)
+                want = None
+            except TreeError as e:
+                want = e.code
+            try:
+                getattr(ca, kind)(sid, t) if kind != "remove" else ca.remove(sid)
+                got = None
+            except CaError as e:
+                got = e.name
+            assert got == want, (kind, sid)
+            ids = m.sequences()
+            model_and_lib_agree(m, ca)
+
+
+def test_errors_leave_state_unchanged():
+    ca = ChunkAttention(2, 3, device=None)
+    ca.insert(1, list(range(130)))   # 3 chunks: full pool
+    snap = ca.export_table()
+    for fn, code in ((lambda: ca.insert(1, [5]), "dup_seq"),
+                     (lambda: ca.insert(2, []), "invalid_arg"),
+                     (lambda: ca.insert(2, [7]), "no_capacity"),
+                     (lambda: ca.append(9, [1]), "unknown_seq"),
+                     (lambda: ca.append(1, list(range(63))), "no_capacity"),
+                     (lambda: ca.remove(9), "unknown_seq")):
+        with pytest.raises(CaError) as ei:
+            fn()
+        assert ei.value.name == code
+        after = ca.export_table()
+        assert np.array_equal(snap[0], after[0]) and snap[1] == after[1]
+    ca.append(1, list(range(62)))     # fills the last chunk (2 + 62 = 64)
+    assert ca.stats()["unique_tokens"] == 192
+
+
+def test_attach_pool_only_while_empty_and_attend_needs_device():
+    lib = _capi.load()
+    ca = ChunkAttention(2, 4, device=None)
+    ca.insert(1, [1, 2])
+    assert lib.ca_attach_pool(ca.ctx, None, 8) == -10
+    assert lib.ca_attend(ca.ctx, ctypes.c_void_p(256), ctypes.c_void_p(256), None) == -9
+    ca.remove(1)
+    assert lib.ca_attach_pool(ca.ctx, None, 8) == 0
+    assert lib.ca_attend(ca.ctx, ctypes.c_void_p(256), ctypes.c_void_p(256), None) == -9
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_workload_tables_and_plan_sizes(k):
+    wl = make_config(k, heads=1)
+    m = PrefixTreeModel(64, 10_000)
+    ca = ChunkAttention(32, 10_000, device=None)
+    for i in range(wl.n_seq):
+        t = wl.seq_tokens(i)
+        assert ca.insert(i, t) == m.insert(i, t)
+    model_and_lib_agree(m, ca)
+    st = ca.stats()
+    assert st["attended_tokens"] == wl.attended_tokens()
+    assert st["unique_kv_bytes"] == st["unique_tokens"] * 4 * 32 * 128
+    rows, _ = m.table()
+    shared = [r for r in rows if r[5] - r[4] >= 2]
+    private = [r for r in rows if r[5] - r[4] == 1]
+    assert st["shared_chunks"] == len(shared)
+    # every shared chunk is read once per 32-row block, every private chunk once
+    assert st["cf_chunk_reads"] == sum((r[5] - r[4] + 31) // 32 for r in shared)
+    assert st["sf_chunk_reads"] == len(private)

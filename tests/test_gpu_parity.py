@@ -1,0 +1,215 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar (elementwise): |gpu - oracle| <= 2e-3 + 1e-2 * |oracle| for fp16 I/O with
+fp32 accumulation; rel-L2 is also reported and gated at 1e-3.  Cases: the
+five seeded workloads at full size (all rows for 1-4, a row sample for the
+multi-branch tree), tiny trees that exercise padded MFMA rows (ranges 2-15,
+16, 32, > 32), partial chunks, sequences ending inside the tree, duplicates,
+appends and removals, the unshared comparator layout, and every task-size
+setting.  Inputs come from the seeded generators in ``workloads``."""
+
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from workloads import from_token_lists, make_config
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL, REL_L2 = 2e-3, 1e-2, 1e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=2)
+def cached_config(k):
+    return make_config(k)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def build_ca(wl, share=True, cf_group=None, sf_group=None, capacity=None):
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import ChunkAttention, load_workload, slots_needed
+    from decode_attention_prefix_tree_amd import _capi
+    cap = capacity or slots_needed(wl, share=share) + 4
+    ca = ChunkAttention(wl.heads, cap, device="cuda:0", share=share)
+    if cf_group:
+        ca.set_option(_capi.CA_OPT_CF_CHUNKS_PER_TASK, cf_group)
+    if sf_group:
+        ca.set_option(_capi.CA_OPT_SF_CHUNKS_PER_TASK, sf_group)
+    load_workload(ca, wl, device="cuda:0")
+    torch.cuda.synchronize()
+    return ca
+
+
+def run_step(ca, q_np):
+    torch = _torch()
+    q = torch.from_numpy(np.ascontiguousarray(q_np)).to("cuda:0")
+    out = ca.attend(q)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def assert_parity(got, ref, label):
+    rep = A.allclose_report(got, ref, ATOL, RTOL)
+    _say(f"{label}: max_abs={rep['max_abs']:.3e} rel_l2={rep['rel_l2']:.3e} bad={rep['n_bad']}")
+    assert rep["ok"], (label, rep)
+    assert rep["rel_l2"] <= REL_L2, (label, rep)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_workload_full(k):
+    _say(f"workload {k}")
+    wl = cached_config(k)
+    ca = build_ca(wl)
+    got = run_step(ca, wl.q)
+    ref = A.decode_workload(wl)
+    assert_parity(got, ref, f"config{k}")
+
+
+def test_multi_branch_sampled_rows():
+    _say("workload 5")
+    wl = cached_config(5)
+    ca = build_ca(wl)
+    got = run_step(ca, wl.q)
+    rows = sorted({0, 31, 32, 63, 64, 95, 96, 127} | set(np.random.default_rng(5).choice(128, 8, replace=False)))
+    ref = A.decode_workload(wl, rows)
+    assert_parity(got[rows], ref, "config5")
+    assert np.isfinite(got).all()
+
+
+def tiny_tree_cases():
+    rng = np.random.default_rng(77)
+    cases = {}
+    # one shared prefix, range R for R in 2..15, 16, 32, 40 (two row blocks), ragged suffixes
+    for R in (2, 3, 7, 15, 16, 17, 31, 32, 33, 40, 70):
+        pre = list(rng.integers(0, 50, size=int(rng.integers(1, 200))))
+        seqs = [pre + [1000 + i] + list(rng.integers(0, 50, size=int(rng.integers(0, 150)))) for i in range(R)]
+        cases[f"shared_R{R}"] = seqs
+    # interior-ending sequences and duplicates
+    base = list(rng.integers(0, 9, size=300))
+    cases["interior_and_dups"] = [base[:70], base[:70], base, base[:128], base[:129], base[:1], base + [3, 3]]
+    # a deep random tree: divergences inside chunks at many depths
+    seqs = []
+    for i in range(24):
+        parent = seqs[int(rng.integers(0, len(seqs)))] if seqs else []
+        cut = int(rng.integers(0, len(parent) + 1))
+        seqs.append(parent[:cut] + [2000 + i] + list(rng.integers(0, 5, size=int(rng.integers(1, 180)))))
+    cases["deep_random"] = seqs
+    # single sequence of a single token; and all-private short sequences
+    cases["single_token"] = [[5]]
+    cases["all_private"] = [[100 * i + j for j in range(int(rng.integers(1, 140)))] for i in range(9)]
+    return cases
+
+
+@pytest.mark.parametrize("name", list(tiny_tree_cases()))
+def test_tiny_trees(name):
+    _say(f"tiny tree {name}")
+    seqs = tiny_tree_cases()[name]
+    wl = from_token_lists(seqs, heads=3, seed=len(name))
+    ca = build_ca(wl)
+    got = run_step(ca, wl.q)
+    ref = A.decode_workload(wl)
+    assert_parity(got, ref, name)
+
+
+@pytest.mark.parametrize("cf_group,sf_group", [(1, 1), (2, 3), (8, 8), (16, 2), (64, 256)])
+def test_task_sizes(cf_group, sf_group):
+    _say(f"task sizes {cf_group} {sf_group}")
+    wl = cached_config(1)
+    ca = build_ca(wl, cf_group=cf_group, sf_group=sf_group)
+    assert_parity(run_step(ca, wl.q), A.decode_workload(wl), f"cf{cf_group}/sf{sf_group}")
+    seqs = tiny_tree_cases()["deep_random"]
+    wl2 = from_token_lists(seqs, heads=2, seed=9)
+    ca2 = build_ca(wl2, cf_group=cf_group, sf_group=sf_group)
+    assert_parity(run_step(ca2, wl2.q), A.decode_workload(wl2), f"deep cf{cf_group}/sf{sf_group}")
+
+
+def test_unshared_comparator_layout():
+    _say("unshared")
+    wl = cached_config(1)
+    ca = build_ca(wl, share=False)
+    st = ca.stats()
+    assert st["shared_chunks"] == 0 and st["unique_tokens"] == wl.attended_tokens()
+    assert_parity(run_step(ca, wl.q), A.decode_workload(wl), "unshared config1")
+
+
+def test_deterministic_bitwise():
+    _say("determinism")
+    wl = cached_config(1)
+    ca = build_ca(wl)
+    a = run_step(ca, wl.q)
+    b = run_step(ca, wl.q)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_append_and_remove_between_steps():
+    _say("append/remove")
+    torch = _torch()
+    rng = np.random.default_rng(3)
+    H = 4
+    pre = list(range(100))
+    seqs = [pre + [500 + i] * int(rng.integers(1, 90)) for i in range(6)]
+    wl = from_token_lists(seqs, heads=H, seed=11)
+    ca = build_ca(wl, capacity=64)
+    kv = {i: list(wl.seq_kv(i)) for i in range(wl.n_seq)}
+    live = list(range(wl.n_seq))
+    for step in range(6):
+        # append 1..70 tokens to some sequences (in place and across chunk edges)
+        for i in list(live):
+            if rng.random() < 0.7:
+                n = int(rng.integers(1, 70))
+                k = rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+                v = rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+                ca.append(i, list(rng.integers(0, 9, size=n)), torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+                kv[i][0] = np.concatenate([kv[i][0], k])
+                kv[i][1] = np.concatenate([kv[i][1], v])
+        if step == 2:
+            ca.remove(live.pop(1))
+        if step == 4:
+            ca.remove(live.pop(0))
+        q = rng.standard_normal((len(live), H, 128), dtype=np.float32).astype(np.float16)
+        got = run_step(ca, q)
+        ref = A.decode_step(q, [kv[i] for i in live])
+        assert_parity(got, ref, f"append step {step}")
+
+
+def test_phases_equal_fused_call():
+    _say("phases")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import _capi
+    wl = cached_config(1)
+    ca = build_ca(wl)
+    q = torch.from_numpy(wl.q).cuda()
+    ref = ca.attend(q).clone()
+    out = torch.empty_like(q)
+    ca.prepare()
+    for ph in (_capi.CA_PHASE_CHUNK_FIRST, _capi.CA_PHASE_SEQUENCE_FIRST, _capi.CA_PHASE_MERGE):
+        ca.attend_phase(ph, q, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_errors_on_device_context():
+    _say("errors")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import CaError, ChunkAttention
+    ca = ChunkAttention(2, 2, device="cuda:0")
+    q = torch.zeros((0, 2, 128), dtype=torch.float16, device="cuda:0")
+    with pytest.raises(CaError) as ei:
+        ca.attend(q)
+    assert ei.value.name == "empty"
+    k = torch.zeros((200, 2, 128), dtype=torch.float16, device="cuda:0")
+    with pytest.raises(CaError) as ei:
+        ca.insert(1, list(range(200)), k, k)
+    assert ei.value.name == "no_capacity"
