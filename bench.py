@@ -3,10 +3,12 @@
 
 One step = one ca_attend (chunk-first, sequence-first and merge kernels) over
 the whole batch, with the chunk table already uploaded and Q resident in HBM.
-Before each timed step a 1 GiB scratch buffer is rewritten (outside the
-timing events) so neither the 256 MB Infinity Cache nor the L2s hold KV: the
-figures are cold-cache HBM figures.  Warm (back-to-back) figures are reported
-alongside, labelled.
+Before each timed step a 1 GiB scratch buffer is read (outside the timing
+events), so neither the 256 MB Infinity Cache nor the L2s hold KV: the
+figures are cold-cache HBM figures.  The flush only reads, so the caches hold
+clean lines that cost nothing to evict (a writing flush would leave dirty
+lines whose write-back competes with the step).  Warm (back-to-back) figures
+are reported alongside, labelled.
 
 Prints one JSON line:
   value        attended KV tokens/s (sum of sequence lengths / step time)
@@ -47,19 +49,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--profile-only", action="store_true",
-                    help="only warmup + timed steps of the main path (for rocprofv3 runs)")
+                    help="only the per-kernel timing loop (for rocprofv3 runs); prints its event means")
     return ap.parse_args()
 
 
 class Flusher:
-    """Rewrites a 1 GiB buffer: evicts KV from the Infinity Cache and L2s."""
+    """Reads a 1 GiB buffer: evicts KV from the Infinity Cache and L2s and
+    leaves only clean lines behind."""
 
     def __init__(self, torch):
-        self.buf = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
-        self.buf.zero_()
+        self.torch = torch
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        self.acc = torch.empty((), dtype=torch.float32, device="cuda")
 
     def __call__(self):
-        self.buf.add_(1)
+        # same dtype in and out: one reduction kernel, no conversion copy
+        self.torch.sum(self.buf, dim=0, out=self.acc)
 
 
 def time_steps(torch, fn, steps, flush=None):
@@ -76,12 +81,11 @@ def time_steps(torch, fn, steps, flush=None):
     return np.array([a.elapsed_time(b) for a, b in ev])
 
 
-def time_phases(torch, ca, q, out, steps, flush):
-    """Per-kernel event times (ms): chunk-first, sequence-first, merge."""
-    from decode_attention_prefix_tree_amd import _capi
-    phases = (_capi.CA_PHASE_CHUNK_FIRST, _capi.CA_PHASE_SEQUENCE_FIRST, _capi.CA_PHASE_MERGE)
+def time_launches(torch, ca, q, out, steps, flush, phases):
+    """Event times (ms) of each launch in `phases` (ca_attend_phase ids),
+    launched one after another on the current stream, cold."""
     ca.prepare()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
         flush()
@@ -90,8 +94,7 @@ def time_phases(torch, ca, q, out, steps, flush):
             ca.attend_phase(ph, q, out)
             ev[i][j + 1].record()
     torch.cuda.synchronize()
-    t = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)] for i in range(steps)])
-    return t
+    return np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(len(phases))] for i in range(steps)])
 
 
 def cpu_baseline(wl, seconds_target):
@@ -163,19 +166,27 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    from decode_attention_prefix_tree_amd import _capi
+    step_launches = (_capi.CA_PHASE_PARTIALS, _capi.CA_PHASE_MERGE)
+    if args.profile_only:
+        lt = time_launches(torch, ca, q, out, args.steps, flush, step_launches)
+        print(json.dumps({"launch_us_mean": {"partials_kernel": float(lt[:, 0].mean()) * 1e3,
+                                             "merge_kernel": float(lt[:, 1].mean()) * 1e3},
+                          "steps": args.steps, "config": args.config}), flush=True)
+        return
+
     log(f"timing {args.steps} cold steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     cold = time_steps(torch, step, args.steps, flush)
     wall = time.perf_counter() - wall0
-    if args.profile_only:
-        log(f"cold mean {cold.mean()*1e3:.1f} us")
-        return
 
     log("timing warm steps")
     warm = time_steps(torch, step, args.steps)
-    log("timing phases")
-    ph = time_phases(torch, ca, q, out, args.steps, flush)
+    log("timing launches")
+    lt = time_launches(torch, ca, q, out, args.steps, flush, step_launches)
+    ph = time_launches(torch, ca, q, out, args.steps, flush,
+                       (_capi.CA_PHASE_CHUNK_FIRST, _capi.CA_PHASE_SEQUENCE_FIRST))
 
     unique_b = st["unique_kv_bytes"]
     per_tok = 4 * wl.heads * wl.head_dim
@@ -184,16 +195,14 @@ def main():
     t_mean = float(cold.mean()) * 1e-3
     value = st["attended_tokens"] / t_mean
 
-    # dominant kernel by measured time
-    names = ["chunk_first", "sequence_first", "merge"]
-    algo = [shared_b, private_b, 0]
-    dom = int(np.argmax(ph.mean(axis=0)))
-    dom_t = float(ph[:, dom].mean()) * 1e-3
-    roof = {"kernel": names[dom], "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
-            "achieved": algo[dom] / dom_t / 1e9 if algo[dom] else None,
-            "traffic": None,
-            "bytes_per_launch": algo[dom], "avg_launch_us": dom_t * 1e6}
-    roof["frac"] = roof["achieved"] / HBM_PEAK_GBPS if roof["achieved"] else None
+    # The dominant kernel: the partials launch of a step (chunk-first and
+    # sequence-first blocks in one grid).  Its algorithmic bytes are the
+    # unique KV bytes (each shared chunk once, each private chunk once).
+    dom_t = float(lt[:, 0].mean()) * 1e-3
+    roof = {"kernel": "partials_kernel", "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
+            "achieved": unique_b / dom_t / 1e9, "traffic": None,
+            "bytes_per_launch": unique_b, "avg_launch_us": dom_t * 1e6}
+    roof["frac"] = roof["achieved"] / HBM_PEAK_GBPS
 
     result = {
         "metric": METRIC,
@@ -209,7 +218,7 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": CONFIG_NAMES[args.config], "n_seq": wl.n_seq, "heads": wl.heads,
-                   "head_dim": wl.head_dim, "chunk": wl.chunk, "cache": "cold (1 GiB rewrite before each step)"},
+                   "head_dim": wl.head_dim, "chunk": wl.chunk, "cache": "cold (1 GiB read before each step)"},
         "unique_kv_gbps": unique_b / t_mean / 1e9,
         "hbm_frac_unique": unique_b / t_mean / 1e9 / HBM_PEAK_GBPS,
         "queries_per_s": wl.n_seq / t_mean,
@@ -217,7 +226,9 @@ def main():
                     "p50": float(np.median(cold)) * 1e3, "p90": float(np.percentile(cold, 90)) * 1e3},
         "warm_step_us": {"mean": float(warm.mean()) * 1e3, "p50": float(np.median(warm)) * 1e3,
                          "unique_kv_gbps": unique_b / (float(warm.mean()) * 1e-3) / 1e9},
-        "phase_us": {n: float(ph[:, j].mean()) * 1e3 for j, n in enumerate(names)},
+        "launch_us": {"partials_kernel": float(lt[:, 0].mean()) * 1e3, "merge_kernel": float(lt[:, 1].mean()) * 1e3},
+        "phase_alone_us": {"chunk_first": float(ph[:, 0].mean()) * 1e3, "sequence_first": float(ph[:, 1].mean()) * 1e3,
+                           "sequence_first_gbps": private_b / (float(ph[:, 1].mean()) * 1e-3) / 1e9},
         "tokens": {"attended": st["attended_tokens"], "unique": st["unique_tokens"],
                    "shared": st["shared_tokens"], "private": st["private_tokens"]},
         "timed_wall_s": wall,

@@ -18,9 +18,11 @@ CA_OK = 0
 CA_CREATE_UNSHARED = 1
 CA_OPT_CF_CHUNKS_PER_TASK = 1
 CA_OPT_SF_CHUNKS_PER_TASK = 2
+CA_OPT_FUSED_MERGE = 3
 CA_PHASE_CHUNK_FIRST = 1
 CA_PHASE_SEQUENCE_FIRST = 2
 CA_PHASE_MERGE = 3
+CA_PHASE_PARTIALS = 4
 
 ERROR_NAMES = {
     -1: "invalid_arg", -2: "unsupported", -3: "no_capacity", -4: "dup_seq", -5: "unknown_seq",

@@ -4,7 +4,10 @@
 
 The host parts (manager, C-ABI) and the kernels go into one shared library.
 HIP code is compiled without packed-fp32 instructions (the
-``-packed-fp32-ops`` target feature is switched off).
+``-packed-fp32-ops`` target feature is switched off) and without implicit
+FMA contraction (``-ffp-contract=off``): fused multiply-adds appear only where
+the source calls fmaf, so every instantiation of a kernel rounds the same way
+and the one-launch and two-launch steps agree bit for bit.
 """
 
 from __future__ import annotations
@@ -36,7 +39,7 @@ def hipcc() -> str:
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}", "-I/opt/rocm/include"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-munsafe-fp-atomics"]
+             "-ffp-contract=off"]
 
 
 def _run(cmd, verbose):

@@ -21,7 +21,8 @@ struct ca_ctx {
   bool pool_attached = false;
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  int cf_group = 4, sf_group = 8;
+  int cf_group = 8, sf_group = 4;
+  bool fused_merge = false;
 
   // plan cache: rebuilt after the tree changes, uploaded when stale
   chunkattn::Plan plan;
@@ -29,6 +30,7 @@ struct ca_ctx {
   uint64_t version = 1, uploaded_version = 0;
   void* uploaded_ws = nullptr;
   size_t off_cf = 0, off_sf = 0, off_refs = 0, off_qrow = 0, off_seqparts = 0, off_partlist = 0;
+  size_t off_arrivals = 0;
   size_t table_bytes = 0, off_part_o = 0, off_part_ms = 0, total_bytes = 0;
   int64_t rebuilds = 0;
   double last_rebuild_ms = 0.0;
@@ -90,6 +92,10 @@ void ensure_plan(ca_ctx* c) {
   off = align_up(off + p.seq_parts.size() * sizeof(int32_t));
   c->off_partlist = off;
   off = align_up(off + p.part_list.size() * sizeof(int32_t));
+  // arrival counters of the fused merge: uploaded as zeros with the table,
+  // and every step leaves them at zero again
+  c->off_arrivals = off;
+  off = align_up(off + p.dfs_seq.size() * static_cast<size_t>(c->heads) * sizeof(int32_t));
   c->table_bytes = off;
   c->off_part_o = off;
   off = align_up(off + static_cast<size_t>(p.n_parts) * c->heads * c->head_dim * sizeof(float));
@@ -154,6 +160,7 @@ chunkattn::StepArgs step_args(ca_ctx* c, const void* q, void* out) {
   a.part_list = reinterpret_cast<const int32_t*>(w + c->off_partlist);
   a.part_o = reinterpret_cast<float*>(w + c->off_part_o);
   a.part_ms = reinterpret_cast<float*>(w + c->off_part_ms);
+  a.arrivals = reinterpret_cast<int*>(w + c->off_arrivals);
   a.heads = c->heads;
   a.n_cf_units = static_cast<int>(p.cf_units.size());
   a.n_sf_tasks = static_cast<int>(p.sf_tasks.size());
@@ -281,6 +288,9 @@ int ca_set_option(ca_ctx* ctx, int option, int value) {
     } else if (option == CA_OPT_SF_CHUNKS_PER_TASK) {
       if (value < 1 || value > 256) throw Error(CA_E_INVALID_ARG, "sequence-first group must be 1..256");
       ctx->sf_group = value;
+    } else if (option == CA_OPT_FUSED_MERGE) {
+      if (value != 0 && value != 1) throw Error(CA_E_INVALID_ARG, "fused merge is 0 or 1");
+      ctx->fused_merge = value != 0;
     } else {
       throw Error(CA_E_UNSUPPORTED, "unknown option");
     }
@@ -348,9 +358,11 @@ int ca_attend_phase(ca_ctx* ctx, int phase, const void* q_dev, void* out_dev, vo
     upload(ctx, stream);
     chunkattn::StepArgs a = step_args(ctx, q_dev, out_dev);
     if (phase == CA_PHASE_CHUNK_FIRST)
-      launch(chunkattn::launch_chunk_first(a, stream), "chunk_first");
+      launch(chunkattn::launch_partials(a, chunkattn::kPartsChunkFirst, false, stream), "partials");
     else if (phase == CA_PHASE_SEQUENCE_FIRST)
-      launch(chunkattn::launch_sequence_first(a, stream), "sequence_first");
+      launch(chunkattn::launch_partials(a, chunkattn::kPartsSequenceFirst, false, stream), "partials");
+    else if (phase == CA_PHASE_PARTIALS)
+      launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, false, stream), "partials");
     else if (phase == CA_PHASE_MERGE)
       launch(chunkattn::launch_merge(a, stream), "merge");
     else
@@ -364,9 +376,12 @@ int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream) {
     check_step(ctx, q_dev, out_dev);
     upload(ctx, stream);
     chunkattn::StepArgs a = step_args(ctx, q_dev, out_dev);
-    launch(chunkattn::launch_chunk_first(a, stream), "chunk_first");
-    launch(chunkattn::launch_sequence_first(a, stream), "sequence_first");
-    launch(chunkattn::launch_merge(a, stream), "merge");
+    if (ctx->fused_merge) {
+      launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, true, stream), "partials+merge");
+    } else {
+      launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, false, stream), "partials");
+      launch(chunkattn::launch_merge(a, stream), "merge");
+    }
     return CA_OK;
   });
 }

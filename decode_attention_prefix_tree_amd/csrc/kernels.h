@@ -31,6 +31,7 @@ struct StepArgs {
   const int32_t* part_list;    // partial ids
   float* part_o;               // [n_parts][H][128]
   float* part_ms;              // [n_parts][H][2]: running max (log2 units), sum
+  int* arrivals;               // [n_seq][H] partials done this step; 0 between steps
   int heads;
   int n_cf_units;
   int n_sf_tasks;
@@ -38,11 +39,17 @@ struct StepArgs {
   float scale_log2e;           // (1/sqrt(128)) * log2(e)
 };
 
+// Which blocks of the partials kernel to launch.
+enum PartialsPart { kPartsBoth = 0, kPartsChunkFirst = 1, kPartsSequenceFirst = 2 };
+
 // Each returns a hipError_t value (0 = success) from the launch.
 int launch_kv_write(void* pool, int heads, const KvOpBatch& batch, int n_ops, const void* k_src,
                     const void* v_src, void* stream);
-int launch_chunk_first(const StepArgs& a, void* stream);
-int launch_sequence_first(const StepArgs& a, void* stream);
+// One grid with the chunk-first blocks first and the sequence-first blocks
+// after them; `part` restricts the launch to one side.  With fuse_merge the
+// last block to finish a (sequence, head) also merges it and writes out (the
+// whole step in one launch; needs part == kPartsBoth).
+int launch_partials(const StepArgs& a, int part, bool fuse_merge, void* stream);
 int launch_merge(const StepArgs& a, void* stream);
 
 }  // namespace chunkattn

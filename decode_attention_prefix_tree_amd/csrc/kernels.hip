@@ -130,35 +130,156 @@ __global__ __launch_bounds__(256) void kv_write_kernel(_Float16* pool, int heads
   }
 }
 
-// ---------------------------------------------------------------------------
-// Chunk-first: one block per (unit = run of shared chunks x 32-row block,
-// head).  Wave w takes chunks w, w+4, ... of the run; lane (half, i) owns
-// query row i.  Per chunk: S^T[64 keys x 32 rows] = K Q^T (16 MFMA), online
-// softmax along keys (each lane holds 32 keys of its row, its twin lane the
-// other 32), O^T[128 x 32] += V^T P^T (16 MFMA).  The four waves' states are
-// merged in LDS and one partial per row is written.
-constexpr int kOStride = 132;  // padded row stride of the LDS merge buffer
+// Step-local communication between blocks (the fused merge).  Partials are
+// written with agent-scope relaxed atomic stores and read back with
+// agent-scope atomic loads: both are coherent across the XCDs by themselves
+// (global_store/global_load with sc1), so no cache-wide write-back or
+// invalidate is needed.  A writer waits for its stores to complete before it
+// counts its arrival, so the block that sees the final count reads complete
+// data.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__global__ __launch_bounds__(256) void chunk_first_kernel(StepArgs a) {
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+// ---------------------------------------------------------------------------
+// Merge of one (sequence, head) by one wave: folds the sequence's partials in
+// the fixed order of its list (shared runs root first, then private tasks):
+// M = max m_j, o = sum e^{m_j - M} o_j, s = sum e^{m_j - M} s_j,
+// out = o / s in fp16.  Lane j fetches partial j's (m, s) and all lanes then
+// fetch o rows eight partials at a time, so the loads of a round are in
+// flight together; lane l owns dims 2l, 2l+1.  Partials are taken 64 at a
+// time; a later round rescales what the earlier ones summed.
+template <bool kCoherent>
+__device__ __forceinline__ float ld(const float* p) {
+  if constexpr (kCoherent) return load_agent(p);
+  return *p;
+}
+
+template <bool kCoherent>
+__device__ __forceinline__ void merge_one(const StepArgs& a, int pos, int head, int lane) {
+  const int H = a.heads;
+  const int first = a.seq_parts[2 * pos], cnt = a.seq_parts[2 * pos + 1];
+  float s = 0.f, o0 = 0.f, o1 = 0.f, M = -INFINITY;
+  for (int j0 = 0; j0 < cnt; j0 += 64) {
+    // lane j holds partial j0+j: its id, running max and sum
+    const int n = min(64, cnt - j0);
+    int my_pid = 0;
+    float my_m = -INFINITY, my_s = 0.f;
+    if (lane < n) {
+      my_pid = a.part_list[first + j0 + lane];
+      const size_t pid = static_cast<size_t>(my_pid) * H + head;
+      my_m = ld<kCoherent>(a.part_ms + pid * 2);
+      my_s = ld<kCoherent>(a.part_ms + pid * 2 + 1);
+    }
+    float Mr = fmaxf(my_m, __shfl_xor(my_m, 32));
+    Mr = fmaxf(M, wave_max32(Mr));
+    // rescale what earlier rounds accumulated (only with more than 64 partials)
+    const float r = M == -INFINITY ? 0.f : exp2f(M - Mr);
+    o0 *= r;
+    o1 *= r;
+    s *= r;
+    M = Mr;
+    const float my_w = lane < n ? exp2f(my_m - M) : 0.f;
+    s += wave_sum64(my_w * my_s);
+    // the o rows of all partials are independent loads: issue 8 at a time
+    for (int j = 0; j < n; j += 8) {
+      float2 ov[8];
+      float wv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int jj = min(j + u, n - 1);
+        wv[u] = j + u < n ? __shfl(my_w, jj) : 0.f;
+        const size_t pid = static_cast<size_t>(__shfl(my_pid, jj)) * H + head;
+        const float* src = a.part_o + pid * D + 2 * lane;
+        if constexpr (kCoherent) {
+          ov[u].x = load_agent(src);
+          ov[u].y = load_agent(src + 1);
+        } else {
+          ov[u] = *reinterpret_cast<const float2*>(src);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        o0 = fmaf(wv[u], ov[u].x, o0);
+        o1 = fmaf(wv[u], ov[u].y, o1);
+      }
+    }
+  }
+  const float inv = 1.0f / s;
+  const int qrow = a.dfs_qrow[pos];
+  _Float16* out = static_cast<_Float16*>(a.out) + (static_cast<size_t>(qrow) * H + head) * D + 2 * lane;
+  h2 res = {static_cast<_Float16>(o0 * inv), static_cast<_Float16>(o1 * inv)};
+  *reinterpret_cast<h2*>(out) = res;
+}
+
+// Arrival of one partial of (pos, head).  Called after the caller's partial
+// stores and an agent-scope release fence; returns true for the block whose
+// partial completes the set, which then owns the merge (and clears the
+// counter for the next step after an acquire fence).
+__device__ __forceinline__ bool arrive(const StepArgs& a, int pos, int head) {
+  const int old = atomicAdd(a.arrivals + pos * a.heads + head, 1);
+  return old == a.seq_parts[2 * pos + 1] - 1;
+}
+
+__device__ __forceinline__ void merge_and_reset(const StepArgs& a, int pos, int head, int lane) {
+  merge_one<true>(a, pos, head, lane);
+  if (lane == 0)
+    __hip_atomic_store(a.arrivals + pos * a.heads + head, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Partials.  One grid holds both phases: blocks [0, n_cf) are chunk-first
+// blocks and come first so they start first, the rest are sequence-first
+// blocks, so the two phases run at the same time with no launch between
+// them.  256 threads (4 waves) per block; a block owns one task and its
+// waves take the task's chunks w, w+4, ...  Both paths fit 168 VGPRs and
+// 46 KiB of LDS, so three blocks share a CU.
+
+constexpr int kOStride = 132;                        // padded row stride of wave states
+constexpr int kQBytes = 32 * D * 2;                  // Q block in operand order, fp16
+constexpr int kStateFloats = 32 * kOStride + 64;     // one wave state: O rows, then (m, l)
+constexpr int kSmemBytes = kQBytes + 2 * kStateFloats * 4;
+
+__device__ __forceinline__ float weight(float m, float M) {
+  // e^(m - M) in base 2; an empty state (m = -inf) weighs 0 even when M = -inf
+  return m == -INFINITY ? 0.f : exp2f(m - M);
+}
+
+// Chunk-first: unit = (run of shared chunks, 32-row block), one head.
+// Lane (half, i) owns query row i.  Per 32-key half of a chunk:
+// S^T[32 keys x 32 rows] = K Q^T (8 MFMA; Q^T comes from LDS), online softmax
+// along keys (the lane holds 16 keys of its row, its twin lane the other 16),
+// O^T[128 x 32] += V^T P^T (8 MFMA).  P^T needs no exchange: the V tile
+// stores keys in the order the S^T accumulators hold them.
+template <bool kFuse>
+__device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical, char* smem) {
   const int unit = logical % a.n_cf_units, head = logical / a.n_cf_units;
   const int* u = a.cf_units + unit * 8;
   const int chunk_begin = u[0], n_chunks = u[1], row_begin = u[2], n_rows = u[3], part_base = u[4];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, i = lane & 31;
+  // wave index in an SGPR: chunk lookups and tile bases stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, half = lane >> 5, i = lane & 31;
   const int H = a.heads;
   const _Float16* pool = static_cast<const _Float16*>(a.pool);
 
-  h8 qb[8];
-  {
-    const bool ok = i < n_rows;
-    const int qrow = a.dfs_qrow[row_begin + (ok ? i : 0)];
-    const _Float16* qp = static_cast<const _Float16*>(a.q) + (static_cast<size_t>(qrow) * H + head) * D;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      h8 v = *reinterpret_cast<const h8*>(qp + kk * 16 + half * 8);
-      qb[kk] = ok ? v : h8{};
+  // Q rows of the block into LDS in B-operand order: piece (kk, lane) at
+  // (kk*64 + lane)*8 halves holds Q[row lane%32][16kk + 8(lane/32) .. +8].
+  _Float16* q_lds = reinterpret_cast<_Float16*>(smem);
+  for (int p = threadIdx.x; p < 32 * 16; p += 256) {
+    const int row = p >> 4, c16 = p & 15, kk = c16 >> 1, hf = c16 & 1;
+    h8 v = h8{};
+    if (row < n_rows) {
+      const int qrow = a.dfs_qrow[row_begin + row];
+      v = *reinterpret_cast<const h8*>(static_cast<const _Float16*>(a.q) +
+                                       (static_cast<size_t>(qrow) * H + head) * D + c16 * 8);
     }
+    *reinterpret_cast<h8*>(q_lds + ((kk * 64 + hf * 32 + row) * 8)) = v;
   }
+  __syncthreads();
 
   float m = -INFINITY, l = 0.f;
   f16v acc[4];
@@ -170,119 +291,162 @@ __global__ __launch_bounds__(256) void chunk_first_kernel(StepArgs a) {
     const int nvalid = a.chunk_refs[2 * (chunk_begin + c) + 1];
     const _Float16* kt = pool + tile_base(slot, head, H, 0);
     const _Float16* vt = kt + TILE;
-
-    f16v s0 = f16v{}, s1 = f16v{};
+    // The halves stay a loop: unrolled, the second half's loads would be
+    // hoisted over the first half's MFMAs and the block would not fit three
+    // waves per SIMD.
+#pragma unroll 1
+    for (int jb = 0; jb < 2; ++jb) {
+      h8 kr[8], vr[8];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      h8 k0 = *reinterpret_cast<const h8*>(kt + ((0 * 8 + kk) * 64 + lane) * 8);
-      h8 k1 = *reinterpret_cast<const h8*>(kt + ((1 * 8 + kk) * 64 + lane) * 8);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qb[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qb[kk], s1, 0, 0, 0);
-    }
-    h8 va[16];
+      for (int kk = 0; kk < 8; ++kk) kr[kk] = *reinterpret_cast<const h8*>(kt + ((jb * 8 + kk) * 64 + lane) * 8);
 #pragma unroll
-    for (int L = 0; L < 16; ++L) va[L] = *reinterpret_cast<const h8*>(vt + (L * 64 + lane) * 8);
-
-    // s0[r] is key 8*(r/4) + 4*half + r%4 of row i; s1 the same key + 32.
-    float mx = -INFINITY;
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * half + (r & 3);
-      const float x0 = key < nvalid ? s0[r] * a.scale_log2e : -INFINITY;
-      const float x1 = key + 32 < nvalid ? s1[r] * a.scale_log2e : -INFINITY;
-      s0[r] = x0;
-      s1[r] = x1;
-      mx = fmaxf(mx, fmaxf(x0, x1));
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx);
-    const float alpha = exp2f(m - mnew);
-    float psum = 0.f;
-    h8 pb[4];
+        for (int t = 0; t < 2; ++t)
+          vr[nb * 2 + t] = *reinterpret_cast<const h8*>(vt + ((nb * 4 + 2 * jb + t) * 64 + lane) * 8);
+      f16v sc = f16v{};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p0 = exp2f(s0[r] - mnew);
-      const float p1 = exp2f(s1[r] - mnew);
-      psum += p0 + p1;
-      pb[(r >> 3)][r & 7] = static_cast<_Float16>(p0);
-      pb[2 + (r >> 3)][r & 7] = static_cast<_Float16>(p1);
-    }
-    l = l * alpha + psum;
-    m = mnew;
+      for (int kk = 0; kk < 8; ++kk) {
+        const h8 qb = *reinterpret_cast<const h8*>(q_lds + (kk * 64 + lane) * 8);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kr[kk], qb, sc, 0, 0, 0);
+      }
+      // sc[r] is key 32jb + 8(r/4) + 4half + r%4 of row i
+      float mx = -INFINITY;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      acc[nb] *= alpha;
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * jb + 8 * (r >> 2) + 4 * half + (r & 3);
+        const float x = key < nvalid ? sc[r] * a.scale_log2e : -INFINITY;
+        sc[r] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m, mx);
+      if (mnew == -INFINITY) continue;  // every key of this half is past the fill
+      const float alpha = weight(m, mnew);
+      float psum = 0.f;
+      h8 pb[2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[nb * 4 + s], pb[s], acc[nb], 0, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f(sc[r] - mnew);
+        psum += p;
+        pb[r >> 3][r & 7] = static_cast<_Float16>(p);
+      }
+      l = l * alpha + psum;
+      m = mnew;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        acc[nb] *= alpha;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vr[nb * 2 + t], pb[t], acc[nb], 0, 0, 0);
+      }
     }
   }
   l += __shfl_xor(l, 32);
 
-  __shared__ float lds_o[4][32][kOStride];
-  __shared__ float lds_m[4][32];
-  __shared__ float lds_l[4][32];
+  // Pairwise merge of the four wave states: (w0 + w2) + (w1 + w3).
+  float* st = reinterpret_cast<float*>(smem + kQBytes);
+  auto put = [&](int slotw) {
+    float* o = st + slotw * kStateFloats;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f4 v = {acc[nb][4 * g + 0], acc[nb][4 * g + 1], acc[nb][4 * g + 2], acc[nb][4 * g + 3]};
-      *reinterpret_cast<f4*>(&lds_o[wave][i][32 * nb + 8 * g + 4 * half]) = v;
+      for (int g = 0; g < 4; ++g) {
+        f4 v = {acc[nb][4 * g + 0], acc[nb][4 * g + 1], acc[nb][4 * g + 2], acc[nb][4 * g + 3]};
+        *reinterpret_cast<f4*>(o + i * kOStride + 32 * nb + 8 * g + 4 * half) = v;
+      }
+    if (half == 0) {
+      o[32 * kOStride + 2 * i] = m;
+      o[32 * kOStride + 2 * i + 1] = l;
     }
-  if (half == 0) {
-    lds_m[wave][i] = m;
-    lds_l[wave][i] = l;
-  }
+  };
+  auto take = [&](int slotw) {
+    const float* o = st + slotw * kStateFloats;
+    const float mb = o[32 * kOStride + 2 * i], lb = o[32 * kOStride + 2 * i + 1];
+    const float M = fmaxf(m, mb);
+    const float wa = weight(m, M), wb = weight(mb, M);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f4 v = *reinterpret_cast<const f4*>(o + i * kOStride + 32 * nb + 8 * g + 4 * half);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[nb][4 * g + e] = wa * acc[nb][4 * g + e] + wb * v[e];
+      }
+    m = M;
+    l = wa * l + wb * lb;
+  };
+  if (wave >= 2) put(wave - 2);
   __syncthreads();
-
-  const int row = threadIdx.x >> 3, d0 = (threadIdx.x & 7) * 16;
-  if (row < n_rows) {
-    float M = -INFINITY;
+  if (wave < 2) take(wave);
+  __syncthreads();
+  if (wave == 1) put(0);
+  __syncthreads();
+  if (wave != 0) return;
+  take(0);
+  if (i < n_rows) {
+    const size_t pid = static_cast<size_t>(part_base + i) * H + head;
+    float* po = a.part_o + pid * D;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, lds_m[w][row]);
-    float wt[4], s = 0.f;
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      wt[w] = exp2f(lds_m[w][row] - M);
-      s += wt[w] * lds_l[w][row];
+      for (int g = 0; g < 4; ++g) {
+        f4 v = {acc[nb][4 * g + 0], acc[nb][4 * g + 1], acc[nb][4 * g + 2], acc[nb][4 * g + 3]};
+        float* dst = po + 32 * nb + 8 * g + 4 * half;
+        if constexpr (kFuse) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) store_agent(dst + e, v[e]);
+        } else {
+          *reinterpret_cast<f4*>(dst) = v;
+        }
+      }
+    if (half == 0) {
+      if constexpr (kFuse) {
+        store_agent(a.part_ms + pid * 2 + 0, m);
+        store_agent(a.part_ms + pid * 2 + 1, l);
+      } else {
+        a.part_ms[pid * 2 + 0] = m;
+        a.part_ms[pid * 2 + 1] = l;
+      }
     }
-    const size_t pid = static_cast<size_t>(part_base + row) * H + head;
-    float* po = a.part_o + pid * D + d0;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f4 o = f4{};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) o += wt[w] * *reinterpret_cast<const f4*>(&lds_o[w][row][d0 + 4 * g]);
-      *reinterpret_cast<f4*>(po + 4 * g) = o;
-    }
-    if ((threadIdx.x & 7) == 0) {
-      a.part_ms[pid * 2 + 0] = M;
-      a.part_ms[pid * 2 + 1] = s;
-    }
+  }
+  if constexpr (!kFuse) return;
+  wait_stores();
+  const bool last = half == 0 && i < n_rows && arrive(a, row_begin + i, head);
+  uint64_t todo = __ballot(last);
+  while (todo) {
+    const int r = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    merge_and_reset(a, row_begin + r, head, lane);
   }
 }
 
-// ---------------------------------------------------------------------------
-// Sequence-first: one block per (task = some private chunks of one sequence,
-// head).  Wave w takes chunks w, w+4, ...  Lane (half, i): for K it holds
-// dims [16kk + 8half, +8) of keys i and 32+i, so a score needs one exchange
-// with the twin lane; for V it holds dims 32nb + i at 8 keys per load, and
-// reads the matching probabilities from a 64-entry LDS row.
-__global__ __launch_bounds__(256) void sequence_first_kernel(StepArgs a) {
-  const int task = blockIdx.x % a.n_sf_tasks, head = blockIdx.x / a.n_sf_tasks;
+// Sequence-first: task = some private chunks of one sequence, one head.
+// Lane (half, i): for K it holds dims [16kk + 8half, +8) of keys i and 32+i,
+// so a score needs one exchange with the twin lane; for V it holds dim
+// 32nb + i at 8 keys per load and reads the matching probabilities from a
+// 64-entry LDS row of its wave.  Three waves per SIMD keep about 384 KiB of
+// loads in flight per CU.
+template <bool kFuse>
+__device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logical) {
+  const int task = logical % a.n_sf_tasks, head = logical / a.n_sf_tasks;
   const int* t = a.sf_tasks + task * 4;
   const int chunk_begin = t[0], n_chunks = t[1], dfs_pos = t[2], part_id = t[3];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, i = lane & 31;
+  // wave index in an SGPR: chunk lookups and tile bases stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, half = lane >> 5, i = lane & 31;
   const int H = a.heads;
   const _Float16* pool = static_cast<const _Float16*>(a.pool);
 
-  h8 qv[8];
-  {
+  // The query row is the same for the four waves: keep it in LDS (256 B)
+  // rather than in 32 VGPRs of every lane.
+  __shared__ __attribute__((aligned(16))) _Float16 q_lds[D];
+  if (threadIdx.x < D / 8) {
     const int qrow = a.dfs_qrow[dfs_pos];
     const _Float16* qp = static_cast<const _Float16*>(a.q) + (static_cast<size_t>(qrow) * H + head) * D;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qv[kk] = *reinterpret_cast<const h8*>(qp + kk * 16 + half * 8);
+    *reinterpret_cast<h8*>(q_lds + threadIdx.x * 8) = *reinterpret_cast<const h8*>(qp + threadIdx.x * 8);
   }
+  __syncthreads();
 
   __shared__ float p_lds[4][64];
   float m = -INFINITY, l = 0.f;
@@ -301,18 +465,20 @@ __global__ __launch_bounds__(256) void sequence_first_kernel(StepArgs a) {
 
     float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
+    for (int kk = 0; kk < 8; ++kk) {
+      const h8 qv = *reinterpret_cast<const h8*>(q_lds + kk * 16 + half * 8);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        d0 = __builtin_amdgcn_fdot2(lo2(ka[kk], j), lo2(qv[kk], j), d0, false);
-        d1 = __builtin_amdgcn_fdot2(lo2(ka[8 + kk], j), lo2(qv[kk], j), d1, false);
+        d0 = __builtin_amdgcn_fdot2(lo2(ka[kk], j), lo2(qv, j), d0, false);
+        d1 = __builtin_amdgcn_fdot2(lo2(ka[8 + kk], j), lo2(qv, j), d1, false);
       }
+    }
     d0 += __shfl_xor(d0, 32);
     d1 += __shfl_xor(d1, 32);
     const float x0 = i < nvalid ? d0 * a.scale_log2e : -INFINITY;
     const float x1 = i + 32 < nvalid ? d1 * a.scale_log2e : -INFINITY;
     const float mx = wave_max32(fmaxf(x0, x1));
-    const float mnew = fmaxf(m, mx);
+    const float mnew = fmaxf(m, mx);  // finite: key 0 of a chunk is always filled
     const float alpha = exp2f(m - mnew);
     const float p0 = exp2f(x0 - mnew), p1 = exp2f(x1 - mnew);
     l = l * alpha + (half == 0 ? p0 + p1 : 0.f);
@@ -365,7 +531,8 @@ __global__ __launch_bounds__(256) void sequence_first_kernel(StepArgs a) {
   }
   __syncthreads();
   if (threadIdx.x < D) {
-    float M = fmaxf(fmaxf(w_m[0], w_m[1]), fmaxf(w_m[2], w_m[3]));
+    // wave 0 always has a chunk, so M is finite and empty waves weigh 0
+    const float M = fmaxf(fmaxf(w_m[0], w_m[1]), fmaxf(w_m[2], w_m[3]));
     float o = 0.f, s = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -374,43 +541,47 @@ __global__ __launch_bounds__(256) void sequence_first_kernel(StepArgs a) {
       s += wt * w_l[w];
     }
     const size_t pid = static_cast<size_t>(part_id) * H + head;
-    a.part_o[pid * D + threadIdx.x] = o;
-    if (threadIdx.x == 0) {
-      a.part_ms[pid * 2 + 0] = M;
-      a.part_ms[pid * 2 + 1] = s;
+    if constexpr (kFuse) {
+      store_agent(a.part_o + pid * D + threadIdx.x, o);
+      if (threadIdx.x == 0) {
+        store_agent(a.part_ms + pid * 2 + 0, M);
+        store_agent(a.part_ms + pid * 2 + 1, s);
+      }
+      wait_stores();
+    } else {
+      a.part_o[pid * D + threadIdx.x] = o;
+      if (threadIdx.x == 0) {
+        a.part_ms[pid * 2 + 0] = M;
+        a.part_ms[pid * 2 + 1] = s;
+      }
     }
   }
+  if constexpr (!kFuse) return;
+  __shared__ int is_last;
+  __syncthreads();
+  if (threadIdx.x == 0) is_last = arrive(a, dfs_pos, head);
+  __syncthreads();
+  if (is_last && wave == 0) merge_and_reset(a, dfs_pos, head, lane);
 }
 
-// ---------------------------------------------------------------------------
-// Merge: one wave per (sequence, head).  Folds the sequence's partials in the
-// fixed order of its list (shared runs root first, then private tasks):
-// M = max m_j, o = sum e^{m_j - M} o_j, s = sum e^{m_j - M} s_j, out = o / s.
-__global__ __launch_bounds__(64) void merge_kernel(StepArgs a) {
-  const int H = a.heads;
-  const int pos = blockIdx.x / H, head = blockIdx.x % H, lane = threadIdx.x;
-  const int first = a.seq_parts[2 * pos], cnt = a.seq_parts[2 * pos + 1];
-  float M = -INFINITY;
-  for (int j = lane; j < cnt; j += 64) {
-    const size_t pid = static_cast<size_t>(a.part_list[first + j]) * H + head;
-    M = fmaxf(M, a.part_ms[pid * 2]);
-  }
-  M = fmaxf(M, __shfl_xor(M, 32));
-  M = wave_max32(M);
-  float s = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int j = 0; j < cnt; ++j) {
-    const size_t pid = static_cast<size_t>(a.part_list[first + j]) * H + head;
-    const float wt = exp2f(a.part_ms[pid * 2] - M);
-    s += wt * a.part_ms[pid * 2 + 1];
-    const float2 o = *reinterpret_cast<const float2*>(a.part_o + pid * D + 2 * lane);
-    o0 += wt * o.x;
-    o1 += wt * o.y;
-  }
-  const float inv = 1.0f / s;
-  const int qrow = a.dfs_qrow[pos];
-  _Float16* out = static_cast<_Float16*>(a.out) + (static_cast<size_t>(qrow) * H + head) * D + 2 * lane;
-  h2 r = {static_cast<_Float16>(o0 * inv), static_cast<_Float16>(o1 * inv)};
-  *reinterpret_cast<h2*>(out) = r;
+// n_cf: chunk-first blocks of the step; first: index of this launch's first
+// block in the step's grid (0, or n_cf to launch only the sequence-first part).
+// kFuse: also merge (last block per (sequence, head)): the launch is the step.
+template <bool kFuse>
+__global__ __launch_bounds__(256, 3) void partials_kernel(StepArgs a, int n_cf, int first) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int b = blockIdx.x + first;
+  if (b < n_cf)
+    chunk_first_block<kFuse>(a, xcd_remap(b, n_cf), smem);
+  else
+    sequence_first_block<kFuse>(a, b - n_cf);
+}
+
+// Merge of every (sequence, head), four per block (the unfused step).
+__global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= a.n_seq * a.heads) return;
+  merge_one<false>(a, item / a.heads, item % a.heads, threadIdx.x & 63);
 }
 
 }  // namespace
@@ -425,24 +596,23 @@ int launch_kv_write(void* pool, int heads, const KvOpBatch& batch, int n_ops, co
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_chunk_first(const StepArgs& a, void* stream) {
-  if (a.n_cf_units <= 0) return 0;
-  dim3 grid(a.n_cf_units * a.heads);
-  hipLaunchKernelGGL(chunk_first_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
-  return static_cast<int>(hipGetLastError());
-}
-
-int launch_sequence_first(const StepArgs& a, void* stream) {
-  if (a.n_sf_tasks <= 0) return 0;
-  dim3 grid(a.n_sf_tasks * a.heads);
-  hipLaunchKernelGGL(sequence_first_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
+int launch_partials(const StepArgs& a, int part, bool fuse_merge, void* stream) {
+  const int n_cf = a.n_cf_units * a.heads, n_sf = a.n_sf_tasks * a.heads;
+  const int first = part == kPartsSequenceFirst ? n_cf : 0;
+  const int count = part == kPartsChunkFirst ? n_cf : part == kPartsSequenceFirst ? n_sf : n_cf + n_sf;
+  if (count <= 0) return 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fuse_merge && part == kPartsBoth)
+    hipLaunchKernelGGL(partials_kernel<true>, dim3(count), dim3(256), 0, st, a, n_cf, first);
+  else
+    hipLaunchKernelGGL(partials_kernel<false>, dim3(count), dim3(256), 0, st, a, n_cf, first);
   return static_cast<int>(hipGetLastError());
 }
 
 int launch_merge(const StepArgs& a, void* stream) {
   if (a.n_seq <= 0) return 0;
-  dim3 grid(a.n_seq * a.heads);
-  hipLaunchKernelGGL(merge_kernel, grid, dim3(64), 0, static_cast<hipStream_t>(stream), a);
+  dim3 grid((a.n_seq * a.heads + 3) / 4);
+  hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -67,15 +67,24 @@ enum {
 
 /* ca_set_option keys. */
 enum {
-  CA_OPT_CF_CHUNKS_PER_TASK = 1, /* chunks of one shared run per chunk-first task (1..64), default 4 */
-  CA_OPT_SF_CHUNKS_PER_TASK = 2  /* private chunks per sequence-first task (1..256), default 8 */
+  CA_OPT_CF_CHUNKS_PER_TASK = 1, /* chunks of one shared run per chunk-first task (1..64), default 8 */
+  CA_OPT_SF_CHUNKS_PER_TASK = 2, /* private chunks per sequence-first task (1..256), default 4 */
+  CA_OPT_FUSED_MERGE = 3         /* 0 (default): a step is a partials launch and a merge launch;
+                                    1: one launch, the last block to finish a (sequence, head)
+                                    merges it (slower today: each block ends with dependent
+                                    round trips to memory) */
 };
 
-/* ca_attend_phase phases (the three kernels of one step, in order). */
+/* ca_attend_phase phases.  A step is CA_PHASE_PARTIALS (one launch holding
+ * the chunk-first and the sequence-first work) followed by CA_PHASE_MERGE.
+ * CA_PHASE_CHUNK_FIRST and CA_PHASE_SEQUENCE_FIRST launch only one side of
+ * the partials launch, to time the two phases apart; run both (either order)
+ * in place of CA_PHASE_PARTIALS. */
 enum {
   CA_PHASE_CHUNK_FIRST = 1,
   CA_PHASE_SEQUENCE_FIRST = 2,
-  CA_PHASE_MERGE = 3
+  CA_PHASE_MERGE = 3,
+  CA_PHASE_PARTIALS = 4
 };
 
 typedef struct ca_ctx ca_ctx;
@@ -165,15 +174,21 @@ int ca_remove(ca_ctx* ctx, int64_t seq_id);
 /* One decode step.  q_dev: fp16 [n_live][heads][head_dim]; out_dev: fp16
  * [n_live][heads][head_dim]; row r belongs to the r-th live sequence in
  * ascending seq_id order (ca_list_sequences).  Uploads the chunk table if the
- * tree changed since the last upload, then enqueues the chunk-first,
- * sequence-first and merge kernels on `stream`.  No host synchronisation.
+ * tree changed since the last upload, then enqueues the step on `stream`: one
+ * launch whose blocks compute the chunk-first and sequence-first partials and
+ * whose last block per (sequence, head) merges them (CA_OPT_FUSED_MERGE), or
+ * a partials launch and a merge launch.  The result does not depend on which
+ * block finishes last: the merge folds the partials in a fixed order.  Steps
+ * of one context must not overlap (they share the workspace).  No host
+ * synchronisation.
  * Errors: CA_E_EMPTY, CA_E_WORKSPACE, CA_E_NO_POOL, CA_E_HIP. */
 int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream);
 
-/* The same step split into its parts, for measuring each kernel: call
+/* The same step split into its launches, for measuring each kernel: call
  * ca_prepare once (uploads the table if needed), then ca_attend_phase with
- * CA_PHASE_CHUNK_FIRST, CA_PHASE_SEQUENCE_FIRST and CA_PHASE_MERGE in that
- * order on one stream.  Same arguments and errors as ca_attend. */
+ * CA_PHASE_PARTIALS (or CA_PHASE_CHUNK_FIRST and CA_PHASE_SEQUENCE_FIRST)
+ * and then CA_PHASE_MERGE, on one stream.  Same arguments and errors as
+ * ca_attend, plus CA_E_INVALID_ARG for an unknown phase. */
 int ca_prepare(ca_ctx* ctx, void* stream);
 int ca_attend_phase(ca_ctx* ctx, int phase, const void* q_dev, void* out_dev, void* stream);
 

@@ -198,6 +198,11 @@ def test_phases_equal_fused_call():
         ca.attend_phase(ph, q, out)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+    out2 = torch.empty_like(q)
+    for ph in (_capi.CA_PHASE_PARTIALS, _capi.CA_PHASE_MERGE):
+        ca.attend_phase(ph, q, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, ref)
 
 
 def test_errors_on_device_context():
@@ -213,3 +218,56 @@ def test_errors_on_device_context():
     with pytest.raises(CaError) as ei:
         ca.insert(1, list(range(200)), k, k)
     assert ei.value.name == "no_capacity"
+
+
+@pytest.mark.parametrize("name", ["config1", "shared_R70", "deep_random", "interior_and_dups"])
+def test_fused_merge_matches_two_launch_step(name):
+    """The one-launch step (last block per (sequence, head) merges) equals the
+    partials + merge launches bit for bit, step after step (the arrival
+    counters must return to zero) and after the tree changes."""
+    _say(f"fused merge {name}")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import _capi
+    if name == "config1":
+        wl = cached_config(1)
+    else:
+        wl = from_token_lists(tiny_tree_cases()[name], heads=3, seed=21)
+    ca = build_ca(wl, capacity=None)
+    q = torch.from_numpy(np.ascontiguousarray(wl.q)).cuda()
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 0)
+    ref = ca.attend(q).clone()
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 1)
+    for _ in range(4):
+        got = ca.attend(q)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref)
+    assert_parity(got.cpu().numpy(), A.decode_workload(wl), f"fused {name}")
+    # a tree change re-uploads the table (and zeroed counters)
+    extra = [10**6 + j for j in range(70)]
+    k = torch.zeros((70, wl.heads, 128), dtype=torch.float16, device="cuda:0")
+    ca.insert(10**5, extra, k, k)
+    q2 = torch.cat([q, torch.zeros((1, wl.heads, 128), dtype=torch.float16, device="cuda:0")])
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 0)
+    ref2 = ca.attend(q2).clone()
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 1)
+    for _ in range(3):
+        assert torch.equal(ca.attend(q2), ref2)
+
+
+def test_more_than_64_partials_per_sequence():
+    """One private chunk per sequence-first task and long sequences: the merge
+    folds more than 64 partials per (sequence, head) in several rounds."""
+    _say("many partials")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import _capi
+    rng = np.random.default_rng(8)
+    shared = list(range(64 * 3 + 7))
+    seqs = [shared + [9000 + i] + list(rng.integers(0, 7, size=64 * 70 + int(rng.integers(0, 64))))
+            for i in range(3)]
+    wl = from_token_lists(seqs, heads=2, seed=4)
+    ca = build_ca(wl, cf_group=1, sf_group=1)
+    assert ca.stats()["partials"] > 3 * 64
+    got = run_step(ca, wl.q)
+    assert_parity(got, A.decode_workload(wl), "many partials")
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 1)
+    assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
