@@ -170,8 +170,17 @@ def main():
     step_launches = (_capi.CA_PHASE_PARTIALS, _capi.CA_PHASE_MERGE)
     if args.profile_only:
         lt = time_launches(torch, ca, q, out, args.steps, flush, step_launches)
+        # Calibration for hardware byte counters: a plain device copy of a known
+        # size (256 MiB read + 256 MiB written), cold like the steps.
+        src = torch.ones(1 << 27, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            flush()
+            dst.copy_(src)
+        torch.cuda.synchronize()
         print(json.dumps({"launch_us_mean": {"partials_kernel": float(lt[:, 0].mean()) * 1e3,
                                              "merge_kernel": float(lt[:, 1].mean()) * 1e3},
+                          "unique_kv_bytes": st["unique_kv_bytes"], "copy_calibration_bytes": src.numel() * 2,
                           "steps": args.steps, "config": args.config}), flush=True)
         return
 

@@ -23,8 +23,8 @@ struct StepArgs {
   const void* pool;            // fp16 slots: [slot][head][K|V][64 x 128 tile]
   const void* q;               // fp16 [n_live][H][128], ascending seq id
   void* out;                   // fp16 [n_live][H][128]
-  const int32_t* cf_units;     // 8 ints per unit (CfUnit)
-  const int32_t* sf_tasks;     // 4 ints per task (SfTask)
+  const int32_t* cf_units;     // 32 ints per unit (CfUnit)
+  const int32_t* sf_tasks;     // 16 ints per task (SfTask)
   const int32_t* chunk_refs;   // (slot, n_valid) pairs
   const int32_t* dfs_qrow;     // caller row per DFS position
   const int32_t* seq_parts;    // (first, count) per DFS position

@@ -60,23 +60,51 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return xcd * q + min(xcd, r) + local;
 }
 
+// Cross-lane steps that need no address registers: DPP within quads and
+// rows of 16, ds_swizzle across the two rows of a 32-lane half, and gfx950's
+// v_permlane32_swap across the two halves of the wave.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+__device__ __forceinline__ float swap16(float x) {  // lane i <- lane i^16, within 32
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+
+// x[i] + x[i^32] (or the max) on every lane: the swap leaves the low half's
+// values in one result and the high half's in the other, on all 64 lanes.
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(p[0]) + __int_as_float(p[1]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+}
+
+// max over the 32 lanes of each half-wave (butterfly: once quads agree, the
+// mirrors pair lanes of different groups)
 __device__ __forceinline__ float wave_max32(float x) {
-  // max over the 32 lanes of each half-wave
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 8));
-  x = fmaxf(x, __shfl_xor(x, 4));
-  x = fmaxf(x, __shfl_xor(x, 2));
-  x = fmaxf(x, __shfl_xor(x, 1));
+  x = fmaxf(x, dpp<kQuadXor1>(x));
+  x = fmaxf(x, dpp<kQuadXor2>(x));
+  x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kRowMirror>(x));
+  x = fmaxf(x, swap16(x));
   return x;
 }
 
 __device__ __forceinline__ float wave_sum64(float x) {
-  x += __shfl_xor(x, 32);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 8);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 1);
+  x = sum_halves(x);
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  x += dpp<kRowHalfMirror>(x);
+  x += dpp<kRowMirror>(x);
+  x += swap16(x);
   return x;
 }
 
@@ -175,7 +203,7 @@ __device__ __forceinline__ void merge_one(const StepArgs& a, int pos, int head, 
       my_m = ld<kCoherent>(a.part_ms + pid * 2);
       my_s = ld<kCoherent>(a.part_ms + pid * 2 + 1);
     }
-    float Mr = fmaxf(my_m, __shfl_xor(my_m, 32));
+    float Mr = max_halves(my_m);
     Mr = fmaxf(M, wave_max32(Mr));
     // rescale what earlier rounds accumulated (only with more than 64 partials)
     const float r = M == -INFINITY ? 0.f : exp2f(M - Mr);
@@ -192,8 +220,8 @@ __device__ __forceinline__ void merge_one(const StepArgs& a, int pos, int head, 
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int jj = min(j + u, n - 1);
-        wv[u] = j + u < n ? __shfl(my_w, jj) : 0.f;
-        const size_t pid = static_cast<size_t>(__shfl(my_pid, jj)) * H + head;
+        wv[u] = j + u < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), jj)) : 0.f;
+        const size_t pid = static_cast<size_t>(__builtin_amdgcn_readlane(my_pid, jj)) * H + head;
         const float* src = a.part_o + pid * D + 2 * lane;
         if constexpr (kCoherent) {
           ov[u].x = load_agent(src);
@@ -258,7 +286,7 @@ __device__ __forceinline__ float weight(float m, float M) {
 template <bool kFuse>
 __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical, char* smem) {
   const int unit = logical % a.n_cf_units, head = logical / a.n_cf_units;
-  const int* u = a.cf_units + unit * 8;
+  const int* u = a.cf_units + unit * 32;
   const int chunk_begin = u[0], n_chunks = u[1], row_begin = u[2], n_rows = u[3], part_base = u[4];
   // wave index in an SGPR: chunk lookups and tile bases stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -287,8 +315,8 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
   for (int nb = 0; nb < 4; ++nb) acc[nb] = f16v{};
 
   for (int c = wave; c < n_chunks; c += 4) {
-    const int slot = a.chunk_refs[2 * (chunk_begin + c)];
-    const int nvalid = a.chunk_refs[2 * (chunk_begin + c) + 1];
+    const int slot = c < 8 ? u[8 + c] : a.chunk_refs[2 * (chunk_begin + c)];
+    const int nvalid = c < 8 ? u[16 + c] : a.chunk_refs[2 * (chunk_begin + c) + 1];
     const _Float16* kt = pool + tile_base(slot, head, H, 0);
     const _Float16* vt = kt + TILE;
     // The halves stay a loop: unrolled, the second half's loads would be
@@ -319,7 +347,7 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
         sc[r] = x;
         mx = fmaxf(mx, x);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_halves(mx);
       const float mnew = fmaxf(m, mx);
       if (mnew == -INFINITY) continue;  // every key of this half is past the fill
       const float alpha = weight(m, mnew);
@@ -342,7 +370,7 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
       }
     }
   }
-  l += __shfl_xor(l, 32);
+  l = sum_halves(l);
 
   // Pairwise merge of the four wave states: (w0 + w2) + (w1 + w3).
   float* st = reinterpret_cast<float*>(smem + kQBytes);
@@ -430,8 +458,8 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
 template <bool kFuse>
 __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logical) {
   const int task = logical % a.n_sf_tasks, head = logical / a.n_sf_tasks;
-  const int* t = a.sf_tasks + task * 4;
-  const int chunk_begin = t[0], n_chunks = t[1], dfs_pos = t[2], part_id = t[3];
+  const int* t = a.sf_tasks + task * 16;
+  const int chunk_begin = t[0], n_chunks = t[1], dfs_pos = t[2], part_id = t[3], qrow = t[4];
   // wave index in an SGPR: chunk lookups and tile bases stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, half = lane >> 5, i = lane & 31;
@@ -442,7 +470,6 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
   // rather than in 32 VGPRs of every lane.
   __shared__ __attribute__((aligned(16))) _Float16 q_lds[D];
   if (threadIdx.x < D / 8) {
-    const int qrow = a.dfs_qrow[dfs_pos];
     const _Float16* qp = static_cast<const _Float16*>(a.q) + (static_cast<size_t>(qrow) * H + head) * D;
     *reinterpret_cast<h8*>(q_lds + threadIdx.x * 8) = *reinterpret_cast<const h8*>(qp + threadIdx.x * 8);
   }
@@ -453,8 +480,8 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 
   for (int c = wave; c < n_chunks; c += 4) {
-    const int slot = a.chunk_refs[2 * (chunk_begin + c)];
-    const int nvalid = a.chunk_refs[2 * (chunk_begin + c) + 1];
+    const int slot = c < 4 ? t[8 + c] : a.chunk_refs[2 * (chunk_begin + c)];
+    const int nvalid = c < 4 ? t[12 + c] : a.chunk_refs[2 * (chunk_begin + c) + 1];
     const _Float16* kt = pool + tile_base(slot, head, H, 0);
     const _Float16* vt = kt + TILE;
     h8 ka[16], va[16];
@@ -473,8 +500,8 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
         d1 = __builtin_amdgcn_fdot2(lo2(ka[8 + kk], j), lo2(qv, j), d1, false);
       }
     }
-    d0 += __shfl_xor(d0, 32);
-    d1 += __shfl_xor(d1, 32);
+    d0 = sum_halves(d0);
+    d1 = sum_halves(d1);
     const float x0 = i < nvalid ? d0 * a.scale_log2e : -INFINITY;
     const float x1 = i + 32 < nvalid ? d1 * a.scale_log2e : -INFINITY;
     const float mx = wave_max32(fmaxf(x0, x1));
@@ -516,7 +543,7 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) acc[nb] += __shfl_xor(acc[nb], 32);
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = sum_halves(acc[nb]);
   l = wave_sum64(l);
 
   __shared__ float w_o[4][D];

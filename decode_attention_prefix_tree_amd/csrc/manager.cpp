@@ -284,6 +284,10 @@ void Manager::build_plan(int cf_group, int sf_group, Plan* plan) const {
         u.row_begin = tasks[t].b + rb * 32;
         u.n_rows = std::min(32, tasks[t].e - tasks[t].b - rb * 32);
         u.part_base = tasks[t].part_base + rb * 32;
+        for (int c = 0; c < kCfInline && c < u.n_chunks; ++c) {
+          u.slot[c] = P.chunk_refs[2 * (u.chunk_begin + c)];
+          u.n_valid[c] = P.chunk_refs[2 * (u.chunk_begin + c) + 1];
+        }
         P.cf_units.push_back(u);
       }
     }
@@ -318,7 +322,13 @@ void Manager::build_plan(int cf_group, int sf_group, Plan* plan) const {
       st.n_chunks = static_cast<int32_t>(stop - j);
       st.dfs_pos = i;
       st.part_id = P.n_parts++;
+      st.qrow = P.dfs_qrow[i];
       for (size_t q = j; q < stop; ++q) {
+        const int c = static_cast<int>(q - j);
+        if (c < kSfInline) {
+          st.slot[c] = R(priv[q], 6);
+          st.n_valid[c] = R(priv[q], 3);
+        }
         P.chunk_refs.push_back(R(priv[q], 6));
         P.chunk_refs.push_back(R(priv[q], 3));
       }

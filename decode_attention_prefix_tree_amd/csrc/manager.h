@@ -57,20 +57,35 @@ struct KvOp {
 
 // Per-step work plan built from the DFS order.  All ids are int32 so the
 // arrays go to the device as they are.
+// Records are read by a block with one scalar load; the first chunk refs of
+// the task ride along, so a block can start its tile loads after a single
+// round trip to memory.
+constexpr int kCfInline = 8;   // chunk refs carried by a chunk-first unit
+constexpr int kSfInline = 4;   // chunk refs carried by a sequence-first task
+
 struct CfUnit {        // chunk-first: one 32-row block of one run of shared chunks
-  int32_t chunk_begin; // into chunk_refs (pairs)
+  int32_t chunk_begin; // into chunk_refs (pairs); refs past kCfInline are read there
   int32_t n_chunks;
   int32_t row_begin;   // DFS position of the block's first row
   int32_t n_rows;      // 1..32
   int32_t part_base;   // partial id of the block's first row
   int32_t pad[3];
+  int32_t slot[kCfInline];
+  int32_t n_valid[kCfInline];
+  int32_t pad2[8];     // 128 bytes
 };
 struct SfTask {        // sequence-first: some private chunks of one sequence
-  int32_t chunk_begin;
+  int32_t chunk_begin; // into chunk_refs; refs past kSfInline are read there
   int32_t n_chunks;
   int32_t dfs_pos;
   int32_t part_id;
+  int32_t qrow;        // caller row of the sequence
+  int32_t pad[3];
+  int32_t slot[kSfInline];
+  int32_t n_valid[kSfInline];  // 64 bytes
 };
+
+static_assert(sizeof(CfUnit) == 128 && sizeof(SfTask) == 64, "record layouts are read by the kernels");
 
 struct Plan {
   std::vector<int32_t> rows;        // canonical table, 7 ints per row
