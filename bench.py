@@ -97,6 +97,26 @@ def time_launches(torch, ca, q, out, steps, flush, phases):
     return np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(len(phases))] for i in range(steps)])
 
 
+def recorded_traffic(config):
+    """HBM bytes per partials launch from the committed counter summary, if it
+    was taken on this workload with the kernel source as it is now; else None."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    prof = os.path.join(root, "profiles", f"partials_kernel_workload{config}_traffic.md")
+    src = os.path.join(root, "decode_attention_prefix_tree_amd", "csrc", "kernels.hip")
+    if not os.path.exists(prof):
+        return None
+    fields = {}
+    for line in open(prof):
+        if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_launch", "kernel_source_sha256"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != digest:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(wl, seconds_target):
     """fp64 oracle on a bounded sample of rows, threads over sequences."""
     from concurrent.futures import ThreadPoolExecutor
@@ -209,7 +229,7 @@ def main():
     # unique KV bytes (each shared chunk once, each private chunk once).
     dom_t = float(lt[:, 0].mean()) * 1e-3
     roof = {"kernel": "partials_kernel", "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
-            "achieved": unique_b / dom_t / 1e9, "traffic": None,
+            "achieved": unique_b / dom_t / 1e9, "traffic": recorded_traffic(args.config),
             "bytes_per_launch": unique_b, "avg_launch_us": dom_t * 1e6}
     roof["frac"] = roof["achieved"] / HBM_PEAK_GBPS
 
