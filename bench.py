@@ -265,25 +265,37 @@ def main():
     }
 
     if not args.no_comparator:
+        def comparator(kind, **kw):
+            cmp_ca = ChunkAttention(wl.heads, slots_needed(wl, share=kw.get("share", True)) + 8,
+                                    device="cuda:0", **kw)
+            load_workload(cmp_ca, wl)
+            cmp_ca.ensure_workspace()
+            out2 = torch.empty_like(q)
+
+            def cstep():
+                cmp_ca.attend(q, out2)
+
+            for _ in range(args.warmup):
+                cstep()
+            cc = time_steps(torch, cstep, args.steps, flush)
+            tc = float(cc.mean()) * 1e-3
+            cst = cmp_ca.stats()
+            res = {"kind": kind, "ms_per_step": tc * 1e3, "attended_tokens_per_s": cst["attended_tokens"] / tc,
+                   "stored_kv_gbps": cst["unique_kv_bytes"] / tc / 1e9,
+                   "read_kv_gbps": (cst["sf_chunk_reads"] + cst["cf_chunk_reads"]) * 4 * 64 * wl.heads * 128
+                   / tc / 1e9,
+                   "speedup": tc / t_mean}
+            del cmp_ca
+            torch.cuda.synchronize()
+            return res
+
         log("comparator: unshared paged layout")
-        cmp_ca = ChunkAttention(wl.heads, slots_needed(wl, share=False) + 8, device="cuda:0", share=False)
-        load_workload(cmp_ca, wl)
-        cmp_ca.ensure_workspace()
-        out2 = torch.empty_like(q)
-
-        def cstep():
-            cmp_ca.attend(q, out2)
-
-        for _ in range(args.warmup):
-            cstep()
-        cc = time_steps(torch, cstep, args.steps, flush)
-        tc = float(cc.mean()) * 1e-3
-        cst = cmp_ca.stats()
-        result["comparator"] = {
-            "kind": "unshared paged decode (own HIP kernel, 64-token blocks per sequence)",
-            "ms_per_step": tc * 1e3, "attended_tokens_per_s": cst["attended_tokens"] / tc,
-            "attended_kv_gbps": cst["attended_kv_bytes"] / tc / 1e9, "speedup": tc / t_mean}
-        del cmp_ca
+        result["comparator"] = comparator(
+            "unshared paged decode (own HIP kernel, every sequence keeps its own 64-token blocks)", share=False)
+        log("comparator: shared pages, no chunk-first phase")
+        result["comparator_shared_pages"] = comparator(
+            "shared pages without two-phase partition (prefix stored once, every sequence streams its "
+            "whole path)", two_phase=False)
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

@@ -16,6 +16,7 @@ HEADER = os.path.join(ROOT, "include", "chunkattn.h")
 
 CA_OK = 0
 CA_CREATE_UNSHARED = 1
+CA_CREATE_NO_CHUNK_FIRST = 2
 CA_OPT_CF_CHUNKS_PER_TASK = 1
 CA_OPT_SF_CHUNKS_PER_TASK = 2
 CA_OPT_FUSED_MERGE = 3
@@ -58,6 +59,7 @@ class ca_stats_t(ctypes.Structure):
         ("attended_kv_bytes", ctypes.c_int64),
         ("shared_tokens", ctypes.c_int64),
         ("private_tokens", ctypes.c_int64),
+        ("fill_refreshes", ctypes.c_int64),
     ]
 
 
@@ -75,6 +77,8 @@ _SIGS = {
                              _c.c_void_p, _c.c_void_p, _c.POINTER(_c.c_int32)]),
     "ca_append": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.POINTER(_c.c_int32), _c.c_int32, _c.c_void_p,
                              _c.c_void_p, _c.c_void_p]),
+    "ca_append_batch": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.POINTER(_c.c_int64), _c.POINTER(_c.c_int32),
+                                   _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "ca_remove": (_c.c_int, [_c.c_void_p, _c.c_int64]),
     "ca_attend": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "ca_prepare": (_c.c_int, [_c.c_void_p, _c.c_void_p]),

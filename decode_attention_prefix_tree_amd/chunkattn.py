@@ -38,15 +38,17 @@ class ChunkAttention:
     heads: head count; capacity_slots: pool size in 64-token chunk slots.
     device: a torch device for the pool, or None for a host-only context
     (tree and tables only; attend is unavailable).  share=False builds the
-    unshared paged layout (every sequence keeps its own chunks).
+    unshared paged layout (every sequence keeps its own chunks);
+    two_phase=False keeps the shared layout but runs no chunk-first phase
+    (every sequence streams its whole path).
     """
 
     def __init__(self, heads: int, capacity_slots: int, device="cuda", share: bool = True,
-                 head_dim: int = HEAD_DIM, chunk_size: int = CHUNK):
+                 head_dim: int = HEAD_DIM, chunk_size: int = CHUNK, two_phase: bool = True):
         self.lib = load()
         self.heads, self.head_dim, self.chunk = heads, head_dim, chunk_size
         ctx = ctypes.c_void_p()
-        flags = 0 if share else _capi.CA_CREATE_UNSHARED
+        flags = (0 if share else _capi.CA_CREATE_UNSHARED) | (0 if two_phase else _capi.CA_CREATE_NO_CHUNK_FIRST)
         rc = self.lib.ca_create_ex(heads, head_dim, chunk_size, flags, ctypes.byref(ctx))
         if rc != 0:
             raise CaError(rc, "ca_create_ex failed")
@@ -111,6 +113,17 @@ class ChunkAttention:
         t = _tokens(tokens)
         kp, vp = self._kv(k, v, len(t)) if len(t) else (None, None)
         check(self.ctx, self.lib.ca_append(self.ctx, seq_id, _ptr_i32(t), len(t), kp, vp, self._stream(stream)))
+
+    def append_batch(self, seq_ids, tokens, k=None, v=None, stream=None) -> None:
+        """One token per sequence: tokens[j] with K/V row j goes to seq_ids[j]."""
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64).reshape(-1))
+        t = _tokens(tokens)
+        if len(ids) != len(t):
+            raise ValueError("one token per sequence id")
+        kp, vp = self._kv(k, v, len(t)) if len(t) else (None, None)
+        check(self.ctx, self.lib.ca_append_batch(self.ctx, len(ids),
+                                                 ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                                 _ptr_i32(t), kp, vp, self._stream(stream)))
 
     def remove(self, seq_id: int) -> None:
         check(self.ctx, self.lib.ca_remove(self.ctx, seq_id))

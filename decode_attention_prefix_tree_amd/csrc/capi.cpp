@@ -27,6 +27,8 @@ struct ca_ctx {
   // plan cache: rebuilt after the tree changes, uploaded when stale
   chunkattn::Plan plan;
   bool plan_valid = false;
+  bool fills_stale = false;  // plan structure current, chunk fills grew since
+  int64_t fill_refreshes = 0;
   uint64_t version = 1, uploaded_version = 0;
   void* uploaded_ws = nullptr;
   size_t off_cf = 0, off_sf = 0, off_refs = 0, off_qrow = 0, off_seqparts = 0, off_partlist = 0;
@@ -74,10 +76,33 @@ void touch(ca_ctx* c) {
   c->version += 1;
 }
 
+// After appends: if they only grew chunks in place, the plan keeps its shape
+// and only its fill counts are refreshed; otherwise it is rebuilt.
+void touch_after_append(ca_ctx* c) {
+  if (c->plan_valid && c->mgr.fills_only()) {
+    c->fills_stale = true;
+    c->version += 1;
+  } else {
+    touch(c);
+  }
+}
+
 void ensure_plan(ca_ctx* c) {
-  if (c->plan_valid) return;
+  if (c->plan_valid) {
+    if (c->fills_stale) {
+      auto t0 = std::chrono::steady_clock::now();
+      c->mgr.refresh_fills(&c->plan);
+      c->fills_stale = false;
+      c->fill_refreshes += 1;
+      c->last_rebuild_ms =
+          std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    }
+    return;
+  }
   auto t0 = std::chrono::steady_clock::now();
-  c->mgr.build_plan(c->cf_group, c->sf_group, &c->plan);
+  c->mgr.build_plan(c->cf_group, c->sf_group, (c->flags & CA_CREATE_NO_CHUNK_FIRST) == 0, &c->plan);
+  c->mgr.clear_structural();
+  c->fills_stale = false;
   const chunkattn::Plan& p = c->plan;
   size_t off = 0;
   c->off_cf = off;
@@ -233,7 +258,7 @@ int ca_create_ex(int heads, int head_dim, int chunk_size, int flags, ca_ctx** ou
   *out = nullptr;
   if (heads < 1) return CA_E_INVALID_ARG;
   if (head_dim != chunkattn::kHeadDim || chunk_size != chunkattn::kChunk) return CA_E_UNSUPPORTED;
-  if (flags & ~CA_CREATE_UNSHARED) return CA_E_UNSUPPORTED;
+  if (flags & ~(CA_CREATE_UNSHARED | CA_CREATE_NO_CHUNK_FIRST)) return CA_E_UNSUPPORTED;
   try {
     *out = new ca_ctx(heads, head_dim, chunk_size, flags);
   } catch (...) {
@@ -326,7 +351,23 @@ int ca_append(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n, con
       throw Error(CA_E_INVALID_ARG, "k_dev and v_dev are required when a device pool is attached");
     std::vector<chunkattn::KvOp> ops;
     ctx->mgr.append(seq_id, tokens, n, &ops);
-    touch(ctx);
+    touch_after_append(ctx);
+    if (device) run_kv_ops(ctx, ops, k_dev, v_dev, stream);
+    return CA_OK;
+  });
+}
+
+int ca_append_batch(ca_ctx* ctx, int32_t n, const int64_t* seq_ids, const int32_t* tokens, const void* k_dev,
+                    const void* v_dev, void* stream) {
+  CA_GUARD(ctx, {
+    if (!ctx->pool_attached) throw Error(CA_E_NO_POOL, "attach a pool (or a NULL pool) first");
+    if (n < 1 || seq_ids == nullptr || tokens == nullptr) throw Error(CA_E_INVALID_ARG, "append batch needs n >= 1");
+    const bool device = ctx->pool != nullptr;
+    if (device && (k_dev == nullptr || v_dev == nullptr))
+      throw Error(CA_E_INVALID_ARG, "k_dev and v_dev are required when a device pool is attached");
+    std::vector<chunkattn::KvOp> ops;
+    ctx->mgr.append_batch(seq_ids, tokens, n, &ops);
+    touch_after_append(ctx);
     if (device) run_kv_ops(ctx, ops, k_dev, v_dev, stream);
     return CA_OK;
   });
@@ -438,6 +479,7 @@ int ca_stats(ca_ctx* ctx, ca_stats_t* out) {
     s.attended_kv_bytes = p.attended_tokens * per_tok;
     s.shared_tokens = p.shared_tokens;
     s.private_tokens = p.unique_tokens - p.shared_tokens;
+    s.fill_refreshes = ctx->fill_refreshes;
     *out = s;
     return CA_OK;
   });

@@ -8,7 +8,9 @@ namespace chunkattn {
 
 constexpr int kHeadDim = 128;
 constexpr int kChunk = 64;
-constexpr int kOpsPerLaunch = 32;
+constexpr int kOpsPerLaunch = 64;  // 2 KiB of kernel arguments
+constexpr int kCfInline = 8;   // chunk refs carried by a chunk-first unit record
+constexpr int kSfInline = 4;   // chunk refs carried by a sequence-first task record
 
 struct KvOpDev {
   int32_t dst_slot, dst_key0, n_rows, src_row0, src_slot, from_pool, zero_rest, pad;

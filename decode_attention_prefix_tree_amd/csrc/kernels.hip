@@ -315,8 +315,8 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
   for (int nb = 0; nb < 4; ++nb) acc[nb] = f16v{};
 
   for (int c = wave; c < n_chunks; c += 4) {
-    const int slot = c < 8 ? u[8 + c] : a.chunk_refs[2 * (chunk_begin + c)];
-    const int nvalid = c < 8 ? u[16 + c] : a.chunk_refs[2 * (chunk_begin + c) + 1];
+    const int slot = c < kCfInline ? u[8 + c] : a.chunk_refs[2 * (chunk_begin + c)];
+    const int nvalid = c < kCfInline ? u[16 + c] : a.chunk_refs[2 * (chunk_begin + c) + 1];
     const _Float16* kt = pool + tile_base(slot, head, H, 0);
     const _Float16* vt = kt + TILE;
     // The halves stay a loop: unrolled, the second half's loads would be
@@ -480,8 +480,8 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 
   for (int c = wave; c < n_chunks; c += 4) {
-    const int slot = c < 4 ? t[8 + c] : a.chunk_refs[2 * (chunk_begin + c)];
-    const int nvalid = c < 4 ? t[12 + c] : a.chunk_refs[2 * (chunk_begin + c) + 1];
+    const int slot = c < kSfInline ? t[8 + c] : a.chunk_refs[2 * (chunk_begin + c)];
+    const int nvalid = c < kSfInline ? t[12 + c] : a.chunk_refs[2 * (chunk_begin + c) + 1];
     const _Float16* kt = pool + tile_base(slot, head, H, 0);
     const _Float16* vt = kt + TILE;
     h8 ka[16], va[16];

@@ -122,10 +122,11 @@ int32_t Manager::insert(int64_t seq, const int32_t* tokens, int32_t n, std::vect
   end_[seq] = cur;
   len_[seq] = n;
   for (int32_t x = cur; x != 0; x = nodes_[x].parent) nodes_[x].ref += 1;
+  structural_ = true;
   return matched;
 }
 
-void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops) {
+void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops, int32_t src_base) {
   auto it = end_.find(seq);
   if (it == end_.end()) throw Error(kUnknownSeq, "sequence id not live");
   if (n < 1 || tokens == nullptr) throw Error(kInvalidArg, "append needs at least one token");
@@ -140,7 +141,7 @@ void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<
   if (take > 0) {
     Node& nd = nodes_[e];
     nd.tokens.insert(nd.tokens.end(), tokens, tokens + take);
-    if (ops) ops->push_back(KvOp{nd.slot, fill, take, 0, -1, 0, 0});
+    if (ops) ops->push_back(KvOp{nd.slot, fill, take, src_base, -1, 0, 0});
   }
   len_[seq] += n;
   if (take == n) return;
@@ -155,18 +156,37 @@ void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<
     nd.tokens.assign(tokens + i, tokens + i + piece);
     nd.ref = 1;
     nodes_[cur].children.push_back(idx);
-    if (ops) ops->push_back(KvOp{nd.slot, 0, piece, i, -1, 0, 1});
+    if (ops) ops->push_back(KvOp{nd.slot, 0, piece, src_base + i, -1, 0, 1});
     cur = idx;
     pos += piece;
     i += piece;
   }
   nodes_[cur].ended.push_back(seq);
   end_[seq] = cur;
+  structural_ = true;
+}
+
+void Manager::append_batch(const int64_t* seqs, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops) {
+  if (n < 1 || seqs == nullptr || tokens == nullptr) throw Error(kInvalidArg, "append batch needs n >= 1");
+  std::map<int64_t, int32_t> seen;
+  int64_t need = 0;
+  for (int32_t j = 0; j < n; ++j) {
+    auto it = end_.find(seqs[j]);
+    if (it == end_.end()) throw Error(kUnknownSeq, "sequence id not live: " + std::to_string(seqs[j]));
+    if (!seen.emplace(seqs[j], j).second) throw Error(kInvalidArg, "sequence id repeated in a batch");
+    const Node& e = nodes_[it->second];
+    if (!(e.ref == 1 && static_cast<int32_t>(e.tokens.size()) < C_)) ++need;
+  }
+  if (need > free_slots())
+    throw Error(kNoCapacity, "need " + std::to_string(need) + " chunk slots, " +
+                                 std::to_string(free_slots()) + " free");
+  for (int32_t j = 0; j < n; ++j) append(seqs[j], tokens + j, 1, ops, j);
 }
 
 void Manager::remove(int64_t seq) {
   auto it = end_.find(seq);
   if (it == end_.end()) throw Error(kUnknownSeq, "sequence id not live");
+  structural_ = true;
   int32_t e = it->second;
   end_.erase(it);
   len_.erase(seq);
@@ -196,7 +216,7 @@ int32_t Manager::seq_len(int64_t seq) const {
   return it->second;
 }
 
-void Manager::build_plan(int cf_group, int sf_group, Plan* plan) const {
+void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan) const {
   Plan& P = *plan;
   P = Plan();
 
@@ -227,6 +247,7 @@ void Manager::build_plan(int cf_group, int sf_group, Plan* plan) const {
     row_node.push_back(f.node);
     P.rows.insert(P.rows.end(), {nd.id, f.parent_row, nd.start, static_cast<int32_t>(nd.tokens.size()),
                                  static_cast<int32_t>(P.dfs_seq.size()), -1, nd.slot});
+    P.row_node.push_back(f.node);
     for (int64_t s : nd.ended) {
       P.dfs_seq.push_back(s);
       P.dfs_qrow.push_back(qrow.at(s));
@@ -252,6 +273,7 @@ void Manager::build_plan(int cf_group, int sf_group, Plan* plan) const {
     if (e - b < 2) continue;
     ++P.shared_chunks;
     P.shared_tokens += R(r, 3);
+    if (!two_phase) continue;
     int32_t t = p >= 0 ? task_of_row[p] : -1;
     if (t >= 0 && tasks[t].b == b && tasks[t].e == e && tasks[t].last_row == p && tasks[t].n_chunks < cf_group) {
       tasks[t].n_chunks += 1;
@@ -273,6 +295,7 @@ void Manager::build_plan(int cf_group, int sf_group, Plan* plan) const {
       for (int32_t r : task_rows[t]) {
         P.chunk_refs.push_back(R(r, 6));
         P.chunk_refs.push_back(R(r, 3));
+        P.ref_node.push_back(row_node[r]);
       }
       tasks[t].part_base = parts;
       parts += tasks[t].e - tasks[t].b;
@@ -331,6 +354,7 @@ void Manager::build_plan(int cf_group, int sf_group, Plan* plan) const {
         }
         P.chunk_refs.push_back(R(priv[q], 6));
         P.chunk_refs.push_back(R(priv[q], 3));
+        P.ref_node.push_back(row_node[priv[q]]);
       }
       P.sf_chunk_reads += st.n_chunks;
       P.sf_tasks.push_back(st);
@@ -339,6 +363,30 @@ void Manager::build_plan(int cf_group, int sf_group, Plan* plan) const {
     P.seq_parts[2 * i] = first;
     P.seq_parts[2 * i + 1] = static_cast<int32_t>(P.part_list.size()) - first;
   }
+  // Longest sequence-first tasks first: they start earliest, and the four
+  // waves of a block get tasks of about the same length.
+  std::stable_sort(P.sf_tasks.begin(), P.sf_tasks.end(),
+                   [](const SfTask& x, const SfTask& y) { return x.n_chunks > y.n_chunks; });
+}
+
+void Manager::refresh_fills(Plan* plan) const {
+  Plan& P = *plan;
+  P.unique_tokens = P.attended_tokens = P.shared_tokens = 0;
+  const size_t n_rows = P.row_node.size();
+  for (size_t r = 0; r < n_rows; ++r) {
+    const int32_t fill = static_cast<int32_t>(nodes_[P.row_node[r]].tokens.size());
+    int32_t* row = &P.rows[r * 7];
+    row[3] = fill;
+    P.unique_tokens += fill;
+    P.attended_tokens += static_cast<int64_t>(fill) * (row[5] - row[4]);
+    if (row[5] - row[4] >= 2) P.shared_tokens += fill;
+  }
+  for (size_t k = 0; k < P.ref_node.size(); ++k)
+    P.chunk_refs[2 * k + 1] = static_cast<int32_t>(nodes_[P.ref_node[k]].tokens.size());
+  for (CfUnit& u : P.cf_units)
+    for (int c = 0; c < kCfInline && c < u.n_chunks; ++c) u.n_valid[c] = P.chunk_refs[2 * (u.chunk_begin + c) + 1];
+  for (SfTask& t : P.sf_tasks)
+    for (int c = 0; c < kSfInline && c < t.n_chunks; ++c) t.n_valid[c] = P.chunk_refs[2 * (t.chunk_begin + c) + 1];
 }
 
 }  // namespace chunkattn

@@ -33,6 +33,8 @@
 #include <string>
 #include <vector>
 
+#include "kernels.h"
+
 namespace chunkattn {
 
 // Status codes mirror the CA_E_* values of the C header.
@@ -57,11 +59,9 @@ struct KvOp {
 
 // Per-step work plan built from the DFS order.  All ids are int32 so the
 // arrays go to the device as they are.
-// Records are read by a block with one scalar load; the first chunk refs of
-// the task ride along, so a block can start its tile loads after a single
-// round trip to memory.
-constexpr int kCfInline = 8;   // chunk refs carried by a chunk-first unit
-constexpr int kSfInline = 4;   // chunk refs carried by a sequence-first task
+// Records are read by a block (a wave) with one scalar load; the first chunk
+// refs of the task ride along (kCfInline, kSfInline in kernels.h), so it can
+// start its tile loads after a single round trip to memory.
 
 struct CfUnit {        // chunk-first: one 32-row block of one run of shared chunks
   int32_t chunk_begin; // into chunk_refs (pairs); refs past kCfInline are read there
@@ -95,6 +95,8 @@ struct Plan {
   int64_t cf_tasks = 0;
   std::vector<SfTask> sf_tasks;
   std::vector<int32_t> chunk_refs;  // (slot, n_valid) pairs
+  std::vector<int32_t> row_node;    // manager node index of each table row
+  std::vector<int32_t> ref_node;    // manager node index of each chunk ref
   std::vector<int32_t> seq_parts;   // (first, count) into part_list, per DFS position
   std::vector<int32_t> part_list;   // partial ids, per sequence in merge order
   int32_t n_parts = 0;
@@ -119,15 +121,30 @@ class Manager {
 
   // Mutations return the device copies they need (possibly none).
   int32_t insert(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops);
-  void append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops);
+  // src_base: row of the caller's K/V that holds the first appended token.
+  void append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops, int32_t src_base = 0);
+  // One token for each of n sequences (token j, K/V row j).  All checks run
+  // before anything changes (unknown or repeated id, too few free slots).
+  void append_batch(const int64_t* seqs, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops);
+
+  // True when the last mutations only grew chunks in place (no chunk created
+  // or freed, no sequence joined or left) since the last clear_structural().
+  bool fills_only() const { return !structural_; }
+  void clear_structural() { structural_ = false; }
   void remove(int64_t seq);
 
   std::vector<int64_t> sequences() const;  // ascending
   int32_t seq_len(int64_t seq) const;
 
   // Build the canonical table and the work plan.  cf_group / sf_group: chunks
-  // per chunk-first task and per sequence-first task.
-  void build_plan(int cf_group, int sf_group, Plan* plan) const;
+  // per chunk-first task and per sequence-first task.  Without two_phase every
+  // chunk on a sequence's path, shared or not, goes to that sequence's
+  // sequence-first tasks (physically shared pages, no chunk-first phase).
+  void build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan) const;
+  // Bring a plan built for the current structure up to date with chunk fills
+  // that grew since: fill counts in the table, the chunk refs and the refs
+  // carried inline by task records, and the token totals.
+  void refresh_fills(Plan* plan) const;
 
  private:
   struct Node {
@@ -149,6 +166,7 @@ class Manager {
 
   int C_;
   bool share_;
+  bool structural_ = true;
   int64_t capacity_ = 0;
   int32_t next_id_ = 0;
   int64_t n_nodes_ = 0;

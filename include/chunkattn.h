@@ -62,7 +62,14 @@ enum {
    * every chunk is private and a step runs the sequence-first phase over each
    * sequence's whole block list.  This is the unshared paged layout used as
    * the comparator (PagedAttention-style block tables; summary section 4.1). */
-  CA_CREATE_UNSHARED = 1
+  CA_CREATE_UNSHARED = 1,
+  /* Keep the prefix tree (a shared prefix is stored once) but run no
+   * chunk-first phase: every sequence streams its whole path, shared chunks
+   * included, in the sequence-first phase, so a shared chunk is read once per
+   * sequence that holds it.  This is the "physically shared KV without
+   * two-phase partition" baseline (PagedAttn*, summary section 4.1 and
+   * Table 3), used as the second comparator. */
+  CA_CREATE_NO_CHUNK_FIRST = 2
 };
 
 /* ca_set_option keys. */
@@ -109,6 +116,7 @@ typedef struct ca_stats_t {
   int64_t attended_kv_bytes; /* attended_tokens * 4 * heads * head_dim */
   int64_t shared_tokens;     /* tokens held in chunks with >= 2 references */
   int64_t private_tokens;    /* tokens held in chunks with one reference */
+  int64_t fill_refreshes;    /* plan updates that only refreshed chunk fills */
 } ca_stats_t;
 
 /* Bytes of one chunk slot: K and V, all heads, fp16 = 4 * heads * chunk_size
@@ -162,6 +170,18 @@ int ca_insert(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n,
  * Errors: CA_E_UNKNOWN_SEQ, CA_E_INVALID_ARG, CA_E_NO_CAPACITY. */
 int ca_append(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n,
               const void* k_dev, const void* v_dev, void* stream);
+
+/* One decode token for each of n >= 1 live sequences: token tokens[j] with
+ * K/V row j of k_dev, v_dev (fp16 [n][heads][head_dim]) goes to seq_ids[j].
+ * Same placement rules as ca_append; all KV writes go out in batched
+ * launches.  When every append lands in place (a private, non-full last
+ * chunk), the cached chunk table keeps its shape and the next step only
+ * refreshes its fill counts (the table is rebuilt when a chunk fills up or a
+ * sequence joins or leaves: summary section 3.3).  Errors: CA_E_UNKNOWN_SEQ,
+ * CA_E_INVALID_ARG (an id repeated in the batch), CA_E_NO_CAPACITY; all are
+ * detected before anything changes. */
+int ca_append_batch(ca_ctx* ctx, int32_t n, const int64_t* seq_ids, const int32_t* tokens,
+                    const void* k_dev, const void* v_dev, void* stream);
 
 /* Remove a finished sequence: every chunk on its path loses one reference and
  * chunks left without references return their slots (explainer, "dynamic

@@ -203,3 +203,78 @@ def test_workload_tables_and_plan_sizes(k):
     # every shared chunk is read once per 32-row block, every private chunk once
     assert st["cf_chunk_reads"] == sum((r[5] - r[4] + 31) // 32 for r in shared)
     assert st["sf_chunk_reads"] == len(private)
+
+
+@pytest.mark.parametrize("k", [2, 5])
+def test_no_chunk_first_mode_keeps_tree_and_streams_whole_paths(k):
+    """The PagedAttn*-style mode shares storage exactly like the two-phase
+    context but plans every path chunk, shared ones included, per sequence."""
+    wl = make_config(k, heads=1)
+    ca2 = ChunkAttention(32, 10_000, device=None)
+    ca1 = ChunkAttention(32, 10_000, device=None, two_phase=False)
+    for i in range(wl.n_seq):
+        t = wl.seq_tokens(i)
+        assert ca1.insert(i, t) == ca2.insert(i, t)
+    r1, o1 = ca1.export_table()
+    r2, o2 = ca2.export_table()
+    assert np.array_equal(r1, r2) and o1 == o2
+    s1, s2 = ca1.stats(), ca2.stats()
+    assert s1["unique_tokens"] == s2["unique_tokens"] and s1["shared_chunks"] == s2["shared_chunks"] > 0
+    assert s1["cf_tasks"] == 0 and s1["cf_units"] == 0
+    # every (sequence, chunk-on-its-path) pair is one chunk read per head
+    assert s1["sf_chunk_reads"] == int(sum((r[5] - r[4]) for r in r1))
+    assert s2["sf_chunk_reads"] + s2["shared_chunks"] < s1["sf_chunk_reads"]
+
+
+def test_append_batch_matches_model_through_fill_refreshes():
+    rng = np.random.default_rng(77)
+    m = PrefixTreeModel(64, 400)
+    ca = ChunkAttention(2, 400, device=None)
+    shared = list(range(100))
+    ids = [3, 9, 11, 20, 21]
+    for n, s in enumerate(ids):
+        t = shared + [1000 + n] * int(rng.integers(1, 70))
+        assert ca.insert(s, t) == m.insert(s, t)
+    ca.insert(50, shared[:40])          # ends inside a shared chunk
+    m.insert(50, shared[:40])
+    model_and_lib_agree(m, ca)
+    live = ids + [50]
+    for step in range(150):
+        batch = [s for s in live if rng.random() < 0.8] or [live[0]]
+        toks = [int(x) for x in rng.integers(0, 5, size=len(batch))]
+        ca.append_batch(batch, toks)
+        for s, t in zip(batch, toks):
+            m.append(s, [t])
+        model_and_lib_agree(m, ca)
+        if step == 60:
+            ca.remove(11)
+            m.remove(11)
+            live.remove(11)
+    st = ca.stats()
+    assert st["fill_refreshes"] > 50 and st["table_rebuilds"] > 3
+
+
+def test_append_batch_errors_change_nothing():
+    ca = ChunkAttention(2, 3, device=None)
+    ca.insert(1, list(range(64)))      # full private chunk
+    ca.insert(2, list(range(100, 130)))
+    snap = ca.export_table()
+    for args, code in (([[1, 7], [5, 5]], "unknown_seq"),
+                       ([[2, 2], [5, 5]], "invalid_arg"),
+                       ([[], []], "invalid_arg")):
+        with pytest.raises(CaError) as ei:
+            ca.append_batch(*args)
+        assert ei.value.name == code
+        after = ca.export_table()
+        assert np.array_equal(snap[0], after[0]) and snap[1] == after[1]
+    # seq 1 needs a new chunk (its chunk is full), seq 2 appends in place: one free slot is enough
+    ca.append_batch([1, 2], [5, 6])
+    assert ca.stats()["free_slots"] == 0
+    ca.insert(4, list(range(64)))       # shares seq 1's first chunk, needs no slot
+    snap = ca.export_table()
+    # seq 4 ends on a shared full chunk -> needs a new chunk, none free
+    with pytest.raises(CaError) as ei:
+        ca.append_batch([2, 4], [7, 8])
+    assert ei.value.name == "no_capacity"
+    after = ca.export_table()
+    assert np.array_equal(snap[0], after[0]) and snap[1] == after[1]

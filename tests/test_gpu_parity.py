@@ -37,12 +37,12 @@ def _torch():
     return torch
 
 
-def build_ca(wl, share=True, cf_group=None, sf_group=None, capacity=None):
+def build_ca(wl, share=True, cf_group=None, sf_group=None, capacity=None, two_phase=True):
     torch = _torch()
     from decode_attention_prefix_tree_amd import ChunkAttention, load_workload, slots_needed
     from decode_attention_prefix_tree_amd import _capi
     cap = capacity or slots_needed(wl, share=share) + 4
-    ca = ChunkAttention(wl.heads, cap, device="cuda:0", share=share)
+    ca = ChunkAttention(wl.heads, cap, device="cuda:0", share=share, two_phase=two_phase)
     if cf_group:
         ca.set_option(_capi.CA_OPT_CF_CHUNKS_PER_TASK, cf_group)
     if sf_group:
@@ -142,6 +142,20 @@ def test_unshared_comparator_layout():
     st = ca.stats()
     assert st["shared_chunks"] == 0 and st["unique_tokens"] == wl.attended_tokens()
     assert_parity(run_step(ca, wl.q), A.decode_workload(wl), "unshared config1")
+
+
+@pytest.mark.parametrize("name", ["config1", "config2", "deep_random", "interior_and_dups"])
+def test_shared_pages_without_chunk_first(name):
+    """PagedAttn*-style comparator: shared storage, every path streamed per sequence."""
+    _say(f"no chunk-first {name}")
+    if name.startswith("config"):
+        wl = cached_config(int(name[-1]))
+    else:
+        wl = from_token_lists(tiny_tree_cases()[name], heads=3, seed=5)
+    ca = build_ca(wl, two_phase=False)
+    st = ca.stats()
+    assert st["cf_units"] == 0
+    assert_parity(run_step(ca, wl.q), A.decode_workload(wl), f"no-cf {name}")
 
 
 def test_deterministic_bitwise():
@@ -271,3 +285,36 @@ def test_more_than_64_partials_per_sequence():
     assert_parity(got, A.decode_workload(wl), "many partials")
     ca.set_option(_capi.CA_OPT_FUSED_MERGE, 1)
     assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
+
+
+@pytest.mark.parametrize("two_phase", [True, False])
+def test_decode_progression_batched_appends(two_phase):
+    """One token per sequence per step through ca_append_batch (in-place fills
+    refresh the cached table, full chunks rebuild it), attended each step and
+    checked against the oracle on the sequences' full K/V."""
+    _say(f"decode progression two_phase={two_phase}")
+    torch = _torch()
+    rng = np.random.default_rng(12)
+    H = 2
+    shared = list(range(130))
+    seqs = [shared + [700 + i] * int(rng.integers(1, 40)) for i in range(7)]
+    wl = from_token_lists(seqs, heads=H, seed=13)
+    ca = build_ca(wl, capacity=80, two_phase=two_phase)
+    kv = {i: list(wl.seq_kv(i)) for i in range(wl.n_seq)}
+    live = list(range(wl.n_seq))
+    for step in range(90):
+        k = rng.standard_normal((len(live), H, 128), dtype=np.float32).astype(np.float16)
+        v = rng.standard_normal((len(live), H, 128), dtype=np.float32).astype(np.float16)
+        ca.append_batch(live, list(rng.integers(0, 50, size=len(live))),
+                        torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+        for j, s in enumerate(live):
+            kv[s][0] = np.concatenate([kv[s][0], k[j:j + 1]])
+            kv[s][1] = np.concatenate([kv[s][1], v[j:j + 1]])
+        if step == 45:
+            ca.remove(live.pop(2))
+        q = rng.standard_normal((len(live), H, 128), dtype=np.float32).astype(np.float16)
+        got = run_step(ca, q)
+        if step % 15 == 14 or step == 89:
+            assert_parity(got, A.decode_step(q, [kv[s] for s in live]), f"decode step {step}")
+    st = ca.stats()
+    assert st["fill_refreshes"] > 60
