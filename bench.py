@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-comparator", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--decode", action="store_true",
+                    help="decode progression instead: n_s = 2048 shared prompt tokens, one token appended per "
+                         "sequence per step (completion length n_c sweep at batch 32, batch sweep at n_c = 512)")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the per-kernel timing loop (for rocprofv3 runs); prints its event means")
     return ap.parse_args()
@@ -97,13 +100,21 @@ def time_launches(torch, ca, q, out, steps, flush, phases):
     return np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(len(phases))] for i in range(steps)])
 
 
+def step_kernel_digest():
+    """sha256 over the device sources of the decode-step kernels."""
+    import hashlib
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "decode_attention_prefix_tree_amd", "csrc")
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "kernels.h", "tile_layout.h"):
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
 def recorded_traffic(config):
     """HBM bytes per partials launch from the committed counter summary, if it
     was taken on this workload with the kernel source as it is now; else None."""
-    import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     prof = os.path.join(root, "profiles", f"partials_kernel_workload{config}_traffic.md")
-    src = os.path.join(root, "decode_attention_prefix_tree_amd", "csrc", "kernels.hip")
     if not os.path.exists(prof):
         return None
     fields = {}
@@ -111,7 +122,7 @@ def recorded_traffic(config):
         if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_launch", "kernel_source_sha256"):
             k, v = line.split(":", 1)
             fields[k] = v.strip()
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    digest = step_kernel_digest()
     if fields.get("kernel_source_sha256") != digest:
         return None
     return int(fields["traffic_bytes_per_launch"])
@@ -155,6 +166,82 @@ def cpu_baseline(wl, seconds_target):
                       f"fp64 numpy, {used} threads over sequences, BLAS 1 thread, {dt:.2f} s"}
 
 
+def decode_progression(torch, n_seq, n_shared, checkpoints, two_phase, flush, window=16, heads=32, seed=7):
+    """Decode steps from a fully shared prompt: each step appends one token per
+    sequence (ca_append_batch) and attends.  Returns, per checkpoint n_c (the
+    completion length reached), the mean cold GPU time of the append and the
+    attend over the `window` steps ending there, and the host time per step."""
+    from decode_attention_prefix_tree_amd import ChunkAttention
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    max_c = max(checkpoints)
+    cap = (n_shared + 63) // 64 + n_seq * ((max_c + 63) // 64 + 1) + 8
+    ca = ChunkAttention(heads, cap, device="cuda:0", two_phase=two_phase)
+    ks = torch.randn((n_shared, heads, 128), generator=gen, device="cuda").half()
+    vs = torch.randn((n_shared, heads, 128), generator=gen, device="cuda").half()
+    prompt = np.arange(n_shared, dtype=np.int32)
+    for i in range(n_seq):
+        ca.insert(i, prompt, ks, vs)
+    ids = list(range(n_seq))
+    out = torch.empty((n_seq, heads, 128), dtype=torch.float16, device="cuda")
+    res, pending = {}, []
+    for c in range(1, max_c + 1):
+        k = torch.randn((n_seq, heads, 128), generator=gen, device="cuda").half()
+        v = torch.randn((n_seq, heads, 128), generator=gen, device="cuda").half()
+        q = torch.randn((n_seq, heads, 128), generator=gen, device="cuda").half()
+        timed = any(cp - window < c <= cp for cp in checkpoints)
+        if timed:
+            flush()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            h0 = time.perf_counter()
+            e[0].record()
+            ca.append_batch(ids, np.full(n_seq, c, np.int32), k, v)
+            e[1].record()
+            ca.attend(q, out)
+            e[2].record()
+            pending.append((c, e, time.perf_counter() - h0))
+        else:
+            ca.append_batch(ids, np.full(n_seq, c, np.int32), k, v)
+            ca.attend(q, out)
+        if c in checkpoints:
+            torch.cuda.synchronize()
+            rows = [(e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), h) for cc, e, h in pending]
+            app = float(np.mean([r[0] for r in rows])) * 1e3
+            att = float(np.mean([r[1] for r in rows])) * 1e3
+            host = float(np.mean([r[2] for r in rows])) * 1e6
+            st = ca.stats()
+            res[c] = {"append_us": app, "attend_us": att, "host_us_per_step": host,
+                      "generated_tokens_per_s": n_seq / ((app + att) * 1e-6),
+                      "attended_tokens_per_s": st["attended_tokens"] / (att * 1e-6),
+                      "unique_kv_gbps": st["unique_kv_bytes"] / (att * 1e-6) / 1e9,
+                      "table_rebuilds": st["table_rebuilds"], "table_uploads": st["table_uploads"],
+                      "patched_appends": st["patched_appends"]}
+            pending = []
+    del ca
+    torch.cuda.synchronize()
+    return res
+
+
+def decode_main(args, torch):
+    flush = Flusher(torch)
+    line = {"metric": "decode progression: generated tokens/s (one batched append + one attend per step)",
+            "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "dtype": "f16", "data": "synthetic",
+            "config": {"workload": "n_s = 2048 shared prompt tokens, heads 32, head_dim 128, chunk 64",
+                       "cache": "cold (1 GiB read before each timed step)"}}
+    for name, two_phase in (("two_phase", True), ("shared_pages_no_chunk_first", False)):
+        log(f"decode n_c sweep, {name}")
+        line.setdefault("nc_sweep_batch32", {})[name] = decode_progression(
+            torch, 32, 2048, [512, 1024, 2048], two_phase, flush)
+        log(f"decode batch sweep, {name}")
+        line.setdefault("batch_sweep_nc512", {})[name] = {
+            b: decode_progression(torch, b, 2048, [512], two_phase, flush)[512] for b in (16, 32, 64, 96)}
+    sw = line["nc_sweep_batch32"]
+    line["speedup_vs_shared_pages"] = {
+        nc: (sw["shared_pages_no_chunk_first"][nc]["append_us"] + sw["shared_pages_no_chunk_first"][nc]["attend_us"])
+        / (sw["two_phase"][nc]["append_us"] + sw["two_phase"][nc]["attend_us"]) for nc in sw["two_phase"]}
+    line["value"] = sw["two_phase"][512]["generated_tokens_per_s"]
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -167,6 +254,9 @@ def main():
     from workloads import CONFIG_NAMES, make_config
 
     torch.cuda.set_device(0)
+    if args.decode:
+        decode_main(args, torch)
+        return
     log(f"building workload {args.config}")
     wl = make_config(args.config)
     ca = ChunkAttention(wl.heads, slots_needed(wl) + 8, device="cuda:0")

@@ -60,6 +60,8 @@ class ca_stats_t(ctypes.Structure):
         ("shared_tokens", ctypes.c_int64),
         ("private_tokens", ctypes.c_int64),
         ("fill_refreshes", ctypes.c_int64),
+        ("table_uploads", ctypes.c_int64),
+        ("patched_appends", ctypes.c_int64),
     ]
 
 

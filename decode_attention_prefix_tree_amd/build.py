@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
 HOST_SOURCES = ["manager.cpp", "capi.cpp"]
-HIP_SOURCES = ["kernels.hip"]
+HIP_SOURCES = ["kernels.hip", "kv_write.hip"]
 
 
 def hipcc() -> str:

@@ -4,12 +4,14 @@
 
 #include <chrono>
 #include <cmath>
+#include <cstddef>
 #include <cstring>
 #include <exception>
 #include <string>
 
 #include "../../include/chunkattn.h"
 #include "kernels.h"
+#include "kv_write.h"
 #include "manager.h"
 
 using chunkattn::Error;
@@ -28,7 +30,7 @@ struct ca_ctx {
   chunkattn::Plan plan;
   bool plan_valid = false;
   bool fills_stale = false;  // plan structure current, chunk fills grew since
-  int64_t fill_refreshes = 0;
+  int64_t fill_refreshes = 0, table_uploads = 0, patched_appends = 0;
   uint64_t version = 1, uploaded_version = 0;
   void* uploaded_ws = nullptr;
   size_t off_cf = 0, off_sf = 0, off_refs = 0, off_qrow = 0, off_seqparts = 0, off_partlist = 0;
@@ -37,23 +39,28 @@ struct ca_ctx {
   int64_t rebuilds = 0;
   double last_rebuild_ms = 0.0;
 
-  // pinned staging for the table upload; the event marks when the last copy
-  // out of it has finished so it can be rewritten
-  void* stage = nullptr;
-  size_t stage_bytes = 0;
-  hipEvent_t stage_done = nullptr;
-  bool stage_pending = false;
+  // pinned staging for the table upload, a ring of three buffers: each event
+  // marks when the copy out of its buffer has finished, so a buffer is
+  // rewritten without waiting on the most recent uploads
+  static constexpr int kStages = 3;
+  void* stage[kStages] = {nullptr, nullptr, nullptr};
+  size_t stage_bytes[kStages] = {0, 0, 0};
+  hipEvent_t stage_done[kStages] = {nullptr, nullptr, nullptr};
+  bool stage_pending[kStages] = {false, false, false};
+  int stage_next = 0;
 
   std::string err;
 
   ca_ctx(int H, int D, int C, int f) : heads(H), head_dim(D), chunk(C), flags(f),
                                        mgr(C, (f & CA_CREATE_UNSHARED) == 0) {}
   ~ca_ctx() {
-    if (stage_done) {
-      if (stage_pending) (void)hipEventSynchronize(stage_done);
-      (void)hipEventDestroy(stage_done);
+    for (int b = 0; b < kStages; ++b) {
+      if (stage_done[b]) {
+        if (stage_pending[b]) (void)hipEventSynchronize(stage_done[b]);
+        (void)hipEventDestroy(stage_done[b]);
+      }
+      if (stage[b]) (void)hipHostFree(stage[b]);
     }
-    if (stage) (void)hipHostFree(stage);
   }
 };
 
@@ -87,9 +94,13 @@ void touch_after_append(ca_ctx* c) {
   }
 }
 
-void ensure_plan(ca_ctx* c) {
+bool device_table_current(const ca_ctx* c) { return c->uploaded_version == c->version && c->uploaded_ws == c->ws; }
+
+// with_fills: the host plan's fill counts are needed too (an upload, an
+// export, stats); a step whose device table is current does not need them.
+void ensure_plan(ca_ctx* c, bool with_fills = true) {
   if (c->plan_valid) {
-    if (c->fills_stale) {
+    if (c->fills_stale && with_fills) {
       auto t0 = std::chrono::steady_clock::now();
       c->mgr.refresh_fills(&c->plan);
       c->fills_stale = false;
@@ -139,20 +150,24 @@ void put(char* base, size_t off, const std::vector<T>& v) {
 }
 
 void upload(ca_ctx* c, void* stream) {
-  if (c->uploaded_version == c->version && c->uploaded_ws == c->ws) return;
-  if (c->stage_pending) {
-    hip_check(hipEventSynchronize(c->stage_done), "hipEventSynchronize");
-    c->stage_pending = false;
+  if (device_table_current(c)) return;
+  ensure_plan(c);
+  const int b = c->stage_next;
+  c->stage_next = (b + 1) % ca_ctx::kStages;
+  if (c->stage_pending[b]) {
+    hip_check(hipEventSynchronize(c->stage_done[b]), "hipEventSynchronize");
+    c->stage_pending[b] = false;
   }
-  if (c->stage_bytes < c->table_bytes) {
-    if (c->stage) hip_check(hipHostFree(c->stage), "hipHostFree");
-    c->stage = nullptr;
+  if (c->stage_bytes[b] < c->table_bytes) {
+    if (c->stage[b]) hip_check(hipHostFree(c->stage[b]), "hipHostFree");
+    c->stage[b] = nullptr;
     size_t want = align_up(c->table_bytes * 2);
-    hip_check(hipHostMalloc(&c->stage, want, hipHostMallocDefault), "hipHostMalloc");
-    c->stage_bytes = want;
+    hip_check(hipHostMalloc(&c->stage[b], want, hipHostMallocDefault), "hipHostMalloc");
+    c->stage_bytes[b] = want;
   }
-  if (!c->stage_done) hip_check(hipEventCreateWithFlags(&c->stage_done, hipEventDisableTiming), "hipEventCreate");
-  char* s = static_cast<char*>(c->stage);
+  if (!c->stage_done[b])
+    hip_check(hipEventCreateWithFlags(&c->stage_done[b], hipEventDisableTiming), "hipEventCreate");
+  char* s = static_cast<char*>(c->stage[b]);
   const chunkattn::Plan& p = c->plan;
   std::memset(s, 0, c->table_bytes);
   put(s, c->off_cf, p.cf_units);
@@ -161,11 +176,11 @@ void upload(ca_ctx* c, void* stream) {
   put(s, c->off_qrow, p.dfs_qrow);
   put(s, c->off_seqparts, p.seq_parts);
   put(s, c->off_partlist, p.part_list);
-  hip_check(hipMemcpyAsync(c->ws, c->stage, c->table_bytes, hipMemcpyHostToDevice,
-                           static_cast<hipStream_t>(stream)),
+  hip_check(hipMemcpyAsync(c->ws, s, c->table_bytes, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)),
             "hipMemcpyAsync(table)");
-  hip_check(hipEventRecord(c->stage_done, static_cast<hipStream_t>(stream)), "hipEventRecord");
-  c->stage_pending = true;
+  hip_check(hipEventRecord(c->stage_done[b], static_cast<hipStream_t>(stream)), "hipEventRecord");
+  c->stage_pending[b] = true;
+  c->table_uploads += 1;
   c->uploaded_version = c->version;
   c->uploaded_ws = c->ws;
 }
@@ -198,7 +213,7 @@ void check_step(ca_ctx* c, const void* q, void* out) {
   if (!c->pool_attached || c->pool == nullptr) throw Error(CA_E_NO_POOL, "no device pool attached");
   if (c->mgr.live() == 0) throw Error(CA_E_EMPTY, "no live sequence");
   if (q == nullptr || out == nullptr) throw Error(CA_E_INVALID_ARG, "q and out must be device pointers");
-  ensure_plan(c);
+  ensure_plan(c, !device_table_current(c));
   if (c->ws == nullptr || c->ws_bytes < c->total_bytes)
     throw Error(CA_E_WORKSPACE, "workspace of " + std::to_string(c->total_bytes) + " bytes needed, " +
                                     std::to_string(c->ws_bytes) + " attached");
@@ -213,18 +228,75 @@ void launch(int e, const char* what) {
   if (e != 0) throw Error(CA_E_HIP, std::string(what) + ": " + hipGetErrorString(static_cast<hipError_t>(e)));
 }
 
-void run_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* k, const void* v, void* stream) {
+// The device table entries that hold one chunk's fill count: its chunk ref
+// and, for one of a task's first refs, the copy inline in the task record
+// (offsets in int32 units into the workspace, -1 for none).
+struct FillPatch {
+  int32_t ref_off, task_off, val;
+};
+
+// Appends that only grew private chunks in place, on a context whose table is
+// already on the device: the write launch stores the new fill counts into the
+// table, so the next step needs no upload.  Returns false, and fills nothing,
+// otherwise.  out gets one entry per op.
+bool fill_patches(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, std::vector<FillPatch>* out) {
+  out->clear();
+  if (!c->plan_valid || !c->mgr.fills_only() || c->ws == nullptr || !device_table_current(c)) return false;
+  const chunkattn::Plan& p = c->plan;
+  const int32_t refs = static_cast<int32_t>(c->off_refs / sizeof(int32_t));
+  const int32_t tasks = static_cast<int32_t>(c->off_sf / sizeof(int32_t));
+  constexpr int32_t kTaskInts = sizeof(chunkattn::SfTask) / sizeof(int32_t);
+  constexpr int32_t kFillField = offsetof(chunkattn::SfTask, n_valid) / sizeof(int32_t);
+  for (const chunkattn::KvOp& o : ops) {
+    auto it = o.node >= 0 ? p.private_ref.find(o.node) : p.private_ref.end();
+    if (it == p.private_ref.end()) {
+      out->clear();
+      return false;
+    }
+    const int32_t k = it->second;
+    const int32_t task_off =
+        p.ref_pos[k] < chunkattn::kSfInline ? tasks + p.ref_task[k] * kTaskInts + kFillField + p.ref_pos[k] : -1;
+    out->push_back(FillPatch{refs + 2 * k + 1, task_off, o.dst_key0 + o.n_rows});
+  }
+  return true;
+}
+
+// Launch the copies, kOpsPerLaunch at a time; the patches of an op (if any)
+// ride with the launch that writes its chunk.
+void run_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* k, const void* v, void* stream,
+                const std::vector<FillPatch>& patches = {}) {
   chunkattn::KvOpBatch batch{};
+  chunkattn::TablePatches tp{};
   int n = 0;
+  int32_t* table = static_cast<int32_t*>(c->ws);
   for (size_t i = 0; i < ops.size(); ++i) {
     const chunkattn::KvOp& o = ops[i];
     batch.ops[n++] = chunkattn::KvOpDev{o.dst_slot, o.dst_key0, o.n_rows, o.src_row0,
                                         o.src_slot, o.from_pool, o.zero_rest, 0};
+    if (!patches.empty()) {
+      const FillPatch& f = patches[i];
+      tp.off[tp.n] = f.ref_off;
+      tp.val[tp.n++] = f.val;
+      if (f.task_off >= 0) {
+        tp.off[tp.n] = f.task_off;
+        tp.val[tp.n++] = f.val;
+      }
+    }
     if (n == chunkattn::kOpsPerLaunch || i + 1 == ops.size()) {
-      launch(chunkattn::launch_kv_write(c->pool, c->heads, batch, n, k, v, stream), "kv_write");
+      launch(chunkattn::launch_kv_write(c->pool, c->heads, batch, n, k, v, table, tp, stream), "kv_write");
       n = 0;
+      tp.n = 0;
     }
   }
+}
+
+// Bookkeeping after appends whose fill counts went to the device with the
+// writes: the host plan is refreshed lazily, the device copy is current.
+void touch_patched(ca_ctx* c) {
+  c->patched_appends += 1;
+  c->fills_stale = true;
+  c->version += 1;
+  c->uploaded_version = c->version;
 }
 
 #define CA_GUARD(ctx, ...)                                                    \
@@ -289,7 +361,7 @@ int ca_attach_pool(ca_ctx* ctx, void* dev, int64_t capacity_slots) {
 int ca_workspace_bytes(ca_ctx* ctx, size_t* out) {
   CA_GUARD(ctx, {
     if (out == nullptr) throw Error(CA_E_INVALID_ARG, "out is NULL");
-    ensure_plan(ctx);
+    ensure_plan(ctx, false);
     *out = ctx->total_bytes;
     return CA_OK;
   });
@@ -350,9 +422,13 @@ int ca_append(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n, con
     if (device && (k_dev == nullptr || v_dev == nullptr))
       throw Error(CA_E_INVALID_ARG, "k_dev and v_dev are required when a device pool is attached");
     std::vector<chunkattn::KvOp> ops;
+    std::vector<FillPatch> patches;
     ctx->mgr.append(seq_id, tokens, n, &ops);
-    touch_after_append(ctx);
-    if (device) run_kv_ops(ctx, ops, k_dev, v_dev, stream);
+    if (device && fill_patches(ctx, ops, &patches))
+      touch_patched(ctx);
+    else
+      touch_after_append(ctx);
+    if (device) run_kv_ops(ctx, ops, k_dev, v_dev, stream, patches);
     return CA_OK;
   });
 }
@@ -366,9 +442,13 @@ int ca_append_batch(ca_ctx* ctx, int32_t n, const int64_t* seq_ids, const int32_
     if (device && (k_dev == nullptr || v_dev == nullptr))
       throw Error(CA_E_INVALID_ARG, "k_dev and v_dev are required when a device pool is attached");
     std::vector<chunkattn::KvOp> ops;
+    std::vector<FillPatch> patches;
     ctx->mgr.append_batch(seq_ids, tokens, n, &ops);
-    touch_after_append(ctx);
-    if (device) run_kv_ops(ctx, ops, k_dev, v_dev, stream);
+    if (device && fill_patches(ctx, ops, &patches))
+      touch_patched(ctx);
+    else
+      touch_after_append(ctx);
+    if (device) run_kv_ops(ctx, ops, k_dev, v_dev, stream, patches);
     return CA_OK;
   });
 }
@@ -385,7 +465,7 @@ int ca_prepare(ca_ctx* ctx, void* stream) {
   CA_GUARD(ctx, {
     if (!ctx->pool_attached || ctx->pool == nullptr) throw Error(CA_E_NO_POOL, "no device pool attached");
     if (ctx->mgr.live() == 0) throw Error(CA_E_EMPTY, "no live sequence");
-    ensure_plan(ctx);
+    ensure_plan(ctx, false);
     if (ctx->ws == nullptr || ctx->ws_bytes < ctx->total_bytes)
       throw Error(CA_E_WORKSPACE, "workspace too small");
     upload(ctx, stream);
@@ -480,6 +560,8 @@ int ca_stats(ca_ctx* ctx, ca_stats_t* out) {
     s.shared_tokens = p.shared_tokens;
     s.private_tokens = p.unique_tokens - p.shared_tokens;
     s.fill_refreshes = ctx->fill_refreshes;
+    s.table_uploads = ctx->table_uploads;
+    s.patched_appends = ctx->patched_appends;
     *out = s;
     return CA_OK;
   });

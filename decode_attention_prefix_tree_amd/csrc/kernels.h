@@ -1,4 +1,4 @@
-// Host-callable launchers of the gfx950 kernels.  Plain types only, so the
+// Host-callable launchers of the gfx950 decode-step kernels.  Plain types only, so the
 // C-ABI layer and the manager never see HIP device code.
 #pragma once
 
@@ -8,17 +8,8 @@ namespace chunkattn {
 
 constexpr int kHeadDim = 128;
 constexpr int kChunk = 64;
-constexpr int kOpsPerLaunch = 64;  // 2 KiB of kernel arguments
 constexpr int kCfInline = 8;   // chunk refs carried by a chunk-first unit record
 constexpr int kSfInline = 4;   // chunk refs carried by a sequence-first task record
-
-struct KvOpDev {
-  int32_t dst_slot, dst_key0, n_rows, src_row0, src_slot, from_pool, zero_rest, pad;
-};
-
-struct KvOpBatch {
-  KvOpDev ops[kOpsPerLaunch];
-};
 
 // Arguments of one decode step.  All pointers are device addresses.
 struct StepArgs {
@@ -45,8 +36,6 @@ struct StepArgs {
 enum PartialsPart { kPartsBoth = 0, kPartsChunkFirst = 1, kPartsSequenceFirst = 2 };
 
 // Each returns a hipError_t value (0 = success) from the launch.
-int launch_kv_write(void* pool, int heads, const KvOpBatch& batch, int n_ops, const void* k_src,
-                    const void* v_src, void* stream);
 // One grid with the chunk-first blocks first and the sequence-first blocks
 // after them; `part` restricts the launch to one side.  With fuse_merge the
 // last block to finish a (sequence, head) also merges it and writes out (the

@@ -8,50 +8,18 @@
 // log-sum-exp (explainer 0h-n0.github.io/posts/paper-2402-15220, output
 // combination formula; m is a running max, s and o are unnormalised).
 //
-// Chunk tile layout.  Slot s, head h: K tile at ((s*H + h)*2 + 0) * 8192
-// halves, V tile right after it.  Within a tile the 64 x 128 fp16 elements
-// are ordered so that every MFMA operand fetch is one contiguous 1 KB wave
-// load (64 lanes x 16 bytes):
-//  * K, as the A operand of S^T = K * Q^T (v_mfma_f32_32x32x16_f16, A lane
-//    l = half*32 + i holds A[i][8*half + e], e < 8): load index
-//    L = (key/32)*8 + dim/16, lane (dim/8 % 2)*32 + key%32, element dim%8.
-//  * V, as the A operand of O^T = V^T * P^T: load index L = (dim/32)*4 +
-//    key/16, lane ((key/4) % 2)*32 + dim%32, element (key%4) + 4*((key/8)%2).
-//    That key order is the order in which the S^T accumulators of a lane
-//    hold P^T, so P goes from the first product to the second without any
-//    lane exchange.
+// The chunk tile layout is described in tile_layout.h.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 
 #include "kernels.h"
+#include "tile_layout.h"
 
 namespace chunkattn {
 
 namespace {
-
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef float f16v __attribute__((ext_vector_type(16)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-constexpr int D = kHeadDim;
-constexpr int C = kChunk;
-constexpr int TILE = C * D;  // halves per tile
-
-__device__ __forceinline__ size_t tile_base(int slot, int head, int heads, int kv) {
-  return ((static_cast<size_t>(slot) * heads + head) * 2 + kv) * TILE;
-}
-
-__device__ __forceinline__ int k_off(int key, int dim) {
-  return ((((key >> 5) * 8 + (dim >> 4)) * 2 + ((dim >> 3) & 1)) * 32 + (key & 31)) * 8 + (dim & 7);
-}
-
-__device__ __forceinline__ int v_off(int key, int dim) {
-  return ((((dim >> 5) * 4 + (key >> 4)) * 2 + ((key >> 2) & 1)) * 32 + (dim & 31)) * 8 +
-         ((key & 3) | (((key >> 3) & 1) << 2));
-}
 
 // Blocks are handed to the 8 XCDs round robin; give each XCD a contiguous
 // range of logical ids so work that reads the same chunk shares an L2.
@@ -114,47 +82,6 @@ __device__ __forceinline__ h2 lo2(h8 v, int j) {
     case 1: return __builtin_shufflevector(v, v, 2, 3);
     case 2: return __builtin_shufflevector(v, v, 4, 5);
     default: return __builtin_shufflevector(v, v, 6, 7);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// KV writes: caller rows or another slot's rows into one slot's tiles.
-// grid (n_ops, heads, 2), 256 threads; each thread writes 4 x 16 bytes.
-__global__ __launch_bounds__(256) void kv_write_kernel(_Float16* pool, int heads, KvOpBatch batch,
-                                                       const _Float16* k_src, const _Float16* v_src) {
-  const KvOpDev op = batch.ops[blockIdx.x];
-  const int head = blockIdx.y, kv = blockIdx.z;
-  _Float16* dst = pool + tile_base(op.dst_slot, head, heads, kv);
-  const _Float16* src_pool = op.from_pool ? pool + tile_base(op.src_slot, head, heads, kv) : nullptr;
-  const _Float16* src = kv ? v_src : k_src;
-  for (int u = threadIdx.x; u < TILE / 8; u += 256) {
-    const int L = u >> 6, lane = u & 63, half = lane >> 5, i = lane & 31;
-    h8 cur = *reinterpret_cast<const h8*>(dst + u * 8);
-    h8 val;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      int key, dim;
-      if (kv == 0) {
-        key = (L >> 3) * 32 + i;
-        dim = (L & 7) * 16 + half * 8 + e;
-      } else {
-        key = (L & 3) * 16 + half * 4 + (e & 3) + ((e >> 2) << 3);
-        dim = (L >> 2) * 32 + i;
-      }
-      const int r = key - op.dst_key0;
-      _Float16 x;
-      if (r >= 0 && r < op.n_rows) {
-        const int sr = op.src_row0 + r;
-        if (op.from_pool)
-          x = src_pool[kv == 0 ? k_off(sr, dim) : v_off(sr, dim)];
-        else
-          x = src[(static_cast<size_t>(sr) * heads + head) * D + dim];
-      } else {
-        x = op.zero_rest ? static_cast<_Float16>(0.0f) : cur[e];
-      }
-      val[e] = x;
-    }
-    *reinterpret_cast<h8*>(dst + u * 8) = val;
   }
 }
 
@@ -612,16 +539,6 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
 }
 
 }  // namespace
-
-int launch_kv_write(void* pool, int heads, const KvOpBatch& batch, int n_ops, const void* k_src,
-                    const void* v_src, void* stream) {
-  if (n_ops <= 0) return 0;
-  dim3 grid(n_ops, heads, 2);
-  hipLaunchKernelGGL(kv_write_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<_Float16*>(pool), heads, batch, static_cast<const _Float16*>(k_src),
-                     static_cast<const _Float16*>(v_src));
-  return static_cast<int>(hipGetLastError());
-}
 
 int launch_partials(const StepArgs& a, int part, bool fuse_merge, void* stream) {
   const int n_cf = a.n_cf_units * a.heads, n_sf = a.n_sf_tasks * a.heads;

@@ -1,0 +1,36 @@
+// Host-callable launcher of the KV write kernel: copies new tokens' K/V (or
+// another slot's keys, after a chunk split) into chunk tiles.  Plain types
+// only, so the C-ABI layer never sees HIP device code.
+#pragma once
+
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace chunkattn {
+
+constexpr int kOpsPerLaunch = 64;  // 2 KiB of kernel arguments
+
+struct KvOpDev {
+  int32_t dst_slot, dst_key0, n_rows, src_row0, src_slot, from_pool, zero_rest, pad;
+};
+
+struct KvOpBatch {
+  KvOpDev ops[kOpsPerLaunch];
+};
+
+// int32 stores into the device chunk table done by the same launch (fill
+// counts of chunks that grew in place), offsets in int32 units.
+constexpr int kMaxPatches = 2 * kOpsPerLaunch;
+struct TablePatches {
+  int32_t n;
+  int32_t off[kMaxPatches];
+  int32_t val[kMaxPatches];
+};
+
+// Returns a hipError_t value (0 = success) from the launch.  Block 0 also
+// does the table stores (table: the workspace base, device address).
+int launch_kv_write(void* pool, int heads, const KvOpBatch& batch, int n_ops, const void* k_src,
+                    const void* v_src, int32_t* table, const TablePatches& patches, void* stream);
+
+}  // namespace chunkattn

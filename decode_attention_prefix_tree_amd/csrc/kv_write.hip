@@ -1,0 +1,89 @@
+// gfx950 kernel that writes new tokens' K and V into chunk tiles (the
+// layout of tile_layout.h): rows of the caller's [row][head][128] fp16 K/V,
+// or keys of another slot when a chunk split moves a tail into a new slot
+// (prefix tree of chunks: paperlayer.ai summary of arXiv 2402.15220v4,
+// section 3.1).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kv_write.h"
+#include "tile_layout.h"
+
+namespace chunkattn {
+
+namespace {
+
+// KV writes: caller rows or another slot's rows into one slot's tiles.
+// grid (n_ops, heads, 2), 256 threads; a thread owns 4 of the tile's 1024
+// 16-byte units.  Without zero_rest only the units holding a written key are
+// read and rewritten (a one-token append touches 16 K units and 128 V units
+// of a head, not the whole 32 KiB pair).  Block (0, 0, 0) also stores the
+// fill counts of chunks that grew in place into the device chunk table, so
+// the next step on the stream sees them without a table upload.
+__global__ __launch_bounds__(256) void kv_write_kernel(_Float16* pool, int heads, KvOpBatch batch,
+                                                       const _Float16* k_src, const _Float16* v_src,
+                                                       int32_t* table, TablePatches patches) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && static_cast<int>(threadIdx.x) < patches.n)
+    table[patches.off[threadIdx.x]] = patches.val[threadIdx.x];
+  const KvOpDev op = batch.ops[blockIdx.x];
+  const int head = blockIdx.y, kv = blockIdx.z;
+  _Float16* dst = pool + tile_base(op.dst_slot, head, heads, kv);
+  const _Float16* src_pool = op.from_pool ? pool + tile_base(op.src_slot, head, heads, kv) : nullptr;
+  const _Float16* src = kv ? v_src : k_src;
+  const int lo = op.dst_key0, hi = op.dst_key0 + op.n_rows;  // written keys [lo, hi)
+  for (int u = threadIdx.x; u < TILE / 8; u += 256) {
+    const int L = u >> 6, lane = u & 63, half = lane >> 5, i = lane & 31;
+    if (!op.zero_rest) {
+      bool touched;
+      if (kv == 0) {
+        const int key = (L >> 3) * 32 + i;
+        touched = key >= lo && key < hi;
+      } else {
+        const int k0 = (L & 3) * 16 + half * 4;  // keys k0..k0+3 and k0+8..k0+11
+        touched = (k0 < hi && k0 + 4 > lo) || (k0 + 8 < hi && k0 + 12 > lo);
+      }
+      if (!touched) continue;
+    }
+    const h8 cur = op.zero_rest ? h8{} : *reinterpret_cast<const h8*>(dst + u * 8);
+    h8 val;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int key, dim;
+      if (kv == 0) {
+        key = (L >> 3) * 32 + i;
+        dim = (L & 7) * 16 + half * 8 + e;
+      } else {
+        key = (L & 3) * 16 + half * 4 + (e & 3) + ((e >> 2) << 3);
+        dim = (L >> 2) * 32 + i;
+      }
+      const int r = key - op.dst_key0;
+      _Float16 x;
+      if (r >= 0 && r < op.n_rows) {
+        const int sr = op.src_row0 + r;
+        if (op.from_pool)
+          x = src_pool[kv == 0 ? k_off(sr, dim) : v_off(sr, dim)];
+        else
+          x = src[(static_cast<size_t>(sr) * heads + head) * D + dim];
+      } else {
+        x = op.zero_rest ? static_cast<_Float16>(0.0f) : cur[e];
+      }
+      val[e] = x;
+    }
+    *reinterpret_cast<h8*>(dst + u * 8) = val;
+  }
+}
+
+}  // namespace
+
+int launch_kv_write(void* pool, int heads, const KvOpBatch& batch, int n_ops, const void* k_src,
+                    const void* v_src, int32_t* table, const TablePatches& patches, void* stream) {
+  if (n_ops <= 0) return 0;
+  dim3 grid(n_ops, heads, 2);
+  hipLaunchKernelGGL(kv_write_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<_Float16*>(pool), heads, batch, static_cast<const _Float16*>(k_src),
+                     static_cast<const _Float16*>(v_src), table, patches);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace chunkattn

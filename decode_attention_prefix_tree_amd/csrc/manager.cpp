@@ -141,7 +141,7 @@ void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<
   if (take > 0) {
     Node& nd = nodes_[e];
     nd.tokens.insert(nd.tokens.end(), tokens, tokens + take);
-    if (ops) ops->push_back(KvOp{nd.slot, fill, take, src_base, -1, 0, 0});
+    if (ops) ops->push_back(KvOp{nd.slot, fill, take, src_base, -1, 0, 0, e});
   }
   len_[seq] += n;
   if (take == n) return;
@@ -367,6 +367,16 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
   // waves of a block get tasks of about the same length.
   std::stable_sort(P.sf_tasks.begin(), P.sf_tasks.end(),
                    [](const SfTask& x, const SfTask& y) { return x.n_chunks > y.n_chunks; });
+  // where each chunk ref lives, so a fill change can be patched in place
+  P.ref_task.assign(P.ref_node.size(), -1);
+  P.ref_pos.assign(P.ref_node.size(), -1);
+  for (size_t t = 0; t < P.sf_tasks.size(); ++t)
+    for (int c = 0; c < P.sf_tasks[t].n_chunks; ++c) {
+      const int32_t k = P.sf_tasks[t].chunk_begin + c;
+      P.ref_task[k] = static_cast<int32_t>(t);
+      P.ref_pos[k] = c;
+      if (nodes_[P.ref_node[k]].ref == 1) P.private_ref[P.ref_node[k]] = k;
+    }
 }
 
 void Manager::refresh_fills(Plan* plan) const {

@@ -55,6 +55,7 @@ struct KvOp {
   int32_t src_slot;   // only for from_pool
   int32_t from_pool;
   int32_t zero_rest;
+  int32_t node = -1;  // manager node written (host bookkeeping only)
 };
 
 // Per-step work plan built from the DFS order.  All ids are int32 so the
@@ -97,6 +98,9 @@ struct Plan {
   std::vector<int32_t> chunk_refs;  // (slot, n_valid) pairs
   std::vector<int32_t> row_node;    // manager node index of each table row
   std::vector<int32_t> ref_node;    // manager node index of each chunk ref
+  std::vector<int32_t> ref_task;    // sequence-first task holding the ref (-1: chunk-first)
+  std::vector<int32_t> ref_pos;     // position of the ref within that task
+  std::map<int32_t, int32_t> private_ref;  // node -> its ref, for chunks of one sequence
   std::vector<int32_t> seq_parts;   // (first, count) into part_list, per DFS position
   std::vector<int32_t> part_list;   // partial ids, per sequence in merge order
   int32_t n_parts = 0;

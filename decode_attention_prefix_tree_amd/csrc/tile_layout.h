@@ -1,0 +1,48 @@
+// Device-side layout of the chunk pool, shared by the decode-step kernels
+// and the KV write kernel.
+//
+// Chunk tile layout.  Slot s, head h: K tile at ((s*H + h)*2 + 0) * 8192
+// halves, V tile right after it.  Within a tile the 64 x 128 fp16 elements
+// are ordered so that every MFMA operand fetch is one contiguous 1 KB wave
+// load (64 lanes x 16 bytes):
+//  * K, as the A operand of S^T = K * Q^T (v_mfma_f32_32x32x16_f16, A lane
+//    l = half*32 + i holds A[i][8*half + e], e < 8): load index
+//    L = (key/32)*8 + dim/16, lane (dim/8 % 2)*32 + key%32, element dim%8.
+//  * V, as the A operand of O^T = V^T * P^T: load index L = (dim/32)*4 +
+//    key/16, lane ((key/4) % 2)*32 + dim%32, element (key%4) + 4*((key/8)%2).
+//    That key order is the order in which the S^T accumulators of a lane
+//    hold P^T, so P goes from the first product to the second without any
+//    lane exchange.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+
+#include "kernels.h"
+
+namespace chunkattn {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = kHeadDim;
+constexpr int C = kChunk;
+constexpr int TILE = C * D;  // halves per tile
+
+__device__ __forceinline__ size_t tile_base(int slot, int head, int heads, int kv) {
+  return ((static_cast<size_t>(slot) * heads + head) * 2 + kv) * TILE;
+}
+
+__device__ __forceinline__ int k_off(int key, int dim) {
+  return ((((key >> 5) * 8 + (dim >> 4)) * 2 + ((dim >> 3) & 1)) * 32 + (key & 31)) * 8 + (dim & 7);
+}
+
+__device__ __forceinline__ int v_off(int key, int dim) {
+  return ((((dim >> 5) * 4 + (key >> 4)) * 2 + ((key >> 2) & 1)) * 32 + (dim & 31)) * 8 +
+         ((key & 3) | (((key >> 3) & 1) << 2));
+}
+
+}  // namespace chunkattn

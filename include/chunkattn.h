@@ -117,6 +117,9 @@ typedef struct ca_stats_t {
   int64_t shared_tokens;     /* tokens held in chunks with >= 2 references */
   int64_t private_tokens;    /* tokens held in chunks with one reference */
   int64_t fill_refreshes;    /* plan updates that only refreshed chunk fills */
+  int64_t table_uploads;     /* host-to-device copies of the chunk table */
+  int64_t patched_appends;   /* appends whose fill counts the write launch
+                                stored into the device table itself */
 } ca_stats_t;
 
 /* Bytes of one chunk slot: K and V, all heads, fp16 = 4 * heads * chunk_size
@@ -167,6 +170,8 @@ int ca_insert(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n,
  * decoding appends to leaf chunks or grows new chunks).  Writes into the
  * sequence's last chunk only if that chunk is private and not full, else
  * grows new private chunks.  k_dev, v_dev: fp16 [n][heads][head_dim].
+ * An append that lands wholly in place keeps the table's shape, as in
+ * ca_append_batch (fill counts stored on the device by the write launch).
  * Errors: CA_E_UNKNOWN_SEQ, CA_E_INVALID_ARG, CA_E_NO_CAPACITY. */
 int ca_append(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n,
               const void* k_dev, const void* v_dev, void* stream);
@@ -175,11 +180,14 @@ int ca_append(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n,
  * K/V row j of k_dev, v_dev (fp16 [n][heads][head_dim]) goes to seq_ids[j].
  * Same placement rules as ca_append; all KV writes go out in batched
  * launches.  When every append lands in place (a private, non-full last
- * chunk), the cached chunk table keeps its shape and the next step only
- * refreshes its fill counts (the table is rebuilt when a chunk fills up or a
- * sequence joins or leaves: summary section 3.3).  Errors: CA_E_UNKNOWN_SEQ,
- * CA_E_INVALID_ARG (an id repeated in the batch), CA_E_NO_CAPACITY; all are
- * detected before anything changes. */
+ * chunk), the cached chunk table keeps its shape (it is rebuilt when a chunk
+ * fills up or a sequence joins or leaves: summary section 3.3); if the table
+ * is then already on the device, the write launch also stores the new fill
+ * counts into the workspace copy, so the next step uploads nothing.  Those
+ * stores are ordered on `stream` like the K/V writes: enqueue appends and
+ * steps of one context on one stream (or order them with events).
+ * Errors: CA_E_UNKNOWN_SEQ, CA_E_INVALID_ARG (an id repeated in the batch),
+ * CA_E_NO_CAPACITY; all are detected before anything changes. */
 int ca_append_batch(ca_ctx* ctx, int32_t n, const int64_t* seq_ids, const int32_t* tokens,
                     const void* k_dev, const void* v_dev, void* stream);
 

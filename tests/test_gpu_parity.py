@@ -287,11 +287,31 @@ def test_more_than_64_partials_per_sequence():
     assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
 
 
+def _host_shadow(wl, two_phase):
+    """A context without a device pool that receives the same tree calls: its
+    exported table is the reference for the device context's."""
+    from decode_attention_prefix_tree_amd import ChunkAttention
+    sh = ChunkAttention(wl.heads, 4096, device=None, two_phase=two_phase)
+    for i in range(wl.n_seq):
+        sh.insert(i, wl.seq_tokens(i))
+    return sh
+
+
+def _same_table(a, b, label):
+    ra, oa = a.export_table()
+    rb, ob = b.export_table()
+    assert oa == ob, label
+    assert np.array_equal(ra, rb), label
+
+
 @pytest.mark.parametrize("two_phase", [True, False])
 def test_decode_progression_batched_appends(two_phase):
-    """One token per sequence per step through ca_append_batch (in-place fills
-    refresh the cached table, full chunks rebuild it), attended each step and
-    checked against the oracle on the sequences' full K/V."""
+    """One token per sequence per step through ca_append_batch, attended each
+    step and checked against the oracle on the sequences' full K/V.  Appends
+    that land in place have their fill counts stored into the device table by
+    the write launch (no upload); a chunk that fills up, or a removal, rebuilds
+    and uploads the table.  The exported table matches a host-only context
+    that saw the same calls."""
     _say(f"decode progression two_phase={two_phase}")
     torch = _torch()
     rng = np.random.default_rng(12)
@@ -300,21 +320,74 @@ def test_decode_progression_batched_appends(two_phase):
     seqs = [shared + [700 + i] * int(rng.integers(1, 40)) for i in range(7)]
     wl = from_token_lists(seqs, heads=H, seed=13)
     ca = build_ca(wl, capacity=80, two_phase=two_phase)
+    sh = _host_shadow(wl, two_phase)
     kv = {i: list(wl.seq_kv(i)) for i in range(wl.n_seq)}
     live = list(range(wl.n_seq))
     for step in range(90):
         k = rng.standard_normal((len(live), H, 128), dtype=np.float32).astype(np.float16)
         v = rng.standard_normal((len(live), H, 128), dtype=np.float32).astype(np.float16)
-        ca.append_batch(live, list(rng.integers(0, 50, size=len(live))),
-                        torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+        toks = list(rng.integers(0, 50, size=len(live)))
+        ca.append_batch(live, toks, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+        sh.append_batch(live, toks)
         for j, s in enumerate(live):
             kv[s][0] = np.concatenate([kv[s][0], k[j:j + 1]])
             kv[s][1] = np.concatenate([kv[s][1], v[j:j + 1]])
         if step == 45:
-            ca.remove(live.pop(2))
+            ca.remove(live[2])
+            sh.remove(live.pop(2))
         q = rng.standard_normal((len(live), H, 128), dtype=np.float32).astype(np.float16)
         got = run_step(ca, q)
-        if step % 15 == 14 or step == 89:
-            assert_parity(got, A.decode_step(q, [kv[s] for s in live]), f"decode step {step}")
+        assert_parity(got, A.decode_step(q, [kv[s] for s in live]), f"decode step {step}")
+        if step % 30 == 29:
+            _same_table(ca, sh, f"table after step {step}")
     st = ca.stats()
-    assert st["fill_refreshes"] > 60
+    _say(f"uploads={st['table_uploads']} rebuilds={st['table_rebuilds']} patched={st['patched_appends']}")
+    assert st["patched_appends"] > 60
+    assert st["table_uploads"] <= st["table_rebuilds"] + 2
+    _same_table(ca, sh, "final table")
+
+
+@pytest.mark.parametrize("sf_group", [1, 8])
+def test_patched_single_appends_deep_private_tails(sf_group):
+    """ca_append of one token at a time onto sequences whose private tails span
+    several chunks, so the growing chunk sits at every position of its task
+    (with 8 chunks per task, past the refs carried inline in the record).
+    Midway a fresh workspace is attached: that step uploads the host plan,
+    whose fill counts were refreshed from the tree, and later appends patch
+    the new copy."""
+    _say(f"patched single appends sf_group={sf_group}")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import _capi
+    rng = np.random.default_rng(31)
+    H = 3
+    shared = list(range(70))
+    seqs = [shared + [900 + i] * n for i, n in enumerate([3, 64 * 4 + 10, 64 * 6 + 62, 64 * 7 + 1])]
+    wl = from_token_lists(seqs, heads=H, seed=32)
+    ca = build_ca(wl, capacity=80, sf_group=sf_group)
+    kv = {i: list(wl.seq_kv(i)) for i in range(wl.n_seq)}
+    uploads0 = None
+    for step in range(12):
+        for s in range(wl.n_seq):
+            k = rng.standard_normal((1, H, 128), dtype=np.float32).astype(np.float16)
+            v = rng.standard_normal((1, H, 128), dtype=np.float32).astype(np.float16)
+            ca.append(s, [5], torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+            kv[s][0] = np.concatenate([kv[s][0], k])
+            kv[s][1] = np.concatenate([kv[s][1], v])
+        if step == 6:
+            ws = torch.empty(ca.ws.numel(), dtype=torch.uint8, device="cuda:0")
+            torch.cuda.synchronize()
+            ca.ws = ws
+            assert ca.lib.ca_attach_workspace(ca.ctx, ws.data_ptr(), ws.numel()) == _capi.CA_OK
+        q = rng.standard_normal((wl.n_seq, H, 128), dtype=np.float32).astype(np.float16)
+        got = run_step(ca, q)
+        assert_parity(got, A.decode_step(q, [kv[s] for s in range(wl.n_seq)]), f"step {step}")
+        st = ca.stats()
+        if step == 1:
+            uploads0 = st["table_uploads"]
+        if step > 1:
+            # one upload when the 3rd sequence grows a new chunk (step 2),
+            # one for the new workspace (step 6); the rest are patched
+            assert st["table_uploads"] == uploads0 + (1 if step < 6 else 2), (step, st)
+    assert ca.stats()["patched_appends"] >= 4 * 9
+
+
