@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--no-comparator", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--prefix-len", type=int, default=None,
+                    help="instead of a numbered workload: 32 seq x 32 heads with this shared prefix length "
+                         "(any length, e.g. 1766) and --suffix-len private tokens each")
+    ap.add_argument("--suffix-len", type=int, default=512)
     ap.add_argument("--decode", action="store_true",
                     help="decode progression instead: n_s = 2048 shared prompt tokens, one token appended per "
                          "sequence per step (completion length n_c sweep at batch 32, batch sweep at n_c = 512)")
@@ -251,14 +255,21 @@ def main():
         sys.exit(2)
     import torch
     from decode_attention_prefix_tree_amd import ChunkAttention, load_workload, slots_needed
-    from workloads import CONFIG_NAMES, make_config
+    from workloads import CONFIG_NAMES, make_config, make_prefix_suffix
 
     torch.cuda.set_device(0)
     if args.decode:
         decode_main(args, torch)
         return
-    log(f"building workload {args.config}")
-    wl = make_config(args.config)
+    if args.prefix_len is not None:
+        wl = make_prefix_suffix(args.prefix_len, [args.suffix_len] * 32, heads=32,
+                                seed=2000 + args.prefix_len)
+        workload_name = "prefix-suffix: " + wl.description
+        args.config = None
+    else:
+        wl = make_config(args.config)
+        workload_name = CONFIG_NAMES[args.config]
+    log(f"building workload {workload_name}")
     ca = ChunkAttention(wl.heads, slots_needed(wl) + 8, device="cuda:0")
     load_workload(ca, wl)
     q = torch.from_numpy(wl.q).cuda()
@@ -319,7 +330,7 @@ def main():
     # unique KV bytes (each shared chunk once, each private chunk once).
     dom_t = float(lt[:, 0].mean()) * 1e-3
     roof = {"kernel": "partials_kernel", "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
-            "achieved": unique_b / dom_t / 1e9, "traffic": recorded_traffic(args.config),
+            "achieved": unique_b / dom_t / 1e9, "traffic": recorded_traffic(args.config) if args.config else None,
             "bytes_per_launch": unique_b, "avg_launch_us": dom_t * 1e6}
     roof["frac"] = roof["achieved"] / HBM_PEAK_GBPS
 
@@ -336,7 +347,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": CONFIG_NAMES[args.config], "n_seq": wl.n_seq, "heads": wl.heads,
+        "config": {"workload": workload_name, "n_seq": wl.n_seq, "heads": wl.heads,
                    "head_dim": wl.head_dim, "chunk": wl.chunk, "cache": "cold (1 GiB read before each step)"},
         "unique_kv_gbps": unique_b / t_mean / 1e9,
         "hbm_frac_unique": unique_b / t_mean / 1e9 / HBM_PEAK_GBPS,

@@ -11,7 +11,7 @@ import pytest
 from decode_attention_prefix_tree_amd import CaError, ChunkAttention, _capi
 from oracle.tree_model import PrefixTreeModel, TreeError
 from tests.golden_cases import load_cases
-from workloads import make_config
+from workloads import make_config, make_prefix_suffix
 
 
 def test_library_exports_every_declared_symbol():
@@ -203,6 +203,31 @@ def test_workload_tables_and_plan_sizes(k):
     # every shared chunk is read once per 32-row block, every private chunk once
     assert st["cf_chunk_reads"] == sum((r[5] - r[4] + 31) // 32 for r in shared)
     assert st["sf_chunk_reads"] == len(private)
+
+
+def test_non_aligned_prefix_at_scale():
+    """A 1,766-token shared prefix: the first insert cuts 27 full chunks and
+    a chunk holding the prefix's last 38 tokens and 26 suffix tokens; the
+    second insert splits that chunk at the divergence, so the tree shares 28
+    chunks, the last one partial, and the first sequence's tail starts with a
+    26-token chunk."""
+    wl = make_prefix_suffix(1766, [512] * 32, heads=1, seed=2001)
+    m = PrefixTreeModel(64, 10_000)
+    ca = ChunkAttention(32, 10_000, device=None)
+    for i in range(wl.n_seq):
+        t = wl.seq_tokens(i)
+        assert ca.insert(i, t) == m.insert(i, t)
+    model_and_lib_agree(m, ca)
+    st = ca.stats()
+    rows, _ = m.table()
+    shared = [r for r in rows if r[5] - r[4] >= 2]
+    assert len(shared) == 28 and st["shared_chunks"] == 28
+    assert sorted(r[3] for r in shared)[0] == 38 and sum(r[3] for r in shared) == 1766
+    assert st["unique_tokens"] == 1766 + 32 * 512
+    assert st["attended_tokens"] == 32 * 2278
+    tail0 = sorted((r for r in rows if r[5] - r[4] == 1 and r[4] == 0), key=lambda r: r[2])
+    assert [r[3] for r in tail0] == [26] + [64] * 7 + [38]
+    assert st["cf_chunk_reads"] == 28 and st["sf_chunk_reads"] == 9 + 31 * 8
 
 
 @pytest.mark.parametrize("k", [2, 5])

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 from oracle import attention as A
-from workloads import from_token_lists, make_config
+from workloads import from_token_lists, make_config, make_prefix_suffix
 
 pytestmark = pytest.mark.gpu
 
@@ -75,6 +75,99 @@ def test_workload_full(k):
     got = run_step(ca, wl.q)
     ref = A.decode_workload(wl)
     assert_parity(got, ref, f"config{k}")
+
+
+@pytest.mark.parametrize("two_phase", [True, False])
+def test_non_aligned_prefix_full(two_phase):
+    """A 1,766-token shared prefix (not a multiple of 64) with 512-token
+    suffixes, 32 sequences x 32 heads, every output row: the last shared
+    chunk holds 38 tokens and one private tail starts with a 26-token chunk."""
+    _say(f"prefix 1766 + 512, two_phase={two_phase}")
+    wl = make_prefix_suffix(1766, [512] * 32, heads=32, seed=2001)
+    ca = build_ca(wl, two_phase=two_phase)
+    assert_parity(run_step(ca, wl.q), A.decode_workload(wl), "prefix1766")
+
+
+def test_non_aligned_prefix_ragged_suffixes():
+    """The same prefix with suffix lengths 1..700 drawn per sequence, and with
+    no shared prefix at all (every sequence private, ragged)."""
+    rng = np.random.default_rng(2002)
+    for lp in (1766, 0):
+        suffix = [int(x) for x in rng.integers(1, 701, size=40)]
+        _say(f"prefix {lp} + ragged suffixes")
+        wl = make_prefix_suffix(lp, suffix, heads=8, seed=2003 + lp)
+        ca = build_ca(wl)
+        assert_parity(run_step(ca, wl.q), A.decode_workload(wl), f"prefix{lp} ragged")
+
+
+def test_insert_remove_churn():
+    """Random inserts (a prefix of a live sequence, cut anywhere, plus fresh
+    tokens, or an exact duplicate), removals and multi-token appends, with a
+    step after every operation checked against the oracle and the exported
+    table checked against the independent tree model.  Token ids never repeat
+    outside a copied prefix, so every stored prefix has one set of K/V rows."""
+    _say("churn")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import ChunkAttention
+    from oracle.tree_model import PrefixTreeModel
+    rng = np.random.default_rng(404)
+    H, cap = 4, 160
+    ca = ChunkAttention(H, cap, device="cuda:0")
+    model = PrefixTreeModel(64, cap)
+    live = {}          # seq id -> (tokens list, K [L,H,d], V [L,H,d])
+    fresh = iter(range(1, 1 << 30))
+    next_id = 0
+
+    def rows(n):
+        return (rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16),
+                rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16))
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+    for it in range(70):
+        r = rng.random()
+        if not live or (r < 0.45 and len(live) < 12):
+            if live and rng.random() < 0.8:
+                src = list(live)[int(rng.integers(len(live)))]
+                t0, k0, v0 = live[src]
+                p = int(rng.integers(1, len(t0) + 1))
+                extra = 0 if rng.random() < 0.15 else int(rng.integers(1, 200))
+            else:
+                t0, k0, v0, p, extra = [], None, None, 0, int(rng.integers(1, 300))
+            kn, vn = rows(extra)
+            toks = t0[:p] + [next(fresh) for _ in range(extra)]
+            k = np.concatenate([k0[:p], kn]) if p else kn
+            v = np.concatenate([v0[:p], vn]) if p else vn
+            if model.free_slots() < (len(toks) + 63) // 64 + 1:
+                continue
+            assert ca.insert(next_id, toks, dev(k), dev(v)) == model.insert(next_id, toks)
+            live[next_id] = (toks, k, v)
+            next_id += 1
+        elif r < 0.7 and len(live) > 1:
+            s = list(live)[int(rng.integers(len(live)))]
+            ca.remove(s)
+            model.remove(s)
+            del live[s]
+        else:
+            s = list(live)[int(rng.integers(len(live)))]
+            n = int(rng.integers(1, 90))
+            if model.free_slots() < (n + 63) // 64 + 1:
+                continue
+            kn, vn = rows(n)
+            toks = [next(fresh) for _ in range(n)]
+            ca.append(s, toks, dev(kn), dev(vn))
+            model.append(s, toks)
+            t0, k0, v0 = live[s]
+            live[s] = (t0 + toks, np.concatenate([k0, kn]), np.concatenate([v0, vn]))
+        order = sorted(live)
+        q = rng.standard_normal((len(order), H, 128), dtype=np.float32).astype(np.float16)
+        got = run_step(ca, q)
+        assert_parity(got, A.decode_step(q, [(live[s][1], live[s][2]) for s in order]), f"churn {it}")
+        want_rows, want_order = model.table()
+        got_rows, got_order = ca.export_table()
+        assert [tuple(int(x) for x in row) for row in got_rows] == want_rows, it
+        assert got_order == want_order, it
 
 
 def test_multi_branch_sampled_rows():

@@ -2,7 +2,7 @@
 
 import numpy as np
 
-from workloads import from_token_lists, make_config
+from workloads import from_token_lists, make_config, make_prefix_suffix
 
 
 def test_deterministic_and_shaped():
@@ -40,3 +40,16 @@ def test_token_list_workload_shares_rows_for_shared_prefixes():
     k1, v1 = wl.seq_kv(1)
     assert np.array_equal(k0[:2], k1[:2]) and not np.array_equal(k0[2], k1[2])
     assert np.array_equal(v0[:2], v1[:2])
+
+
+def test_prefix_suffix_workload():
+    wl = make_prefix_suffix(1766, [512] * 4, heads=2, seed=5)
+    again = make_prefix_suffix(1766, [512] * 4, heads=2, seed=5)
+    assert np.array_equal(wl.q, again.q)
+    assert [wl.seq_len(i) for i in range(4)] == [2278] * 4
+    assert wl.unique_tokens() == 1766 + 4 * 512
+    k0, _ = wl.seq_kv(0)
+    k3, _ = wl.seq_kv(3)
+    assert np.array_equal(k0[:1766], k3[:1766]) and not np.array_equal(k0[1766:], k3[1766:])
+    flat = make_prefix_suffix(0, [3, 70], heads=1, seed=5)
+    assert flat.paths == [[0], [1]] and flat.unique_tokens() == 73

@@ -42,6 +42,7 @@ __all__ = [
     "TokenListWorkload",
     "CONFIG_NAMES",
     "make_config",
+    "make_prefix_suffix",
     "from_token_lists",
     "segment_tokens",
 ]
@@ -160,6 +161,30 @@ def make_config(k: int, heads: int | None = None) -> Workload:
     q = rng.standard_normal((len(paths), h, d), dtype=np.float32).astype(np.float16)
     return Workload(name=f"config{k}", heads=h, head_dim=d, chunk=CHUNK, seed=1000 + k,
                     segments=segs, paths=paths, q=q, description=CONFIG_NAMES[k])
+
+
+def make_prefix_suffix(prefix_len: int, suffix_lens: Sequence[int], heads: int, seed: int,
+                       name: str | None = None) -> Workload:
+    """One shared prefix of ``prefix_len`` tokens (0 for none) and one private
+    suffix per sequence, drawn like the single-prefix workloads above: with
+    ``rng = default_rng(seed)``, K then V of the prefix, then of each suffix in
+    sequence order, then the queries.  Neither length needs to be a multiple
+    of the chunk size (a shared system prompt with six plugins reaches 1,766
+    tokens: paperlayer.ai summary of arXiv 2402.15220v4, sections 1 and 2.1)."""
+    rng = np.random.default_rng(seed)
+    d, n = HEAD_DIM, len(suffix_lens)
+    if prefix_len > 0:
+        segs = _draw_segments(rng, [prefix_len] + [int(x) for x in suffix_lens], heads, d)
+        paths = [[0, 1 + i] for i in range(n)]
+    else:
+        segs = _draw_segments(rng, [int(x) for x in suffix_lens], heads, d)
+        paths = [[i] for i in range(n)]
+    q = rng.standard_normal((n, heads, d), dtype=np.float32).astype(np.float16)
+    desc = f"{n} seq, {heads} heads, shared prefix {prefix_len} + private suffixes " + (
+        f"{suffix_lens[0]}" if len(set(int(x) for x in suffix_lens)) == 1 else
+        f"{min(suffix_lens)}..{max(suffix_lens)}")
+    return Workload(name=name or f"prefix{prefix_len}", heads=heads, head_dim=d, chunk=CHUNK, seed=seed,
+                    segments=segs, paths=paths, q=q, description=desc)
 
 
 @dataclass
