@@ -248,12 +248,11 @@ bool fill_patches(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, std::vecto
   constexpr int32_t kTaskInts = sizeof(chunkattn::SfTask) / sizeof(int32_t);
   constexpr int32_t kFillField = offsetof(chunkattn::SfTask, n_valid) / sizeof(int32_t);
   for (const chunkattn::KvOp& o : ops) {
-    auto it = o.node >= 0 ? p.private_ref.find(o.node) : p.private_ref.end();
-    if (it == p.private_ref.end()) {
+    const int32_t k = o.node >= 0 && static_cast<size_t>(o.node) < p.private_ref.size() ? p.private_ref[o.node] : -1;
+    if (k < 0) {
       out->clear();
       return false;
     }
-    const int32_t k = it->second;
     const int32_t task_off =
         p.ref_pos[k] < chunkattn::kSfInline ? tasks + p.ref_task[k] * kTaskInts + kFillField + p.ref_pos[k] : -1;
     out->push_back(FillPatch{refs + 2 * k + 1, task_off, o.dst_key0 + o.n_rows});

@@ -216,9 +216,28 @@ int32_t Manager::seq_len(int64_t seq) const {
   return it->second;
 }
 
+void Plan::clear() {
+  rows.clear();
+  dfs_seq.clear();
+  dfs_qrow.clear();
+  cf_units.clear();
+  sf_tasks.clear();
+  chunk_refs.clear();
+  row_node.clear();
+  ref_node.clear();
+  ref_task.clear();
+  ref_pos.clear();
+  private_ref.clear();
+  seq_parts.clear();
+  part_list.clear();
+  cf_tasks = 0;
+  n_parts = 0;
+  cf_chunk_reads = sf_chunk_reads = shared_chunks = shared_tokens = unique_tokens = attended_tokens = 0;
+}
+
 void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan) const {
   Plan& P = *plan;
-  P = Plan();
+  P.clear();
 
   // Caller row of each sequence: rank in ascending id order.
   std::map<int64_t, int32_t> qrow;
@@ -370,6 +389,7 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
   // where each chunk ref lives, so a fill change can be patched in place
   P.ref_task.assign(P.ref_node.size(), -1);
   P.ref_pos.assign(P.ref_node.size(), -1);
+  P.private_ref.assign(nodes_.size(), -1);
   for (size_t t = 0; t < P.sf_tasks.size(); ++t)
     for (int c = 0; c < P.sf_tasks[t].n_chunks; ++c) {
       const int32_t k = P.sf_tasks[t].chunk_begin + c;

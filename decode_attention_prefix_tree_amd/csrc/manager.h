@@ -100,7 +100,7 @@ struct Plan {
   std::vector<int32_t> ref_node;    // manager node index of each chunk ref
   std::vector<int32_t> ref_task;    // sequence-first task holding the ref (-1: chunk-first)
   std::vector<int32_t> ref_pos;     // position of the ref within that task
-  std::map<int32_t, int32_t> private_ref;  // node -> its ref, for chunks of one sequence
+  std::vector<int32_t> private_ref; // per manager node: its ref if the chunk has one sequence, else -1
   std::vector<int32_t> seq_parts;   // (first, count) into part_list, per DFS position
   std::vector<int32_t> part_list;   // partial ids, per sequence in merge order
   int32_t n_parts = 0;
@@ -110,6 +110,10 @@ struct Plan {
   int64_t shared_tokens = 0;
   int64_t unique_tokens = 0;
   int64_t attended_tokens = 0;
+
+  // Empty every list but keep its storage (plans are rebuilt often while
+  // decoding, at about the same size).
+  void clear();
 };
 
 class Manager {
