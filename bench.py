@@ -348,7 +348,8 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": workload_name, "n_seq": wl.n_seq, "heads": wl.heads,
-                   "head_dim": wl.head_dim, "chunk": wl.chunk, "cache": "cold (1 GiB read before each step)"},
+                   "head_dim": wl.head_dim, "chunk": wl.chunk, "cache": "cold (1 GiB read before each step)",
+                   "cf_chunks_per_task": st["cf_chunks_per_task"], "sf_chunks_per_task": 4},
         "unique_kv_gbps": unique_b / t_mean / 1e9,
         "hbm_frac_unique": unique_b / t_mean / 1e9 / HBM_PEAK_GBPS,
         "queries_per_s": wl.n_seq / t_mean,

@@ -62,6 +62,7 @@ class ca_stats_t(ctypes.Structure):
         ("fill_refreshes", ctypes.c_int64),
         ("table_uploads", ctypes.c_int64),
         ("patched_appends", ctypes.c_int64),
+        ("cf_chunks_per_task", ctypes.c_int64),
     ]
 
 

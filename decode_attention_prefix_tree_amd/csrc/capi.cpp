@@ -23,7 +23,9 @@ struct ca_ctx {
   bool pool_attached = false;
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  int cf_group = 8, sf_group = 4;
+  int cf_group = 0, sf_group = 4;  // cf_group 0: chosen per plan (auto_cf_group)
+  int cf_auto = 8;                 // the last automatic choice
+  int plan_cf_group = 8;           // the group the current plan was built with
   bool fused_merge = false;
 
   // plan cache: rebuilt after the tree changes, uploaded when stale
@@ -98,6 +100,22 @@ bool device_table_current(const ca_ctx* c) { return c->uploaded_version == c->ve
 
 // with_fills: the host plan's fill counts are needed too (an upload, an
 // export, stats); a step whose device table is current does not need them.
+// Chunks per chunk-first task when the caller leaves it open.  A
+// chunk-first wave walks its chunks one 32-key half after another, each
+// half a dependent round trip to memory, and while the step saturates HBM a
+// round trip waits behind everything in flight (about 6 us on MI355X).  The
+// longest such chain should stay within half of the step's own streaming
+// time (unique KV bytes at about 6 TB/s), or the chunk-first blocks become
+// the step's tail; within that bound larger groups mean fewer partials.
+int auto_cf_group(const chunkattn::Plan& p, int heads, int head_dim) {
+  const double kernel_us = static_cast<double>(p.unique_tokens) * 4.0 * heads * head_dim / 6.0e6;
+  for (int g : {16, 8}) {
+    const int halves = 2 * ((g + 3) / 4);
+    if (halves * 6.0 <= 0.5 * kernel_us) return g;
+  }
+  return 4;
+}
+
 void ensure_plan(ca_ctx* c, bool with_fills = true) {
   if (c->plan_valid) {
     if (c->fills_stale && with_fills) {
@@ -111,7 +129,15 @@ void ensure_plan(ca_ctx* c, bool with_fills = true) {
     return;
   }
   auto t0 = std::chrono::steady_clock::now();
-  c->mgr.build_plan(c->cf_group, c->sf_group, (c->flags & CA_CREATE_NO_CHUNK_FIRST) == 0, &c->plan);
+  const bool two_phase = (c->flags & CA_CREATE_NO_CHUNK_FIRST) == 0;
+  const int g = c->cf_group ? c->cf_group : c->cf_auto;
+  c->mgr.build_plan(g, c->sf_group, two_phase, &c->plan);
+  if (c->cf_group == 0 && two_phase && c->plan.shared_chunks > 0) {
+    const int want = auto_cf_group(c->plan, c->heads, c->head_dim);
+    if (want != g) c->mgr.build_plan(want, c->sf_group, two_phase, &c->plan);
+    c->cf_auto = want;
+  }
+  c->plan_cf_group = c->cf_group ? c->cf_group : c->cf_auto;
   c->mgr.clear_structural();
   c->fills_stale = false;
   const chunkattn::Plan& p = c->plan;
@@ -379,7 +405,7 @@ int ca_attach_workspace(ca_ctx* ctx, void* dev, size_t bytes) {
 int ca_set_option(ca_ctx* ctx, int option, int value) {
   CA_GUARD(ctx, {
     if (option == CA_OPT_CF_CHUNKS_PER_TASK) {
-      if (value < 1 || value > 64) throw Error(CA_E_INVALID_ARG, "chunk-first group must be 1..64");
+      if (value < 0 || value > 64) throw Error(CA_E_INVALID_ARG, "chunk-first group must be 0 (auto) or 1..64");
       ctx->cf_group = value;
     } else if (option == CA_OPT_SF_CHUNKS_PER_TASK) {
       if (value < 1 || value > 256) throw Error(CA_E_INVALID_ARG, "sequence-first group must be 1..256");
@@ -561,6 +587,7 @@ int ca_stats(ca_ctx* ctx, ca_stats_t* out) {
     s.fill_refreshes = ctx->fill_refreshes;
     s.table_uploads = ctx->table_uploads;
     s.patched_appends = ctx->patched_appends;
+    s.cf_chunks_per_task = ctx->plan_cf_group;
     *out = s;
     return CA_OK;
   });

@@ -384,7 +384,9 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
 // loads in flight per CU.
 template <bool kFuse>
 __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logical) {
-  const int task = logical % a.n_sf_tasks, head = logical / a.n_sf_tasks;
+  // heads vary fastest: blocks that run together read neighbouring 32 KiB
+  // tiles of the same slots, which keeps HBM accesses close to sequential
+  const int task = logical / a.heads, head = logical % a.heads;
   const int* t = a.sf_tasks + task * 16;
   const int chunk_begin = t[0], n_chunks = t[1], dfs_pos = t[2], part_id = t[3], qrow = t[4];
   // wave index in an SGPR: chunk lookups and tile bases stay scalar

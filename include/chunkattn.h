@@ -74,7 +74,10 @@ enum {
 
 /* ca_set_option keys. */
 enum {
-  CA_OPT_CF_CHUNKS_PER_TASK = 1, /* chunks of one shared run per chunk-first task (1..64), default 8 */
+  CA_OPT_CF_CHUNKS_PER_TASK = 1, /* chunks of one shared run per chunk-first task (1..64), or 0
+                                    (default): chosen per plan, 4, 8 or 16, so that a chunk-first
+                                    wave's chain of dependent tile loads stays well inside the
+                                    step's streaming time (ca_stats reports the choice) */
   CA_OPT_SF_CHUNKS_PER_TASK = 2, /* private chunks per sequence-first task (1..256), default 4 */
   CA_OPT_FUSED_MERGE = 3         /* 0 (default): a step is a partials launch and a merge launch;
                                     1: one launch, the last block to finish a (sequence, head)
@@ -120,6 +123,7 @@ typedef struct ca_stats_t {
   int64_t table_uploads;     /* host-to-device copies of the chunk table */
   int64_t patched_appends;   /* appends whose fill counts the write launch
                                 stored into the device table itself */
+  int64_t cf_chunks_per_task; /* chunk-first group of the current plan */
 } ca_stats_t;
 
 /* Bytes of one chunk slot: K and V, all heads, fp16 = 4 * heads * chunk_size

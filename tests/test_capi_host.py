@@ -230,6 +230,25 @@ def test_non_aligned_prefix_at_scale():
     assert st["cf_chunk_reads"] == 28 and st["sf_chunk_reads"] == 9 + 31 * 8
 
 
+@pytest.mark.parametrize("k,want", [(1, 4), (2, 4), (3, 8), (5, 16)])
+def test_automatic_chunk_first_group(k, want):
+    """With the group left open, the longest chunk-first chain (2 halves per
+    chunk of a wave, about 6 us each) must fit in half of the step's
+    streaming time at 6 TB/s: 285 MB (workload 2) allows one chunk per wave,
+    335 MB two, 1.2 GB four.  An explicit setting wins."""
+    wl = make_config(k, heads=1)
+    ca = ChunkAttention(32, 10_000, device=None)
+    for i in range(wl.n_seq):
+        ca.insert(i, wl.seq_tokens(i))
+    assert ca.stats()["cf_chunks_per_task"] == want
+    ca.set_option(_capi.CA_OPT_CF_CHUNKS_PER_TASK, 8)
+    assert ca.stats()["cf_chunks_per_task"] == 8
+    ca.set_option(_capi.CA_OPT_CF_CHUNKS_PER_TASK, 0)
+    assert ca.stats()["cf_chunks_per_task"] == want
+    with pytest.raises(CaError):
+        ca.set_option(_capi.CA_OPT_CF_CHUNKS_PER_TASK, 65)
+
+
 @pytest.mark.parametrize("k", [2, 5])
 def test_no_chunk_first_mode_keeps_tree_and_streams_whole_paths(k):
     """The PagedAttn*-style mode shares storage exactly like the two-phase
