@@ -228,6 +228,8 @@ chunkattn::StepArgs step_args(ca_ctx* c, const void* q, void* out) {
   a.part_ms = reinterpret_cast<float*>(w + c->off_part_ms);
   a.arrivals = reinterpret_cast<int*>(w + c->off_arrivals);
   a.heads = c->heads;
+  a.dense_parts = p.dense_parts;
+  a.part_stride = p.part_stride;
   a.n_cf_units = static_cast<int>(p.cf_units.size());
   a.n_sf_tasks = static_cast<int>(p.sf_tasks.size());
   a.n_seq = static_cast<int>(p.dfs_seq.size());

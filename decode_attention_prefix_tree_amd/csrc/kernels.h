@@ -10,6 +10,7 @@ constexpr int kHeadDim = 128;
 constexpr int kChunk = 64;
 constexpr int kCfInline = 8;   // chunk refs carried by a chunk-first unit record
 constexpr int kSfInline = 4;   // chunk refs carried by a sequence-first task record
+constexpr int kDenseParts = 16; // most partials per sequence for the dense partial layout
 
 // Arguments of one decode step.  All pointers are device addresses.
 struct StepArgs {
@@ -26,6 +27,8 @@ struct StepArgs {
   float* part_ms;              // [n_parts][H][2]: running max (log2 units), sum
   int* arrivals;               // [n_seq][H] partials done this step; 0 between steps
   int heads;
+  int dense_parts;             // > 0: sequence i's j-th partial is i * dense_parts + j (j < count)
+  int part_stride;             // partial id step between rows of a chunk-first unit
   int n_cf_units;
   int n_sf_tasks;
   int n_seq;

@@ -221,6 +221,7 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
   const int unit = logical % a.n_cf_units, head = logical / a.n_cf_units;
   const int* u = a.cf_units + unit * 32;
   const int chunk_begin = u[0], n_chunks = u[1], row_begin = u[2], n_rows = u[3], part_base = u[4];
+  const int qrow_base = u[5];  // >= 0: the rows' caller rows are qrow_base + row
   // wave index in an SGPR: chunk lookups and tile bases stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, half = lane >> 5, i = lane & 31;
@@ -234,7 +235,7 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
     const int row = p >> 4, c16 = p & 15, kk = c16 >> 1, hf = c16 & 1;
     h8 v = h8{};
     if (row < n_rows) {
-      const int qrow = a.dfs_qrow[row_begin + row];
+      const int qrow = qrow_base >= 0 ? qrow_base + row : a.dfs_qrow[row_begin + row];
       v = *reinterpret_cast<const h8*>(static_cast<const _Float16*>(a.q) +
                                        (static_cast<size_t>(qrow) * H + head) * D + c16 * 8);
     }
@@ -346,7 +347,7 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
   if (wave != 0) return;
   take(0);
   if (i < n_rows) {
-    const size_t pid = static_cast<size_t>(part_base + i) * H + head;
+    const size_t pid = static_cast<size_t>(part_base + i * a.part_stride) * H + head;
     float* po = a.part_o + pid * D;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -539,11 +540,59 @@ __global__ __launch_bounds__(256, 3) void partials_kernel(StepArgs a, int n_cf, 
     sequence_first_block<kFuse>(a, b - n_cf);
 }
 
+// Merge of one (sequence, head) with the dense partial layout: partial j of
+// the sequence at DFS position pos is pos * P + j, so every load of the merge
+// (the count, the caller row, all (m, s) and o rows) is issued at once and
+// the merge costs one round trip to memory.  Slots past the sequence's count
+// are loaded but never used.  Same fold as merge_one: M = max m_j,
+// w_j = e^{m_j - M}, s = sum w_j s_j (wave sum), o = sum w_j o_j in list
+// order, out = o / s in fp16.
+__device__ __forceinline__ void merge_dense(const StepArgs& a, int pos, int head, int lane) {
+  const int H = a.heads, P = a.dense_parts;
+  const int cnt = a.seq_parts[2 * pos + 1];
+  const int qrow = a.dfs_qrow[pos];
+  float my_m = -INFINITY, my_s = 0.f;
+  if (lane < P) {
+    const size_t pid = static_cast<size_t>(pos * P + lane) * H + head;
+    my_m = a.part_ms[pid * 2];
+    my_s = a.part_ms[pid * 2 + 1];
+  }
+  float2 ov[kDenseParts];
+#pragma unroll
+  for (int j = 0; j < kDenseParts; ++j)
+    if (j < P)
+      ov[j] = *reinterpret_cast<const float2*>(a.part_o + (static_cast<size_t>(pos * P + j) * H + head) * D +
+                                               2 * lane);
+  if (lane >= cnt) {
+    my_m = -INFINITY;
+    my_s = 0.f;
+  }
+  const float M = wave_max32(max_halves(my_m));
+  const float my_w = lane < cnt ? exp2f(my_m - M) : 0.f;
+  const float s = wave_sum64(my_w * my_s);
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < kDenseParts; ++j) {
+    if (j < cnt) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+      o0 = fmaf(w, ov[j].x, o0);
+      o1 = fmaf(w, ov[j].y, o1);
+    }
+  }
+  const float inv = 1.0f / s;
+  _Float16* out = static_cast<_Float16*>(a.out) + (static_cast<size_t>(qrow) * H + head) * D + 2 * lane;
+  h2 res = {static_cast<_Float16>(o0 * inv), static_cast<_Float16>(o1 * inv)};
+  *reinterpret_cast<h2*>(out) = res;
+}
+
 // Merge of every (sequence, head), four per block (the unfused step).
 __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= a.n_seq * a.heads) return;
-  merge_one<false>(a, item / a.heads, item % a.heads, threadIdx.x & 63);
+  if (a.dense_parts > 0)
+    merge_dense(a, item / a.heads, item % a.heads, threadIdx.x & 63);
+  else
+    merge_one<false>(a, item / a.heads, item % a.heads, threadIdx.x & 63);
 }
 
 }  // namespace

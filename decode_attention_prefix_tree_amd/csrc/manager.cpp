@@ -13,6 +13,7 @@ constexpr int kNoCapacity = -3;
 constexpr int kDupSeq = -4;
 constexpr int kUnknownSeq = -5;
 constexpr int kState = -10;
+constexpr int kInternal = -11;
 }  // namespace
 
 Manager::Manager(int chunk, bool share) : C_(chunk), share_(share) {
@@ -232,6 +233,8 @@ void Plan::clear() {
   part_list.clear();
   cf_tasks = 0;
   n_parts = 0;
+  dense_parts = 0;
+  part_stride = 1;
   cf_chunk_reads = sf_chunk_reads = shared_chunks = shared_tokens = unique_tokens = attended_tokens = 0;
 }
 
@@ -283,7 +286,7 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
   // as its parent continues the parent's run (a chain: one child, nobody
   // ends at the parent); a run holds at most cf_group chunks.
   std::vector<int32_t> task_of_row(n_rows, -1);
-  struct Task { int32_t b, e, chunk_begin, n_chunks, last_row, part_base; };
+  struct Task { int32_t b, e, chunk_begin, n_chunks, last_row; };
   std::vector<Task> tasks;
   for (int32_t r = 0; r < n_rows; ++r) {
     int32_t b = R(r, 4), e = R(r, 5), p = R(r, 1);
@@ -299,16 +302,16 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
       tasks[t].last_row = r;
     } else {
       t = static_cast<int32_t>(tasks.size());
-      tasks.push_back({b, e, -1, 1, r, 0});
+      tasks.push_back({b, e, -1, 1, r});
     }
     task_of_row[r] = t;
   }
-  // chunk refs of each run, in row order
+  // chunk refs of each run, in row order; its 32-row units (partial ids later)
+  std::vector<int32_t> unit_task;
   {
     std::vector<std::vector<int32_t>> task_rows(tasks.size());
     for (int32_t r = 0; r < n_rows; ++r)
       if (task_of_row[r] >= 0) task_rows[task_of_row[r]].push_back(r);
-    int32_t parts = 0;
     for (size_t t = 0; t < tasks.size(); ++t) {
       tasks[t].chunk_begin = static_cast<int32_t>(P.chunk_refs.size() / 2);
       for (int32_t r : task_rows[t]) {
@@ -316,8 +319,6 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
         P.chunk_refs.push_back(R(r, 3));
         P.ref_node.push_back(row_node[r]);
       }
-      tasks[t].part_base = parts;
-      parts += tasks[t].e - tasks[t].b;
       P.cf_chunk_reads += tasks[t].n_chunks * ((tasks[t].e - tasks[t].b + 31) / 32);
       for (int32_t rb = 0; rb * 32 < tasks[t].e - tasks[t].b; ++rb) {
         CfUnit u{};
@@ -325,33 +326,38 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
         u.n_chunks = tasks[t].n_chunks;
         u.row_begin = tasks[t].b + rb * 32;
         u.n_rows = std::min(32, tasks[t].e - tasks[t].b - rb * 32);
-        u.part_base = tasks[t].part_base + rb * 32;
+        u.qrow_base = P.dfs_qrow[u.row_begin];
+        for (int r = 1; r < u.n_rows; ++r)
+          if (P.dfs_qrow[u.row_begin + r] != u.qrow_base + r) u.qrow_base = -1;
         for (int c = 0; c < kCfInline && c < u.n_chunks; ++c) {
           u.slot[c] = P.chunk_refs[2 * (u.chunk_begin + c)];
           u.n_valid[c] = P.chunk_refs[2 * (u.chunk_begin + c) + 1];
         }
         P.cf_units.push_back(u);
+        unit_task.push_back(static_cast<int32_t>(t));
       }
     }
-    P.n_parts = parts;
     P.cf_tasks = static_cast<int64_t>(tasks.size());
   }
 
   // Pass 3: per sequence, the shared runs on its path (root first) and its
-  // private chunks cut into sequence-first tasks.
-  P.seq_parts.assign(static_cast<size_t>(n_seq) * 2, 0);
+  // private chunks cut into sequence-first tasks.  entries[ent_first[i] + j]
+  // is the j-th partial of sequence i in merge order: a run t (t >= 0) or a
+  // sequence-first task k (-1 - k).
+  std::vector<int32_t> ent_first(static_cast<size_t>(n_seq) + 1, 0), entries;
   std::vector<int32_t> path;
+  int32_t max_parts = 0;
   for (int32_t i = 0; i < n_seq; ++i) {
     path.clear();
     for (int32_t r = end_row[i]; r >= 0; r = R(r, 1)) path.push_back(r);
     std::reverse(path.begin(), path.end());
-    int32_t first = static_cast<int32_t>(P.part_list.size());
+    ent_first[i] = static_cast<int32_t>(entries.size());
     int32_t last_task = -1;
     std::vector<int32_t> priv;
     for (int32_t r : path) {
       int32_t t = task_of_row[r];
       if (t >= 0) {
-        if (t != last_task) P.part_list.push_back(tasks[t].part_base + (i - tasks[t].b));
+        if (t != last_task) entries.push_back(t);
         last_task = t;
       } else {
         priv.push_back(r);
@@ -363,7 +369,7 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
       st.chunk_begin = static_cast<int32_t>(P.chunk_refs.size() / 2);
       st.n_chunks = static_cast<int32_t>(stop - j);
       st.dfs_pos = i;
-      st.part_id = P.n_parts++;
+      st.part_id = -1;
       st.qrow = P.dfs_qrow[i];
       for (size_t q = j; q < stop; ++q) {
         const int c = static_cast<int>(q - j);
@@ -376,11 +382,58 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
         P.ref_node.push_back(row_node[priv[q]]);
       }
       P.sf_chunk_reads += st.n_chunks;
+      entries.push_back(-1 - static_cast<int32_t>(P.sf_tasks.size()));
       P.sf_tasks.push_back(st);
-      P.part_list.push_back(st.part_id);
     }
-    P.seq_parts[2 * i] = first;
-    P.seq_parts[2 * i + 1] = static_cast<int32_t>(P.part_list.size()) - first;
+    max_parts = std::max(max_parts, static_cast<int32_t>(entries.size()) - ent_first[i]);
+  }
+  ent_first[n_seq] = static_cast<int32_t>(entries.size());
+
+  // Partial ids.  Dense (a sequence's j-th partial is i * max_parts + j) when
+  // a sequence has at most kDenseParts partials: the merge then computes
+  // every address from the sequence's position and fetches all of them in
+  // one round trip.  Otherwise compact ids: a run's rows take consecutive
+  // ids, then the sequence-first tasks.
+  P.dense_parts = max_parts <= kDenseParts ? max_parts : 0;
+  std::vector<int32_t> task_part(tasks.size(), -1);  // dense: slot j; compact: base id
+  if (P.dense_parts) {
+    P.part_stride = max_parts;
+    for (int32_t i = 0; i < n_seq; ++i)
+      for (int32_t j = 0; ent_first[i] + j < ent_first[i + 1]; ++j) {
+        const int32_t e = entries[ent_first[i] + j];
+        if (e >= 0) {
+          if (task_part[e] >= 0 && task_part[e] != j) throw Error(kInternal, "plan: run at two list positions");
+          task_part[e] = j;
+        } else {
+          P.sf_tasks[-1 - e].part_id = i * max_parts + j;
+        }
+      }
+    P.n_parts = n_seq * max_parts;
+  } else {
+    P.part_stride = 1;
+    int32_t parts = 0;
+    for (size_t t = 0; t < tasks.size(); ++t) {
+      task_part[t] = parts;
+      parts += tasks[t].e - tasks[t].b;
+    }
+    for (SfTask& st : P.sf_tasks) st.part_id = parts++;
+    P.n_parts = parts;
+  }
+  for (size_t k = 0; k < P.cf_units.size(); ++k) {
+    CfUnit& u = P.cf_units[k];
+    const Task& tk = tasks[unit_task[k]];
+    u.part_base = P.dense_parts ? u.row_begin * P.part_stride + task_part[unit_task[k]]
+                                : task_part[unit_task[k]] + (u.row_begin - tk.b);
+  }
+  P.seq_parts.assign(static_cast<size_t>(n_seq) * 2, 0);
+  for (int32_t i = 0; i < n_seq; ++i) {
+    P.seq_parts[2 * i] = static_cast<int32_t>(P.part_list.size());
+    for (int32_t q = ent_first[i]; q < ent_first[i + 1]; ++q) {
+      const int32_t e = entries[q];
+      P.part_list.push_back(e >= 0 ? (P.dense_parts ? i * P.part_stride + task_part[e] : task_part[e] + (i - tasks[e].b))
+                                   : P.sf_tasks[-1 - e].part_id);
+    }
+    P.seq_parts[2 * i + 1] = ent_first[i + 1] - ent_first[i];
   }
   // Longest sequence-first tasks first: they start earliest, and the four
   // waves of a block get tasks of about the same length.

@@ -69,8 +69,9 @@ struct CfUnit {        // chunk-first: one 32-row block of one run of shared chu
   int32_t n_chunks;
   int32_t row_begin;   // DFS position of the block's first row
   int32_t n_rows;      // 1..32
-  int32_t part_base;   // partial id of the block's first row
-  int32_t pad[3];
+  int32_t part_base;   // partial id of the block's first row; row r's is part_base + r * part_stride
+  int32_t qrow_base;   // caller row of the first row if the rows' caller rows are consecutive, else -1
+  int32_t pad[2];
   int32_t slot[kCfInline];
   int32_t n_valid[kCfInline];
   int32_t pad2[8];     // 128 bytes
@@ -103,7 +104,9 @@ struct Plan {
   std::vector<int32_t> private_ref; // per manager node: its ref if the chunk has one sequence, else -1
   std::vector<int32_t> seq_parts;   // (first, count) into part_list, per DFS position
   std::vector<int32_t> part_list;   // partial ids, per sequence in merge order
-  int32_t n_parts = 0;
+  int32_t n_parts = 0;              // partial slots (dense: n_seq * dense_parts)
+  int32_t dense_parts = 0;          // > 0: sequence i's j-th partial has id i * dense_parts + j
+  int32_t part_stride = 1;          // id step between consecutive rows of a chunk-first unit
   int64_t cf_chunk_reads = 0;       // per head
   int64_t sf_chunk_reads = 0;       // per head
   int64_t shared_chunks = 0;
