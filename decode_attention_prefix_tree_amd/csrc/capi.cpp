@@ -27,6 +27,7 @@ struct ca_ctx {
   int cf_auto = 8;                 // the last automatic choice
   int plan_cf_group = 8;           // the group the current plan was built with
   bool fused_merge = false;
+  unsigned fuse_epoch = 0;          // one-launch steps since the last table upload
 
   // plan cache: rebuilt after the tree changes, uploaded when stale
   chunkattn::Plan plan;
@@ -207,6 +208,7 @@ void upload(ca_ctx* c, void* stream) {
   hip_check(hipEventRecord(c->stage_done[b], static_cast<hipStream_t>(stream)), "hipEventRecord");
   c->stage_pending[b] = true;
   c->table_uploads += 1;
+  c->fuse_epoch = 0;  // the upload zeroed the arrival counters
   c->uploaded_version = c->version;
   c->uploaded_ws = c->ws;
 }
@@ -226,7 +228,7 @@ chunkattn::StepArgs step_args(ca_ctx* c, const void* q, void* out) {
   a.part_list = reinterpret_cast<const int32_t*>(w + c->off_partlist);
   a.part_o = reinterpret_cast<float*>(w + c->off_part_o);
   a.part_ms = reinterpret_cast<float*>(w + c->off_part_ms);
-  a.arrivals = reinterpret_cast<int*>(w + c->off_arrivals);
+  a.arrivals = reinterpret_cast<unsigned*>(w + c->off_arrivals);
   a.heads = c->heads;
   a.dense_parts = p.dense_parts;
   a.part_stride = p.part_stride;
@@ -506,11 +508,11 @@ int ca_attend_phase(ca_ctx* ctx, int phase, const void* q_dev, void* out_dev, vo
     upload(ctx, stream);
     chunkattn::StepArgs a = step_args(ctx, q_dev, out_dev);
     if (phase == CA_PHASE_CHUNK_FIRST)
-      launch(chunkattn::launch_partials(a, chunkattn::kPartsChunkFirst, false, stream), "partials");
+      launch(chunkattn::launch_partials(a, chunkattn::kPartsChunkFirst, false, 0, stream), "partials");
     else if (phase == CA_PHASE_SEQUENCE_FIRST)
-      launch(chunkattn::launch_partials(a, chunkattn::kPartsSequenceFirst, false, stream), "partials");
+      launch(chunkattn::launch_partials(a, chunkattn::kPartsSequenceFirst, false, 0, stream), "partials");
     else if (phase == CA_PHASE_PARTIALS)
-      launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, false, stream), "partials");
+      launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, false, 0, stream), "partials");
     else if (phase == CA_PHASE_MERGE)
       launch(chunkattn::launch_merge(a, stream), "merge");
     else
@@ -525,9 +527,9 @@ int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream) {
     upload(ctx, stream);
     chunkattn::StepArgs a = step_args(ctx, q_dev, out_dev);
     if (ctx->fused_merge) {
-      launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, true, stream), "partials+merge");
+      launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, true, ++ctx->fuse_epoch, stream), "step");
     } else {
-      launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, false, stream), "partials");
+      launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, false, 0, stream), "partials");
       launch(chunkattn::launch_merge(a, stream), "merge");
     }
     return CA_OK;

@@ -25,7 +25,7 @@ struct StepArgs {
   const int32_t* part_list;    // partial ids
   float* part_o;               // [n_parts][H][128]
   float* part_ms;              // [n_parts][H][2]: running max (log2 units), sum
-  int* arrivals;               // [n_seq][H] partials done this step; 0 between steps
+  unsigned* arrivals;          // [n_seq][H] partials written by one-launch steps since the upload
   int heads;
   int dense_parts;             // > 0: sequence i's j-th partial is i * dense_parts + j (j < count)
   int part_stride;             // partial id step between rows of a chunk-first unit
@@ -40,10 +40,11 @@ enum PartialsPart { kPartsBoth = 0, kPartsChunkFirst = 1, kPartsSequenceFirst = 
 
 // Each returns a hipError_t value (0 = success) from the launch.
 // One grid with the chunk-first blocks first and the sequence-first blocks
-// after them; `part` restricts the launch to one side.  With fuse_merge the
-// last block to finish a (sequence, head) also merges it and writes out (the
-// whole step in one launch; needs part == kPartsBoth).
-int launch_partials(const StepArgs& a, int part, bool fuse_merge, void* stream);
+// after them; `part` restricts the launch to one side.  With fuse_merge (and
+// part == kPartsBoth) merge blocks close the grid and write out: the whole
+// step in one launch; epoch counts the one-launch steps since the table (with
+// its arrival counters) was uploaded, this one included.
+int launch_partials(const StepArgs& a, int part, bool fuse_merge, unsigned epoch, void* stream);
 int launch_merge(const StepArgs& a, void* stream);
 
 }  // namespace chunkattn

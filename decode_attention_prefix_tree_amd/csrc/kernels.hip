@@ -91,12 +91,12 @@ __device__ __forceinline__ h2 lo2(h8 v, int j) {
   }
 }
 
-// Step-local communication between blocks (the fused merge).  Partials are
-// written with agent-scope relaxed atomic stores and read back with
+// Step-local communication between blocks (the one-launch step).  Partials
+// are written with agent-scope relaxed atomic stores and read back with
 // agent-scope atomic loads: both are coherent across the XCDs by themselves
 // (global_store/global_load with sc1), so no cache-wide write-back or
 // invalidate is needed.  A writer waits for its stores to complete before it
-// counts its arrival, so the block that sees the final count reads complete
+// counts its arrival, so a merger that sees the full count reads complete
 // data.
 __device__ __forceinline__ void store_agent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -177,19 +177,105 @@ __device__ __forceinline__ void merge_one(const StepArgs& a, int pos, int head, 
   *reinterpret_cast<h2*>(out) = res;
 }
 
-// Arrival of one partial of (pos, head).  Called after the caller's partial
-// stores and an agent-scope release fence; returns true for the block whose
-// partial completes the set, which then owns the merge (and clears the
-// counter for the next step after an acquire fence).
-__device__ __forceinline__ bool arrive(const StepArgs& a, int pos, int head) {
-  const int old = atomicAdd(a.arrivals + pos * a.heads + head, 1);
-  return old == a.seq_parts[2 * pos + 1] - 1;
+// One more partial of (pos, head) is written (called once the caller's
+// partial stores have completed).  The counters only grow: every one-launch
+// step adds each sequence's partial count, and they restart from zero when the
+// table is uploaded.
+__device__ __forceinline__ void arrive(const StepArgs& a, int pos, int head) {
+  __hip_atomic_fetch_add(a.arrivals + pos * a.heads + head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void merge_and_reset(const StepArgs& a, int pos, int head, int lane) {
-  merge_one<true>(a, pos, head, lane);
-  if (lane == 0)
-    __hip_atomic_store(a.arrivals + pos * a.heads + head, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Merge of one (sequence, head) with the dense partial layout: partial j of
+// the sequence at DFS position pos is pos * P + j, so every load of the merge
+// (all (m, s) and o rows) is issued at once, together with the caller's
+// loads of cnt and qrow, and the merge costs one round trip to memory.
+// Slots past the sequence's count are loaded but never used.  Same fold as
+// merge_one: M = max m_j, w_j = e^{m_j - M}, s = sum w_j s_j (wave sum),
+// o = sum w_j o_j in list order, out = o / s in fp16.
+template <bool kCoherent>
+__device__ __forceinline__ void merge_dense(const StepArgs& a, int pos, int head, int lane, int cnt, int qrow) {
+  const int H = a.heads, P = a.dense_parts;
+  float my_m = -INFINITY, my_s = 0.f;
+  if (lane < P) {
+    const size_t pid = static_cast<size_t>(pos * P + lane) * H + head;
+    my_m = ld<kCoherent>(a.part_ms + pid * 2);
+    my_s = ld<kCoherent>(a.part_ms + pid * 2 + 1);
+  }
+  float2 ov[kDenseParts];
+#pragma unroll
+  for (int j = 0; j < kDenseParts; ++j)
+    if (j < P) {
+      const float* src = a.part_o + (static_cast<size_t>(pos * P + j) * H + head) * D + 2 * lane;
+      if constexpr (kCoherent) {
+        ov[j].x = load_agent(src);
+        ov[j].y = load_agent(src + 1);
+      } else {
+        ov[j] = *reinterpret_cast<const float2*>(src);
+      }
+    }
+  if (lane >= cnt) {
+    my_m = -INFINITY;
+    my_s = 0.f;
+  }
+  const float M = wave_max32(max_halves(my_m));
+  const float my_w = lane < cnt ? exp2f(my_m - M) : 0.f;
+  const float s = wave_sum64(my_w * my_s);
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < kDenseParts; ++j) {
+    if (j < cnt) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+      o0 = fmaf(w, ov[j].x, o0);
+      o1 = fmaf(w, ov[j].y, o1);
+    }
+  }
+  const float inv = 1.0f / s;
+  _Float16* out = static_cast<_Float16*>(a.out) + (static_cast<size_t>(qrow) * H + head) * D + 2 * lane;
+  h2 res = {static_cast<_Float16>(o0 * inv), static_cast<_Float16>(o1 * inv)};
+  *reinterpret_cast<h2*>(out) = res;
+}
+
+// Polls of a merge wave waiting for the partials of its (sequence, head):
+// about 0.1 s in all.  The wait ends long before that (a merge block only
+// waits for blocks before it in the grid, which never wait themselves); if
+// it did not, the wave writes NaN rather than read incomplete partials.
+constexpr int kMaxPolls = 1 << 20;
+
+// Merge blocks close the one-launch step.  They come after every partials
+// block in the grid, so they are dispatched last, into the step's tail, and
+// only ever wait for blocks dispatched before them.  Wave w of merge block mb
+// merges item mb*4 + w = (DFS position, head), once the item's counter has
+// reached epoch * count (epoch = one-launch steps since the table upload).
+__device__ __forceinline__ void merge_block(const StepArgs& a, int mb, unsigned epoch) {
+  const int item = mb * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (item >= a.n_seq * a.heads) return;
+  const int pos = item / a.heads, head = item - pos * a.heads;
+  const int cnt = a.seq_parts[2 * pos + 1];
+  const int qrow = a.dfs_qrow[pos];
+  unsigned* ctr = a.arrivals + item;
+  const unsigned target = epoch * static_cast<unsigned>(cnt);
+  // the first poll goes out with the loads of cnt and qrow
+  unsigned seen = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  bool ok = true;
+  for (int tries = 0; static_cast<int>(seen - target) < 0; ++tries) {
+    if (tries == kMaxPolls) {
+      ok = false;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    seen = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  }
+  // keep the partial loads after the poll
+  asm volatile("" ::: "memory");
+  if (!ok) {
+    _Float16* out = static_cast<_Float16*>(a.out) + (static_cast<size_t>(qrow) * a.heads + head) * D + 2 * lane;
+    *reinterpret_cast<h2*>(out) = h2{static_cast<_Float16>(NAN), static_cast<_Float16>(NAN)};
+    return;
+  }
+  if (a.dense_parts > 0)
+    merge_dense<true>(a, pos, head, lane, cnt, qrow);
+  else
+    merge_one<true>(a, pos, head, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -374,13 +460,7 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
   }
   if constexpr (!kFuse) return;
   wait_stores();
-  const bool last = half == 0 && i < n_rows && arrive(a, row_begin + i, head);
-  uint64_t todo = __ballot(last);
-  while (todo) {
-    const int r = __builtin_ctzll(todo);
-    todo &= todo - 1;
-    merge_and_reset(a, row_begin + r, head, lane);
-  }
+  if (half == 0 && i < n_rows) arrive(a, row_begin + i, head);
 }
 
 // Sequence-first: task = some private chunks of one sequence, one head.
@@ -520,93 +600,52 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
     }
   }
   if constexpr (!kFuse) return;
-  __shared__ int is_last;
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = arrive(a, dfs_pos, head);
-  __syncthreads();
-  if (is_last && wave == 0) merge_and_reset(a, dfs_pos, head, lane);
+  __syncthreads();  // every thread's partial stores have completed
+  if (threadIdx.x == 0) arrive(a, dfs_pos, head);
 }
 
-// n_cf: chunk-first blocks of the step; first: index of this launch's first
-// block in the step's grid (0, or n_cf to launch only the sequence-first part).
-// kFuse: also merge (last block per (sequence, head)): the launch is the step.
+// n_cf, n_sf: chunk-first and sequence-first blocks of the step; first:
+// index of this launch's first block in the step's grid (0, or n_cf to launch
+// only the sequence-first part).  kFuse: the one-launch step, whose grid ends
+// with the merge blocks (epoch: see merge_block).
 template <bool kFuse>
-__global__ __launch_bounds__(256, 3) void partials_kernel(StepArgs a, int n_cf, int first) {
+__global__ __launch_bounds__(256, 3) void partials_kernel(StepArgs a, int n_cf, int n_sf, int first,
+                                                          unsigned epoch) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   const int b = blockIdx.x + first;
   if (b < n_cf)
     chunk_first_block<kFuse>(a, xcd_remap(b, n_cf), smem);
-  else
+  else if (b < n_cf + n_sf)
     sequence_first_block<kFuse>(a, b - n_cf);
-}
-
-// Merge of one (sequence, head) with the dense partial layout: partial j of
-// the sequence at DFS position pos is pos * P + j, so every load of the merge
-// (the count, the caller row, all (m, s) and o rows) is issued at once and
-// the merge costs one round trip to memory.  Slots past the sequence's count
-// are loaded but never used.  Same fold as merge_one: M = max m_j,
-// w_j = e^{m_j - M}, s = sum w_j s_j (wave sum), o = sum w_j o_j in list
-// order, out = o / s in fp16.
-__device__ __forceinline__ void merge_dense(const StepArgs& a, int pos, int head, int lane) {
-  const int H = a.heads, P = a.dense_parts;
-  const int cnt = a.seq_parts[2 * pos + 1];
-  const int qrow = a.dfs_qrow[pos];
-  float my_m = -INFINITY, my_s = 0.f;
-  if (lane < P) {
-    const size_t pid = static_cast<size_t>(pos * P + lane) * H + head;
-    my_m = a.part_ms[pid * 2];
-    my_s = a.part_ms[pid * 2 + 1];
-  }
-  float2 ov[kDenseParts];
-#pragma unroll
-  for (int j = 0; j < kDenseParts; ++j)
-    if (j < P)
-      ov[j] = *reinterpret_cast<const float2*>(a.part_o + (static_cast<size_t>(pos * P + j) * H + head) * D +
-                                               2 * lane);
-  if (lane >= cnt) {
-    my_m = -INFINITY;
-    my_s = 0.f;
-  }
-  const float M = wave_max32(max_halves(my_m));
-  const float my_w = lane < cnt ? exp2f(my_m - M) : 0.f;
-  const float s = wave_sum64(my_w * my_s);
-  float o0 = 0.f, o1 = 0.f;
-#pragma unroll
-  for (int j = 0; j < kDenseParts; ++j) {
-    if (j < cnt) {
-      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
-      o0 = fmaf(w, ov[j].x, o0);
-      o1 = fmaf(w, ov[j].y, o1);
-    }
-  }
-  const float inv = 1.0f / s;
-  _Float16* out = static_cast<_Float16*>(a.out) + (static_cast<size_t>(qrow) * H + head) * D + 2 * lane;
-  h2 res = {static_cast<_Float16>(o0 * inv), static_cast<_Float16>(o1 * inv)};
-  *reinterpret_cast<h2*>(out) = res;
+  else if constexpr (kFuse)
+    merge_block(a, b - n_cf - n_sf, epoch);
 }
 
 // Merge of every (sequence, head), four per block (the unfused step).
 __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= a.n_seq * a.heads) return;
+  const int pos = item / a.heads, head = item - pos * a.heads;
   if (a.dense_parts > 0)
-    merge_dense(a, item / a.heads, item % a.heads, threadIdx.x & 63);
+    merge_dense<false>(a, pos, head, threadIdx.x & 63, a.seq_parts[2 * pos + 1], a.dfs_qrow[pos]);
   else
-    merge_one<false>(a, item / a.heads, item % a.heads, threadIdx.x & 63);
+    merge_one<false>(a, pos, head, threadIdx.x & 63);
 }
 
 }  // namespace
 
-int launch_partials(const StepArgs& a, int part, bool fuse_merge, void* stream) {
+int launch_partials(const StepArgs& a, int part, bool fuse_merge, unsigned epoch, void* stream) {
   const int n_cf = a.n_cf_units * a.heads, n_sf = a.n_sf_tasks * a.heads;
+  const bool fuse = fuse_merge && part == kPartsBoth;
+  const int n_merge = fuse ? (a.n_seq * a.heads + 3) / 4 : 0;
   const int first = part == kPartsSequenceFirst ? n_cf : 0;
-  const int count = part == kPartsChunkFirst ? n_cf : part == kPartsSequenceFirst ? n_sf : n_cf + n_sf;
+  const int count = part == kPartsChunkFirst ? n_cf : part == kPartsSequenceFirst ? n_sf : n_cf + n_sf + n_merge;
   if (count <= 0) return 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (fuse_merge && part == kPartsBoth)
-    hipLaunchKernelGGL(partials_kernel<true>, dim3(count), dim3(256), 0, st, a, n_cf, first);
+  if (fuse)
+    hipLaunchKernelGGL(partials_kernel<true>, dim3(count), dim3(256), 0, st, a, n_cf, n_sf, first, epoch);
   else
-    hipLaunchKernelGGL(partials_kernel<false>, dim3(count), dim3(256), 0, st, a, n_cf, first);
+    hipLaunchKernelGGL(partials_kernel<false>, dim3(count), dim3(256), 0, st, a, n_cf, n_sf, first, epoch);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -79,10 +79,13 @@ enum {
                                     wave's chain of dependent tile loads stays well inside the
                                     step's streaming time (ca_stats reports the choice) */
   CA_OPT_SF_CHUNKS_PER_TASK = 2, /* private chunks per sequence-first task (1..256), default 4 */
-  CA_OPT_FUSED_MERGE = 3         /* 0 (default): a step is a partials launch and a merge launch;
-                                    1: one launch, the last block to finish a (sequence, head)
-                                    merges it (slower today: each block ends with dependent
-                                    round trips to memory) */
+  CA_OPT_FUSED_MERGE = 3         /* 0 (default): a step is a partials launch and a merge launch.
+                                    1: one launch whose grid ends with merge blocks; each waits
+                                    until the partials of its (sequence, head) are written (all
+                                    by blocks earlier in the grid) and merges them.  Both give
+                                    the same bits; the one-launch step is slower on MI355X today
+                                    (its partials must be written coherently across the XCDs,
+                                    and its merge blocks hold CU slots in the step's tail). */
 };
 
 /* ca_attend_phase phases.  A step is CA_PHASE_PARTIALS (one launch holding
@@ -206,13 +209,13 @@ int ca_remove(ca_ctx* ctx, int64_t seq_id);
 /* One decode step.  q_dev: fp16 [n_live][heads][head_dim]; out_dev: fp16
  * [n_live][heads][head_dim]; row r belongs to the r-th live sequence in
  * ascending seq_id order (ca_list_sequences).  Uploads the chunk table if the
- * tree changed since the last upload, then enqueues the step on `stream`: one
- * launch whose blocks compute the chunk-first and sequence-first partials and
- * whose last block per (sequence, head) merges them (CA_OPT_FUSED_MERGE), or
- * a partials launch and a merge launch.  The result does not depend on which
- * block finishes last: the merge folds the partials in a fixed order.  Steps
- * of one context must not overlap (they share the workspace).  No host
- * synchronisation.
+ * tree changed since the last upload, then enqueues the step on `stream`: a
+ * partials launch (chunk-first and sequence-first blocks in one grid) and a
+ * merge launch, or one launch whose last blocks merge (CA_OPT_FUSED_MERGE).
+ * The merge folds the partials in a
+ * fixed order, so the result does not depend on block timing.  Steps of one
+ * context must not overlap (they share the workspace and its arrival
+ * counters).  No host synchronisation.
  * Errors: CA_E_EMPTY, CA_E_WORKSPACE, CA_E_NO_POOL, CA_E_HIP. */
 int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream);
 

@@ -69,12 +69,19 @@ def assert_parity(got, ref, label):
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4])
 def test_workload_full(k):
+    """Every output row of workloads 1-4 against the oracle, in the launch
+    configuration the benchmark times (partials + merge launches), then the
+    same bits from repeated steps and from the one-launch step."""
     _say(f"workload {k}")
+    from decode_attention_prefix_tree_amd import _capi
     wl = cached_config(k)
     ca = build_ca(wl)
     got = run_step(ca, wl.q)
     ref = A.decode_workload(wl)
     assert_parity(got, ref, f"config{k}")
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 1)
+    for _ in range(3):
+        assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
 
 
 @pytest.mark.parametrize("two_phase", [True, False])
@@ -179,6 +186,9 @@ def test_multi_branch_sampled_rows():
     ref = A.decode_workload(wl, rows)
     assert_parity(got[rows], ref, "config5")
     assert np.isfinite(got).all()
+    from decode_attention_prefix_tree_amd import _capi
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 1)
+    assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
 
 
 def tiny_tree_cases():
@@ -329,9 +339,10 @@ def test_errors_on_device_context():
 
 @pytest.mark.parametrize("name", ["config1", "shared_R70", "deep_random", "interior_and_dups"])
 def test_fused_merge_matches_two_launch_step(name):
-    """The one-launch step (last block per (sequence, head) merges) equals the
+    """The one-launch step (merge blocks at the end of the grid) equals the
     partials + merge launches bit for bit, step after step (the arrival
-    counters must return to zero) and after the tree changes."""
+    counters keep growing by each sequence's partial count) and after the
+    tree changes (the upload restarts them)."""
     _say(f"fused merge {name}")
     torch = _torch()
     from decode_attention_prefix_tree_amd import _capi
@@ -374,6 +385,7 @@ def test_more_than_64_partials_per_sequence():
     wl = from_token_lists(seqs, heads=2, seed=4)
     ca = build_ca(wl, cf_group=1, sf_group=1)
     assert ca.stats()["partials"] > 3 * 64
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 0)
     got = run_step(ca, wl.q)
     assert_parity(got, A.decode_workload(wl), "many partials")
     ca.set_option(_capi.CA_OPT_FUSED_MERGE, 1)
