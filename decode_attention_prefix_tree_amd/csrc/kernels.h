@@ -10,6 +10,10 @@ constexpr int kHeadDim = 128;
 constexpr int kChunk = 64;
 constexpr int kCfInline = 8;   // chunk refs carried by a chunk-first unit record
 constexpr int kSfInline = 4;   // chunk refs carried by a sequence-first task record
+// Record fields (int32 index) saying that other blocks of the step read the
+// same chunks, so the block reads them with loads that keep them cached.
+constexpr int kCfReuseField = 6;
+constexpr int kSfReuseField = 5;
 constexpr int kDenseParts = 16; // most partials per sequence for the dense partial layout
 
 // Arguments of one decode step.  All pointers are device addresses.

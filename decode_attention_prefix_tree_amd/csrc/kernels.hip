@@ -76,10 +76,15 @@ __device__ __forceinline__ float wave_sum64(float x) {
   return x;
 }
 
-// KV tiles are read once per step: nontemporal loads stream them without
-// keeping the lines in the caches, which lets HBM reads run closer to peak.
+// A chunk read once per step streams with nontemporal loads, which do not
+// keep its lines in the caches and let HBM reads run closer to peak.  Blocks
+// whose chunks other blocks of the step read too (a shared run of more than
+// 32 rows, or shared chunks without the chunk-first phase) use ordinary
+// loads, so the other readers find the lines in L2 or the Infinity Cache.
+template <bool kNT>
 __device__ __forceinline__ h8 ld_tile(const _Float16* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const h8*>(p));
+  if constexpr (kNT) return __builtin_nontemporal_load(reinterpret_cast<const h8*>(p));
+  return *reinterpret_cast<const h8*>(p);
 }
 
 __device__ __forceinline__ h2 lo2(h8 v, int j) {
@@ -290,6 +295,11 @@ constexpr int kOStride = 132;                        // padded row stride of wav
 constexpr int kQBytes = 32 * D * 2;                  // Q block in operand order, fp16
 constexpr int kStateFloats = 32 * kOStride + 64;     // one wave state: O rows, then (m, l)
 constexpr int kSmemBytes = kQBytes + 2 * kStateFloats * 4;
+// the sequence-first layout of the same scratch
+constexpr int kSfP = D * 2;                // after the query row (fp16)
+constexpr int kSfO = kSfP + 4 * 64 * 4;    // after the probability rows
+constexpr int kSfM = kSfO + 4 * D * 4;     // after the wave states' o rows
+static_assert(kSfM + 8 * 4 <= kSmemBytes, "sequence-first scratch fits the block's LDS");
 
 __device__ __forceinline__ float weight(float m, float M) {
   // e^(m - M) in base 2; an empty state (m = -inf) weighs 0 even when M = -inf
@@ -302,7 +312,7 @@ __device__ __forceinline__ float weight(float m, float M) {
 // along keys (the lane holds 16 keys of its row, its twin lane the other 16),
 // O^T[128 x 32] += V^T P^T (8 MFMA).  P^T needs no exchange: the V tile
 // stores keys in the order the S^T accumulators hold them.
-template <bool kFuse>
+template <bool kFuse, bool kNT>
 __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical, char* smem) {
   const int unit = logical % a.n_cf_units, head = logical / a.n_cf_units;
   const int* u = a.cf_units + unit * 32;
@@ -346,12 +356,12 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
     for (int jb = 0; jb < 2; ++jb) {
       h8 kr[8], vr[8];
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) kr[kk] = ld_tile(kt + ((jb * 8 + kk) * 64 + lane) * 8);
+      for (int kk = 0; kk < 8; ++kk) kr[kk] = ld_tile<kNT>(kt + ((jb * 8 + kk) * 64 + lane) * 8);
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          vr[nb * 2 + t] = ld_tile(vt + ((nb * 4 + 2 * jb + t) * 64 + lane) * 8);
+          vr[nb * 2 + t] = ld_tile<kNT>(vt + ((nb * 4 + 2 * jb + t) * 64 + lane) * 8);
       f16v sc = f16v{};
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
@@ -469,8 +479,8 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
 // 32nb + i at 8 keys per load and reads the matching probabilities from a
 // 64-entry LDS row of its wave.  Three waves per SIMD keep about 384 KiB of
 // loads in flight per CU.
-template <bool kFuse>
-__device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logical) {
+template <bool kFuse, bool kNT>
+__device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logical, char* smem) {
   // heads vary fastest: blocks that run together read neighbouring 32 KiB
   // tiles of the same slots, which keeps HBM accesses close to sequential
   const int task = logical / a.heads, head = logical % a.heads;
@@ -484,14 +494,19 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
 
   // The query row is the same for the four waves: keep it in LDS (256 B)
   // rather than in 32 VGPRs of every lane.
-  __shared__ __attribute__((aligned(16))) _Float16 q_lds[D];
+  // LDS (the block's scratch, shared with the chunk-first layout): query row,
+  // one probability row per wave, the four wave states
+  _Float16* q_lds = reinterpret_cast<_Float16*>(smem);
+  float(*p_lds)[64] = reinterpret_cast<float(*)[64]>(smem + kSfP);
+  float(*w_o)[D] = reinterpret_cast<float(*)[D]>(smem + kSfO);
+  float* w_m = reinterpret_cast<float*>(smem + kSfM);
+  float* w_l = w_m + 4;
   if (threadIdx.x < D / 8) {
     const _Float16* qp = static_cast<const _Float16*>(a.q) + (static_cast<size_t>(qrow) * H + head) * D;
     *reinterpret_cast<h8*>(q_lds + threadIdx.x * 8) = *reinterpret_cast<const h8*>(qp + threadIdx.x * 8);
   }
   __syncthreads();
 
-  __shared__ float p_lds[4][64];
   float m = -INFINITY, l = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 
@@ -502,9 +517,9 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
     const _Float16* vt = kt + TILE;
     h8 ka[16], va[16];
 #pragma unroll
-    for (int L = 0; L < 16; ++L) ka[L] = ld_tile(kt + (L * 64 + lane) * 8);
+    for (int L = 0; L < 16; ++L) ka[L] = ld_tile<kNT>(kt + (L * 64 + lane) * 8);
 #pragma unroll
-    for (int L = 0; L < 16; ++L) va[L] = ld_tile(vt + (L * 64 + lane) * 8);
+    for (int L = 0; L < 16; ++L) va[L] = ld_tile<kNT>(vt + (L * 64 + lane) * 8);
 
     float d0 = 0.f, d1 = 0.f;
 #pragma unroll
@@ -562,8 +577,6 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
   for (int nb = 0; nb < 4; ++nb) acc[nb] = sum_halves(acc[nb]);
   l = wave_sum64(l);
 
-  __shared__ float w_o[4][D];
-  __shared__ float w_m[4], w_l[4];
   if (half == 0) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) w_o[wave][32 * nb + i] = acc[nb];
@@ -613,10 +626,19 @@ __global__ __launch_bounds__(256, 3) void partials_kernel(StepArgs a, int n_cf, 
                                                           unsigned epoch) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   const int b = blockIdx.x + first;
-  if (b < n_cf)
-    chunk_first_block<kFuse>(a, xcd_remap(b, n_cf), smem);
-  else if (b < n_cf + n_sf)
-    sequence_first_block<kFuse>(a, b - n_cf);
+  if (b < n_cf) {
+    const int logical = xcd_remap(b, n_cf);
+    if (a.cf_units[(logical % a.n_cf_units) * 32 + kCfReuseField])
+      chunk_first_block<kFuse, false>(a, logical, smem);
+    else
+      chunk_first_block<kFuse, true>(a, logical, smem);
+  } else if (b < n_cf + n_sf) {
+    const int logical = b - n_cf;
+    if (a.sf_tasks[(logical / a.heads) * 16 + kSfReuseField])
+      sequence_first_block<kFuse, false>(a, logical, smem);
+    else
+      sequence_first_block<kFuse, true>(a, logical, smem);
+  }
   else if constexpr (kFuse)
     merge_block(a, b - n_cf - n_sf, epoch);
 }

@@ -326,6 +326,7 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
         u.n_chunks = tasks[t].n_chunks;
         u.row_begin = tasks[t].b + rb * 32;
         u.n_rows = std::min(32, tasks[t].e - tasks[t].b - rb * 32);
+        u.reuse = tasks[t].e - tasks[t].b > 32 ? 1 : 0;
         u.qrow_base = P.dfs_qrow[u.row_begin];
         for (int r = 1; r < u.n_rows; ++r)
           if (P.dfs_qrow[u.row_begin + r] != u.qrow_base + r) u.qrow_base = -1;
@@ -377,6 +378,7 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
           st.slot[c] = R(priv[q], 6);
           st.n_valid[c] = R(priv[q], 3);
         }
+        if (R(priv[q], 5) - R(priv[q], 4) >= 2) st.reuse = 1;
         P.chunk_refs.push_back(R(priv[q], 6));
         P.chunk_refs.push_back(R(priv[q], 3));
         P.ref_node.push_back(row_node[priv[q]]);

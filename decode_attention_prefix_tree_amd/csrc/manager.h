@@ -25,6 +25,7 @@
 //  * a failing call changes nothing.
 #pragma once
 
+#include <cstddef>
 #include <cstdint>
 #include <functional>
 #include <map>
@@ -71,7 +72,8 @@ struct CfUnit {        // chunk-first: one 32-row block of one run of shared chu
   int32_t n_rows;      // 1..32
   int32_t part_base;   // partial id of the block's first row; row r's is part_base + r * part_stride
   int32_t qrow_base;   // caller row of the first row if the rows' caller rows are consecutive, else -1
-  int32_t pad[2];
+  int32_t reuse;       // 1: other units read these chunks too (run of more than 32 rows)
+  int32_t pad;
   int32_t slot[kCfInline];
   int32_t n_valid[kCfInline];
   int32_t pad2[8];     // 128 bytes
@@ -82,12 +84,15 @@ struct SfTask {        // sequence-first: some private chunks of one sequence
   int32_t dfs_pos;
   int32_t part_id;
   int32_t qrow;        // caller row of the sequence
-  int32_t pad[3];
+  int32_t reuse;       // 1: some chunk is shared (read by other tasks; only without chunk-first)
+  int32_t pad[2];
   int32_t slot[kSfInline];
   int32_t n_valid[kSfInline];  // 64 bytes
 };
 
 static_assert(sizeof(CfUnit) == 128 && sizeof(SfTask) == 64, "record layouts are read by the kernels");
+static_assert(offsetof(CfUnit, reuse) == kCfReuseField * 4 && offsetof(SfTask, reuse) == kSfReuseField * 4,
+              "reuse flags sit where the kernels read them");
 
 struct Plan {
   std::vector<int32_t> rows;        // canonical table, 7 ints per row
