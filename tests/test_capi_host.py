@@ -322,3 +322,29 @@ def test_append_batch_errors_change_nothing():
     assert ei.value.name == "no_capacity"
     after = ca.export_table()
     assert np.array_equal(snap[0], after[0]) and snap[1] == after[1]
+
+
+@pytest.mark.parametrize("n_chunks,expect", [(16, 32), (17, 18)])
+def test_partial_slots_dense_up_to_16_per_sequence(n_chunks, expect):
+    """Partial ids are dense (sequence x list position) while no sequence has
+    more than 16 partials, compact beyond: one sequence with n_chunks private
+    chunks (one per task) and one with a single chunk."""
+    ca = ChunkAttention(2, 64, device=None)
+    ca.set_option(_capi.CA_OPT_SF_CHUNKS_PER_TASK, 1)
+    ca.insert(0, list(range(64 * n_chunks)))
+    ca.insert(1, [10**6 + j for j in range(10)])
+    assert ca.stats()["partials"] == expect
+
+
+def test_partial_slots_of_a_shared_prefix_batch():
+    """32 sequences of 1024 shared + 512 private tokens, 4 chunks per task on
+    both sides: 4 shared runs and 2 private tasks per sequence, 6 partials each."""
+    ca = ChunkAttention(2, 4096, device=None)
+    ca.set_option(_capi.CA_OPT_CF_CHUNKS_PER_TASK, 4)
+    ca.set_option(_capi.CA_OPT_SF_CHUNKS_PER_TASK, 4)
+    shared = list(range(1024))
+    for i in range(32):
+        ca.insert(i, shared + [(1 << 20) + i * 1000 + j for j in range(512)])
+    st = ca.stats()
+    assert st["cf_tasks"] == 4 and st["sf_tasks"] == 64
+    assert st["partials"] == 32 * 6

@@ -392,6 +392,27 @@ def test_more_than_64_partials_per_sequence():
     assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
 
 
+@pytest.mark.parametrize("k", [15, 16])
+def test_dense_and_compact_partial_slots(k):
+    """One shared run plus k private chunks (one per task) gives 1 + k
+    partials: 16 keeps the dense partial slots, 17 switches to compact ids.
+    Both merges against the oracle, and the one-launch step bit for bit."""
+    _say(f"partial slots, k={k}")
+    from decode_attention_prefix_tree_amd import _capi
+    rng = np.random.default_rng(30 + k)
+    shared = list(range(128))
+    seqs = [shared + [9000 + i] + [int(x) for x in rng.integers(0, 7, size=64 * n - 1)]
+            for i, n in enumerate((k, 3, 1))]
+    wl = from_token_lists(seqs, heads=4, seed=31 + k)
+    ca = build_ca(wl, cf_group=8, sf_group=1)
+    st = ca.stats()
+    assert st["partials"] == (3 * 16 if k == 15 else 3 + k + 3 + 1), st["partials"]
+    got = run_step(ca, wl.q)
+    assert_parity(got, A.decode_workload(wl), f"slots k={k}")
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 1)
+    assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
+
+
 def _host_shadow(wl, two_phase):
     """A context without a device pool that receives the same tree calls: its
     exported table is the reference for the device context's."""
