@@ -57,6 +57,9 @@ def parse():
                          "sequence per step (completion length n_c sweep at batch 32, batch sweep at n_c = 512)")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the per-kernel timing loop (for rocprofv3 runs); prints its event means")
+    ap.add_argument("--phases", action="store_true",
+                    help="with --profile-only: launch the chunk-first and sequence-first parts of the partials "
+                         "kernel separately (then the merge), so counters can be read per phase")
     return ap.parse_args()
 
 
@@ -317,7 +320,13 @@ def main():
     from decode_attention_prefix_tree_amd import _capi
     step_launches = (_capi.CA_PHASE_PARTIALS, _capi.CA_PHASE_MERGE)
     if args.profile_only:
-        lt = time_launches(torch, ca, q, out, args.steps, flush, step_launches)
+        if args.phases:
+            names = ("chunk_first", "sequence_first", "merge_kernel")
+            lt = time_launches(torch, ca, q, out, args.steps, flush,
+                               (_capi.CA_PHASE_CHUNK_FIRST, _capi.CA_PHASE_SEQUENCE_FIRST, _capi.CA_PHASE_MERGE))
+        else:
+            names = ("partials_kernel", "merge_kernel")
+            lt = time_launches(torch, ca, q, out, args.steps, flush, step_launches)
         # Calibration for hardware byte counters: a plain device copy of a known
         # size (256 MiB read + 256 MiB written), cold like the steps.
         src = torch.ones(1 << 27, dtype=torch.float16, device="cuda")
@@ -326,8 +335,8 @@ def main():
             flush()
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"launch_us_mean": {"partials_kernel": float(lt[:, 0].mean()) * 1e3,
-                                             "merge_kernel": float(lt[:, 1].mean()) * 1e3},
+        print(json.dumps({"launch_us_mean": {n: float(lt[:, j].mean()) * 1e3 for j, n in enumerate(names)},
+                          "cf_units": st["cf_units"], "heads": wl.heads, "shared_chunks": st["shared_chunks"],
                           "unique_kv_bytes": st["unique_kv_bytes"], "copy_calibration_bytes": src.numel() * 2,
                           "steps": args.steps, "config": args.config}), flush=True)
         return
