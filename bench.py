@@ -49,9 +49,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--prefix-len", type=int, default=None,
-                    help="instead of a numbered workload: 32 seq x 32 heads with this shared prefix length "
-                         "(any length, e.g. 1766) and --suffix-len private tokens each")
+                    help="instead of a numbered workload: --n-seq sequences x 32 heads with this shared prefix "
+                         "length (any length, e.g. 1766) and --suffix-len private tokens each")
     ap.add_argument("--suffix-len", type=int, default=512)
+    ap.add_argument("--n-seq", type=int, default=32, help="sequences of the --prefix-len workload")
     ap.add_argument("--decode", action="store_true",
                     help="decode progression instead: n_s = 2048 shared prompt tokens, one token appended per "
                          "sequence per step (completion length n_c sweep at batch 32, batch sweep at n_c = 512)")
@@ -292,7 +293,7 @@ def main():
         decode_main(args, torch)
         return
     if args.prefix_len is not None:
-        wl = make_prefix_suffix(args.prefix_len, [args.suffix_len] * 32, heads=32,
+        wl = make_prefix_suffix(args.prefix_len, [args.suffix_len] * args.n_seq, heads=32,
                                 seed=2000 + args.prefix_len)
         workload_name = "prefix-suffix: " + wl.description
         args.config = None
@@ -319,8 +320,13 @@ def main():
 
     from decode_attention_prefix_tree_amd import _capi
     step_launches = (_capi.CA_PHASE_PARTIALS, _capi.CA_PHASE_MERGE)
+    one_launch = bool(st["one_launch_step"])
     if args.profile_only:
-        if args.phases:
+        if one_launch and not args.phases:
+            # the step is one launch (merge blocks close the partials grid)
+            names = ("partials_kernel (one-launch step)",)
+            lt = time_steps(torch, step, args.steps, flush)[:, None]
+        elif args.phases:
             names = ("chunk_first", "sequence_first", "merge_kernel")
             lt = time_launches(torch, ca, q, out, args.steps, flush,
                                (_capi.CA_PHASE_CHUNK_FIRST, _capi.CA_PHASE_SEQUENCE_FIRST, _capi.CA_PHASE_MERGE))
@@ -362,11 +368,14 @@ def main():
     value = st["attended_tokens"] / t_mean
 
     # The dominant kernel: the partials launch of a step (chunk-first and
-    # sequence-first blocks in one grid).  Its algorithmic bytes are the
-    # unique KV bytes (each shared chunk once, each private chunk once).
-    dom_t = float(lt[:, 0].mean()) * 1e-3
-    roof = {"kernel": "partials_kernel", "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
-            "achieved": unique_b / dom_t / 1e9, "traffic": recorded_traffic(args.config) if args.config else None,
+    # sequence-first blocks in one grid; in the one-launch step it also holds
+    # the merge blocks, and the step is that launch).  Its algorithmic bytes
+    # are the unique KV bytes (each shared chunk once, each private chunk once).
+    dom_t = t_mean if one_launch else float(lt[:, 0].mean()) * 1e-3
+    roof = {"kernel": "partials_kernel" + (" (one-launch step, merge blocks included)" if one_launch else ""),
+            "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
+            "achieved": unique_b / dom_t / 1e9,
+            "traffic": recorded_traffic(args.config) if args.config and not one_launch else None,
             "bytes_per_launch": unique_b, "avg_launch_us": dom_t * 1e6}
     roof["frac"] = roof["achieved"] / HBM_PEAK_GBPS
 
@@ -385,7 +394,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_name, "n_seq": wl.n_seq, "heads": wl.heads,
                    "head_dim": wl.head_dim, "chunk": wl.chunk, "cache": "cold (1 GiB read before each step)",
-                   "cf_chunks_per_task": st["cf_chunks_per_task"], "sf_chunks_per_task": 4},
+                   "cf_chunks_per_task": st["cf_chunks_per_task"], "sf_chunks_per_task": 4,
+                   "launches_per_step": 1 if one_launch else 2},
         "unique_kv_gbps": unique_b / t_mean / 1e9,
         "hbm_frac_unique": unique_b / t_mean / 1e9 / HBM_PEAK_GBPS,
         "queries_per_s": wl.n_seq / t_mean,

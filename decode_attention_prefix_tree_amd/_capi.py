@@ -63,6 +63,7 @@ class ca_stats_t(ctypes.Structure):
         ("table_uploads", ctypes.c_int64),
         ("patched_appends", ctypes.c_int64),
         ("cf_chunks_per_task", ctypes.c_int64),
+        ("one_launch_step", ctypes.c_int64),
     ]
 
 

@@ -26,7 +26,7 @@ struct ca_ctx {
   int cf_group = 0, sf_group = 4;  // cf_group 0: chosen per plan (auto_cf_group)
   int cf_auto = 8;                 // the last automatic choice
   int plan_cf_group = 8;           // the group the current plan was built with
-  bool fused_merge = false;
+  int fused_merge = 2;              // CA_OPT_FUSED_MERGE: 0 two launches, 1 one launch, 2 chosen per plan
   unsigned fuse_epoch = 0;          // one-launch steps since the last table upload
 
   // plan cache: rebuilt after the tree changes, uploaded when stale
@@ -319,6 +319,21 @@ void run_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* 
   }
 }
 
+// Whether a step is one launch (merge blocks close the partials grid) or a
+// partials launch and a merge launch.  Measured on MI355X, the one-launch step
+// wins once a step merges about 4096 (sequence, head) pairs (128 sequences at
+// 32 heads: 170.2 vs 171.3 us at 1024 shared + 512 private tokens, 212.4 vs
+// 217.3 us on the multi-branch tree) and loses below (64 sequences: 92.6 vs
+// 91.2 us; 32 sequences: 54.1 vs 52.2 us): its coherent partial stores and
+// the merge blocks waiting in the tail cost more than the second launch saves
+// until the merge launch itself grows with the pair count.
+constexpr int64_t kOneLaunchPairs = 4096;
+
+bool one_launch(const ca_ctx* c) {
+  if (c->fused_merge != 2) return c->fused_merge == 1;
+  return static_cast<int64_t>(c->plan.dfs_seq.size()) * c->heads >= kOneLaunchPairs;
+}
+
 // Bookkeeping after appends whose fill counts went to the device with the
 // writes: the host plan is refreshed lazily, the device copy is current.
 void touch_patched(ca_ctx* c) {
@@ -415,8 +430,8 @@ int ca_set_option(ca_ctx* ctx, int option, int value) {
       if (value < 1 || value > 256) throw Error(CA_E_INVALID_ARG, "sequence-first group must be 1..256");
       ctx->sf_group = value;
     } else if (option == CA_OPT_FUSED_MERGE) {
-      if (value != 0 && value != 1) throw Error(CA_E_INVALID_ARG, "fused merge is 0 or 1");
-      ctx->fused_merge = value != 0;
+      if (value < 0 || value > 2) throw Error(CA_E_INVALID_ARG, "fused merge is 0, 1 or 2 (automatic)");
+      ctx->fused_merge = value;
     } else {
       throw Error(CA_E_UNSUPPORTED, "unknown option");
     }
@@ -526,7 +541,7 @@ int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream) {
     check_step(ctx, q_dev, out_dev);
     upload(ctx, stream);
     chunkattn::StepArgs a = step_args(ctx, q_dev, out_dev);
-    if (ctx->fused_merge) {
+    if (one_launch(ctx)) {
       launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, true, ++ctx->fuse_epoch, stream), "step");
     } else {
       launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, false, 0, stream), "partials");
@@ -592,6 +607,7 @@ int ca_stats(ca_ctx* ctx, ca_stats_t* out) {
     s.table_uploads = ctx->table_uploads;
     s.patched_appends = ctx->patched_appends;
     s.cf_chunks_per_task = ctx->plan_cf_group;
+    s.one_launch_step = one_launch(ctx) ? 1 : 0;
     *out = s;
     return CA_OK;
   });

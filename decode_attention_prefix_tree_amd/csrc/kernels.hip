@@ -1,12 +1,14 @@
 // gfx950 (CDNA4) kernels of the ChunkAttention decode step.
 //
 // Two-phase partition (paperlayer.ai summary of arXiv 2402.15220v4, section
-// 3.2 and Figure 2): the chunk-first kernel batches the queries of all
-// sequences that share a chunk into a matrix and runs both products on MFMA;
-// the sequence-first kernel streams each sequence's private chunks; both
-// write partial results (o, m, s) that the merge kernel combines by
-// log-sum-exp (explainer 0h-n0.github.io/posts/paper-2402-15220, output
-// combination formula; m is a running max, s and o are unnormalised).
+// 3.2 and Figure 2): chunk-first blocks batch the queries of all sequences
+// that share a chunk into a matrix and run both products on MFMA;
+// sequence-first blocks stream each sequence's private chunks; both write
+// partial results (o, m, s) that the merge combines by log-sum-exp
+// (explainer 0h-n0.github.io/posts/paper-2402-15220, output combination
+// formula; m is a running max, s and o are unnormalised).  Both phases share
+// one grid; the merge is a second launch or, in the one-launch step, blocks
+// at the end of the same grid.
 //
 // The chunk tile layout is described in tile_layout.h.
 #include <hip/hip_runtime.h>
@@ -289,7 +291,7 @@ __device__ __forceinline__ void merge_block(const StepArgs& a, int mb, unsigned 
 // blocks, so the two phases run at the same time with no launch between
 // them.  256 threads (4 waves) per block; a block owns one task and its
 // waves take the task's chunks w, w+4, ...  Both paths fit 168 VGPRs and
-// 46 KiB of LDS, so three blocks share a CU.
+// share one 42.5 KB LDS scratch, so three blocks share a CU.
 
 constexpr int kOStride = 132;                        // padded row stride of wave states
 constexpr int kQBytes = 32 * D * 2;                  // Q block in operand order, fp16
@@ -440,6 +442,34 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
   __syncthreads();
   if (wave == 1) put(0);
   __syncthreads();
+  if constexpr (kFuse) {
+    // The partials go out coherently (another block merges them), and a
+    // coherent store writes through: wave 0 puts the final state into LDS row
+    // by row, then all four waves store consecutive words, so every store
+    // instruction writes two whole 512-byte rows.
+    if (wave == 0) {
+      take(0);
+      put(0);
+    }
+    __syncthreads();
+    const float* o = st;
+#pragma unroll 4
+    for (int k = 0; k < 32 * D / 256; ++k) {
+      const int idx = k * 256 + threadIdx.x, row = idx / D, col = idx % D;
+      if (row < n_rows)
+        store_agent(a.part_o + (static_cast<size_t>(part_base + row * a.part_stride) * H + head) * D + col,
+                    o[row * kOStride + col]);
+    }
+    if (threadIdx.x < n_rows) {
+      const size_t pid = static_cast<size_t>(part_base + threadIdx.x * a.part_stride) * H + head;
+      store_agent(a.part_ms + pid * 2 + 0, o[32 * kOStride + 2 * threadIdx.x]);
+      store_agent(a.part_ms + pid * 2 + 1, o[32 * kOStride + 2 * threadIdx.x + 1]);
+    }
+    wait_stores();
+    __syncthreads();  // every thread's stores have completed
+    if (threadIdx.x < n_rows) arrive(a, row_begin + threadIdx.x, head);
+    return;
+  }
   if (wave != 0) return;
   take(0);
   if (i < n_rows) {
@@ -450,27 +480,13 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         f4 v = {acc[nb][4 * g + 0], acc[nb][4 * g + 1], acc[nb][4 * g + 2], acc[nb][4 * g + 3]};
-        float* dst = po + 32 * nb + 8 * g + 4 * half;
-        if constexpr (kFuse) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) store_agent(dst + e, v[e]);
-        } else {
-          *reinterpret_cast<f4*>(dst) = v;
-        }
+        *reinterpret_cast<f4*>(po + 32 * nb + 8 * g + 4 * half) = v;
       }
     if (half == 0) {
-      if constexpr (kFuse) {
-        store_agent(a.part_ms + pid * 2 + 0, m);
-        store_agent(a.part_ms + pid * 2 + 1, l);
-      } else {
-        a.part_ms[pid * 2 + 0] = m;
-        a.part_ms[pid * 2 + 1] = l;
-      }
+      a.part_ms[pid * 2 + 0] = m;
+      a.part_ms[pid * 2 + 1] = l;
     }
   }
-  if constexpr (!kFuse) return;
-  wait_stores();
-  if (half == 0 && i < n_rows) arrive(a, row_begin + i, head);
 }
 
 // Sequence-first: task = some private chunks of one sequence, one head.

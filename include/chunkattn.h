@@ -79,13 +79,14 @@ enum {
                                     wave's chain of dependent tile loads stays well inside the
                                     step's streaming time (ca_stats reports the choice) */
   CA_OPT_SF_CHUNKS_PER_TASK = 2, /* private chunks per sequence-first task (1..256), default 4 */
-  CA_OPT_FUSED_MERGE = 3         /* 0 (default): a step is a partials launch and a merge launch.
+  CA_OPT_FUSED_MERGE = 3         /* 0: a step is a partials launch and a merge launch.
                                     1: one launch whose grid ends with merge blocks; each waits
                                     until the partials of its (sequence, head) are written (all
-                                    by blocks earlier in the grid) and merges them.  Both give
-                                    the same bits; the one-launch step is slower on MI355X today
-                                    (its partials must be written coherently across the XCDs,
-                                    and its merge blocks hold CU slots in the step's tail). */
+                                    by blocks earlier in the grid) and merges them.
+                                    2 (default): one launch when the step merges at least 4096
+                                    (sequence, head) pairs, else two (measured crossover on
+                                    MI355X).  All give the same bits; ca_stats reports the
+                                    choice for the current tree. */
 };
 
 /* ca_attend_phase phases.  A step is CA_PHASE_PARTIALS (one launch holding
@@ -127,6 +128,7 @@ typedef struct ca_stats_t {
   int64_t patched_appends;   /* appends whose fill counts the write launch
                                 stored into the device table itself */
   int64_t cf_chunks_per_task; /* chunk-first group of the current plan */
+  int64_t one_launch_step;    /* 1 if ca_attend runs the step as one launch */
 } ca_stats_t;
 
 /* Bytes of one chunk slot: K and V, all heads, fp16 = 4 * heads * chunk_size
@@ -211,7 +213,8 @@ int ca_remove(ca_ctx* ctx, int64_t seq_id);
  * ascending seq_id order (ca_list_sequences).  Uploads the chunk table if the
  * tree changed since the last upload, then enqueues the step on `stream`: a
  * partials launch (chunk-first and sequence-first blocks in one grid) and a
- * merge launch, or one launch whose last blocks merge (CA_OPT_FUSED_MERGE).
+ * merge launch, or one launch whose last blocks merge (CA_OPT_FUSED_MERGE;
+ * by default one launch from 4096 (sequence, head) pairs up).
  * The merge folds the partials in a
  * fixed order, so the result does not depend on block timing.  Steps of one
  * context must not overlap (they share the workspace and its arrival

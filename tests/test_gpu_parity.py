@@ -76,6 +76,7 @@ def test_workload_full(k):
     from decode_attention_prefix_tree_amd import _capi
     wl = cached_config(k)
     ca = build_ca(wl)
+    assert ca.stats()["one_launch_step"] == 0
     got = run_step(ca, wl.q)
     ref = A.decode_workload(wl)
     assert_parity(got, ref, f"config{k}")
@@ -178,16 +179,22 @@ def test_insert_remove_churn():
 
 
 def test_multi_branch_sampled_rows():
+    """Workload 5 at full size (128 sequences x 32 heads: the default step
+    is one launch) on a sample of rows that covers every branch edge, all rows
+    finite, the same bits from repeated steps and from the two-launch step."""
     _say("workload 5")
+    from decode_attention_prefix_tree_amd import _capi
     wl = cached_config(5)
     ca = build_ca(wl)
+    assert ca.stats()["one_launch_step"] == 1
     got = run_step(ca, wl.q)
     rows = sorted({0, 31, 32, 63, 64, 95, 96, 127} | set(np.random.default_rng(5).choice(128, 8, replace=False)))
     ref = A.decode_workload(wl, rows)
     assert_parity(got[rows], ref, "config5")
     assert np.isfinite(got).all()
-    from decode_attention_prefix_tree_amd import _capi
-    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 1)
+    for _ in range(2):
+        assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 0)
     assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
 
 
