@@ -392,11 +392,14 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
   ent_first[n_seq] = static_cast<int32_t>(entries.size());
 
   // Partial ids.  Dense (a sequence's j-th partial is i * max_parts + j) when
-  // a sequence has at most kDenseParts partials: the merge then computes
+  // no sequence has more than kDenseParts partials and the dense slots cost
+  // at most about twice the partials themselves: the merge then computes
   // every address from the sequence's position and fetches all of them in
   // one round trip.  Otherwise compact ids: a run's rows take consecutive
   // ids, then the sequence-first tasks.
-  P.dense_parts = max_parts <= kDenseParts ? max_parts : 0;
+  const int64_t n_entries = static_cast<int64_t>(entries.size());
+  const bool dense = max_parts <= kDenseParts && static_cast<int64_t>(n_seq) * max_parts <= 2 * n_entries + 64;
+  P.dense_parts = dense ? max_parts : 0;
   std::vector<int32_t> task_part(tasks.size(), -1);  // dense: slot j; compact: base id
   if (P.dense_parts) {
     P.part_stride = max_parts;

@@ -368,3 +368,14 @@ def test_launch_mode_follows_merge_pair_count():
     assert small.stats()["one_launch_step"] == 1
     with pytest.raises(CaError):
         small.set_option(_capi.CA_OPT_FUSED_MERGE, 3)
+
+
+def test_partial_slots_compact_when_dense_would_waste_memory():
+    """One sequence with 16 partials among 99 with one: dense slots would
+    take 1600 entries for 115 partials, so the ids stay compact."""
+    ca = ChunkAttention(2, 512, device=None)
+    ca.set_option(_capi.CA_OPT_SF_CHUNKS_PER_TASK, 1)
+    ca.insert(0, list(range(64 * 16)))
+    for i in range(1, 100):
+        ca.insert(i, [10**6 + i * 100 + j for j in range(10)])
+    assert ca.stats()["partials"] == 16 + 99
