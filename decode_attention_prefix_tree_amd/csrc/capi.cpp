@@ -102,17 +102,21 @@ bool device_table_current(const ca_ctx* c) { return c->uploaded_version == c->ve
 // with_fills: the host plan's fill counts are needed too (an upload, an
 // export, stats); a step whose device table is current does not need them.
 // Chunks per chunk-first task when the caller leaves it open.  A
-// chunk-first wave walks its chunks one 32-key half after another, each
-// half a dependent round trip to memory, and while the step saturates HBM a
-// round trip waits behind everything in flight (about 6 us on MI355X).  The
-// longest such chain should stay within half of the step's own streaming
-// time (unique KV bytes at about 6 TB/s), or the chunk-first blocks become
-// the step's tail; within that bound larger groups mean fewer partials.
+// chunk-first wave walks its chunks one 32-key half after another, each half
+// one dependent round trip to memory (all 16 KiB of its tile loads in flight
+// together).  The longest such chain should stay within half of the step's
+// own streaming time (unique KV bytes at about 6 TB/s), or the chunk-first
+// blocks become the step's tail; within that bound larger groups mean fewer
+// partials.  The per-half cost (2.5 us under full load) is calibrated on
+// MI355X: 16 chunks per task (8 halves per wave) are the fastest choice from
+// about 40 us of streaming up (1024 and 4096 shared tokens, 32 sequences;
+// the multi-branch tree), while 32 or 64 make the chains the tail at 4096
+// shared tokens (65.9 and 89.0 us against 59.3 us).
 int auto_cf_group(const chunkattn::Plan& p, int heads, int head_dim) {
   const double kernel_us = static_cast<double>(p.unique_tokens) * 4.0 * heads * head_dim / 6.0e6;
   for (int g : {16, 8}) {
     const int halves = 2 * ((g + 3) / 4);
-    if (halves * 6.0 <= 0.5 * kernel_us) return g;
+    if (halves * 2.5 <= 0.5 * kernel_us) return g;
   }
   return 4;
 }

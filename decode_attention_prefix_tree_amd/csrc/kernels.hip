@@ -343,9 +343,76 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
 
   float m = -INFINITY, l = 0.f;
   f16v acc[4];
+
+  if (n_chunks <= 4) {
+    // At most one chunk per wave: no accumulator has to survive another
+    // chunk's loads, so the wave loads its whole chunk at once (32 KiB in
+    // flight, one round trip, like a sequence-first wave): K 64 VGPRs, V 64,
+    // one half's scores 16 while the first half's K is still live.
+    if (wave < n_chunks) {
+      const int slot = u[8 + wave], nvalid = u[16 + wave];  // inline: wave < 4 <= kCfInline
+      const _Float16* kt = pool + tile_base(slot, head, H, 0);
+      const _Float16* vt = kt + TILE;
+      h8 kr[16], vr[16];
+#pragma unroll
+      for (int L = 0; L < 16; ++L) kr[L] = ld_tile<kNT>(kt + (L * 64 + lane) * 8);
+#pragma unroll
+      for (int L = 0; L < 16; ++L) vr[L] = ld_tile<kNT>(vt + (L * 64 + lane) * 8);
+      // keep every load ahead of the first product (the scheduler would
+      // otherwise trade them for registers, one load per MFMA)
+      __builtin_amdgcn_sched_barrier(0);
+      // One 32-key half after the other, each reading its Q operands from
+      // LDS afresh: holding all eight across both halves would not fit.
+      f16v sc[2];
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        sc[jb] = f16v{};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const h8 qb = *reinterpret_cast<const h8*>(q_lds + (kk * 64 + lane) * 8);
+          sc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kr[jb * 8 + kk], qb, sc[jb], 0, 0, 0);
+        }
+        if (jb == 0) {
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // sc[jb][r] is key 32jb + 8(r/4) + 4half + r%4 of row i
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * jb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const float x = key < nvalid ? sc[jb][r] * a.scale_log2e : -INFINITY;
+          sc[jb][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      m = max_halves(mx);  // finite: key 0 of a chunk is always filled
+      h8 pb[2][2];
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = exp2f(sc[jb][r] - m);
+          l += pr;
+          pb[jb][r >> 3][r & 7] = static_cast<_Float16>(pr);
+        }
+      // the accumulators come to life only here, after the tile loads
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vr[nb * 4], pb[0][0], f16v{}, 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vr[nb * 4 + 1], pb[0][1], acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vr[nb * 4 + 2], pb[1][0], acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vr[nb * 4 + 3], pb[1][1], acc[nb], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[nb] = f16v{};
+    }
+  } else {
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) acc[nb] = f16v{};
-
   for (int c = wave; c < n_chunks; c += 4) {
     const int slot = c < kCfInline ? u[8 + c] : a.chunk_refs[2 * (chunk_begin + c)];
     const int nvalid = c < kCfInline ? u[16 + c] : a.chunk_refs[2 * (chunk_begin + c) + 1];
@@ -364,6 +431,10 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
 #pragma unroll
         for (int t = 0; t < 2; ++t)
           vr[nb * 2 + t] = ld_tile<kNT>(vt + ((nb * 4 + 2 * jb + t) * 64 + lane) * 8);
+      // all 16 loads of the half go out before its first product (left
+      // alone, the scheduler issues K one load per MFMA and V only after the
+      // softmax: two or more dependent round trips per half instead of one)
+      __builtin_amdgcn_sched_barrier(0);
       f16v sc = f16v{};
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
@@ -401,6 +472,7 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
           acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vr[nb * 2 + t], pb[t], acc[nb], 0, 0, 0);
       }
     }
+  }
   }
   l = sum_halves(l);
 
