@@ -420,6 +420,23 @@ def test_dense_and_compact_partial_slots(k):
     assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
 
 
+@pytest.mark.parametrize("heads", [1, 64])
+def test_head_counts(heads):
+    """One head and 64 heads (the kernels index heads only through the
+    tile base and the record layout): a shared prefix with ragged private
+    tails against the oracle, two launches and one launch bit for bit."""
+    _say(f"heads={heads}")
+    from decode_attention_prefix_tree_amd import _capi
+    suffix = [int(x) for x in np.random.default_rng(40 + heads).integers(1, 300, size=12)]
+    wl = make_prefix_suffix(700, suffix, heads=heads, seed=41 + heads)
+    ca = build_ca(wl)
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 0)
+    got = run_step(ca, wl.q)
+    assert_parity(got, A.decode_workload(wl), f"heads={heads}")
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 1)
+    assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
+
+
 def _host_shadow(wl, two_phase):
     """A context without a device pool that receives the same tree calls: its
     exported table is the reference for the device context's."""
