@@ -85,6 +85,8 @@ _SIGS = {
                                    _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "ca_remove": (_c.c_int, [_c.c_void_p, _c.c_int64]),
     "ca_attend": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "ca_decode_step": (_c.c_int, [_c.c_void_p, _c.POINTER(_c.c_int32), _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                  _c.c_void_p, _c.c_void_p]),
     "ca_prepare": (_c.c_int, [_c.c_void_p, _c.c_void_p]),
     "ca_attend_phase": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "ca_list_sequences": (_c.c_int, [_c.c_void_p, _c.POINTER(_c.c_int64), _c.c_int]),

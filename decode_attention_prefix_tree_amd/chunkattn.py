@@ -190,6 +190,26 @@ class ChunkAttention:
                                            ctypes.c_void_p(out.data_ptr()), self._stream(stream)))
         return out
 
+    def decode_step(self, tokens, k, v, q, out=None, stream=None):
+        """Append tokens[r] with K/V row r to the r-th live sequence (ascending
+        id), then attend with q; returns out (ca_decode_step)."""
+        if self.device is None:
+            raise CaError(-9, "host-only context")
+        t = _tokens(tokens)
+        if len(t) != self._n_live:
+            raise ValueError("one token per live sequence")
+        kp, vp = self._kv(k, v, len(t))
+        q, out = self._qo(q, out)
+        self.ensure_workspace()
+        rc = self.lib.ca_decode_step(self.ctx, _ptr_i32(t), kp, vp, ctypes.c_void_p(q.data_ptr()),
+                                     ctypes.c_void_p(out.data_ptr()), self._stream(stream))
+        if rc == -7:
+            # the tokens are stored; the new chunks need a larger workspace
+            self.ensure_workspace()
+            return self.attend(q, out, stream)
+        check(self.ctx, rc)
+        return out
+
     def prepare(self, stream=None) -> None:
         self.ensure_workspace()
         check(self.ctx, self.lib.ca_prepare(self.ctx, self._stream(stream)))

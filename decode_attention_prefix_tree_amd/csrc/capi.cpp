@@ -28,6 +28,7 @@ struct ca_ctx {
   int plan_cf_group = 8;           // the group the current plan was built with
   int fused_merge = 2;              // CA_OPT_FUSED_MERGE: 0 two launches, 1 one launch, 2 chosen per plan
   unsigned fuse_epoch = 0;          // one-launch steps since the last table upload
+  unsigned decode_epoch = 0;        // ca_decode_step launches that grew chunks in the kernel
 
   // plan cache: rebuilt after the tree changes, uploaded when stale
   chunkattn::Plan plan;
@@ -212,7 +213,8 @@ void upload(ca_ctx* c, void* stream) {
   hip_check(hipEventRecord(c->stage_done[b], static_cast<hipStream_t>(stream)), "hipEventRecord");
   c->stage_pending[b] = true;
   c->table_uploads += 1;
-  c->fuse_epoch = 0;  // the upload zeroed the arrival counters
+  c->fuse_epoch = 0;    // the upload zeroed the arrival counters
+  c->decode_epoch = 0;  // and wrote untagged fill counts
   c->uploaded_version = c->version;
   c->uploaded_ws = c->ws;
 }
@@ -240,6 +242,9 @@ chunkattn::StepArgs step_args(ca_ctx* c, const void* q, void* out) {
   a.n_sf_tasks = static_cast<int>(p.sf_tasks.size());
   a.n_seq = static_cast<int>(p.dfs_seq.size());
   a.scale_log2e = static_cast<float>((1.0 / std::sqrt(static_cast<double>(c->head_dim))) * 1.4426950408889634);
+  a.app_k = nullptr;
+  a.app_v = nullptr;
+  a.app_epoch = 0;
   return a;
 }
 
@@ -345,6 +350,15 @@ void touch_patched(ca_ctx* c) {
   c->fills_stale = true;
   c->version += 1;
   c->uploaded_version = c->version;
+}
+
+void launch_step(ca_ctx* c, const chunkattn::StepArgs& a, void* stream) {
+  if (one_launch(c)) {
+    launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, true, ++c->fuse_epoch, stream), "step");
+  } else {
+    launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, false, 0, stream), "partials");
+    launch(chunkattn::launch_merge(a, stream), "merge");
+  }
 }
 
 #define CA_GUARD(ctx, ...)                                                    \
@@ -544,13 +558,43 @@ int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream) {
   CA_GUARD(ctx, {
     check_step(ctx, q_dev, out_dev);
     upload(ctx, stream);
-    chunkattn::StepArgs a = step_args(ctx, q_dev, out_dev);
-    if (one_launch(ctx)) {
-      launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, true, ++ctx->fuse_epoch, stream), "step");
+    launch_step(ctx, step_args(ctx, q_dev, out_dev), stream);
+    return CA_OK;
+  });
+}
+
+int ca_decode_step(ca_ctx* ctx, const int32_t* tokens, const void* k_dev, const void* v_dev, const void* q_dev,
+                   void* out_dev, void* stream) {
+  CA_GUARD(ctx, {
+    if (!ctx->pool_attached || ctx->pool == nullptr) throw Error(CA_E_NO_POOL, "no device pool attached");
+    if (ctx->mgr.live() == 0) throw Error(CA_E_EMPTY, "no live sequence");
+    if (tokens == nullptr || k_dev == nullptr || v_dev == nullptr)
+      throw Error(CA_E_INVALID_ARG, "tokens, k_dev and v_dev are required");
+    const std::vector<int64_t> ids = ctx->mgr.sequences();
+    std::vector<chunkattn::KvOp> ops;
+    std::vector<FillPatch> patches;
+    ctx->mgr.append_batch(ids.data(), tokens, static_cast<int32_t>(ids.size()), &ops);
+    // Every token grew its sequence's private last chunk in place and the
+    // device table is current: the step's own blocks write the tokens.  The
+    // epoch tags the fill counts they store; it restarts (with a clean table)
+    // before it would wrap.
+    const bool in_kernel = fill_patches(ctx, ops, &patches) && ctx->decode_epoch < chunkattn::kEpochMask;
+    if (in_kernel) {
+      touch_patched(ctx);
+      ctx->decode_epoch += 1;
     } else {
-      launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, false, 0, stream), "partials");
-      launch(chunkattn::launch_merge(a, stream), "merge");
+      touch_after_append(ctx);
+      run_kv_ops(ctx, ops, k_dev, v_dev, stream);
     }
+    check_step(ctx, q_dev, out_dev);
+    upload(ctx, stream);
+    chunkattn::StepArgs a = step_args(ctx, q_dev, out_dev);
+    if (in_kernel) {
+      a.app_k = k_dev;
+      a.app_v = v_dev;
+      a.app_epoch = ctx->decode_epoch;
+    }
+    launch_step(ctx, a, stream);
     return CA_OK;
   });
 }

@@ -14,6 +14,14 @@ constexpr int kSfInline = 4;   // chunk refs carried by a sequence-first task re
 // same chunks, so the block reads them with loads that keep them cached.
 constexpr int kCfReuseField = 6;
 constexpr int kSfReuseField = 5;
+// Sequence-first record field: index in the task of the chunk where the
+// sequence ends (where a decoded token is appended), or -1.
+constexpr int kSfAppendField = 6;
+// Fill counts (at most 64) in the device table may carry, above bit 8, the
+// epoch of the decode step that last grew them in the kernel; readers mask.
+constexpr int kFillBits = 8;
+constexpr int kFillMask = (1 << kFillBits) - 1;
+constexpr unsigned kEpochMask = (1u << (32 - kFillBits)) - 1;
 constexpr int kDenseParts = 16; // most partials per sequence for the dense partial layout
 
 // Arguments of one decode step.  All pointers are device addresses.
@@ -37,6 +45,13 @@ struct StepArgs {
   int n_sf_tasks;
   int n_seq;
   float scale_log2e;           // (1/sqrt(128)) * log2(e)
+  // Decode step with in-kernel appends (null when not): row r of app_k /
+  // app_v ([n_live][H][128] fp16) is the new token of the sequence at caller
+  // row r; the block owning that sequence's last chunk writes it into the
+  // pool, uses it, and stores the grown fill count tagged with app_epoch.
+  const void* app_k;
+  const void* app_v;
+  unsigned app_epoch;          // 1 .. kEpochMask
 };
 
 // Which blocks of the partials kernel to launch.

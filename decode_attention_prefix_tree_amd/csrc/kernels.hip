@@ -301,7 +301,8 @@ constexpr int kSmemBytes = kQBytes + 2 * kStateFloats * 4;
 constexpr int kSfP = D * 2;                // after the query row (fp16)
 constexpr int kSfO = kSfP + 4 * 64 * 4;    // after the probability rows
 constexpr int kSfM = kSfO + 4 * D * 4;     // after the wave states' o rows
-static_assert(kSfM + 8 * 4 <= kSmemBytes, "sequence-first scratch fits the block's LDS");
+constexpr int kSfA = kSfM + 8 * 4;         // after the wave states' (m, l): an appended K and V row
+static_assert(kSfA + 2 * D * 2 <= kSmemBytes, "sequence-first scratch fits the block's LDS");
 
 __device__ __forceinline__ float weight(float m, float M) {
   // e^(m - M) in base 2; an empty state (m = -inf) weighs 0 even when M = -inf
@@ -350,7 +351,7 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
     // flight, one round trip, like a sequence-first wave): K 64 VGPRs, V 64,
     // one half's scores 16 while the first half's K is still live.
     if (wave < n_chunks) {
-      const int slot = u[8 + wave], nvalid = u[16 + wave];  // inline: wave < 4 <= kCfInline
+      const int slot = u[8 + wave], nvalid = u[16 + wave] & kFillMask;  // inline: wave < 4 <= kCfInline
       const _Float16* kt = pool + tile_base(slot, head, H, 0);
       const _Float16* vt = kt + TILE;
       h8 kr[16], vr[16];
@@ -415,7 +416,7 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
   for (int nb = 0; nb < 4; ++nb) acc[nb] = f16v{};
   for (int c = wave; c < n_chunks; c += 4) {
     const int slot = c < kCfInline ? u[8 + c] : a.chunk_refs[2 * (chunk_begin + c)];
-    const int nvalid = c < kCfInline ? u[16 + c] : a.chunk_refs[2 * (chunk_begin + c) + 1];
+    const int nvalid = (c < kCfInline ? u[16 + c] : a.chunk_refs[2 * (chunk_begin + c) + 1]) & kFillMask;
     const _Float16* kt = pool + tile_base(slot, head, H, 0);
     const _Float16* vt = kt + TILE;
     // The halves stay a loop: unrolled, the second half's loads would be
@@ -589,20 +590,69 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
   float(*w_o)[D] = reinterpret_cast<float(*)[D]>(smem + kSfO);
   float* w_m = reinterpret_cast<float*>(smem + kSfM);
   float* w_l = w_m + 4;
+  _Float16* new_lds = reinterpret_cast<_Float16*>(smem + kSfA);  // appended token: K row, then V row
+  // In a decode step with in-kernel appends, the chunk (index in the task)
+  // that takes this sequence's new token.
+  const int append_at = a.app_k != nullptr ? t[kSfAppendField] : -1;
   if (threadIdx.x < D / 8) {
     const _Float16* qp = static_cast<const _Float16*>(a.q) + (static_cast<size_t>(qrow) * H + head) * D;
     *reinterpret_cast<h8*>(q_lds + threadIdx.x * 8) = *reinterpret_cast<const h8*>(qp + threadIdx.x * 8);
+  } else if (append_at >= 0 && threadIdx.x < 3 * D / 8) {
+    const int kv = threadIdx.x / (D / 8) - 1, piece = threadIdx.x % (D / 8);
+    const _Float16* src = static_cast<const _Float16*>(kv ? a.app_v : a.app_k) +
+                          (static_cast<size_t>(qrow) * H + head) * D + piece * 8;
+    *reinterpret_cast<h8*>(new_lds + kv * D + piece * 8) = *reinterpret_cast<const h8*>(src);
   }
   __syncthreads();
 
   float m = -INFINITY, l = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 
+  // The appended token goes to key p of chunk append_at, the chunk's fill
+  // before this step: the blocks of the other heads of this task share the
+  // fill count, and one that ran first may already have stored p + 1 tagged
+  // with this step's epoch.  The wave that will read the chunk writes the
+  // token into its tiles before its loop starts, with the very lanes that
+  // later load those 16-byte units, so its loads read it back in program
+  // order; the fill count the loop uses is p + 1.
+  int append_fill = 0;
+  if (append_at >= 0) {
+    const int ac = append_at;
+    const int fill = ac < kSfInline ? t[12 + ac] : a.chunk_refs[2 * (chunk_begin + ac) + 1];
+    const int p = (static_cast<unsigned>(fill) >> kFillBits) == a.app_epoch ? (fill & kFillMask) - 1 : fill & kFillMask;
+    append_fill = p + 1;
+    if ((ac & 3) == wave) {
+      const int slot = ac < kSfInline ? t[8 + ac] : a.chunk_refs[2 * (chunk_begin + ac)];
+      _Float16* kw = const_cast<_Float16*>(pool) + tile_base(slot, head, H, 0);
+      _Float16* vw = kw + TILE;
+      // K: load (p/32)*8 + j, lanes (half, p%32): dims 16j + 8half .. +8
+      if (i == (p & 31)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<h8*>(kw + (((p >> 5) * 8 + j) * 64 + lane) * 8) =
+              *reinterpret_cast<const h8*>(new_lds + j * 16 + half * 8);
+      }
+      // V: load 4nb + p/16, lanes (half (p/4)%2, i): dim 32nb + i, key p at element e
+      if (half == ((p >> 2) & 1)) {
+        const int e = (p & 3) | (((p >> 3) & 1) << 2);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) vw[((nb * 4 + (p >> 4)) * 64 + lane) * 8 + e] = new_lds[D + nb * 32 + i];
+      }
+      if (lane == 0) {
+        const int tagged = append_fill | static_cast<int>(a.app_epoch << kFillBits);
+        const_cast<int32_t*>(a.chunk_refs)[2 * (chunk_begin + ac) + 1] = tagged;
+        if (ac < kSfInline) const_cast<int*>(t)[12 + ac] = tagged;
+      }
+    }
+  }
+
   for (int c = wave; c < n_chunks; c += 4) {
     const int slot = c < kSfInline ? t[8 + c] : a.chunk_refs[2 * (chunk_begin + c)];
-    const int nvalid = c < kSfInline ? t[12 + c] : a.chunk_refs[2 * (chunk_begin + c) + 1];
+    const int fill = c < kSfInline ? t[12 + c] : a.chunk_refs[2 * (chunk_begin + c) + 1];
+    int nvalid = fill & kFillMask;
     const _Float16* kt = pool + tile_base(slot, head, H, 0);
     const _Float16* vt = kt + TILE;
+    if (c == append_at) nvalid = append_fill;
     h8 ka[16], va[16];
 #pragma unroll
     for (int L = 0; L < 16; ++L) ka[L] = ld_tile<kNT>(kt + (L * 64 + lane) * 8);

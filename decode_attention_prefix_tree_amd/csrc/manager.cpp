@@ -372,8 +372,11 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
       st.dfs_pos = i;
       st.part_id = -1;
       st.qrow = P.dfs_qrow[i];
+      st.append_at = -1;
       for (size_t q = j; q < stop; ++q) {
         const int c = static_cast<int>(q - j);
+        // the chunk where the sequence ends takes its next decoded token
+        if (priv[q] == end_row[i]) st.append_at = c;
         if (c < kSfInline) {
           st.slot[c] = R(priv[q], 6);
           st.n_valid[c] = R(priv[q], 3);

@@ -85,14 +85,16 @@ struct SfTask {        // sequence-first: some private chunks of one sequence
   int32_t part_id;
   int32_t qrow;        // caller row of the sequence
   int32_t reuse;       // 1: some chunk is shared (read by other tasks; only without chunk-first)
-  int32_t pad[2];
+  int32_t append_at;   // index (in this task) of the chunk where the sequence ends, or -1
+  int32_t pad;
   int32_t slot[kSfInline];
   int32_t n_valid[kSfInline];  // 64 bytes
 };
 
 static_assert(sizeof(CfUnit) == 128 && sizeof(SfTask) == 64, "record layouts are read by the kernels");
-static_assert(offsetof(CfUnit, reuse) == kCfReuseField * 4 && offsetof(SfTask, reuse) == kSfReuseField * 4,
-              "reuse flags sit where the kernels read them");
+static_assert(offsetof(CfUnit, reuse) == kCfReuseField * 4 && offsetof(SfTask, reuse) == kSfReuseField * 4 &&
+                  offsetof(SfTask, append_at) == kSfAppendField * 4,
+              "record fields sit where the kernels read them");
 
 struct Plan {
   std::vector<int32_t> rows;        // canonical table, 7 ints per row

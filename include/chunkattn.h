@@ -222,6 +222,25 @@ int ca_remove(ca_ctx* ctx, int64_t seq_id);
  * Errors: CA_E_EMPTY, CA_E_WORKSPACE, CA_E_NO_POOL, CA_E_HIP. */
 int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream);
 
+/* One decode step of the whole batch (summary section 3.1: decoding appends
+ * to leaf chunks; section 2.2: one query token per sequence): token tokens[r]
+ * with K/V row r of k_dev, v_dev (fp16 [n_live][heads][head_dim]) is appended
+ * to the r-th live sequence in ascending seq_id order, then every sequence
+ * attends with row r of q_dev; out_dev as for ca_attend.  The result, the
+ * tree and the stored K/V are those of ca_append_batch over all live
+ * sequences followed by ca_attend.  When every token grows its sequence's
+ * private last chunk in place (63 of every 64 steps of a batch that decodes
+ * in lockstep), no separate write launch runs: the block of the step that
+ * reads that chunk writes the token into the pool, uses it, and stores the
+ * grown fill count into the device table; otherwise the writes go out first,
+ * as in ca_append_batch.  The caller keeps k_dev and v_dev alive until the
+ * stream passes the step.  Errors: those of ca_append_batch (which leave
+ * everything unchanged) and of ca_attend; CA_E_WORKSPACE comes after the
+ * tokens were stored (a step that grew new chunks can need a larger
+ * workspace): attach one of ca_workspace_bytes and finish with ca_attend. */
+int ca_decode_step(ca_ctx* ctx, const int32_t* tokens, const void* k_dev, const void* v_dev,
+                   const void* q_dev, void* out_dev, void* stream);
+
 /* The same step split into its launches, for measuring each kernel: call
  * ca_prepare once (uploads the table if needed), then ca_attend_phase with
  * CA_PHASE_PARTIALS (or CA_PHASE_CHUNK_FIRST and CA_PHASE_SEQUENCE_FIRST)

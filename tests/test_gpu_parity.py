@@ -437,6 +437,56 @@ def test_head_counts(heads):
     assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
 
 
+@pytest.mark.parametrize("mode", ["two_launch", "one_launch", "shared_pages"])
+def test_decode_step_equals_append_then_attend(mode):
+    """ca_decode_step (tokens written by the step's own blocks while chunks
+    grow in place, a separate write launch when a chunk fills up or a
+    sequence's last chunk is shared) against ca_append_batch + ca_attend on a
+    twin context: the same bits at every one of 140 steps, the same tables,
+    and the oracle over the grown sequences every 35 steps.  One sequence
+    ends inside the shared prefix, so its first append grows a new chunk."""
+    _say(f"decode step, {mode}")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import _capi
+    rng = np.random.default_rng(50)
+    H = 4
+    shared = list(range(100))
+    seqs = [shared + [5000 + i] + [int(x) for x in rng.integers(0, 9, size=n)]
+            for i, n in enumerate((0, 30, 62, 63, 130, 10))]
+    seqs.append(shared[:40])
+    wl = from_token_lists(seqs, heads=H, seed=51)
+    two_phase = mode != "shared_pages"
+    from decode_attention_prefix_tree_amd import slots_needed
+    cap = slots_needed(wl) + 40
+    a = build_ca(wl, capacity=cap, two_phase=two_phase)
+    b = build_ca(wl, capacity=cap, two_phase=two_phase)
+    for ca in (a, b):
+        ca.set_option(_capi.CA_OPT_FUSED_MERGE, 1 if mode == "one_launch" else 0)
+    n = wl.n_seq
+    kv = [[x.copy() for x in wl.seq_kv(i)] for i in range(n)]
+    for step in range(140):
+        toks = (10**6 + step * 100 + np.arange(n)).astype(np.int32)
+        k = rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+        v = rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+        q = rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+        kt, vt, qt = (torch.from_numpy(x).cuda() for x in (k, v, q))
+        a.append_batch(list(range(n)), toks, kt, vt)
+        ra = a.attend(qt).clone()
+        rb = b.decode_step(toks, kt, vt, qt).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(ra, rb), (mode, step)
+        for i in range(n):
+            kv[i][0] = np.concatenate([kv[i][0], k[i:i + 1]])
+            kv[i][1] = np.concatenate([kv[i][1], v[i:i + 1]])
+        if step % 35 == 0 or step == 139:
+            assert_parity(rb.cpu().numpy(), A.decode_step(q, kv), f"decode {mode} step {step}")
+    ta, oa = a.export_table()
+    tb, ob = b.export_table()
+    assert oa == ob and np.array_equal(ta, tb)
+    st = b.stats()
+    assert st["patched_appends"] >= 100, st
+
+
 def _host_shadow(wl, two_phase):
     """A context without a device pool that receives the same tree calls: its
     exported table is the reference for the device context's."""
