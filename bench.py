@@ -55,7 +55,8 @@ def parse():
     ap.add_argument("--n-seq", type=int, default=32, help="sequences of the --prefix-len workload")
     ap.add_argument("--decode", action="store_true",
                     help="decode progression instead: n_s = 2048 shared prompt tokens, one token appended per "
-                         "sequence per step (completion length n_c sweep at batch 32, batch sweep at n_c = 512)")
+                         "sequence per step (completion length n_c sweep at batch 32, batch sweep at n_c = 512), "
+                         "as ca_decode_step and as append + attend, with the shared-pages comparator")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the per-kernel timing loop (for rocprofv3 runs); prints its event means")
     ap.add_argument("--phases", action="store_true",
@@ -201,11 +202,14 @@ def cpu_baseline(wl, seconds_target):
                       f"{used} threads over sequences, BLAS 1 thread each"}
 
 
-def decode_progression(torch, n_seq, n_shared, checkpoints, two_phase, flush, window=16, heads=32, seed=7):
+def decode_progression(torch, n_seq, n_shared, checkpoints, two_phase, flush, window=16, heads=32, seed=7,
+                       one_call=False):
     """Decode steps from a fully shared prompt: each step appends one token per
-    sequence (ca_append_batch) and attends.  Returns, per checkpoint n_c (the
-    completion length reached), the mean cold GPU time of the append and the
-    attend over the `window` steps ending there, and the host time per step."""
+    sequence and attends, either as ca_append_batch + ca_attend or, with
+    one_call, as ca_decode_step.  Returns, per checkpoint n_c (the completion
+    length reached), the mean cold GPU time of the append and the attend (or
+    of the whole step) over the `window` steps ending there, and the host time
+    per step."""
     from decode_attention_prefix_tree_amd import ChunkAttention
     gen = torch.Generator(device="cuda").manual_seed(seed)
     max_c = max(checkpoints)
@@ -224,18 +228,25 @@ def decode_progression(torch, n_seq, n_shared, checkpoints, two_phase, flush, wi
         v = torch.randn((n_seq, heads, 128), generator=gen, device="cuda").half()
         q = torch.randn((n_seq, heads, 128), generator=gen, device="cuda").half()
         timed = any(cp - window < c <= cp for cp in checkpoints)
+        toks = np.full(n_seq, c, np.int32)
         if timed:
             flush()
             e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             h0 = time.perf_counter()
             e[0].record()
-            ca.append_batch(ids, np.full(n_seq, c, np.int32), k, v)
-            e[1].record()
-            ca.attend(q, out)
+            if one_call:
+                e[1] = e[0]  # one call: the whole step is reported as the attend column
+                ca.decode_step(toks, k, v, q, out)
+            else:
+                ca.append_batch(ids, toks, k, v)
+                e[1].record()
+                ca.attend(q, out)
             e[2].record()
             pending.append((c, e, time.perf_counter() - h0))
+        elif one_call:
+            ca.decode_step(toks, k, v, q, out)
         else:
-            ca.append_batch(ids, np.full(n_seq, c, np.int32), k, v)
+            ca.append_batch(ids, toks, k, v)
             ca.attend(q, out)
         if c in checkpoints:
             torch.cuda.synchronize()
@@ -244,6 +255,7 @@ def decode_progression(torch, n_seq, n_shared, checkpoints, two_phase, flush, wi
             att = float(np.mean([r[1] for r in rows])) * 1e3
             host = float(np.mean([r[2] for r in rows])) * 1e6
             st = ca.stats()
+            # with one_call the append column is 0 and attend is the whole step
             res[c] = {"append_us": app, "attend_us": att, "host_us_per_step": host,
                       "generated_tokens_per_s": n_seq / ((app + att) * 1e-6),
                       "attended_tokens_per_s": st["attended_tokens"] / (att * 1e-6),
@@ -258,22 +270,28 @@ def decode_progression(torch, n_seq, n_shared, checkpoints, two_phase, flush, wi
 
 def decode_main(args, torch):
     flush = Flusher(torch)
-    line = {"metric": "decode progression: generated tokens/s (one batched append + one attend per step)",
+    line = {"metric": "decode progression: generated tokens/s (ca_decode_step: one token per sequence "
+                      "appended and attended per call)",
             "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "dtype": "f16", "data": "synthetic",
             "config": {"workload": "n_s = 2048 shared prompt tokens, heads 32, head_dim 128, chunk 64",
                        "cache": "cold (1 GiB read before each timed step)"}}
-    for name, two_phase in (("two_phase", True), ("shared_pages_no_chunk_first", False)):
+    modes = (("decode_step", True, True), ("two_phase", True, False), ("shared_pages_no_chunk_first", False, False))
+    for name, two_phase, one_call in modes:
         log(f"decode n_c sweep, {name}")
         line.setdefault("nc_sweep_batch32", {})[name] = decode_progression(
-            torch, 32, 2048, [512, 1024, 2048], two_phase, flush)
+            torch, 32, 2048, [512, 1024, 2048], two_phase, flush, one_call=one_call)
         log(f"decode batch sweep, {name}")
         line.setdefault("batch_sweep_nc512", {})[name] = {
-            b: decode_progression(torch, b, 2048, [512], two_phase, flush)[512] for b in (16, 32, 64, 96)}
+            b: decode_progression(torch, b, 2048, [512], two_phase, flush, one_call=one_call)[512]
+            for b in (16, 32, 64, 96)}
     sw = line["nc_sweep_batch32"]
+
+    def step_us(r):
+        return r["append_us"] + r["attend_us"]
+
     line["speedup_vs_shared_pages"] = {
-        nc: (sw["shared_pages_no_chunk_first"][nc]["append_us"] + sw["shared_pages_no_chunk_first"][nc]["attend_us"])
-        / (sw["two_phase"][nc]["append_us"] + sw["two_phase"][nc]["attend_us"]) for nc in sw["two_phase"]}
-    line["value"] = sw["two_phase"][512]["generated_tokens_per_s"]
+        nc: step_us(sw["shared_pages_no_chunk_first"][nc]) / step_us(sw["decode_step"][nc]) for nc in sw["decode_step"]}
+    line["value"] = sw["decode_step"][512]["generated_tokens_per_s"]
     print(json.dumps(line), flush=True)
 
 
