@@ -567,8 +567,10 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
 // so a score needs one exchange with the twin lane; for V it holds dim
 // 32nb + i at 8 keys per load and reads the matching probabilities from a
 // 64-entry LDS row of its wave.  Three waves per SIMD keep about 384 KiB of
-// loads in flight per CU.
-template <bool kFuse, bool kNT>
+// loads in flight per CU.  kAppend: a decode step whose blocks also write the
+// new tokens; the attend-only kernel has no stores into the pool or the
+// table, so its table reads stay scalar loads.
+template <bool kFuse, bool kNT, bool kAppend>
 __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logical, char* smem) {
   // heads vary fastest: blocks that run together read neighbouring 32 KiB
   // tiles of the same slots, which keeps HBM accesses close to sequential
@@ -593,7 +595,7 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
   _Float16* new_lds = reinterpret_cast<_Float16*>(smem + kSfA);  // appended token: K row, then V row
   // In a decode step with in-kernel appends, the chunk (index in the task)
   // that takes this sequence's new token.
-  const int append_at = a.app_k != nullptr ? t[kSfAppendField] : -1;
+  const int append_at = kAppend ? t[kSfAppendField] : -1;
   if (threadIdx.x < D / 8) {
     const _Float16* qp = static_cast<const _Float16*>(a.q) + (static_cast<size_t>(qrow) * H + head) * D;
     *reinterpret_cast<h8*>(q_lds + threadIdx.x * 8) = *reinterpret_cast<const h8*>(qp + threadIdx.x * 8);
@@ -616,7 +618,7 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
   // later load those 16-byte units, so its loads read it back in program
   // order; the fill count the loop uses is p + 1.
   int append_fill = 0;
-  if (append_at >= 0) {
+  if (kAppend && append_at >= 0) {
     const int ac = append_at;
     const int fill = ac < kSfInline ? t[12 + ac] : a.chunk_refs[2 * (chunk_begin + ac) + 1];
     const int p = (static_cast<unsigned>(fill) >> kFillBits) == a.app_epoch ? (fill & kFillMask) - 1 : fill & kFillMask;
@@ -652,7 +654,7 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
     int nvalid = fill & kFillMask;
     const _Float16* kt = pool + tile_base(slot, head, H, 0);
     const _Float16* vt = kt + TILE;
-    if (c == append_at) nvalid = append_fill;
+    if (kAppend && c == append_at) nvalid = append_fill;
     h8 ka[16], va[16];
 #pragma unroll
     for (int L = 0; L < 16; ++L) ka[L] = ld_tile<kNT>(kt + (L * 64 + lane) * 8);
@@ -758,8 +760,9 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
 // n_cf, n_sf: chunk-first and sequence-first blocks of the step; first:
 // index of this launch's first block in the step's grid (0, or n_cf to launch
 // only the sequence-first part).  kFuse: the one-launch step, whose grid ends
-// with the merge blocks (epoch: see merge_block).
-template <bool kFuse>
+// with the merge blocks (epoch: see merge_block).  kAppend: a decode step
+// with in-kernel appends (StepArgs::app_k set).
+template <bool kFuse, bool kAppend>
 __global__ __launch_bounds__(256, 3) void partials_kernel(StepArgs a, int n_cf, int n_sf, int first,
                                                           unsigned epoch) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
@@ -773,9 +776,9 @@ __global__ __launch_bounds__(256, 3) void partials_kernel(StepArgs a, int n_cf, 
   } else if (b < n_cf + n_sf) {
     const int logical = b - n_cf;
     if (a.sf_tasks[(logical / a.heads) * 16 + kSfReuseField])
-      sequence_first_block<kFuse, false>(a, logical, smem);
+      sequence_first_block<kFuse, false, kAppend>(a, logical, smem);
     else
-      sequence_first_block<kFuse, true>(a, logical, smem);
+      sequence_first_block<kFuse, true, kAppend>(a, logical, smem);
   }
   else if constexpr (kFuse)
     merge_block(a, b - n_cf - n_sf, epoch);
@@ -802,10 +805,15 @@ int launch_partials(const StepArgs& a, int part, bool fuse_merge, unsigned epoch
   const int count = part == kPartsChunkFirst ? n_cf : part == kPartsSequenceFirst ? n_sf : n_cf + n_sf + n_merge;
   if (count <= 0) return 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (fuse)
-    hipLaunchKernelGGL(partials_kernel<true>, dim3(count), dim3(256), 0, st, a, n_cf, n_sf, first, epoch);
+  const bool append = a.app_k != nullptr;
+  if (fuse && append)
+    hipLaunchKernelGGL((partials_kernel<true, true>), dim3(count), dim3(256), 0, st, a, n_cf, n_sf, first, epoch);
+  else if (fuse)
+    hipLaunchKernelGGL((partials_kernel<true, false>), dim3(count), dim3(256), 0, st, a, n_cf, n_sf, first, epoch);
+  else if (append)
+    hipLaunchKernelGGL((partials_kernel<false, true>), dim3(count), dim3(256), 0, st, a, n_cf, n_sf, first, epoch);
   else
-    hipLaunchKernelGGL(partials_kernel<false>, dim3(count), dim3(256), 0, st, a, n_cf, n_sf, first, epoch);
+    hipLaunchKernelGGL((partials_kernel<false, false>), dim3(count), dim3(256), 0, st, a, n_cf, n_sf, first, epoch);
   return static_cast<int>(hipGetLastError());
 }
 
