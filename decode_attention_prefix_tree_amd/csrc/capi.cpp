@@ -294,25 +294,50 @@ bool fill_patches(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, std::vecto
     }
     const int32_t task_off =
         p.ref_pos[k] < chunkattn::kSfInline ? tasks + p.ref_task[k] * kTaskInts + kFillField + p.ref_pos[k] : -1;
-    out->push_back(FillPatch{refs + 2 * k + 1, task_off, o.dst_key0 + o.n_rows});
+    out->push_back(FillPatch{refs + 2 * k + 1, task_off, c->mgr.tile_fill(o.dst_key0 + o.n_rows, p.ref_sub[k])});
   }
   return true;
 }
 
-// Launch the copies, kOpsPerLaunch at a time; the patches of an op (if any)
-// ride with the launch that writes its chunk.
+// The pieces of a copy, one per destination 64-key tile: key k of chunk
+// slot s is key (s * C + k) mod 64 of tile (s * C + k) / 64.  A split's tail
+// is read by global pool key, so its source may span two tiles within one
+// piece: no two pieces of a launch write the same tile.  Keys are written in
+// increasing order, so a piece that starts a tile is that tile's first write
+// since its slot was allocated: it zeroes the tile's other keys (unwritten V
+// columns must be finite, they meet zero probabilities).
+void tile_pieces(const chunkattn::KvOp& o, int C, std::vector<chunkattn::KvOpDev>* out) {
+  constexpr int32_t T = chunkattn::kTileKeys;
+  for (int32_t done = 0; done < o.n_rows;) {
+    const int64_t dg = static_cast<int64_t>(o.dst_slot) * C + o.dst_key0 + done;
+    const int32_t key0 = static_cast<int32_t>(dg % T);
+    const int32_t n = std::min<int32_t>(o.n_rows - done, T - key0);
+    const int32_t src0 = o.from_pool ? o.src_slot * C + o.src_row0 + done : o.src_row0 + done;
+    out->push_back(chunkattn::KvOpDev{static_cast<int32_t>(dg / T), key0, n, src0, o.from_pool,
+                                      key0 == 0 ? 1 : 0, 0, 0});
+    done += n;
+  }
+}
+
+// Launch the copies, kOpsPerLaunch tile pieces at a time; the patches of an
+// op (if any) ride with the launch that writes its last piece.
 void run_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* k, const void* v, void* stream,
                 const std::vector<FillPatch>& patches = {}) {
+  std::vector<chunkattn::KvOpDev> pieces;
+  std::vector<int32_t> patch_of;  // per piece: index into patches, or -1
+  for (size_t i = 0; i < ops.size(); ++i) {
+    tile_pieces(ops[i], c->chunk, &pieces);
+    patch_of.resize(pieces.size(), -1);
+    if (!patches.empty()) patch_of.back() = static_cast<int32_t>(i);
+  }
   chunkattn::KvOpBatch batch{};
   chunkattn::TablePatches tp{};
   int n = 0;
   int32_t* table = static_cast<int32_t*>(c->ws);
-  for (size_t i = 0; i < ops.size(); ++i) {
-    const chunkattn::KvOp& o = ops[i];
-    batch.ops[n++] = chunkattn::KvOpDev{o.dst_slot, o.dst_key0, o.n_rows, o.src_row0,
-                                        o.src_slot, o.from_pool, o.zero_rest, 0};
-    if (!patches.empty()) {
-      const FillPatch& f = patches[i];
+  for (size_t i = 0; i < pieces.size(); ++i) {
+    batch.ops[n++] = pieces[i];
+    if (patch_of[i] >= 0) {
+      const FillPatch& f = patches[patch_of[i]];
       tp.off[tp.n] = f.ref_off;
       tp.val[tp.n++] = f.val;
       if (f.task_off >= 0) {
@@ -320,7 +345,7 @@ void run_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* 
         tp.val[tp.n++] = f.val;
       }
     }
-    if (n == chunkattn::kOpsPerLaunch || i + 1 == ops.size()) {
+    if (n == chunkattn::kOpsPerLaunch || i + 1 == pieces.size()) {
       launch(chunkattn::launch_kv_write(c->pool, c->heads, batch, n, k, v, table, tp, stream), "kv_write");
       n = 0;
       tp.n = 0;
@@ -391,7 +416,7 @@ int ca_create_ex(int heads, int head_dim, int chunk_size, int flags, ca_ctx** ou
   if (out == nullptr) return CA_E_INVALID_ARG;
   *out = nullptr;
   if (heads < 1) return CA_E_INVALID_ARG;
-  if (head_dim != chunkattn::kHeadDim || chunk_size != chunkattn::kChunk) return CA_E_UNSUPPORTED;
+  if (head_dim != chunkattn::kHeadDim || (chunk_size != 64 && chunk_size != 128)) return CA_E_UNSUPPORTED;
   if (flags & ~(CA_CREATE_UNSHARED | CA_CREATE_NO_CHUNK_FIRST)) return CA_E_UNSUPPORTED;
   try {
     *out = new ca_ctx(heads, head_dim, chunk_size, flags);

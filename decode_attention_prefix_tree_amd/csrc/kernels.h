@@ -8,6 +8,7 @@ namespace chunkattn {
 
 constexpr int kHeadDim = 128;
 constexpr int kChunk = 64;
+constexpr int kTileKeys = kChunk;  // keys per K/V tile read by the kernels
 constexpr int kCfInline = 8;   // chunk refs carried by a chunk-first unit record
 constexpr int kSfInline = 4;   // chunk refs carried by a sequence-first task record
 // Record fields (int32 index) saying that other blocks of the step read the

@@ -14,7 +14,7 @@ namespace chunkattn {
 
 namespace {
 
-// KV writes: caller rows or another slot's rows into one slot's tiles.
+// KV writes: caller rows or pool keys into one 64-key tile (K and V).
 // grid (n_ops, heads, 2), 256 threads; a thread owns 4 of the tile's 1024
 // 16-byte units.  Without zero_rest only the units holding a written key are
 // read and rewritten (a one-token append touches 16 K units and 128 V units
@@ -28,8 +28,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(_Float16* pool, int heads
     table[patches.off[threadIdx.x]] = patches.val[threadIdx.x];
   const KvOpDev op = batch.ops[blockIdx.x];
   const int head = blockIdx.y, kv = blockIdx.z;
-  _Float16* dst = pool + tile_base(op.dst_slot, head, heads, kv);
-  const _Float16* src_pool = op.from_pool ? pool + tile_base(op.src_slot, head, heads, kv) : nullptr;
+  _Float16* dst = pool + tile_base(op.dst_tile, head, heads, kv);
   const _Float16* src = kv ? v_src : k_src;
   const int lo = op.dst_key0, hi = op.dst_key0 + op.n_rows;  // written keys [lo, hi)
   for (int u = threadIdx.x; u < TILE / 8; u += 256) {
@@ -60,11 +59,13 @@ __global__ __launch_bounds__(256) void kv_write_kernel(_Float16* pool, int heads
       const int r = key - op.dst_key0;
       _Float16 x;
       if (r >= 0 && r < op.n_rows) {
-        const int sr = op.src_row0 + r;
-        if (op.from_pool)
-          x = src_pool[kv == 0 ? k_off(sr, dim) : v_off(sr, dim)];
-        else
+        const int sr = op.src0 + r;
+        if (op.from_pool) {
+          const int t = sr / kTileKeys, key_in = sr % kTileKeys;
+          x = pool[tile_base(t, head, heads, kv) + (kv == 0 ? k_off(key_in, dim) : v_off(key_in, dim))];
+        } else {
           x = src[(static_cast<size_t>(sr) * heads + head) * D + dim];
+        }
       } else {
         x = op.zero_rest ? static_cast<_Float16>(0.0f) : cur[e];
       }

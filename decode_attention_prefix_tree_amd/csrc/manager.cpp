@@ -143,6 +143,8 @@ void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<
     Node& nd = nodes_[e];
     nd.tokens.insert(nd.tokens.end(), tokens, tokens + take);
     if (ops) ops->push_back(KvOp{nd.slot, fill, take, src_base, -1, 0, 0, e});
+    // growing into another 64-key tile adds a tile ref to the plan
+    if (tiles_of(fill + take) != tiles_of(fill)) structural_ = true;
   }
   len_[seq] += n;
   if (take == n) return;
@@ -226,6 +228,7 @@ void Plan::clear() {
   chunk_refs.clear();
   row_node.clear();
   ref_node.clear();
+  ref_sub.clear();
   ref_task.clear();
   ref_pos.clear();
   private_ref.clear();
@@ -297,12 +300,15 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
     P.shared_tokens += R(r, 3);
     if (!two_phase) continue;
     int32_t t = p >= 0 ? task_of_row[p] : -1;
-    if (t >= 0 && tasks[t].b == b && tasks[t].e == e && tasks[t].last_row == p && tasks[t].n_chunks < cf_group) {
-      tasks[t].n_chunks += 1;
+    // n_chunks counts the tile refs of the run (one per chunk of 64)
+    const int32_t nt = tiles_of(R(r, 3));
+    if (t >= 0 && tasks[t].b == b && tasks[t].e == e && tasks[t].last_row == p &&
+        tasks[t].n_chunks + nt <= cf_group) {
+      tasks[t].n_chunks += nt;
       tasks[t].last_row = r;
     } else {
       t = static_cast<int32_t>(tasks.size());
-      tasks.push_back({b, e, -1, 1, r});
+      tasks.push_back({b, e, -1, nt, r});
     }
     task_of_row[r] = t;
   }
@@ -314,11 +320,13 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
       if (task_of_row[r] >= 0) task_rows[task_of_row[r]].push_back(r);
     for (size_t t = 0; t < tasks.size(); ++t) {
       tasks[t].chunk_begin = static_cast<int32_t>(P.chunk_refs.size() / 2);
-      for (int32_t r : task_rows[t]) {
-        P.chunk_refs.push_back(R(r, 6));
-        P.chunk_refs.push_back(R(r, 3));
-        P.ref_node.push_back(row_node[r]);
-      }
+      for (int32_t r : task_rows[t])
+        for (int32_t k = 0; k < tiles_of(R(r, 3)); ++k) {
+          P.chunk_refs.push_back(tile_slot(R(r, 6), k));
+          P.chunk_refs.push_back(tile_fill(R(r, 3), k));
+          P.ref_node.push_back(row_node[r]);
+          P.ref_sub.push_back(k);
+        }
       P.cf_chunk_reads += tasks[t].n_chunks * ((tasks[t].e - tasks[t].b + 31) / 32);
       for (int32_t rb = 0; rb * 32 < tasks[t].e - tasks[t].b; ++rb) {
         CfUnit u{};
@@ -354,14 +362,14 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
     std::reverse(path.begin(), path.end());
     ent_first[i] = static_cast<int32_t>(entries.size());
     int32_t last_task = -1;
-    std::vector<int32_t> priv;
+    std::vector<std::pair<int32_t, int32_t>> priv;  // (row, tile of the row's chunk)
     for (int32_t r : path) {
       int32_t t = task_of_row[r];
       if (t >= 0) {
         if (t != last_task) entries.push_back(t);
         last_task = t;
       } else {
-        priv.push_back(r);
+        for (int32_t k = 0; k < tiles_of(R(r, 3)); ++k) priv.push_back({r, k});
       }
     }
     for (size_t j = 0; j < priv.size(); j += static_cast<size_t>(sf_group)) {
@@ -375,16 +383,20 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
       st.append_at = -1;
       for (size_t q = j; q < stop; ++q) {
         const int c = static_cast<int>(q - j);
-        // the chunk where the sequence ends takes its next decoded token
-        if (priv[q] == end_row[i]) st.append_at = c;
+        const int32_t r = priv[q].first, k = priv[q].second;
+        const int32_t slot = tile_slot(R(r, 6), k), fill = tile_fill(R(r, 3), k);
+        // the last tile of the chunk where the sequence ends takes its next
+        // decoded token
+        if (r == end_row[i] && k + 1 == tiles_of(R(r, 3))) st.append_at = c;
         if (c < kSfInline) {
-          st.slot[c] = R(priv[q], 6);
-          st.n_valid[c] = R(priv[q], 3);
+          st.slot[c] = slot;
+          st.n_valid[c] = fill;
         }
-        if (R(priv[q], 5) - R(priv[q], 4) >= 2) st.reuse = 1;
-        P.chunk_refs.push_back(R(priv[q], 6));
-        P.chunk_refs.push_back(R(priv[q], 3));
-        P.ref_node.push_back(row_node[priv[q]]);
+        if (R(r, 5) - R(r, 4) >= 2) st.reuse = 1;
+        P.chunk_refs.push_back(slot);
+        P.chunk_refs.push_back(fill);
+        P.ref_node.push_back(row_node[r]);
+        P.ref_sub.push_back(k);
       }
       P.sf_chunk_reads += st.n_chunks;
       entries.push_back(-1 - static_cast<int32_t>(P.sf_tasks.size()));
@@ -456,7 +468,10 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
       const int32_t k = P.sf_tasks[t].chunk_begin + c;
       P.ref_task[k] = static_cast<int32_t>(t);
       P.ref_pos[k] = c;
-      if (nodes_[P.ref_node[k]].ref == 1) P.private_ref[P.ref_node[k]] = k;
+      const Node& nd = nodes_[P.ref_node[k]];
+      // a private chunk's appends go to its last tile
+      if (nd.ref == 1 && P.ref_sub[k] + 1 == tiles_of(static_cast<int32_t>(nd.tokens.size())))
+        P.private_ref[P.ref_node[k]] = k;
     }
 }
 
@@ -473,7 +488,7 @@ void Manager::refresh_fills(Plan* plan) const {
     if (row[5] - row[4] >= 2) P.shared_tokens += fill;
   }
   for (size_t k = 0; k < P.ref_node.size(); ++k)
-    P.chunk_refs[2 * k + 1] = static_cast<int32_t>(nodes_[P.ref_node[k]].tokens.size());
+    P.chunk_refs[2 * k + 1] = tile_fill(static_cast<int32_t>(nodes_[P.ref_node[k]].tokens.size()), P.ref_sub[k]);
   for (CfUnit& u : P.cf_units)
     for (int c = 0; c < kCfInline && c < u.n_chunks; ++c) u.n_valid[c] = P.chunk_refs[2 * (u.chunk_begin + c) + 1];
   for (SfTask& t : P.sf_tasks)

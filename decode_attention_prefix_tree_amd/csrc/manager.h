@@ -25,6 +25,7 @@
 //  * a failing call changes nothing.
 #pragma once
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 #include <functional>
@@ -106,6 +107,7 @@ struct Plan {
   std::vector<int32_t> chunk_refs;  // (slot, n_valid) pairs
   std::vector<int32_t> row_node;    // manager node index of each table row
   std::vector<int32_t> ref_node;    // manager node index of each chunk ref
+  std::vector<int32_t> ref_sub;     // 64-key tile of the chunk the ref covers (chunks of 128 span two)
   std::vector<int32_t> ref_task;    // sequence-first task holding the ref (-1: chunk-first)
   std::vector<int32_t> ref_pos;     // position of the ref within that task
   std::vector<int32_t> private_ref; // per manager node: its ref if the chunk has one sequence, else -1
@@ -134,6 +136,14 @@ class Manager {
   int64_t capacity() const { return capacity_; }
   int64_t free_slots() const { return static_cast<int64_t>(free_.size()); }
   int chunk() const { return C_; }
+  // The kernels read 64-key tiles: a chunk of C > 64 tokens is C / 64 tiles
+  // (slot s owns tiles s * C / 64 ...), of which the plan lists those that
+  // hold tokens.
+  int32_t tiles_of(int32_t fill) const { return C_ > kTileKeys ? std::max(1, (fill + kTileKeys - 1) / kTileKeys) : 1; }
+  int32_t tile_slot(int32_t slot, int32_t t) const { return C_ > kTileKeys ? slot * (C_ / kTileKeys) + t : slot; }
+  int32_t tile_fill(int32_t fill, int32_t t) const {
+    return C_ > kTileKeys ? std::min(kTileKeys, fill - t * kTileKeys) : fill;
+  }
   size_t live() const { return end_.size(); }
   int64_t nodes() const { return n_nodes_; }
 

@@ -27,9 +27,9 @@
  *    different streams must be ordered by the caller.
  *  - Element types: K, V, Q and the output are IEEE binary16 (fp16); the
  *    kernels accumulate in fp32.  Token ids are int32.
- *  - v1 supports head_dim 128 and chunk_size 64 (the tuned settings named in
- *    the summary's section 7 and the chunk size of its Table 3); any head
- *    count >= 1.
+ *  - head_dim 128; chunk_size 64 (the chunk size of the summary's Table 3,
+ *    the tuned setting) or 128 (a chunk is then two 64-key tiles, and the
+ *    kernels read only the tiles that hold tokens); any head count >= 1.
  */
 #ifndef CHUNKATTN_H
 #define CHUNKATTN_H
@@ -135,8 +135,8 @@ typedef struct ca_stats_t {
  * * head_dim.  Returns 0 for non-positive arguments. */
 size_t ca_slot_bytes(int heads, int head_dim, int chunk_size);
 
-/* Create a context.  heads >= 1; head_dim must be 128 and chunk_size 64
- * (else CA_E_UNSUPPORTED).  Scale is 1/sqrt(head_dim) computed in fp32.
+/* Create a context.  heads >= 1; head_dim must be 128 and chunk_size 64 or
+ * 128 (else CA_E_UNSUPPORTED).  Scale is 1/sqrt(head_dim) computed in fp32.
  * *out receives the context; the caller owns it and frees it with
  * ca_destroy. */
 int ca_create(int heads, int head_dim, int chunk_size, ca_ctx** out);

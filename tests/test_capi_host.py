@@ -28,6 +28,9 @@ def test_create_rejects_unsupported_shapes():
     ctx = ctypes.c_void_p()
     assert lib.ca_create(8, 64, 64, ctypes.byref(ctx)) == -2
     assert lib.ca_create(8, 128, 32, ctypes.byref(ctx)) == -2
+    assert lib.ca_create(8, 128, 96, ctypes.byref(ctx)) == -2
+    assert lib.ca_create(8, 128, 128, ctypes.byref(ctx)) == 0
+    lib.ca_destroy(ctx)
     assert lib.ca_create(0, 128, 64, ctypes.byref(ctx)) == -1
     assert lib.ca_create_ex(8, 128, 64, 0x100, ctypes.byref(ctx)) == -2
     assert lib.ca_slot_bytes(32, 128, 64) == 4 * 32 * 64 * 128
@@ -113,13 +116,14 @@ def test_golden_tables_at_chunk64_by_token_expansion(case):
             assert got == op.expect
 
 
-def test_random_ops_bit_exact_against_model():
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_random_ops_bit_exact_against_model(chunk):
     rng = np.random.default_rng(1234)
     for trial in range(25):
         cap = int(rng.integers(5, 60))
         share = bool(rng.random() < 0.85)
-        m = PrefixTreeModel(64, cap, share)
-        ca = ChunkAttention(4, cap, device=None, share=share)
+        m = PrefixTreeModel(chunk, cap, share)
+        ca = ChunkAttention(4, cap, device=None, share=share, chunk_size=chunk)
         ids = []
         for step in range(80):
             r = rng.random()
@@ -274,10 +278,11 @@ def test_no_chunk_first_mode_keeps_tree_and_streams_whole_paths(k):
     assert s2["sf_chunk_reads"] + s2["shared_chunks"] < s1["sf_chunk_reads"]
 
 
-def test_append_batch_matches_model_through_fill_refreshes():
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_append_batch_matches_model_through_fill_refreshes(chunk):
     rng = np.random.default_rng(77)
-    m = PrefixTreeModel(64, 400)
-    ca = ChunkAttention(2, 400, device=None)
+    m = PrefixTreeModel(chunk, 400)
+    ca = ChunkAttention(2, 400, device=None, chunk_size=chunk)
     shared = list(range(100))
     ids = [3, 9, 11, 20, 21]
     for n, s in enumerate(ids):
@@ -383,3 +388,50 @@ def test_partial_slots_compact_when_dense_would_waste_memory():
     for i in range(1, 100):
         ca.insert(i, [10**6 + i * 100 + j for j in range(10)])
     assert ca.stats()["partials"] == 16 + 99
+
+
+def _tile_reads(rows):
+    """Per-head tile reads of a plan, from the canonical table: a chunk of n
+    tokens is ceil(n / 64) tiles of 64 keys; a shared chunk (range >= 2) is
+    read once per 32 query rows, a private one once."""
+    cf = sf = 0
+    for r in rows:
+        tiles = max(1, -(-r[3] // 64))
+        rng_ = r[5] - r[4]
+        if rng_ >= 2:
+            cf += tiles * -(-rng_ // 32)
+        else:
+            sf += tiles
+    return cf, sf
+
+
+def test_chunk128_plan_lists_64_key_tiles():
+    m = PrefixTreeModel(128, 64)
+    ca = ChunkAttention(2, 64, device=None, chunk_size=128)
+    shared = list(range(300))
+    for s, n in enumerate([100, 1, 64, 65, 200]):
+        t = shared + [1000 + s] * n
+        assert ca.insert(s, t) == m.insert(s, t)
+    model_and_lib_agree(m, ca)
+    rows, _ = m.table()
+    st = ca.stats()
+    assert (st["cf_chunk_reads"], st["sf_chunk_reads"]) == _tile_reads(rows)
+    # 300 shared tokens: chunks of 128, 128 and 44 (split at the divergence)
+    assert sorted(r[3] for r in rows if r[5] - r[4] >= 2) == [44, 128, 128]
+
+
+def test_chunk128_append_into_second_tile_rebuilds_the_plan():
+    ca = ChunkAttention(2, 8, device=None, chunk_size=128)
+    ca.insert(1, list(range(60)))
+    ca.insert(2, [7] * 10)
+    st0 = ca.stats()
+    for t in range(4):                      # keys 60..63: still the first tile
+        ca.append_batch([1, 2], [500 + t, 600 + t])
+        ca.stats()
+    st1 = ca.stats()
+    assert st1["table_rebuilds"] == st0["table_rebuilds"]
+    assert st1["fill_refreshes"] > st0["fill_refreshes"]
+    ca.append_batch([1, 2], [700, 701])     # key 64 of sequence 1: a second tile
+    st2 = ca.stats()
+    assert st2["table_rebuilds"] == st1["table_rebuilds"] + 1
+    assert st2["sf_chunk_reads"] == 3 and st2["chunks"] == 2

@@ -37,12 +37,12 @@ def _torch():
     return torch
 
 
-def build_ca(wl, share=True, cf_group=None, sf_group=None, capacity=None, two_phase=True):
+def build_ca(wl, share=True, cf_group=None, sf_group=None, capacity=None, two_phase=True, chunk=64):
     torch = _torch()
     from decode_attention_prefix_tree_amd import ChunkAttention, load_workload, slots_needed
     from decode_attention_prefix_tree_amd import _capi
-    cap = capacity or slots_needed(wl, share=share) + 4
-    ca = ChunkAttention(wl.heads, cap, device="cuda:0", share=share, two_phase=two_phase)
+    cap = capacity or slots_needed(wl, chunk=chunk, share=share) + 4
+    ca = ChunkAttention(wl.heads, cap, device="cuda:0", share=share, two_phase=two_phase, chunk_size=chunk)
     if cf_group:
         ca.set_option(_capi.CA_OPT_CF_CHUNKS_PER_TASK, cf_group)
     if sf_group:
@@ -437,15 +437,18 @@ def test_head_counts(heads):
     assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("mode", ["two_launch", "one_launch", "shared_pages"])
-def test_decode_step_equals_append_then_attend(mode):
+def test_decode_step_equals_append_then_attend(mode, chunk):
     """ca_decode_step (tokens written by the step's own blocks while chunks
     grow in place, a separate write launch when a chunk fills up or a
     sequence's last chunk is shared) against ca_append_batch + ca_attend on a
     twin context: the same bits at every one of 140 steps, the same tables,
     and the oracle over the grown sequences every 35 steps.  One sequence
-    ends inside the shared prefix, so its first append grows a new chunk."""
-    _say(f"decode step, {mode}")
+    ends inside the shared prefix, so its first append grows a new chunk.
+    With 128-token chunks the growing chunk also moves on to its second
+    64-key tile (a new tile in the plan: a rebuild, not a patch)."""
+    _say(f"decode step, {mode}, chunk {chunk}")
     torch = _torch()
     from decode_attention_prefix_tree_amd import _capi
     rng = np.random.default_rng(50)
@@ -457,9 +460,9 @@ def test_decode_step_equals_append_then_attend(mode):
     wl = from_token_lists(seqs, heads=H, seed=51)
     two_phase = mode != "shared_pages"
     from decode_attention_prefix_tree_amd import slots_needed
-    cap = slots_needed(wl) + 40
-    a = build_ca(wl, capacity=cap, two_phase=two_phase)
-    b = build_ca(wl, capacity=cap, two_phase=two_phase)
+    cap = slots_needed(wl, chunk=chunk) + 40
+    a = build_ca(wl, capacity=cap, two_phase=two_phase, chunk=chunk)
+    b = build_ca(wl, capacity=cap, two_phase=two_phase, chunk=chunk)
     for ca in (a, b):
         ca.set_option(_capi.CA_OPT_FUSED_MERGE, 1 if mode == "one_launch" else 0)
     n = wl.n_seq
@@ -474,12 +477,12 @@ def test_decode_step_equals_append_then_attend(mode):
         ra = a.attend(qt).clone()
         rb = b.decode_step(toks, kt, vt, qt).clone()
         torch.cuda.synchronize()
-        assert torch.equal(ra, rb), (mode, step)
+        assert torch.equal(ra, rb), (mode, chunk, step)
         for i in range(n):
             kv[i][0] = np.concatenate([kv[i][0], k[i:i + 1]])
             kv[i][1] = np.concatenate([kv[i][1], v[i:i + 1]])
         if step % 35 == 0 or step == 139:
-            assert_parity(rb.cpu().numpy(), A.decode_step(q, kv), f"decode {mode} step {step}")
+            assert_parity(rb.cpu().numpy(), A.decode_step(q, kv), f"decode {mode} chunk {chunk} step {step}")
     ta, oa = a.export_table()
     tb, ob = b.export_table()
     assert oa == ob and np.array_equal(ta, tb)
@@ -591,3 +594,64 @@ def test_patched_single_appends_deep_private_tails(sf_group):
     assert ca.stats()["patched_appends"] >= 4 * 9
 
 
+@pytest.mark.parametrize("two_phase", [True, False])
+@pytest.mark.parametrize("name", ["shared_R40", "shared_R70", "deep_random", "interior_and_dups", "all_private",
+                                  "single_token"])
+def test_chunk128_tiny_trees(name, two_phase):
+    """128-token chunks: each chunk is one or two 64-key tiles in the plan;
+    divergences split chunks anywhere in either tile."""
+    _say(f"chunk 128 tiny tree {name} two_phase={two_phase}")
+    seqs = tiny_tree_cases()[name]
+    wl = from_token_lists(seqs, heads=3, seed=len(name) + 128)
+    ca = build_ca(wl, chunk=128, two_phase=two_phase)
+    assert_parity(run_step(ca, wl.q), A.decode_workload(wl), f"c128 {name}")
+
+
+def test_chunk128_non_aligned_prefix_ragged_suffixes():
+    """A 1766-token shared prefix (13 chunks of 128 and one of 102) with
+    suffixes of 1..700 tokens, 8 heads, against the oracle."""
+    rng = np.random.default_rng(2128)
+    suffix = [int(x) for x in rng.integers(1, 701, size=40)]
+    wl = make_prefix_suffix(1766, suffix, heads=8, seed=2129)
+    _say("chunk 128 prefix 1766 + ragged suffixes")
+    ca = build_ca(wl, chunk=128)
+    assert_parity(run_step(ca, wl.q), A.decode_workload(wl), "c128 prefix1766 ragged")
+
+
+def _k_off(key, dim):
+    """Position of K[key][dim] in a 64-key tile (the MFMA A-operand order)."""
+    return ((((key >> 5) * 8 + (dim >> 4)) * 2 + ((dim >> 3) & 1)) * 32 + (key & 31)) * 8 + (dim & 7)
+
+
+def _v_off(key, dim):
+    """Position of V[key][dim] in a 64-key tile."""
+    return ((((dim >> 5) * 4 + (key >> 4)) * 2 + ((key >> 2) & 1)) * 32 + (dim & 31)) * 8 + \
+        ((key & 3) | (((key >> 3) & 1) << 2))
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("name", ["deep_random", "interior_and_dups"])
+def test_pool_holds_each_chunks_kv(name, chunk):
+    """KV scatter: after the inserts (divergences split chunks anywhere, so
+    split tails are copied pool to pool, across tile boundaries at 128), key
+    j of every table row sits at global pool key slot * chunk + j, in tile
+    order, bit for bit equal to the caller's K and V of that token."""
+    _say(f"pool contents {name} chunk {chunk}")
+    torch = _torch()
+    wl = from_token_lists(tiny_tree_cases()[name], heads=3, seed=9)
+    ca = build_ca(wl, chunk=chunk)
+    rows, order = ca.export_table()
+    pool = ca.pool.view(torch.float16).cpu().numpy().reshape(-1, wl.heads, 2, 64 * 128)
+    keys = np.arange(64)[:, None]
+    dims = np.arange(128)[None, :]
+    koff, voff = _k_off(keys, dims), _v_off(keys, dims)
+    n_keys = 0
+    for r in rows:
+        start, n, sb, slot = int(r[2]), int(r[3]), int(r[4]), int(r[6])
+        k, v = wl.seq_kv(order[sb])
+        for j in range(n):
+            t, kk = divmod(slot * chunk + j, 64)
+            assert np.array_equal(pool[t][:, 0][:, koff[kk]], k[start + j]), (r, j)
+            assert np.array_equal(pool[t][:, 1][:, voff[kk]], v[start + j]), (r, j)
+            n_keys += 1
+    assert n_keys == sum(int(r[3]) for r in rows)
