@@ -52,6 +52,8 @@ def parse():
                     help="instead of a numbered workload: --n-seq sequences x 32 heads with this shared prefix "
                          "length (any length, e.g. 1766) and --suffix-len private tokens each")
     ap.add_argument("--suffix-len", type=int, default=512)
+    ap.add_argument("--chunk", type=int, default=64, choices=(32, 64, 128),
+                    help="chunk size of the cache (the workloads are defined at 64)")
     ap.add_argument("--n-seq", type=int, default=32, help="sequences of the --prefix-len workload")
     ap.add_argument("--decode", action="store_true",
                     help="decode progression instead: n_s = 2048 shared prompt tokens, one token appended per "
@@ -319,7 +321,7 @@ def main():
         wl = make_config(args.config)
         workload_name = CONFIG_NAMES[args.config]
     log(f"building workload {workload_name}")
-    ca = ChunkAttention(wl.heads, slots_needed(wl) + 8, device="cuda:0")
+    ca = ChunkAttention(wl.heads, slots_needed(wl, chunk=args.chunk) + 8, device="cuda:0", chunk_size=args.chunk)
     load_workload(ca, wl)
     q = torch.from_numpy(wl.q).cuda()
     out = torch.empty_like(q)
@@ -411,7 +413,7 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": workload_name, "n_seq": wl.n_seq, "heads": wl.heads,
-                   "head_dim": wl.head_dim, "chunk": wl.chunk, "cache": "cold (1 GiB read before each step)",
+                   "head_dim": wl.head_dim, "chunk": args.chunk, "cache": "cold (1 GiB read before each step)",
                    "cf_chunks_per_task": st["cf_chunks_per_task"], "sf_chunks_per_task": 4,
                    "launches_per_step": 1 if one_launch else 2},
         "unique_kv_gbps": unique_b / t_mean / 1e9,

@@ -245,6 +245,7 @@ chunkattn::StepArgs step_args(ca_ctx* c, const void* q, void* out) {
   a.app_k = nullptr;
   a.app_v = nullptr;
   a.app_epoch = 0;
+  a.half_tiles = c->chunk < chunkattn::kTileKeys ? 1 : 0;
   return a;
 }
 
@@ -300,21 +301,25 @@ bool fill_patches(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, std::vecto
 }
 
 // The pieces of a copy, one per destination 64-key tile: key k of chunk
-// slot s is key (s * C + k) mod 64 of tile (s * C + k) / 64.  A split's tail
-// is read by global pool key, so its source may span two tiles within one
-// piece: no two pieces of a launch write the same tile.  Keys are written in
-// increasing order, so a piece that starts a tile is that tile's first write
-// since its slot was allocated: it zeroes the tile's other keys (unwritten V
+// slot s is key (s * C + k) mod 64 of tile (s * C + k) / 64 (chunks of 32
+// pair up in a tile, chunks of 128 span two).  A split's tail is read by
+// global pool key, so its source may span two tiles within one piece: no two
+// pieces of a launch write the same tile, and two chunks sharing a tile
+// never share a 16-byte unit.  Keys are written in increasing order, so a
+// piece that starts a chunk's part of a tile is that part's first write
+// since the slot was allocated: it clears the part's other keys (unwritten V
 // columns must be finite, they meet zero probabilities).
 void tile_pieces(const chunkattn::KvOp& o, int C, std::vector<chunkattn::KvOpDev>* out) {
   constexpr int32_t T = chunkattn::kTileKeys;
+  const int32_t part = std::min<int32_t>(C, T);  // keys of one chunk in one tile
   for (int32_t done = 0; done < o.n_rows;) {
     const int64_t dg = static_cast<int64_t>(o.dst_slot) * C + o.dst_key0 + done;
     const int32_t key0 = static_cast<int32_t>(dg % T);
     const int32_t n = std::min<int32_t>(o.n_rows - done, T - key0);
     const int32_t src0 = o.from_pool ? o.src_slot * C + o.src_row0 + done : o.src_row0 + done;
+    const bool first = dg % part == 0;
     out->push_back(chunkattn::KvOpDev{static_cast<int32_t>(dg / T), key0, n, src0, o.from_pool,
-                                      key0 == 0 ? 1 : 0, 0, 0});
+                                      first ? key0 : 0, first ? key0 + part : 0, 0});
     done += n;
   }
 }
@@ -416,7 +421,8 @@ int ca_create_ex(int heads, int head_dim, int chunk_size, int flags, ca_ctx** ou
   if (out == nullptr) return CA_E_INVALID_ARG;
   *out = nullptr;
   if (heads < 1) return CA_E_INVALID_ARG;
-  if (head_dim != chunkattn::kHeadDim || (chunk_size != 64 && chunk_size != 128)) return CA_E_UNSUPPORTED;
+  if (head_dim != chunkattn::kHeadDim || (chunk_size != 32 && chunk_size != 64 && chunk_size != 128))
+    return CA_E_UNSUPPORTED;
   if (flags & ~(CA_CREATE_UNSHARED | CA_CREATE_NO_CHUNK_FIRST)) return CA_E_UNSUPPORTED;
   try {
     *out = new ca_ctx(heads, head_dim, chunk_size, flags);
@@ -437,7 +443,9 @@ int ca_attach_pool(ca_ctx* ctx, void* dev, int64_t capacity_slots) {
     if (capacity_slots < 0) throw Error(CA_E_INVALID_ARG, "negative capacity");
     if (dev != nullptr && (reinterpret_cast<uintptr_t>(dev) % kAlign) != 0)
       throw Error(CA_E_INVALID_ARG, "pool must be 256-byte aligned");
-    ctx->mgr.set_capacity(capacity_slots);
+    // Chunks of 32 pair up in 64-key tiles and a tile spans every head, so
+    // the slots are used in pairs: an odd last slot is left out.
+    ctx->mgr.set_capacity(ctx->chunk < chunkattn::kTileKeys ? capacity_slots & ~int64_t{1} : capacity_slots);
     ctx->pool = dev;
     ctx->pool_attached = true;
     touch(ctx);

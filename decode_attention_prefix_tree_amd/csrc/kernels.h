@@ -53,6 +53,9 @@ struct StepArgs {
   const void* app_k;
   const void* app_v;
   unsigned app_epoch;          // 1 .. kEpochMask
+  // Chunks of 32 tokens: chunk slot s is half s % 2 (keys 32 * (s % 2) ..
+  // +32) of tile s / 2, and a chunk ref's slot field is s.
+  int half_tiles;
 };
 
 // Which blocks of the partials kernel to launch.

@@ -315,7 +315,7 @@ __device__ __forceinline__ float weight(float m, float M) {
 // along keys (the lane holds 16 keys of its row, its twin lane the other 16),
 // O^T[128 x 32] += V^T P^T (8 MFMA).  P^T needs no exchange: the V tile
 // stores keys in the order the S^T accumulators hold them.
-template <bool kFuse, bool kNT>
+template <bool kFuse, bool kNT, bool kHalf>
 __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical, char* smem) {
   const int unit = logical % a.n_cf_units, head = logical / a.n_cf_units;
   const int* u = a.cf_units + unit * 32;
@@ -345,7 +345,7 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
   float m = -INFINITY, l = 0.f;
   f16v acc[4];
 
-  if (n_chunks <= 4) {
+  if (!kHalf && n_chunks <= 4) {
     // At most one chunk per wave: no accumulator has to survive another
     // chunk's loads, so the wave loads its whole chunk at once (32 KiB in
     // flight, one round trip, like a sequence-first wave): K 64 VGPRs, V 64,
@@ -417,13 +417,17 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
   for (int c = wave; c < n_chunks; c += 4) {
     const int slot = c < kCfInline ? u[8 + c] : a.chunk_refs[2 * (chunk_begin + c)];
     const int nvalid = (c < kCfInline ? u[16 + c] : a.chunk_refs[2 * (chunk_begin + c) + 1]) & kFillMask;
-    const _Float16* kt = pool + tile_base(slot, head, H, 0);
-    const _Float16* vt = kt + TILE;
+    // a 32-token chunk is one half of its tile: the tile pointers move to
+    // that half (K blocks 8h.., V blocks 4nb + 2h ..) and the loop below
+    // runs once, over keys 0..31 of the half
+    const int tile = kHalf ? slot >> 1 : slot, hh = kHalf ? slot & 1 : 0;
+    const _Float16* kt = pool + tile_base(tile, head, H, 0) + hh * 8 * 512;
+    const _Float16* vt = pool + tile_base(tile, head, H, 1) + hh * 2 * 512;
     // The halves stay a loop: unrolled, the second half's loads would be
     // hoisted over the first half's MFMAs and the block would not fit three
     // waves per SIMD.
 #pragma unroll 1
-    for (int jb = 0; jb < 2; ++jb) {
+    for (int jb = 0; jb < (kHalf ? 1 : 2); ++jb) {
       h8 kr[8], vr[8];
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) kr[kk] = ld_tile<kNT>(kt + ((jb * 8 + kk) * 64 + lane) * 8);
@@ -570,7 +574,7 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
 // loads in flight per CU.  kAppend: a decode step whose blocks also write the
 // new tokens; the attend-only kernel has no stores into the pool or the
 // table, so its table reads stay scalar loads.
-template <bool kFuse, bool kNT, bool kAppend>
+template <bool kFuse, bool kNT, bool kAppend, bool kHalf>
 __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logical, char* smem) {
   // heads vary fastest: blocks that run together read neighbouring 32 KiB
   // tiles of the same slots, which keeps HBM accesses close to sequential
@@ -621,10 +625,13 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
   if (kAppend && append_at >= 0) {
     const int ac = append_at;
     const int fill = ac < kSfInline ? t[12 + ac] : a.chunk_refs[2 * (chunk_begin + ac) + 1];
-    const int p = (static_cast<unsigned>(fill) >> kFillBits) == a.app_epoch ? (fill & kFillMask) - 1 : fill & kFillMask;
+    int p = (static_cast<unsigned>(fill) >> kFillBits) == a.app_epoch ? (fill & kFillMask) - 1 : fill & kFillMask;
     append_fill = p + 1;
     if ((ac & 3) == wave) {
-      const int slot = ac < kSfInline ? t[8 + ac] : a.chunk_refs[2 * (chunk_begin + ac)];
+      const int cslot = ac < kSfInline ? t[8 + ac] : a.chunk_refs[2 * (chunk_begin + ac)];
+      // key p of a 32-token chunk is key 32 * (slot % 2) + p of its tile
+      const int slot = kHalf ? cslot >> 1 : cslot;
+      if (kHalf) p += (cslot & 1) * 32;
       _Float16* kw = const_cast<_Float16*>(pool) + tile_base(slot, head, H, 0);
       _Float16* vw = kw + TILE;
       // K: load (p/32)*8 + j, lanes (half, p%32): dims 16j + 8half .. +8
@@ -652,14 +659,18 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
     const int slot = c < kSfInline ? t[8 + c] : a.chunk_refs[2 * (chunk_begin + c)];
     const int fill = c < kSfInline ? t[12 + c] : a.chunk_refs[2 * (chunk_begin + c) + 1];
     int nvalid = fill & kFillMask;
-    const _Float16* kt = pool + tile_base(slot, head, H, 0);
-    const _Float16* vt = kt + TILE;
+    // a 32-token chunk is one half of its tile: its K blocks 8h .. 8h+7 and
+    // V blocks 4nb + 2h, +1 land where keys 0..31 of a whole tile would
+    const int tile = kHalf ? slot >> 1 : slot, hh = kHalf ? slot & 1 : 0;
+    const _Float16* kt = pool + tile_base(tile, head, H, 0) + hh * 8 * 512;
+    const _Float16* vt = pool + tile_base(tile, head, H, 1) + hh * 2 * 512;
     if (kAppend && c == append_at) nvalid = append_fill;
     h8 ka[16], va[16];
 #pragma unroll
-    for (int L = 0; L < 16; ++L) ka[L] = ld_tile<kNT>(kt + (L * 64 + lane) * 8);
+    for (int L = 0; L < (kHalf ? 8 : 16); ++L) ka[L] = ld_tile<kNT>(kt + (L * 64 + lane) * 8);
 #pragma unroll
-    for (int L = 0; L < 16; ++L) va[L] = ld_tile<kNT>(vt + (L * 64 + lane) * 8);
+    for (int L = 0; L < 16; ++L)
+      if (!kHalf || (L & 3) < 2) va[L] = ld_tile<kNT>(vt + (L * 64 + lane) * 8);
 
     float d0 = 0.f, d1 = 0.f;
 #pragma unroll
@@ -668,13 +679,13 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         d0 = __builtin_amdgcn_fdot2(lo2(ka[kk], j), lo2(qv, j), d0, false);
-        d1 = __builtin_amdgcn_fdot2(lo2(ka[8 + kk], j), lo2(qv, j), d1, false);
+        if (!kHalf) d1 = __builtin_amdgcn_fdot2(lo2(ka[8 + kk], j), lo2(qv, j), d1, false);
       }
     }
     d0 = sum_halves(d0);
-    d1 = sum_halves(d1);
+    if (!kHalf) d1 = sum_halves(d1);
     const float x0 = i < nvalid ? d0 * a.scale_log2e : -INFINITY;
-    const float x1 = i + 32 < nvalid ? d1 * a.scale_log2e : -INFINITY;
+    const float x1 = !kHalf && i + 32 < nvalid ? d1 * a.scale_log2e : -INFINITY;
     const float mx = wave_max32(fmaxf(x0, x1));
     const float mnew = fmaxf(m, mx);  // finite: key 0 of a chunk is always filled
     const float alpha = exp2f(m - mnew);
@@ -691,7 +702,7 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[nb] *= alpha;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < (kHalf ? 2 : 4); ++s) {
       const f4 pa = *reinterpret_cast<const f4*>(&p_lds[wave][16 * s + 4 * half]);
       const f4 pc = *reinterpret_cast<const f4*>(&p_lds[wave][16 * s + 8 + 4 * half]);
 #pragma unroll
@@ -762,7 +773,7 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
 // only the sequence-first part).  kFuse: the one-launch step, whose grid ends
 // with the merge blocks (epoch: see merge_block).  kAppend: a decode step
 // with in-kernel appends (StepArgs::app_k set).
-template <bool kFuse, bool kAppend>
+template <bool kFuse, bool kAppend, bool kHalf>
 __global__ __launch_bounds__(256, 3) void partials_kernel(StepArgs a, int n_cf, int n_sf, int first,
                                                           unsigned epoch) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
@@ -770,15 +781,15 @@ __global__ __launch_bounds__(256, 3) void partials_kernel(StepArgs a, int n_cf, 
   if (b < n_cf) {
     const int logical = xcd_remap(b, n_cf);
     if (a.cf_units[(logical % a.n_cf_units) * 32 + kCfReuseField])
-      chunk_first_block<kFuse, false>(a, logical, smem);
+      chunk_first_block<kFuse, false, kHalf>(a, logical, smem);
     else
-      chunk_first_block<kFuse, true>(a, logical, smem);
+      chunk_first_block<kFuse, true, kHalf>(a, logical, smem);
   } else if (b < n_cf + n_sf) {
     const int logical = b - n_cf;
     if (a.sf_tasks[(logical / a.heads) * 16 + kSfReuseField])
-      sequence_first_block<kFuse, false, kAppend>(a, logical, smem);
+      sequence_first_block<kFuse, false, kAppend, kHalf>(a, logical, smem);
     else
-      sequence_first_block<kFuse, true, kAppend>(a, logical, smem);
+      sequence_first_block<kFuse, true, kAppend, kHalf>(a, logical, smem);
   }
   else if constexpr (kFuse)
     merge_block(a, b - n_cf - n_sf, epoch);
@@ -806,14 +817,20 @@ int launch_partials(const StepArgs& a, int part, bool fuse_merge, unsigned epoch
   if (count <= 0) return 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool append = a.app_k != nullptr;
-  if (fuse && append)
-    hipLaunchKernelGGL((partials_kernel<true, true>), dim3(count), dim3(256), 0, st, a, n_cf, n_sf, first, epoch);
-  else if (fuse)
-    hipLaunchKernelGGL((partials_kernel<true, false>), dim3(count), dim3(256), 0, st, a, n_cf, n_sf, first, epoch);
-  else if (append)
-    hipLaunchKernelGGL((partials_kernel<false, true>), dim3(count), dim3(256), 0, st, a, n_cf, n_sf, first, epoch);
-  else
-    hipLaunchKernelGGL((partials_kernel<false, false>), dim3(count), dim3(256), 0, st, a, n_cf, n_sf, first, epoch);
+  const dim3 grid(count), block(256);
+#define CA_LAUNCH(F, A, HT) hipLaunchKernelGGL((partials_kernel<F, A, HT>), grid, block, 0, st, a, n_cf, n_sf, first, epoch)
+  if (a.half_tiles) {
+    if (fuse && append) CA_LAUNCH(true, true, true);
+    else if (fuse) CA_LAUNCH(true, false, true);
+    else if (append) CA_LAUNCH(false, true, true);
+    else CA_LAUNCH(false, false, true);
+  } else {
+    if (fuse && append) CA_LAUNCH(true, true, false);
+    else if (fuse) CA_LAUNCH(true, false, false);
+    else if (append) CA_LAUNCH(false, true, false);
+    else CA_LAUNCH(false, false, false);
+  }
+#undef CA_LAUNCH
   return static_cast<int>(hipGetLastError());
 }
 

@@ -14,9 +14,11 @@ constexpr int kOpsPerLaunch = 64;  // 2 KiB of kernel arguments
 // One copy into one 64-key tile: keys [dst_key0, dst_key0 + n_rows) of tile
 // dst_tile.  Source row r is caller row src0 + r, or (from_pool) key
 // (src0 + r) % 64 of pool tile (src0 + r) / 64, so a chunk split's tail may
-// come from two tiles.  zero_rest: the tile's other keys become zeros.
+// come from two tiles.  Keys in [zero_lo, zero_hi) that are not written
+// become zeros (a chunk's first write clears the chunk's part of the tile);
+// every other key keeps its value.
 struct KvOpDev {
-  int32_t dst_tile, dst_key0, n_rows, src0, from_pool, zero_rest, pad0, pad1;
+  int32_t dst_tile, dst_key0, n_rows, src0, from_pool, zero_lo, zero_hi, pad;
 };
 
 struct KvOpBatch {

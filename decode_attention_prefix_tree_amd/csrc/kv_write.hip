@@ -16,9 +16,10 @@ namespace {
 
 // KV writes: caller rows or pool keys into one 64-key tile (K and V).
 // grid (n_ops, heads, 2), 256 threads; a thread owns 4 of the tile's 1024
-// 16-byte units.  Without zero_rest only the units holding a written key are
-// read and rewritten (a one-token append touches 16 K units and 128 V units
-// of a head, not the whole 32 KiB pair).  Block (0, 0, 0) also stores the
+// 16-byte units.  Unless the piece clears the whole tile, only the units
+// holding a written or cleared key are read and rewritten (a one-token
+// append touches 16 K units and 128 V units of a head, not the whole 32 KiB
+// pair).  Block (0, 0, 0) also stores the
 // fill counts of chunks that grew in place into the device chunk table, so
 // the next step on the stream sees them without a table upload.
 __global__ __launch_bounds__(256) void kv_write_kernel(_Float16* pool, int heads, KvOpBatch batch,
@@ -31,20 +32,23 @@ __global__ __launch_bounds__(256) void kv_write_kernel(_Float16* pool, int heads
   _Float16* dst = pool + tile_base(op.dst_tile, head, heads, kv);
   const _Float16* src = kv ? v_src : k_src;
   const int lo = op.dst_key0, hi = op.dst_key0 + op.n_rows;  // written keys [lo, hi)
+  const int zlo = op.zero_lo, zhi = op.zero_hi;                // cleared keys [zlo, zhi)
+  const bool whole = zlo == 0 && zhi == C;  // every unit rewritten, none read
   for (int u = threadIdx.x; u < TILE / 8; u += 256) {
     const int L = u >> 6, lane = u & 63, half = lane >> 5, i = lane & 31;
-    if (!op.zero_rest) {
+    if (!whole) {
       bool touched;
       if (kv == 0) {
         const int key = (L >> 3) * 32 + i;
-        touched = key >= lo && key < hi;
+        touched = (key >= lo && key < hi) || (key >= zlo && key < zhi);
       } else {
         const int k0 = (L & 3) * 16 + half * 4;  // keys k0..k0+3 and k0+8..k0+11
-        touched = (k0 < hi && k0 + 4 > lo) || (k0 + 8 < hi && k0 + 12 > lo);
+        touched = (k0 < hi && k0 + 4 > lo) || (k0 + 8 < hi && k0 + 12 > lo) ||
+                  (k0 < zhi && k0 + 4 > zlo) || (k0 + 8 < zhi && k0 + 12 > zlo);
       }
       if (!touched) continue;
     }
-    const h8 cur = op.zero_rest ? h8{} : *reinterpret_cast<const h8*>(dst + u * 8);
+    const h8 cur = whole ? h8{} : *reinterpret_cast<const h8*>(dst + u * 8);
     h8 val;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(_Float16* pool, int heads
           x = src[(static_cast<size_t>(sr) * heads + head) * D + dim];
         }
       } else {
-        x = op.zero_rest ? static_cast<_Float16>(0.0f) : cur[e];
+        x = key >= zlo && key < zhi ? static_cast<_Float16>(0.0f) : cur[e];
       }
       val[e] = x;
     }

@@ -106,7 +106,7 @@ int32_t Manager::insert(int64_t seq, const int32_t* tokens, int32_t n, std::vect
     for (int64_t s : t.ended) end_[s] = tail;
     t.ref = head.ref;
     if (ops)
-      ops->push_back(KvOp{t.slot, 0, static_cast<int32_t>(t.tokens.size()), split_at, head.slot, 1, 1});
+      ops->push_back(KvOp{t.slot, 0, static_cast<int32_t>(t.tokens.size()), split_at, head.slot, 1});
     cur = split_node;
   }
   while (pos < n) {
@@ -115,7 +115,7 @@ int32_t Manager::insert(int64_t seq, const int32_t* tokens, int32_t n, std::vect
     Node& nd = nodes_[idx];
     nd.tokens.assign(tokens + pos, tokens + pos + take);
     nodes_[cur].children.push_back(idx);
-    if (ops) ops->push_back(KvOp{nd.slot, 0, take, pos, -1, 0, 1});
+    if (ops) ops->push_back(KvOp{nd.slot, 0, take, pos, -1, 0});
     cur = idx;
     pos += take;
   }
@@ -142,7 +142,7 @@ void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<
   if (take > 0) {
     Node& nd = nodes_[e];
     nd.tokens.insert(nd.tokens.end(), tokens, tokens + take);
-    if (ops) ops->push_back(KvOp{nd.slot, fill, take, src_base, -1, 0, 0, e});
+    if (ops) ops->push_back(KvOp{nd.slot, fill, take, src_base, -1, 0, e});
     // growing into another 64-key tile adds a tile ref to the plan
     if (tiles_of(fill + take) != tiles_of(fill)) structural_ = true;
   }
@@ -159,7 +159,7 @@ void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<
     nd.tokens.assign(tokens + i, tokens + i + piece);
     nd.ref = 1;
     nodes_[cur].children.push_back(idx);
-    if (ops) ops->push_back(KvOp{nd.slot, 0, piece, src_base + i, -1, 0, 1});
+    if (ops) ops->push_back(KvOp{nd.slot, 0, piece, src_base + i, -1, 0});
     cur = idx;
     pos += piece;
     i += piece;

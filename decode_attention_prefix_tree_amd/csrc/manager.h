@@ -47,8 +47,10 @@ struct Error : std::runtime_error {
 
 // A device-side copy the host asks for after a tree mutation.  Either rows
 // from the caller's K/V ([row][head][dim], fp16) or rows of another slot are
-// written to key positions [dst_key0, dst_key0 + n_rows) of dst_slot; with
-// zero_rest the other keys of the slot are cleared.
+// written to key positions [dst_key0, dst_key0 + n_rows) of dst_slot.  A
+// write that starts at key 0 is the chunk's first since its slot was
+// allocated (keys are written in order), so the chunk's other keys are
+// cleared with it.
 struct KvOp {
   int32_t dst_slot;
   int32_t dst_key0;
@@ -56,7 +58,6 @@ struct KvOp {
   int32_t src_row0;   // caller row (from_pool == 0) or source key (from_pool == 1)
   int32_t src_slot;   // only for from_pool
   int32_t from_pool;
-  int32_t zero_rest;
   int32_t node = -1;  // manager node written (host bookkeeping only)
 };
 

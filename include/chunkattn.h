@@ -28,8 +28,9 @@
  *  - Element types: K, V, Q and the output are IEEE binary16 (fp16); the
  *    kernels accumulate in fp32.  Token ids are int32.
  *  - head_dim 128; chunk_size 64 (the chunk size of the summary's Table 3,
- *    the tuned setting) or 128 (a chunk is then two 64-key tiles, and the
- *    kernels read only the tiles that hold tokens); any head count >= 1.
+ *    the tuned setting), 128 (a chunk is two 64-key tiles, and the kernels
+ *    read only the tiles that hold tokens) or 32 (two chunks share a 64-key
+ *    tile, each read as one half); any head count >= 1.
  */
 #ifndef CHUNKATTN_H
 #define CHUNKATTN_H
@@ -135,8 +136,8 @@ typedef struct ca_stats_t {
  * * head_dim.  Returns 0 for non-positive arguments. */
 size_t ca_slot_bytes(int heads, int head_dim, int chunk_size);
 
-/* Create a context.  heads >= 1; head_dim must be 128 and chunk_size 64 or
- * 128 (else CA_E_UNSUPPORTED).  Scale is 1/sqrt(head_dim) computed in fp32.
+/* Create a context.  heads >= 1; head_dim must be 128 and chunk_size 32, 64
+ * or 128 (else CA_E_UNSUPPORTED).  Scale is 1/sqrt(head_dim) computed in fp32.
  * *out receives the context; the caller owns it and frees it with
  * ca_destroy. */
 int ca_create(int heads, int head_dim, int chunk_size, ca_ctx** out);
@@ -144,9 +145,11 @@ int ca_create_ex(int heads, int head_dim, int chunk_size, int flags, ca_ctx** ou
 void ca_destroy(ca_ctx* ctx);
 
 /* Lend the context a device pool of capacity_slots slots, each
- * ca_slot_bytes() long, 256-byte aligned.  Layout inside the pool:
- * slot-major, then head, then K tile and V tile of 64 x 128 fp16 each (tile
- * element order is private to the library).  dev may be NULL: the context
+ * ca_slot_bytes() long, 256-byte aligned.  Layout inside the pool: 64-key
+ * tiles, tile-major, then head, then K tile and V tile of 64 x 128 fp16 each
+ * (tile element order is private to the library); a slot of 64 tokens is one
+ * tile, of 128 two, and two slots of 32 share one.  With chunk_size 32 the
+ * slots are used in pairs: an odd last slot is left out of the capacity.  dev may be NULL: the context
  * then manages the tree and tables on the host only and every call that
  * needs the device returns CA_E_NO_POOL.  Allowed only while no sequence is
  * live (CA_E_STATE otherwise).  The caller keeps the memory alive and owns it. */

@@ -27,10 +27,11 @@ def test_create_rejects_unsupported_shapes():
     lib = _capi.load()
     ctx = ctypes.c_void_p()
     assert lib.ca_create(8, 64, 64, ctypes.byref(ctx)) == -2
-    assert lib.ca_create(8, 128, 32, ctypes.byref(ctx)) == -2
+    assert lib.ca_create(8, 128, 16, ctypes.byref(ctx)) == -2
     assert lib.ca_create(8, 128, 96, ctypes.byref(ctx)) == -2
-    assert lib.ca_create(8, 128, 128, ctypes.byref(ctx)) == 0
-    lib.ca_destroy(ctx)
+    for c in (32, 128):
+        assert lib.ca_create(8, 128, c, ctypes.byref(ctx)) == 0
+        lib.ca_destroy(ctx)
     assert lib.ca_create(0, 128, 64, ctypes.byref(ctx)) == -1
     assert lib.ca_create_ex(8, 128, 64, 0x100, ctypes.byref(ctx)) == -2
     assert lib.ca_slot_bytes(32, 128, 64) == 4 * 32 * 64 * 128
@@ -116,11 +117,13 @@ def test_golden_tables_at_chunk64_by_token_expansion(case):
             assert got == op.expect
 
 
-@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("chunk", [32, 64, 128])
 def test_random_ops_bit_exact_against_model(chunk):
     rng = np.random.default_rng(1234)
     for trial in range(25):
         cap = int(rng.integers(5, 60))
+        if chunk == 32:
+            cap -= cap % 2  # 32-token chunks pair up in 64-key tiles: even capacities
         share = bool(rng.random() < 0.85)
         m = PrefixTreeModel(chunk, cap, share)
         ca = ChunkAttention(4, cap, device=None, share=share, chunk_size=chunk)
@@ -278,7 +281,7 @@ def test_no_chunk_first_mode_keeps_tree_and_streams_whole_paths(k):
     assert s2["sf_chunk_reads"] + s2["shared_chunks"] < s1["sf_chunk_reads"]
 
 
-@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("chunk", [32, 64, 128])
 def test_append_batch_matches_model_through_fill_refreshes(chunk):
     rng = np.random.default_rng(77)
     m = PrefixTreeModel(chunk, 400)
@@ -435,3 +438,19 @@ def test_chunk128_append_into_second_tile_rebuilds_the_plan():
     st2 = ca.stats()
     assert st2["table_rebuilds"] == st1["table_rebuilds"] + 1
     assert st2["sf_chunk_reads"] == 3 and st2["chunks"] == 2
+
+
+def test_chunk32_capacity_in_pairs_and_plan():
+    """32-token chunks pair up in 64-key tiles: an odd last slot is left out,
+    and the plan lists one ref per chunk."""
+    ca = ChunkAttention(2, 7, device=None, chunk_size=32)
+    assert ca.stats()["capacity_slots"] == 6
+    m = PrefixTreeModel(32, 6)
+    for s, t in enumerate([list(range(70)), list(range(40)) + [9] * 5, [5] * 20]):
+        assert ca.insert(s, t) == m.insert(s, t)
+    model_and_lib_agree(m, ca)
+    rows, _ = m.table()
+    cf = sum(-(-(r[5] - r[4]) // 32) for r in rows if r[5] - r[4] >= 2)
+    sf = sum(1 for r in rows if r[5] - r[4] < 2)
+    st = ca.stats()
+    assert (st["cf_chunk_reads"], st["sf_chunk_reads"]) == (cf, sf)

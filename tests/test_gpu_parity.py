@@ -437,7 +437,7 @@ def test_head_counts(heads):
     assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
 
 
-@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("chunk", [32, 64, 128])
 @pytest.mark.parametrize("mode", ["two_launch", "one_launch", "shared_pages"])
 def test_decode_step_equals_append_then_attend(mode, chunk):
     """ca_decode_step (tokens written by the step's own blocks while chunks
@@ -447,7 +447,8 @@ def test_decode_step_equals_append_then_attend(mode, chunk):
     and the oracle over the grown sequences every 35 steps.  One sequence
     ends inside the shared prefix, so its first append grows a new chunk.
     With 128-token chunks the growing chunk also moves on to its second
-    64-key tile (a new tile in the plan: a rebuild, not a patch)."""
+    64-key tile (a new tile in the plan: a rebuild, not a patch); with 32,
+    two sequences' chunks may share a tile and grow in the same step."""
     _say(f"decode step, {mode}, chunk {chunk}")
     torch = _torch()
     from decode_attention_prefix_tree_amd import _capi
@@ -594,28 +595,31 @@ def test_patched_single_appends_deep_private_tails(sf_group):
     assert ca.stats()["patched_appends"] >= 4 * 9
 
 
+@pytest.mark.parametrize("chunk", [32, 128])
 @pytest.mark.parametrize("two_phase", [True, False])
 @pytest.mark.parametrize("name", ["shared_R40", "shared_R70", "deep_random", "interior_and_dups", "all_private",
                                   "single_token"])
-def test_chunk128_tiny_trees(name, two_phase):
-    """128-token chunks: each chunk is one or two 64-key tiles in the plan;
-    divergences split chunks anywhere in either tile."""
-    _say(f"chunk 128 tiny tree {name} two_phase={two_phase}")
+def test_chunk_sizes_tiny_trees(name, two_phase, chunk):
+    """128-token chunks are one or two 64-key tiles in the plan; 32-token
+    chunks are halves of a tile (two chunks per tile, read half by half).
+    Divergences split chunks anywhere."""
+    _say(f"chunk {chunk} tiny tree {name} two_phase={two_phase}")
     seqs = tiny_tree_cases()[name]
-    wl = from_token_lists(seqs, heads=3, seed=len(name) + 128)
-    ca = build_ca(wl, chunk=128, two_phase=two_phase)
-    assert_parity(run_step(ca, wl.q), A.decode_workload(wl), f"c128 {name}")
+    wl = from_token_lists(seqs, heads=3, seed=len(name) + chunk)
+    ca = build_ca(wl, chunk=chunk, two_phase=two_phase)
+    assert_parity(run_step(ca, wl.q), A.decode_workload(wl), f"c{chunk} {name}")
 
 
-def test_chunk128_non_aligned_prefix_ragged_suffixes():
-    """A 1766-token shared prefix (13 chunks of 128 and one of 102) with
+@pytest.mark.parametrize("chunk", [32, 128])
+def test_chunk_sizes_non_aligned_prefix_ragged_suffixes(chunk):
+    """A 1766-token shared prefix (ending mid-chunk at 32 and at 128) with
     suffixes of 1..700 tokens, 8 heads, against the oracle."""
     rng = np.random.default_rng(2128)
     suffix = [int(x) for x in rng.integers(1, 701, size=40)]
     wl = make_prefix_suffix(1766, suffix, heads=8, seed=2129)
-    _say("chunk 128 prefix 1766 + ragged suffixes")
-    ca = build_ca(wl, chunk=128)
-    assert_parity(run_step(ca, wl.q), A.decode_workload(wl), "c128 prefix1766 ragged")
+    _say(f"chunk {chunk} prefix 1766 + ragged suffixes")
+    ca = build_ca(wl, chunk=chunk)
+    assert_parity(run_step(ca, wl.q), A.decode_workload(wl), f"c{chunk} prefix1766 ragged")
 
 
 def _k_off(key, dim):
@@ -629,7 +633,7 @@ def _v_off(key, dim):
         ((key & 3) | (((key >> 3) & 1) << 2))
 
 
-@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("chunk", [32, 64, 128])
 @pytest.mark.parametrize("name", ["deep_random", "interior_and_dups"])
 def test_pool_holds_each_chunks_kv(name, chunk):
     """KV scatter: after the inserts (divergences split chunks anywhere, so
@@ -641,7 +645,9 @@ def test_pool_holds_each_chunks_kv(name, chunk):
     wl = from_token_lists(tiny_tree_cases()[name], heads=3, seed=9)
     ca = build_ca(wl, chunk=chunk)
     rows, order = ca.export_table()
-    pool = ca.pool.view(torch.float16).cpu().numpy().reshape(-1, wl.heads, 2, 64 * 128)
+    flat = ca.pool.view(torch.float16).cpu().numpy()
+    tile_halves = wl.heads * 2 * 64 * 128  # one 64-key tile, every head, K and V
+    pool = flat[:flat.size // tile_halves * tile_halves].reshape(-1, wl.heads, 2, 64 * 128)
     keys = np.arange(64)[:, None]
     dims = np.arange(128)[None, :]
     koff, voff = _k_off(keys, dims), _v_off(keys, dims)
