@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 from oracle import attention as A
-from workloads import from_token_lists, make_config, make_prefix_suffix
+from workloads import from_token_lists, make_config, make_long_sequence, make_prefix_suffix
 
 pytestmark = pytest.mark.gpu
 
@@ -661,3 +661,33 @@ def test_pool_holds_each_chunks_kv(name, chunk):
             assert np.array_equal(pool[t][:, 1][:, voff[kk]], v[start + j]), (r, j)
             n_keys += 1
     assert n_keys == sum(int(r[3]) for r in rows)
+
+
+def test_one_sequence_of_65536_tokens():
+    """The longest single context here: one private sequence of 65,536 tokens
+    (1,024 chunks, 256 sequence-first tasks per head, 256 partials merged
+    through the compact list), 8 heads, against the oracle."""
+    _say("one sequence of 65536 tokens")
+    wl = make_long_sequence(65536, heads=8, seed=65536)
+    ca = build_ca(wl)
+    assert ca.stats()["partials"] == 256
+    assert_parity(run_step(ca, wl.q), A.decode_workload(wl), "65536 tokens")
+
+
+def test_256_sequences_one_launch():
+    """A large batch: 256 sequences x 16 heads (4,096 merges, so the default
+    step is one launch) sharing a 2,048-token prefix, private suffixes of
+    1..300 tokens; sampled rows against the oracle, all rows against the
+    two-launch step bit for bit."""
+    _say("256 sequences, one launch")
+    from decode_attention_prefix_tree_amd import _capi
+    rng = np.random.default_rng(256)
+    wl = make_prefix_suffix(2048, [int(x) for x in rng.integers(1, 301, size=256)], heads=16, seed=257)
+    ca = build_ca(wl)
+    assert ca.stats()["one_launch_step"] == 1
+    got = run_step(ca, wl.q)
+    rows = sorted({0, 1, 127, 128, 254, 255} | set(int(x) for x in rng.choice(256, 18, replace=False)))
+    assert_parity(got[rows], A.decode_workload(wl, rows), "256 seq sampled")
+    assert np.isfinite(got).all()
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 0)
+    assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))

@@ -43,6 +43,7 @@ __all__ = [
     "CONFIG_NAMES",
     "make_config",
     "make_prefix_suffix",
+    "make_long_sequence",
     "from_token_lists",
     "segment_tokens",
 ]
@@ -185,6 +186,19 @@ def make_prefix_suffix(prefix_len: int, suffix_lens: Sequence[int], heads: int, 
         f"{min(suffix_lens)}..{max(suffix_lens)}")
     return Workload(name=name or f"prefix{prefix_len}", heads=heads, head_dim=d, chunk=CHUNK, seed=seed,
                     segments=segs, paths=paths, q=q, description=desc)
+
+
+def make_long_sequence(length: int, heads: int, seed: int) -> Workload:
+    """One private sequence of ``length`` tokens, longer than a segment may
+    be: a chain of segments of at most 8,192 tokens, K then V of each drawn in
+    order with ``rng = default_rng(seed)``, then the query."""
+    rng = np.random.default_rng(seed)
+    pieces = [min(1 << _TOKEN_BITS, length - i) for i in range(0, length, 1 << _TOKEN_BITS)]
+    segs = _draw_segments(rng, pieces, heads, HEAD_DIM)
+    q = rng.standard_normal((1, heads, HEAD_DIM), dtype=np.float32).astype(np.float16)
+    return Workload(name=f"long{length}", heads=heads, head_dim=HEAD_DIM, chunk=CHUNK, seed=seed,
+                    segments=segs, paths=[list(range(len(pieces)))], q=q,
+                    description=f"1 seq of {length} tokens, {heads} heads")
 
 
 @dataclass
