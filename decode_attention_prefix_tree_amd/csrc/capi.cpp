@@ -102,7 +102,7 @@ bool device_table_current(const ca_ctx* c) { return c->uploaded_version == c->ve
 
 // with_fills: the host plan's fill counts are needed too (an upload, an
 // export, stats); a step whose device table is current does not need them.
-// Chunks per chunk-first task when the caller leaves it open.  A
+// Chunk refs per chunk-first task when the caller leaves it open.  A
 // chunk-first wave walks its chunks one 32-key half after another, each half
 // one dependent round trip to memory (all 16 KiB of its tile loads in flight
 // together).  The longest such chain should stay within half of the step's
@@ -113,13 +113,18 @@ bool device_table_current(const ca_ctx* c) { return c->uploaded_version == c->ve
 // about 40 us of streaming up (1024 and 4096 shared tokens, 32 sequences;
 // the multi-branch tree), while 32 or 64 make the chains the tail at 4096
 // shared tokens (65.9 and 89.0 us against 59.3 us).
-int auto_cf_group(const chunkattn::Plan& p, int heads, int head_dim) {
+// The group counts chunk refs: a 64-key tile (two halves) at C >= 64, one
+// half at C = 32, so 32-token chunks take twice as many refs per chain.
+int auto_cf_group(const chunkattn::Plan& p, int heads, int head_dim, int chunk) {
   const double kernel_us = static_cast<double>(p.unique_tokens) * 4.0 * heads * head_dim / 6.0e6;
+  const int halves_per_ref = chunk < chunkattn::kTileKeys ? 1 : 2;
+  const int refs_per_tile = 2 / halves_per_ref;
   for (int g : {16, 8}) {
-    const int halves = 2 * ((g + 3) / 4);
-    if (halves * 2.5 <= 0.5 * kernel_us) return g;
+    const int refs = g * refs_per_tile;
+    const int halves = halves_per_ref * ((refs + 3) / 4);
+    if (halves * 2.5 <= 0.5 * kernel_us) return refs;
   }
-  return 4;
+  return 4 * refs_per_tile;
 }
 
 void ensure_plan(ca_ctx* c, bool with_fills = true) {
@@ -139,7 +144,7 @@ void ensure_plan(ca_ctx* c, bool with_fills = true) {
   const int g = c->cf_group ? c->cf_group : c->cf_auto;
   c->mgr.build_plan(g, c->sf_group, two_phase, &c->plan);
   if (c->cf_group == 0 && two_phase && c->plan.shared_chunks > 0) {
-    const int want = auto_cf_group(c->plan, c->heads, c->head_dim);
+    const int want = auto_cf_group(c->plan, c->heads, c->head_dim, c->chunk);
     if (want != g) c->mgr.build_plan(want, c->sf_group, two_phase, &c->plan);
     c->cf_auto = want;
   }

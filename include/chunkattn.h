@@ -75,11 +75,13 @@ enum {
 
 /* ca_set_option keys. */
 enum {
-  CA_OPT_CF_CHUNKS_PER_TASK = 1, /* chunks of one shared run per chunk-first task (1..64), or 0
-                                    (default): chosen per plan, 4, 8 or 16, so that a chunk-first
-                                    wave's chain of dependent tile loads stays well inside the
-                                    step's streaming time (ca_stats reports the choice) */
-  CA_OPT_SF_CHUNKS_PER_TASK = 2, /* private chunks per sequence-first task (1..256), default 4 */
+  CA_OPT_CF_CHUNKS_PER_TASK = 1, /* chunk refs of one shared run per chunk-first task (1..64), or
+                                    0 (default): chosen per plan, 4, 8 or 16 (8, 16 or 32 with
+                                    32-token chunks), so that a chunk-first wave's chain of
+                                    dependent tile loads stays well inside the step's streaming
+                                    time (ca_stats reports the choice).  A ref is a 64-key tile
+                                    (a chunk of 128 is two), or half a tile with chunks of 32. */
+  CA_OPT_SF_CHUNKS_PER_TASK = 2, /* private chunk refs per sequence-first task (1..256), default 4 */
   CA_OPT_FUSED_MERGE = 3         /* 0: a step is a partials launch and a merge launch.
                                     1: one launch whose grid ends with merge blocks; each waits
                                     until the partials of its (sequence, head) are written (all
