@@ -665,12 +665,22 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
     const _Float16* kt = pool + tile_base(tile, head, H, 0) + hh * 8 * 512;
     const _Float16* vt = pool + tile_base(tile, head, H, 1) + hh * 2 * 512;
     if (kAppend && c == append_at) nvalid = append_fill;
+    // Keys past the fill get zero weight, so the tile blocks that hold only
+    // such keys are not fetched from memory: a K load block covers 32 keys,
+    // a V block 16, and a block wholly past the fill reads the chunk's first
+    // block of its row again (already on its way: a cache hit).  Its finite
+    // values meet zero probabilities, so the result is unchanged.
+    // (The choice is one wave-uniform base per 32-key K half and per 16-key
+    // V group, so every load keeps its immediate offset.)
+    const _Float16* kb[2] = {kt, nvalid > 32 ? kt + 8 * 512 : kt};
+    const _Float16* vb[4] = {vt, nvalid > 16 ? vt + 512 : vt, nvalid > 32 ? vt + 2 * 512 : vt,
+                             nvalid > 48 ? vt + 3 * 512 : vt};
     h8 ka[16], va[16];
 #pragma unroll
-    for (int L = 0; L < (kHalf ? 8 : 16); ++L) ka[L] = ld_tile<kNT>(kt + (L * 64 + lane) * 8);
+    for (int L = 0; L < (kHalf ? 8 : 16); ++L) ka[L] = ld_tile<kNT>(kb[L >> 3] + ((L & 7) * 64 + lane) * 8);
 #pragma unroll
     for (int L = 0; L < 16; ++L)
-      if (!kHalf || (L & 3) < 2) va[L] = ld_tile<kNT>(vt + (L * 64 + lane) * 8);
+      if (!kHalf || (L & 3) < 2) va[L] = ld_tile<kNT>(vb[L & 3] + ((L & ~3) * 64 + lane) * 8);
 
     float d0 = 0.f, d1 = 0.f;
 #pragma unroll
