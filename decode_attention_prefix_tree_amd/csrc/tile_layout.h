@@ -1,8 +1,10 @@
 // Device-side layout of the chunk pool, shared by the decode-step kernels
 // and the KV write kernel.
 //
-// Chunk tile layout.  Slot s, head h: K tile at ((s*H + h)*2 + 0) * 8192
-// halves, V tile right after it.  Within a tile the 64 x 128 fp16 elements
+// Tile layout.  The pool is a sequence of 64-key tiles; tile t, head h: K
+// tile at ((t*H + h)*2 + 0) * 8192 halves, V tile right after it (a chunk
+// slot of 64 tokens is one tile, of 128 two, two slots of 32 share one).
+// Within a tile the 64 x 128 fp16 elements
 // are ordered so that every MFMA operand fetch is one contiguous 1 KB wave
 // load (64 lanes x 16 bytes):
 //  * K, as the A operand of S^T = K * Q^T (v_mfma_f32_32x32x16_f16, A lane
@@ -32,8 +34,8 @@ constexpr int D = kHeadDim;
 constexpr int C = kChunk;
 constexpr int TILE = C * D;  // halves per tile
 
-__device__ __forceinline__ size_t tile_base(int slot, int head, int heads, int kv) {
-  return ((static_cast<size_t>(slot) * heads + head) * 2 + kv) * TILE;
+__device__ __forceinline__ size_t tile_base(int tile, int head, int heads, int kv) {
+  return ((static_cast<size_t>(tile) * heads + head) * 2 + kv) * TILE;
 }
 
 __device__ __forceinline__ int k_off(int key, int dim) {
