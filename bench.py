@@ -414,7 +414,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_name, "n_seq": wl.n_seq, "heads": wl.heads,
                    "head_dim": wl.head_dim, "chunk": args.chunk, "cache": "cold (1 GiB read before each step)",
-                   "cf_chunks_per_task": st["cf_chunks_per_task"], "sf_chunks_per_task": 4,
+                   "cf_chunks_per_task": st["cf_chunks_per_task"], "sf_chunks_per_task": st["sf_chunks_per_task"],
                    "launches_per_step": 1 if one_launch else 2},
         "unique_kv_gbps": unique_b / t_mean / 1e9,
         "hbm_frac_unique": unique_b / t_mean / 1e9 / HBM_PEAK_GBPS,

@@ -64,6 +64,7 @@ class ca_stats_t(ctypes.Structure):
         ("patched_appends", ctypes.c_int64),
         ("cf_chunks_per_task", ctypes.c_int64),
         ("one_launch_step", ctypes.c_int64),
+        ("sf_chunks_per_task", ctypes.c_int64),
     ]
 
 

@@ -23,7 +23,7 @@ struct ca_ctx {
   bool pool_attached = false;
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  int cf_group = 0, sf_group = 4;  // cf_group 0: chosen per plan (auto_cf_group)
+  int cf_group = 0, sf_group = 0;  // 0: chosen per plan (auto_cf_group, sf_min_tasks)
   int cf_auto = 8;                 // the last automatic choice
   int plan_cf_group = 8;           // the group the current plan was built with
   int fused_merge = 2;              // CA_OPT_FUSED_MERGE: 0 two launches, 1 one launch, 2 chosen per plan
@@ -127,6 +127,20 @@ int auto_cf_group(const chunkattn::Plan& p, int heads, int head_dim, int chunk) 
   return 4 * refs_per_tile;
 }
 
+// Sequence-first tasks a plan should have when the group is left open: the
+// blocks of a step (tasks x heads) should fill the chip's resident block
+// slots (three 256-thread blocks on each of 256 CUs) about 2.5 times, or the
+// last round leaves CUs idle.  Measured on MI355X: 32 sequences with 512
+// private tokens each take 50.4 us with 4 refs per task (2048 blocks) and
+// 53.0 us with 8 (1024 blocks); the multi-branch tree, whose suffixes of
+// 64..1024 tokens give 4096 blocks even with 16 refs per task, takes 200.6 us
+// with 16 against 206.9 us with 4 (one partial per sequence instead of up to
+// four).
+int64_t sf_min_tasks(int heads) {
+  constexpr int64_t kResidentBlocks = 3 * 256;
+  return (kResidentBlocks * 5 / 2 + heads - 1) / heads;
+}
+
 void ensure_plan(ca_ctx* c, bool with_fills = true) {
   if (c->plan_valid) {
     if (c->fills_stale && with_fills) {
@@ -142,10 +156,11 @@ void ensure_plan(ca_ctx* c, bool with_fills = true) {
   auto t0 = std::chrono::steady_clock::now();
   const bool two_phase = (c->flags & CA_CREATE_NO_CHUNK_FIRST) == 0;
   const int g = c->cf_group ? c->cf_group : c->cf_auto;
-  c->mgr.build_plan(g, c->sf_group, two_phase, &c->plan);
+  const int64_t sf_min = sf_min_tasks(c->heads);
+  c->mgr.build_plan(g, c->sf_group, two_phase, &c->plan, sf_min);
   if (c->cf_group == 0 && two_phase && c->plan.shared_chunks > 0) {
     const int want = auto_cf_group(c->plan, c->heads, c->head_dim, c->chunk);
-    if (want != g) c->mgr.build_plan(want, c->sf_group, two_phase, &c->plan);
+    if (want != g) c->mgr.build_plan(want, c->sf_group, two_phase, &c->plan, sf_min);
     c->cf_auto = want;
   }
   c->plan_cf_group = c->cf_group ? c->cf_group : c->cf_auto;
@@ -483,7 +498,7 @@ int ca_set_option(ca_ctx* ctx, int option, int value) {
       if (value < 0 || value > 64) throw Error(CA_E_INVALID_ARG, "chunk-first group must be 0 (auto) or 1..64");
       ctx->cf_group = value;
     } else if (option == CA_OPT_SF_CHUNKS_PER_TASK) {
-      if (value < 1 || value > 256) throw Error(CA_E_INVALID_ARG, "sequence-first group must be 1..256");
+      if (value < 0 || value > 256) throw Error(CA_E_INVALID_ARG, "sequence-first group must be 0 (auto) or 1..256");
       ctx->sf_group = value;
     } else if (option == CA_OPT_FUSED_MERGE) {
       if (value < 0 || value > 2) throw Error(CA_E_INVALID_ARG, "fused merge is 0, 1 or 2 (automatic)");
@@ -693,6 +708,7 @@ int ca_stats(ca_ctx* ctx, ca_stats_t* out) {
     s.table_uploads = ctx->table_uploads;
     s.patched_appends = ctx->patched_appends;
     s.cf_chunks_per_task = ctx->plan_cf_group;
+    s.sf_chunks_per_task = ctx->plan.sf_group;
     s.one_launch_step = one_launch(ctx) ? 1 : 0;
     *out = s;
     return CA_OK;

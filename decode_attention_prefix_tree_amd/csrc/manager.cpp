@@ -235,13 +235,14 @@ void Plan::clear() {
   seq_parts.clear();
   part_list.clear();
   cf_tasks = 0;
+  sf_group = 0;
   n_parts = 0;
   dense_parts = 0;
   part_stride = 1;
   cf_chunk_reads = sf_chunk_reads = shared_chunks = shared_tokens = unique_tokens = attended_tokens = 0;
 }
 
-void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan) const {
+void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan, int64_t sf_min_tasks) const {
   Plan& P = *plan;
   P.clear();
 
@@ -350,39 +351,65 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan)
   }
 
   // Pass 3: per sequence, the shared runs on its path (root first) and its
-  // private chunks cut into sequence-first tasks.  entries[ent_first[i] + j]
-  // is the j-th partial of sequence i in merge order: a run t (t >= 0) or a
-  // sequence-first task k (-1 - k).
-  std::vector<int32_t> ent_first(static_cast<size_t>(n_seq) + 1, 0), entries;
+  // private chunk refs; then the refs cut into sequence-first tasks.
+  // entries[ent_first[i] + j] is the j-th partial of sequence i in merge
+  // order: a run t (t >= 0) or a sequence-first task k (-1 - k).
+  std::vector<int32_t> run_first(static_cast<size_t>(n_seq) + 1, 0), runs;
+  std::vector<int32_t> priv_first(static_cast<size_t>(n_seq) + 1, 0);
+  std::vector<std::pair<int32_t, int32_t>> priv;  // (row, tile of the row's chunk)
   std::vector<int32_t> path;
-  int32_t max_parts = 0;
   for (int32_t i = 0; i < n_seq; ++i) {
     path.clear();
     for (int32_t r = end_row[i]; r >= 0; r = R(r, 1)) path.push_back(r);
     std::reverse(path.begin(), path.end());
-    ent_first[i] = static_cast<int32_t>(entries.size());
+    run_first[i] = static_cast<int32_t>(runs.size());
+    priv_first[i] = static_cast<int32_t>(priv.size());
     int32_t last_task = -1;
-    std::vector<std::pair<int32_t, int32_t>> priv;  // (row, tile of the row's chunk)
     for (int32_t r : path) {
       int32_t t = task_of_row[r];
       if (t >= 0) {
-        if (t != last_task) entries.push_back(t);
+        if (t != last_task) runs.push_back(t);
         last_task = t;
       } else {
         for (int32_t k = 0; k < tiles_of(R(r, 3)); ++k) priv.push_back({r, k});
       }
     }
-    for (size_t j = 0; j < priv.size(); j += static_cast<size_t>(sf_group)) {
-      size_t stop = std::min(priv.size(), j + static_cast<size_t>(sf_group));
+  }
+  run_first[n_seq] = static_cast<int32_t>(runs.size());
+  priv_first[n_seq] = static_cast<int32_t>(priv.size());
+  if (sf_group <= 0) {
+    // Left open: the largest of 16, 8 and 4 refs per task that still makes
+    // at least sf_min_tasks tasks, so that the last round of blocks on the
+    // chip stays well filled; longer tasks mean fewer partials to write and
+    // merge.
+    sf_group = 4;
+    for (int g : {16, 8}) {
+      int64_t tasks = 0;
+      for (int32_t i = 0; i < n_seq; ++i) tasks += (priv_first[i + 1] - priv_first[i] + g - 1) / g;
+      if (tasks >= sf_min_tasks) {
+        sf_group = g;
+        break;
+      }
+    }
+  }
+  P.sf_group = sf_group;
+  std::vector<int32_t> ent_first(static_cast<size_t>(n_seq) + 1, 0), entries;
+  int32_t max_parts = 0;
+  for (int32_t i = 0; i < n_seq; ++i) {
+    ent_first[i] = static_cast<int32_t>(entries.size());
+    entries.insert(entries.end(), runs.begin() + run_first[i], runs.begin() + run_first[i + 1]);
+    const int32_t p0 = priv_first[i], p1 = priv_first[i + 1];
+    for (int32_t j = p0; j < p1; j += sf_group) {
+      const int32_t stop = std::min(p1, j + sf_group);
       SfTask st{};
       st.chunk_begin = static_cast<int32_t>(P.chunk_refs.size() / 2);
-      st.n_chunks = static_cast<int32_t>(stop - j);
+      st.n_chunks = stop - j;
       st.dfs_pos = i;
       st.part_id = -1;
       st.qrow = P.dfs_qrow[i];
       st.append_at = -1;
-      for (size_t q = j; q < stop; ++q) {
-        const int c = static_cast<int>(q - j);
+      for (int32_t q = j; q < stop; ++q) {
+        const int c = q - j;
         const int32_t r = priv[q].first, k = priv[q].second;
         const int32_t slot = tile_slot(R(r, 6), k), fill = tile_fill(R(r, 3), k);
         // the last tile of the chunk where the sequence ends takes its next

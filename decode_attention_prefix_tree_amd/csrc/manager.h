@@ -104,6 +104,7 @@ struct Plan {
   std::vector<int32_t> dfs_qrow;    // caller row of each DFS position
   std::vector<CfUnit> cf_units;
   int64_t cf_tasks = 0;
+  int32_t sf_group = 0;             // private chunk refs per sequence-first task
   std::vector<SfTask> sf_tasks;
   std::vector<int32_t> chunk_refs;  // (slot, n_valid) pairs
   std::vector<int32_t> row_node;    // manager node index of each table row
@@ -169,7 +170,9 @@ class Manager {
   // per chunk-first task and per sequence-first task.  Without two_phase every
   // chunk on a sequence's path, shared or not, goes to that sequence's
   // sequence-first tasks (physically shared pages, no chunk-first phase).
-  void build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan) const;
+  // sf_group <= 0: chosen per plan, the largest of 16, 8, 4 that gives at
+  // least sf_min_tasks sequence-first tasks (Plan::sf_group says which).
+  void build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan, int64_t sf_min_tasks = 0) const;
   // Bring a plan built for the current structure up to date with chunk fills
   // that grew since: fill counts in the table, the chunk refs and the refs
   // carried inline by task records, and the token totals.

@@ -81,7 +81,10 @@ enum {
                                     dependent tile loads stays well inside the step's streaming
                                     time (ca_stats reports the choice).  A ref is a 64-key tile
                                     (a chunk of 128 is two), or half a tile with chunks of 32. */
-  CA_OPT_SF_CHUNKS_PER_TASK = 2, /* private chunk refs per sequence-first task (1..256), default 4 */
+  CA_OPT_SF_CHUNKS_PER_TASK = 2, /* private chunk refs per sequence-first task (1..256), or 0
+                                    (default): chosen per plan, the largest of 16, 8 and 4 that
+                                    still gives the step about 2.5 rounds of blocks over the
+                                    chip's resident block slots (ca_stats reports the choice) */
   CA_OPT_FUSED_MERGE = 3         /* 0: a step is a partials launch and a merge launch.
                                     1: one launch whose grid ends with merge blocks; each waits
                                     until the partials of its (sequence, head) are written (all
@@ -132,6 +135,7 @@ typedef struct ca_stats_t {
                                 stored into the device table itself */
   int64_t cf_chunks_per_task; /* chunk-first group of the current plan */
   int64_t one_launch_step;    /* 1 if ca_attend runs the step as one launch */
+  int64_t sf_chunks_per_task; /* sequence-first group of the current plan */
 } ca_stats_t;
 
 /* Bytes of one chunk slot: K and V, all heads, fp16 = 4 * heads * chunk_size

@@ -457,3 +457,27 @@ def test_chunk32_capacity_in_pairs_and_plan():
     sf = sum(1 for r in rows if r[5] - r[4] < 2)
     st = ca.stats()
     assert (st["cf_chunk_reads"], st["sf_chunk_reads"]) == (cf, sf)
+
+
+@pytest.mark.parametrize("case,want", [("w1", 4), ("w2", 4), ("w3", 4), ("w4", 16), ("w5", 16)])
+def test_automatic_sequence_first_group(case, want):
+    """With the group left open, the largest of 16, 8 and 4 private refs per
+    task that still gives 1920 / heads tasks (about 2.5 rounds of blocks over
+    3 x 256 resident block slots): 32 sequences with 8 private chunks each
+    stay at 4 (2048 blocks at 32 heads); 32 chunks each (workload 4) and the
+    multi-branch tree's ragged suffixes reach 16.  An explicit setting wins."""
+    wl = make_config(int(case[1:]), heads=1)
+    ca = ChunkAttention(32, 10_000, device=None)
+    for i in range(wl.n_seq):
+        ca.insert(i, wl.seq_tokens(i))
+    st = ca.stats()
+    assert st["sf_chunks_per_task"] == want
+    # every sequence's private refs cut into tasks of that size
+    rows, _ = ca.export_table()
+    assert st["sf_tasks"] >= 1920 // 32 or want == 4
+    ca.set_option(_capi.CA_OPT_SF_CHUNKS_PER_TASK, 2)
+    assert ca.stats()["sf_chunks_per_task"] == 2
+    ca.set_option(_capi.CA_OPT_SF_CHUNKS_PER_TASK, 0)
+    assert ca.stats()["sf_chunks_per_task"] == want
+    with pytest.raises(CaError):
+        ca.set_option(_capi.CA_OPT_SF_CHUNKS_PER_TASK, 257)
