@@ -691,3 +691,44 @@ def test_256_sequences_one_launch():
     assert np.isfinite(got).all()
     ca.set_option(_capi.CA_OPT_FUSED_MERGE, 0)
     assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_decode_step_growing_chunk_past_inline_refs(chunk):
+    """ca_decode_step with 16 private refs per sequence-first task and private
+    tails of 5..11 chunks: the chunk that takes each step's token sits past
+    the 4 refs a task record carries inline, so the step's blocks read and
+    grow its fill count in the chunk table.  Same bits as append + attend at
+    every one of 70 steps, oracle every 35."""
+    _say(f"decode step past inline refs, chunk {chunk}")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import _capi, slots_needed
+    rng = np.random.default_rng(61)
+    H = 2
+    shared = list(range(70))
+    seqs = [shared + [9000 + i] + [int(x) for x in rng.integers(0, 7, size=n)]
+            for i, n in enumerate((300, 450, 700, 520, 333))]
+    wl = from_token_lists(seqs, heads=H, seed=62)
+    cap = slots_needed(wl, chunk=chunk) + 40
+    a = build_ca(wl, capacity=cap, chunk=chunk, sf_group=16)
+    b = build_ca(wl, capacity=cap, chunk=chunk, sf_group=16)
+    n = wl.n_seq
+    kv = [[x.copy() for x in wl.seq_kv(i)] for i in range(n)]
+    for step in range(70):
+        toks = (2 * 10**6 + step * 100 + np.arange(n)).astype(np.int32)
+        k = rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+        v = rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+        q = rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+        kt, vt, qt = (torch.from_numpy(x).cuda() for x in (k, v, q))
+        a.append_batch(list(range(n)), toks, kt, vt)
+        ra = a.attend(qt).clone()
+        rb = b.decode_step(toks, kt, vt, qt).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(ra, rb), (chunk, step)
+        for i in range(n):
+            kv[i][0] = np.concatenate([kv[i][0], k[i:i + 1]])
+            kv[i][1] = np.concatenate([kv[i][1], v[i:i + 1]])
+        if step % 35 == 0 or step == 69:
+            assert_parity(rb.cpu().numpy(), A.decode_step(q, kv), f"decode past inline chunk {chunk} step {step}")
+    st = b.stats()
+    assert st["sf_chunks_per_task"] == 16 and st["patched_appends"] >= 40, st
