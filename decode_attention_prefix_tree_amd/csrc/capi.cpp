@@ -379,14 +379,16 @@ void run_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* 
 }
 
 // Whether a step is one launch (merge blocks close the partials grid) or a
-// partials launch and a merge launch.  Measured on MI355X, the one-launch step
-// wins once a step merges about 4096 (sequence, head) pairs (128 sequences at
-// 32 heads: 170.2 vs 171.3 us at 1024 shared + 512 private tokens, 212.4 vs
-// 217.3 us on the multi-branch tree) and loses below (64 sequences: 92.6 vs
-// 91.2 us; 32 sequences: 54.1 vs 52.2 us): its coherent partial stores and
-// the merge blocks waiting in the tail cost more than the second launch saves
-// until the merge launch itself grows with the pair count.
-constexpr int64_t kOneLaunchPairs = 4096;
+// partials launch and a merge launch.  Measured on MI355X (with the automatic
+// task groups), the one-launch step wins once a step merges about 3072
+// (sequence, head) pairs (1024 shared + 512 private tokens at 32 heads: 96
+// sequences 130.5 vs 131.6 us, 128 sequences 169.9 vs 174.0 us; the
+// multi-branch tree 200.9 vs 211.8 us), ties at 2048 (64 sequences: 92.1 vs
+// 91.8 us) and loses below (32 sequences: 53.5 vs 50.4 us): its coherent
+// partial stores and the merge blocks waiting in the tail cost more than the
+// second launch saves until the merge launch itself grows with the pair
+// count.
+constexpr int64_t kOneLaunchPairs = 3072;
 
 bool one_launch(const ca_ctx* c) {
   if (c->fused_merge != 2) return c->fused_merge == 1;

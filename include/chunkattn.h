@@ -89,7 +89,7 @@ enum {
                                     1: one launch whose grid ends with merge blocks; each waits
                                     until the partials of its (sequence, head) are written (all
                                     by blocks earlier in the grid) and merges them.
-                                    2 (default): one launch when the step merges at least 4096
+                                    2 (default): one launch when the step merges at least 3072
                                     (sequence, head) pairs, else two (measured crossover on
                                     MI355X).  All give the same bits; ca_stats reports the
                                     choice for the current tree. */
@@ -223,7 +223,7 @@ int ca_remove(ca_ctx* ctx, int64_t seq_id);
  * tree changed since the last upload, then enqueues the step on `stream`: a
  * partials launch (chunk-first and sequence-first blocks in one grid) and a
  * merge launch, or one launch whose last blocks merge (CA_OPT_FUSED_MERGE;
- * by default one launch from 4096 (sequence, head) pairs up).
+ * by default one launch from 3072 (sequence, head) pairs up).
  * The merge folds the partials in a
  * fixed order, so the result does not depend on block timing.  Steps of one
  * context must not overlap (they share the workspace and its arrival

@@ -366,15 +366,15 @@ def test_partial_slots_of_a_shared_prefix_batch():
 
 
 def test_launch_mode_follows_merge_pair_count():
-    """By default a step is one launch from 4096 (sequence, head) pairs up
-    (128 sequences at 32 heads), two launches below; the option overrides."""
+    """By default a step is one launch from 3072 (sequence, head) pairs up
+    (96 sequences at 32 heads), two launches below; the option overrides."""
     def ctx(n_seq):
         ca = ChunkAttention(32, 1024, device=None)
         for i in range(n_seq):
             ca.insert(i, [i * 100 + j for j in range(3)])
         return ca
-    assert ctx(127).stats()["one_launch_step"] == 0
-    big = ctx(128)
+    assert ctx(95).stats()["one_launch_step"] == 0
+    big = ctx(96)
     assert big.stats()["one_launch_step"] == 1
     big.set_option(_capi.CA_OPT_FUSED_MERGE, 0)
     assert big.stats()["one_launch_step"] == 0
