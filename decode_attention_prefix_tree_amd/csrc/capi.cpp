@@ -625,6 +625,7 @@ int ca_decode_step(ca_ctx* ctx, const int32_t* tokens, const void* k_dev, const 
     if (ctx->mgr.live() == 0) throw Error(CA_E_EMPTY, "no live sequence");
     if (tokens == nullptr || k_dev == nullptr || v_dev == nullptr)
       throw Error(CA_E_INVALID_ARG, "tokens, k_dev and v_dev are required");
+    if (q_dev == nullptr || out_dev == nullptr) throw Error(CA_E_INVALID_ARG, "q and out must be device pointers");
     const std::vector<int64_t> ids = ctx->mgr.sequences();
     std::vector<chunkattn::KvOp> ops;
     std::vector<FillPatch> patches;
@@ -641,7 +642,15 @@ int ca_decode_step(ca_ctx* ctx, const int32_t* tokens, const void* k_dev, const 
       touch_after_append(ctx);
       run_kv_ops(ctx, ops, k_dev, v_dev, stream);
     }
-    check_step(ctx, q_dev, out_dev);
+    try {
+      check_step(ctx, q_dev, out_dev);
+    } catch (const Error&) {
+      // The step cannot run as it is (a larger workspace is needed, or it
+      // exceeds the kernels' index range): store the tokens and their fill
+      // counts now, as ca_append_batch does, so the tree and the device agree.
+      if (in_kernel) run_kv_ops(ctx, ops, k_dev, v_dev, stream, patches);
+      throw;
+    }
     upload(ctx, stream);
     chunkattn::StepArgs a = step_args(ctx, q_dev, out_dev);
     if (in_kernel) {

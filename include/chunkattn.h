@@ -243,10 +243,12 @@ int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream);
  * reads that chunk writes the token into the pool, uses it, and stores the
  * grown fill count into the device table; otherwise the writes go out first,
  * as in ca_append_batch.  The caller keeps k_dev and v_dev alive until the
- * stream passes the step.  Errors: those of ca_append_batch (which leave
- * everything unchanged) and of ca_attend; CA_E_WORKSPACE comes after the
- * tokens were stored (a step that grew new chunks can need a larger
- * workspace): attach one of ca_workspace_bytes and finish with ca_attend. */
+ * stream passes the step.  Errors: those of ca_append_batch, and
+ * CA_E_INVALID_ARG for a NULL q_dev or out_dev, leave everything unchanged;
+ * CA_E_WORKSPACE (a step that grew new chunks can need a larger workspace)
+ * and CA_E_UNSUPPORTED (a step beyond the kernels' index range) come after
+ * the tokens were stored: attach a workspace of ca_workspace_bytes and finish
+ * with ca_attend. */
 int ca_decode_step(ca_ctx* ctx, const int32_t* tokens, const void* k_dev, const void* v_dev,
                    const void* q_dev, void* out_dev, void* stream);
 

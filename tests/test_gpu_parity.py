@@ -342,6 +342,18 @@ def test_errors_on_device_context():
     with pytest.raises(CaError) as ei:
         ca.insert(1, list(range(200)), k, k)
     assert ei.value.name == "no_capacity"
+    # a decode step with no query or output pointer changes nothing
+    import ctypes
+    ca.insert(1, list(range(40)), k[:40], k[:40])
+    one = torch.ones((1, 2, 128), dtype=torch.float16, device="cuda:0")
+    ca.attend(one)
+    tok = (ctypes.c_int32 * 1)(7)
+    p = ctypes.c_void_p(one.data_ptr())
+    for qp, op in ((None, p), (p, None)):
+        rc = ca.lib.ca_decode_step(ca.ctx, tok, p, p, qp, op, ca._stream())
+        assert rc == -1, rc
+    assert ca.stats()["unique_tokens"] == 40
+    torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("name", ["config1", "shared_R70", "deep_random", "interior_and_dups"])
