@@ -185,9 +185,13 @@ class ChunkAttention:
         if self.device is None:
             raise CaError(-9, "host-only context")
         q, out = self._qo(q, out)
-        self.ensure_workspace()
-        check(self.ctx, self.lib.ca_attend(self.ctx, ctypes.c_void_p(q.data_ptr()),
-                                           ctypes.c_void_p(out.data_ptr()), self._stream(stream)))
+        args = (self.ctx, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(out.data_ptr()), self._stream(stream))
+        rc = self.lib.ca_attend(*args)
+        if rc == -7:
+            # the tree outgrew the workspace (nothing was launched): grow it
+            self.ensure_workspace()
+            rc = self.lib.ca_attend(*args)
+        check(self.ctx, rc)
         return out
 
     def decode_step(self, tokens, k, v, q, out=None, stream=None):
@@ -200,11 +204,11 @@ class ChunkAttention:
             raise ValueError("one token per live sequence")
         kp, vp = self._kv(k, v, len(t))
         q, out = self._qo(q, out)
-        self.ensure_workspace()
         rc = self.lib.ca_decode_step(self.ctx, _ptr_i32(t), kp, vp, ctypes.c_void_p(q.data_ptr()),
                                      ctypes.c_void_p(out.data_ptr()), self._stream(stream))
         if rc == -7:
-            # the tokens are stored; the new chunks need a larger workspace
+            # the tokens are stored; the tree outgrew the workspace: grow it
+            # and run the step's attention
             self.ensure_workspace()
             return self.attend(q, out, stream)
         check(self.ctx, rc)
