@@ -171,12 +171,19 @@ void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<
 
 void Manager::append_batch(const int64_t* seqs, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops) {
   if (n < 1 || seqs == nullptr || tokens == nullptr) throw Error(kInvalidArg, "append batch needs n >= 1");
-  std::map<int64_t, int32_t> seen;
+  // The first offending entry decides the error (an unknown id before a
+  // repeat at the same position); repeats are found by sorting (id, position).
+  std::vector<std::pair<int64_t, int32_t>> order(static_cast<size_t>(n));
+  for (int32_t j = 0; j < n; ++j) order[j] = {seqs[j], j};
+  std::sort(order.begin(), order.end());
+  int32_t first_repeat = n;
+  for (int32_t j = 1; j < n; ++j)
+    if (order[j].first == order[j - 1].first) first_repeat = std::min(first_repeat, order[j].second);
   int64_t need = 0;
   for (int32_t j = 0; j < n; ++j) {
     auto it = end_.find(seqs[j]);
     if (it == end_.end()) throw Error(kUnknownSeq, "sequence id not live: " + std::to_string(seqs[j]));
-    if (!seen.emplace(seqs[j], j).second) throw Error(kInvalidArg, "sequence id repeated in a batch");
+    if (j == first_repeat) throw Error(kInvalidArg, "sequence id repeated in a batch");
     const Node& e = nodes_[it->second];
     if (!(e.ref == 1 && static_cast<int32_t>(e.tokens.size()) < C_)) ++need;
   }
