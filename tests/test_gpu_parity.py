@@ -686,20 +686,21 @@ def test_one_sequence_of_65536_tokens():
     assert_parity(run_step(ca, wl.q), A.decode_workload(wl), "65536 tokens")
 
 
-def test_256_sequences_one_launch():
+@pytest.mark.parametrize("chunk", [32, 64, 128])
+def test_256_sequences_one_launch(chunk):
     """A large batch: 256 sequences x 16 heads (4,096 merges, so the default
     step is one launch) sharing a 2,048-token prefix, private suffixes of
-    1..300 tokens; sampled rows against the oracle, all rows against the
-    two-launch step bit for bit."""
-    _say("256 sequences, one launch")
+    1..300 tokens, at each chunk size; sampled rows against the oracle, all
+    rows against the two-launch step bit for bit."""
+    _say(f"256 sequences, one launch, chunk {chunk}")
     from decode_attention_prefix_tree_amd import _capi
     rng = np.random.default_rng(256)
     wl = make_prefix_suffix(2048, [int(x) for x in rng.integers(1, 301, size=256)], heads=16, seed=257)
-    ca = build_ca(wl)
+    ca = build_ca(wl, chunk=chunk)
     assert ca.stats()["one_launch_step"] == 1
     got = run_step(ca, wl.q)
     rows = sorted({0, 1, 127, 128, 254, 255} | set(int(x) for x in rng.choice(256, 18, replace=False)))
-    assert_parity(got[rows], A.decode_workload(wl, rows), "256 seq sampled")
+    assert_parity(got[rows], A.decode_workload(wl, rows), f"256 seq sampled, chunk {chunk}")
     assert np.isfinite(got).all()
     ca.set_option(_capi.CA_OPT_FUSED_MERGE, 0)
     assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
