@@ -353,7 +353,7 @@ void run_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* 
   for (size_t i = 0; i < ops.size(); ++i) {
     tile_pieces(ops[i], c->chunk, &pieces);
     patch_of.resize(pieces.size(), -1);
-    if (!patches.empty()) patch_of.back() = static_cast<int32_t>(i);
+    if (!patches.empty() && !pieces.empty()) patch_of.back() = static_cast<int32_t>(i);
   }
   chunkattn::KvOpBatch batch{};
   chunkattn::TablePatches tp{};

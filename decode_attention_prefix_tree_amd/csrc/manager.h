@@ -140,7 +140,8 @@ class Manager {
   int chunk() const { return C_; }
   // The kernels read 64-key tiles: a chunk of C > 64 tokens is C / 64 tiles
   // (slot s owns tiles s * C / 64 ...), of which the plan lists those that
-  // hold tokens.
+  // hold tokens; a chunk of 32 is half of tile s / 2 and its ref carries s
+  // itself (the kernels find the tile and the half).
   int32_t tiles_of(int32_t fill) const { return C_ > kTileKeys ? std::max(1, (fill + kTileKeys - 1) / kTileKeys) : 1; }
   int32_t tile_slot(int32_t slot, int32_t t) const { return C_ > kTileKeys ? slot * (C_ / kTileKeys) + t : slot; }
   int32_t tile_fill(int32_t fill, int32_t t) const {
