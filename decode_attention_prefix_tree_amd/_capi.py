@@ -20,6 +20,7 @@ CA_CREATE_NO_CHUNK_FIRST = 2
 CA_OPT_CF_CHUNKS_PER_TASK = 1
 CA_OPT_SF_CHUNKS_PER_TASK = 2
 CA_OPT_FUSED_MERGE = 3
+CA_OPT_MERGE_POLL_LIMIT = 4
 CA_PHASE_CHUNK_FIRST = 1
 CA_PHASE_SEQUENCE_FIRST = 2
 CA_PHASE_MERGE = 3

@@ -27,6 +27,7 @@ struct ca_ctx {
   int cf_auto = 8;                 // the last automatic choice
   int plan_cf_group = 8;           // the group the current plan was built with
   int fused_merge = 2;              // CA_OPT_FUSED_MERGE: 0 two launches, 1 one launch, 2 chosen per plan
+  int merge_poll_limit = 0;         // CA_OPT_MERGE_POLL_LIMIT (0: the kernels' own bound)
   unsigned fuse_epoch = 0;          // one-launch steps since the last table upload
   unsigned decode_epoch = 0;        // ca_decode_step launches that grew chunks in the kernel
 
@@ -266,6 +267,7 @@ chunkattn::StepArgs step_args(ca_ctx* c, const void* q, void* out) {
   a.app_v = nullptr;
   a.app_epoch = 0;
   a.half_tiles = c->chunk < chunkattn::kTileKeys ? 1 : 0;
+  a.max_polls = c->merge_poll_limit;
   return a;
 }
 
@@ -502,6 +504,9 @@ int ca_set_option(ca_ctx* ctx, int option, int value) {
     } else if (option == CA_OPT_SF_CHUNKS_PER_TASK) {
       if (value < 0 || value > 256) throw Error(CA_E_INVALID_ARG, "sequence-first group must be 0 (auto) or 1..256");
       ctx->sf_group = value;
+    } else if (option == CA_OPT_MERGE_POLL_LIMIT) {
+      if (value < 0) throw Error(CA_E_INVALID_ARG, "merge poll limit must be >= 0");
+      ctx->merge_poll_limit = value;
     } else if (option == CA_OPT_FUSED_MERGE) {
       if (value < 0 || value > 2) throw Error(CA_E_INVALID_ARG, "fused merge is 0, 1 or 2 (automatic)");
       ctx->fused_merge = value;

@@ -56,6 +56,9 @@ struct StepArgs {
   // Chunks of 32 tokens: chunk slot s is half s % 2 (keys 32 * (s % 2) ..
   // +32) of tile s / 2, and a chunk ref's slot field is s.
   int half_tiles;
+  // One-launch step: polls a merge wave makes before it gives up and writes
+  // NaN (0: the built-in bound, about 0.1 s).
+  int max_polls;
 };
 
 // Which blocks of the partials kernel to launch.

@@ -264,8 +264,9 @@ __device__ __forceinline__ void merge_block(const StepArgs& a, int mb, unsigned 
   // the first poll goes out with the loads of cnt and qrow
   unsigned seen = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   bool ok = true;
+  const int limit = a.max_polls > 0 ? a.max_polls : kMaxPolls;
   for (int tries = 0; static_cast<int>(seen - target) < 0; ++tries) {
-    if (tries == kMaxPolls) {
+    if (tries == limit) {
       ok = false;
       break;
     }

@@ -85,7 +85,7 @@ enum {
                                     (default): chosen per plan, the largest of 16, 8 and 4 that
                                     still gives the step about 2.5 rounds of blocks over the
                                     chip's resident block slots (ca_stats reports the choice) */
-  CA_OPT_FUSED_MERGE = 3         /* 0: a step is a partials launch and a merge launch.
+  CA_OPT_FUSED_MERGE = 3,        /* 0: a step is a partials launch and a merge launch.
                                     1: one launch whose grid ends with merge blocks; each waits
                                     until the partials of its (sequence, head) are written (all
                                     by blocks earlier in the grid) and merges them.
@@ -93,6 +93,11 @@ enum {
                                     (sequence, head) pairs, else two (measured crossover on
                                     MI355X).  All give the same bits; ca_stats reports the
                                     choice for the current tree. */
+  CA_OPT_MERGE_POLL_LIMIT = 4    /* one-launch step: how many times a merge wave checks that
+                                    its partials have arrived before it gives up and writes
+                                    NaN for its (sequence, head); 0 (default): the library's
+                                    own bound (about 0.1 s, never reached in practice).  For
+                                    exercising that failure path. */
 };
 
 /* ca_attend_phase phases.  A step is CA_PHASE_PARTIALS (one launch holding

@@ -745,3 +745,31 @@ def test_decode_step_growing_chunk_past_inline_refs(chunk):
             assert_parity(rb.cpu().numpy(), A.decode_step(q, kv), f"decode past inline chunk {chunk} step {step}")
     st = b.stats()
     assert st["sf_chunks_per_task"] == 16 and st["patched_appends"] >= 40, st
+
+
+def test_one_launch_merge_that_gives_up_writes_nan():
+    """The one-launch step's merge waits for its partials for a bounded number
+    of polls.  With the bound cut to one poll from the host, merge waves whose
+    producers are still running give up: every (sequence, head) is then either
+    the two-launch result bit for bit or all NaN, never a merge of incomplete
+    partials.  With the default bound restored the next step is exact."""
+    _say("one-launch merge with a one-poll wait")
+    from decode_attention_prefix_tree_amd import _capi
+    wl = cached_config(2)
+    ca = build_ca(wl)
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 0)
+    ref = run_step(ca, wl.q)
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, 1)
+    ca.set_option(_capi.CA_OPT_MERGE_POLL_LIMIT, 1)
+    got = run_step(ca, wl.q)
+    nan_pairs = 0
+    for s_ in range(wl.n_seq):
+        for h in range(wl.heads):
+            if np.isnan(got[s_, h].astype(np.float32)).all():
+                nan_pairs += 1
+            else:
+                assert np.array_equal(got[s_, h].view(np.uint16), ref[s_, h].view(np.uint16)), (s_, h)
+    _say(f"pairs that gave up: {nan_pairs} of {wl.n_seq * wl.heads}")
+    ca.set_option(_capi.CA_OPT_MERGE_POLL_LIMIT, 0)
+    for _ in range(2):
+        assert np.array_equal(run_step(ca, wl.q).view(np.uint16), ref.view(np.uint16))
