@@ -773,3 +773,52 @@ def test_one_launch_merge_that_gives_up_writes_nan():
     ca.set_option(_capi.CA_OPT_MERGE_POLL_LIMIT, 0)
     for _ in range(2):
         assert np.array_equal(run_step(ca, wl.q).view(np.uint16), ref.view(np.uint16))
+
+
+def test_random_trees_options_and_decode_steps():
+    """30 seeded random trees (1..40 sequences, each a prefix of an earlier one
+    cut anywhere plus a fresh tail, so divergences split chunks at every
+    depth) at random chunk sizes, head counts, launch modes, task groups and
+    with or without the chunk-first phase; each attended and then advanced by
+    up to three decode steps, every result against the oracle."""
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import ChunkAttention, load_workload, slots_needed, _capi
+    rng = np.random.default_rng(4242)
+    for case in range(30):
+        seqs = []
+        for i in range(int(rng.integers(1, 41))):
+            if seqs and rng.random() < 0.7:
+                parent = seqs[int(rng.integers(0, len(seqs)))]
+                cut = int(rng.integers(0, len(parent) + 1))
+            else:
+                parent, cut = [], 0
+            seqs.append(parent[:cut] + [10000 + i] + [int(x) for x in rng.integers(0, 6, size=int(rng.integers(0, 400)))])
+        heads = int(rng.choice([1, 2, 3, 5, 8]))
+        chunk = int(rng.choice([32, 64, 128]))
+        fused, cfg, sfg = int(rng.choice([0, 1, 2])), int(rng.choice([0, 1, 2, 4, 16])), int(rng.choice([0, 1, 3, 4, 16]))
+        two_phase = bool(rng.random() < 0.85)
+        label = (f"random case {case}: {len(seqs)} seq, {heads} heads, chunk {chunk}, fused {fused}, "
+                 f"cf {cfg}, sf {sfg}, two_phase {two_phase}")
+        _say(label)
+        wl = from_token_lists(seqs, heads=heads, seed=int(rng.integers(0, 1 << 30)))
+        ca = ChunkAttention(heads, slots_needed(wl, chunk=chunk) + 8 + 4 * wl.n_seq, device="cuda:0",
+                            two_phase=two_phase, chunk_size=chunk)
+        ca.set_option(_capi.CA_OPT_FUSED_MERGE, fused)
+        ca.set_option(_capi.CA_OPT_CF_CHUNKS_PER_TASK, cfg)
+        ca.set_option(_capi.CA_OPT_SF_CHUNKS_PER_TASK, sfg)
+        load_workload(ca, wl, device="cuda:0")
+        assert_parity(run_step(ca, wl.q), A.decode_workload(wl), label)
+        kv = [[x.copy() for x in wl.seq_kv(i)] for i in range(wl.n_seq)]
+        n = wl.n_seq
+        for step in range(int(rng.integers(0, 4))):
+            k = rng.standard_normal((n, heads, 128), dtype=np.float32).astype(np.float16)
+            v = rng.standard_normal((n, heads, 128), dtype=np.float32).astype(np.float16)
+            q = rng.standard_normal((n, heads, 128), dtype=np.float32).astype(np.float16)
+            toks = (3 * 10**6 + step * 1000 + np.arange(n)).astype(np.int32)
+            out = ca.decode_step(toks, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), torch.from_numpy(q).cuda())
+            torch.cuda.synchronize()
+            for i in range(n):
+                kv[i][0] = np.concatenate([kv[i][0], k[i:i + 1]])
+                kv[i][1] = np.concatenate([kv[i][1], v[i:i + 1]])
+            assert_parity(out.cpu().numpy(), A.decode_step(q, kv), f"{label}, decode step {step}")
+        del ca
