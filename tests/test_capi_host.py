@@ -383,6 +383,13 @@ def test_launch_mode_follows_merge_pair_count():
     assert small.stats()["one_launch_step"] == 1
     with pytest.raises(CaError):
         small.set_option(_capi.CA_OPT_FUSED_MERGE, 3)
+    # the merge's poll bound: 0 (the library's own) or any positive count
+    for value in (1, 1000, 0):
+        small.set_option(_capi.CA_OPT_MERGE_POLL_LIMIT, value)
+    with pytest.raises(CaError):
+        small.set_option(_capi.CA_OPT_MERGE_POLL_LIMIT, -1)
+    with pytest.raises(CaError):
+        small.set_option(99, 0)
 
 
 def test_partial_slots_compact_when_dense_would_waste_memory():
