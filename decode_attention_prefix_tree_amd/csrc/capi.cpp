@@ -445,7 +445,9 @@ int ca_create_ex(int heads, int head_dim, int chunk_size, int flags, ca_ctx** ou
   if (out == nullptr) return CA_E_INVALID_ARG;
   *out = nullptr;
   if (heads < 1) return CA_E_INVALID_ARG;
-  if (head_dim != chunkattn::kHeadDim || (chunk_size != 32 && chunk_size != 64 && chunk_size != 128))
+  // Any chunk size up to 64 (or 128) for the tree and tables; a device pool
+  // needs 32, 64 or 128 (ca_attach_pool).
+  if (head_dim != chunkattn::kHeadDim || chunk_size < 1 || (chunk_size > 64 && chunk_size != 128))
     return CA_E_UNSUPPORTED;
   if (flags & ~(CA_CREATE_UNSHARED | CA_CREATE_NO_CHUNK_FIRST)) return CA_E_UNSUPPORTED;
   try {
@@ -465,11 +467,13 @@ void ca_destroy(ca_ctx* ctx) { delete ctx; }
 int ca_attach_pool(ca_ctx* ctx, void* dev, int64_t capacity_slots) {
   CA_GUARD(ctx, {
     if (capacity_slots < 0) throw Error(CA_E_INVALID_ARG, "negative capacity");
+    if (dev != nullptr && ctx->chunk != 32 && ctx->chunk != 64 && ctx->chunk != 128)
+      throw Error(CA_E_UNSUPPORTED, "a device pool needs chunk size 32, 64 or 128");
     if (dev != nullptr && (reinterpret_cast<uintptr_t>(dev) % kAlign) != 0)
       throw Error(CA_E_INVALID_ARG, "pool must be 256-byte aligned");
     // Chunks of 32 pair up in 64-key tiles and a tile spans every head, so
     // the slots are used in pairs: an odd last slot is left out.
-    ctx->mgr.set_capacity(ctx->chunk < chunkattn::kTileKeys ? capacity_slots & ~int64_t{1} : capacity_slots);
+    ctx->mgr.set_capacity(ctx->chunk == 32 ? capacity_slots & ~int64_t{1} : capacity_slots);
     ctx->pool = dev;
     ctx->pool_attached = true;
     touch(ctx);

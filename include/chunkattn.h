@@ -147,8 +147,10 @@ typedef struct ca_stats_t {
  * * head_dim.  Returns 0 for non-positive arguments. */
 size_t ca_slot_bytes(int heads, int head_dim, int chunk_size);
 
-/* Create a context.  heads >= 1; head_dim must be 128 and chunk_size 32, 64
- * or 128 (else CA_E_UNSUPPORTED).  Scale is 1/sqrt(head_dim) computed in fp32.
+/* Create a context.  heads >= 1; head_dim must be 128 and chunk_size 1..64 or
+ * 128 (else CA_E_UNSUPPORTED); a device pool (ca_attach_pool) further needs
+ * chunk_size 32, 64 or 128, other sizes serve host-only contexts (tree and
+ * tables).  Scale is 1/sqrt(head_dim) computed in fp32.
  * *out receives the context; the caller owns it and frees it with
  * ca_destroy. */
 int ca_create(int heads, int head_dim, int chunk_size, ca_ctx** out);
@@ -160,9 +162,10 @@ void ca_destroy(ca_ctx* ctx);
  * tiles, tile-major, then head, then K tile and V tile of 64 x 128 fp16 each
  * (tile element order is private to the library); a slot of 64 tokens is one
  * tile, of 128 two, and two slots of 32 share one.  With chunk_size 32 the
- * slots are used in pairs: an odd last slot is left out of the capacity.  dev may be NULL: the context
- * then manages the tree and tables on the host only and every call that
- * needs the device returns CA_E_NO_POOL.  Allowed only while no sequence is
+ * slots are used in pairs: an odd last slot is left out of the capacity.
+ * dev may be NULL: the context then manages the tree and tables on the host
+ * only and every call that needs the device returns CA_E_NO_POOL.  A device
+ * pool needs chunk_size 32, 64 or 128 (CA_E_UNSUPPORTED otherwise).  Allowed only while no sequence is
  * live (CA_E_STATE otherwise).  The caller keeps the memory alive and owns it. */
 int ca_attach_pool(ca_ctx* ctx, void* dev, int64_t capacity_slots);
 

@@ -27,11 +27,16 @@ def test_create_rejects_unsupported_shapes():
     lib = _capi.load()
     ctx = ctypes.c_void_p()
     assert lib.ca_create(8, 64, 64, ctypes.byref(ctx)) == -2
-    assert lib.ca_create(8, 128, 16, ctypes.byref(ctx)) == -2
-    assert lib.ca_create(8, 128, 96, ctypes.byref(ctx)) == -2
+    for c in (0, 65, 96, 129):
+        assert lib.ca_create(8, 128, c, ctypes.byref(ctx)) == -2
     for c in (32, 128):
         assert lib.ca_create(8, 128, c, ctypes.byref(ctx)) == 0
         lib.ca_destroy(ctx)
+    # any size up to 64 serves the tree and tables; a device pool needs 32, 64 or 128
+    assert lib.ca_create(8, 128, 3, ctypes.byref(ctx)) == 0
+    assert lib.ca_attach_pool(ctx, None, 10) == 0
+    assert lib.ca_attach_pool(ctx, ctypes.c_void_p(1 << 20), 10) == -2
+    lib.ca_destroy(ctx)
     assert lib.ca_create(0, 128, 64, ctypes.byref(ctx)) == -1
     assert lib.ca_create_ex(8, 128, 64, 0x100, ctypes.byref(ctx)) == -2
     assert lib.ca_slot_bytes(32, 128, 64) == 4 * 32 * 64 * 128
@@ -488,3 +493,52 @@ def test_automatic_sequence_first_group(case, want):
     assert ca.stats()["sf_chunks_per_task"] == want
     with pytest.raises(CaError):
         ca.set_option(_capi.CA_OPT_SF_CHUNKS_PER_TASK, 257)
+
+
+@pytest.mark.parametrize("chunk", [2, 3, 4])
+def test_tiny_chunks_random_ops_bit_exact_against_model(chunk):
+    """Chunks of 2, 3 and 4 tokens, a vocabulary of 2 or 3 and sequences of at
+    most 12 tokens, with inserts, appends (single and batched) and removals
+    interleaved: nearly every call splits, shares or opens chunks.  Tables,
+    DFS order, counts and free slots bit for bit equal to the tree model; a
+    failing call (unknown id, no capacity) fails alike and changes nothing.
+    A batch of appends is all or nothing: the model applies it to a copy."""
+    import copy
+    rng = np.random.default_rng(100 + chunk)
+    for trial in range(40):
+        vocab = int(rng.integers(2, 4))
+        cap = int(rng.integers(8, 60))
+        share = bool(rng.random() < 0.9)
+        m = PrefixTreeModel(chunk, cap, share)
+        ca = ChunkAttention(2, cap, device=None, share=share, chunk_size=chunk)
+        for step in range(60):
+            live = m.sequences()
+            r = rng.random()
+            toks = [int(x) for x in rng.integers(0, vocab, size=int(rng.integers(1, 13)))]
+            if r < 0.4 or not live:
+                kind, args = "insert", (int(rng.integers(0, 30)), toks)
+            elif r < 0.6:
+                kind, args = "append", (int(rng.choice(live)), toks[:int(rng.integers(1, 4))])
+            elif r < 0.8:
+                batch = [int(x) for x in rng.choice(live, size=int(rng.integers(1, len(live) + 1)), replace=False)]
+                kind, args = "append_batch", (batch, [int(x) for x in rng.integers(0, vocab, size=len(batch))])
+            else:
+                kind, args = "remove", (int(rng.choice(live)),)
+            try:
+                if kind == "append_batch":
+                    trial_model = copy.deepcopy(m)
+                    for sid, t in zip(*args):
+                        trial_model.append(sid, [t])
+                    m = trial_model
+                else:
+                    getattr(m, kind)(*args)
+                want = None
+            except TreeError as e:
+                want = e.code
+            try:
+                getattr(ca, kind)(*args)
+                got = None
+            except CaError as e:
+                got = e.name
+            assert got == want, (chunk, trial, step, kind)
+            model_and_lib_agree(m, ca)
