@@ -822,3 +822,49 @@ def test_random_trees_options_and_decode_steps():
                 kv[i][1] = np.concatenate([kv[i][1], v[i:i + 1]])
             assert_parity(out.cpu().numpy(), A.decode_step(q, kv), f"{label}, decode step {step}")
         del ca
+
+
+def test_workspace_too_small():
+    """With a workspace below ca_workspace_bytes, ca_attend returns
+    CA_E_WORKSPACE and launches nothing; ca_decode_step returns it after the
+    tokens were stored, and attaching a large enough workspace and calling
+    ca_attend finishes that step (oracle over the grown sequences)."""
+    _say("workspace too small")
+    torch = _torch()
+    import ctypes
+    from decode_attention_prefix_tree_amd import ChunkAttention, _capi
+    rng = np.random.default_rng(77)
+    seqs = [list(range(100)) + [500 + i] * int(rng.integers(1, 90)) for i in range(6)]
+    wl = from_token_lists(seqs, heads=2, seed=78)
+    ca = build_ca(wl, capacity=64)
+    lib, ctx = ca.lib, ca.ctx
+    need = ctypes.c_size_t(0)
+    assert lib.ca_workspace_bytes(ctx, ctypes.byref(need)) == 0 and need.value > 4096
+    tiny = torch.empty(4096, dtype=torch.uint8, device="cuda:0")
+    assert lib.ca_attach_workspace(ctx, ctypes.c_void_p(tiny.data_ptr()), tiny.numel()) == 0
+    q = torch.from_numpy(np.ascontiguousarray(wl.q)).cuda()
+    out = torch.zeros_like(q)
+    rc = lib.ca_attend(ctx, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(out.data_ptr()), ca._stream())
+    torch.cuda.synchronize()
+    assert rc == -7 and not out.any()
+    # a decode step: the tokens are stored, the attention is not run
+    n = wl.n_seq
+    k = rng.standard_normal((n, 2, 128), dtype=np.float32).astype(np.float16)
+    v = rng.standard_normal((n, 2, 128), dtype=np.float32).astype(np.float16)
+    q2 = rng.standard_normal((n, 2, 128), dtype=np.float32).astype(np.float16)
+    kt, vt, qt = (torch.from_numpy(x).cuda() for x in (k, v, q2))
+    toks = (ctypes.c_int32 * n)(*range(9000, 9000 + n))
+    before = ca.stats()["unique_tokens"]
+    rc = lib.ca_decode_step(ctx, toks, ctypes.c_void_p(kt.data_ptr()), ctypes.c_void_p(vt.data_ptr()),
+                            ctypes.c_void_p(qt.data_ptr()), ctypes.c_void_p(out.data_ptr()), ca._stream())
+    assert rc == -7
+    assert ca.stats()["unique_tokens"] == before + n
+    assert lib.ca_workspace_bytes(ctx, ctypes.byref(need)) == 0
+    big = torch.empty(need.value, dtype=torch.uint8, device="cuda:0")
+    assert lib.ca_attach_workspace(ctx, ctypes.c_void_p(big.data_ptr()), big.numel()) == 0
+    rc = lib.ca_attend(ctx, ctypes.c_void_p(qt.data_ptr()), ctypes.c_void_p(out.data_ptr()), ca._stream())
+    torch.cuda.synchronize()
+    assert rc == 0
+    kv = [[np.concatenate([a, b[i:i + 1]]) for a, b in zip(wl.seq_kv(i), (k, v))] for i in range(n)]
+    assert_parity(out.cpu().numpy(), A.decode_step(q2, kv), "after growing the workspace")
+    ca.ws = big  # keep it alive with the context
