@@ -59,6 +59,9 @@ def parse():
                     help="decode progression instead: n_s = 2048 shared prompt tokens, one token appended per "
                          "sequence per step (completion length n_c sweep at batch 32, batch sweep at n_c = 512), "
                          "as ca_decode_step and as append + attend, with the shared-pages comparator")
+    ap.add_argument("--decode-only", default=None, metavar="MODE:BATCH:NC",
+                    help="with --decode: one run only, e.g. decode_step:32:512 (modes decode_step, two_phase, "
+                         "shared_pages_no_chunk_first), for profiling one configuration")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the per-kernel timing loop (for rocprofv3 runs); prints its event means")
     ap.add_argument("--phases", action="store_true",
@@ -278,6 +281,15 @@ def decode_main(args, torch):
             "config": {"workload": "n_s = 2048 shared prompt tokens, heads 32, head_dim 128, chunk 64",
                        "cache": "cold (1 GiB read before each timed step)"}}
     modes = (("decode_step", True, True), ("two_phase", True, False), ("shared_pages_no_chunk_first", False, False))
+    if args.decode_only:
+        mode, batch, nc = args.decode_only.split(":")
+        two_phase, one_call = {m[0]: m[1:] for m in modes}[mode]
+        line["config"].update({"mode": mode, "batch": int(batch), "n_c": int(nc)})
+        r = decode_progression(torch, int(batch), 2048, [int(nc)], two_phase, flush, one_call=one_call)[int(nc)]
+        line.update(r)
+        line["value"] = r["generated_tokens_per_s"]
+        print(json.dumps(line), flush=True)
+        return
     for name, two_phase, one_call in modes:
         log(f"decode n_c sweep, {name}")
         line.setdefault("nc_sweep_batch32", {})[name] = decode_progression(
