@@ -432,7 +432,7 @@ def test_dense_and_compact_partial_slots(k):
     assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
 
 
-@pytest.mark.parametrize("heads", [1, 64])
+@pytest.mark.parametrize("heads", [1, 64, 128])
 def test_head_counts(heads):
     """One head and 64 heads (the kernels index heads only through the
     tile base and the record layout): a shared prefix with ragged private
