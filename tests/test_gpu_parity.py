@@ -2,8 +2,7 @@
 
 Bar (elementwise): |gpu - oracle| <= 2e-3 + 1e-2 * |oracle| for fp16 I/O with
 fp32 accumulation; rel-L2 is also reported and gated at 1e-3.  Cases: the
-five seeded workloads at full size (all rows for 1-4, a row sample for the
-multi-branch tree), tiny trees that exercise padded MFMA rows (ranges 2-15,
+five seeded workloads at full size (every row), tiny trees that exercise padded MFMA rows (ranges 2-15,
 16, 32, > 32), partial chunks, sequences ending inside the tree, duplicates,
 appends and removals, the unshared comparator layout, and every task-size
 setting.  Inputs come from the seeded generators in ``workloads``."""
@@ -178,20 +177,17 @@ def test_insert_remove_churn():
         assert got_order == want_order, it
 
 
-def test_multi_branch_sampled_rows():
+def test_multi_branch_all_rows():
     """Workload 5 at full size (128 sequences x 32 heads: the default step
-    is one launch) on a sample of rows that covers every branch edge, all rows
-    finite, the same bits from repeated steps and from the two-launch step."""
+    is one launch), every output row against the oracle, then the same bits
+    from repeated steps and from the two-launch step."""
     _say("workload 5")
     from decode_attention_prefix_tree_amd import _capi
     wl = cached_config(5)
     ca = build_ca(wl)
     assert ca.stats()["one_launch_step"] == 1
     got = run_step(ca, wl.q)
-    rows = sorted({0, 31, 32, 63, 64, 95, 96, 127} | set(np.random.default_rng(5).choice(128, 8, replace=False)))
-    ref = A.decode_workload(wl, rows)
-    assert_parity(got[rows], ref, "config5")
-    assert np.isfinite(got).all()
+    assert_parity(got, A.decode_workload(wl), "config5")
     for _ in range(2):
         assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
     ca.set_option(_capi.CA_OPT_FUSED_MERGE, 0)
@@ -690,8 +686,8 @@ def test_one_sequence_of_65536_tokens():
 def test_256_sequences_one_launch(chunk):
     """A large batch: 256 sequences x 16 heads (4,096 merges, so the default
     step is one launch) sharing a 2,048-token prefix, private suffixes of
-    1..300 tokens, at each chunk size; sampled rows against the oracle, all
-    rows against the two-launch step bit for bit."""
+    1..300 tokens, at each chunk size; every row against the oracle and
+    against the two-launch step bit for bit."""
     _say(f"256 sequences, one launch, chunk {chunk}")
     from decode_attention_prefix_tree_amd import _capi
     rng = np.random.default_rng(256)
@@ -699,9 +695,7 @@ def test_256_sequences_one_launch(chunk):
     ca = build_ca(wl, chunk=chunk)
     assert ca.stats()["one_launch_step"] == 1
     got = run_step(ca, wl.q)
-    rows = sorted({0, 1, 127, 128, 254, 255} | set(int(x) for x in rng.choice(256, 18, replace=False)))
-    assert_parity(got[rows], A.decode_workload(wl, rows), f"256 seq sampled, chunk {chunk}")
-    assert np.isfinite(got).all()
+    assert_parity(got, A.decode_workload(wl), f"256 seq, chunk {chunk}")
     ca.set_option(_capi.CA_OPT_FUSED_MERGE, 0)
     assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
 
