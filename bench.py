@@ -10,15 +10,23 @@ clean lines that cost nothing to evict (a writing flush would leave dirty
 lines whose write-back competes with the step).  Warm (back-to-back) figures
 are reported alongside, labelled.
 
-Prints one JSON line:
+Prints one JSON line.  Its top level is the headline workload (by default
+the multi-branch tree: 128 sequences x 32 heads, a 1,024-token root, four
+1,024-token branches, private suffixes of 64..1,024 tokens):
   value        attended KV tokens/s (sum of sequence lengths / step time)
   roofline     the dominant kernel's unique-KV bytes / its own average
-               duration, against the 8 TB/s HBM peak
+               duration (HIP events on the launching stream), against the
+               8 TB/s HBM peak; traffic as recorded by the counter passes
+               under profiles/ for the same kernel source
   comparator   the same step on the unshared paged layout (every sequence
                keeps its own copy of every chunk; no chunk-first phase)
+  comparator_shared_pages  the prefix stored once but no chunk-first phase
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
+per_config holds the same figures for the other workloads (and the 1,766-token
+prefix, and chunk sizes 32 and 128), decode_point one decode-progression
+point (batch 32, 2,048 shared prompt tokens, 512 completion tokens).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5] [--headline-only]
 """
 
 from __future__ import annotations
@@ -44,10 +52,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: 32 seq, 1024+512)")
+    ap.add_argument("--config", type=int, default=5,
+                    help="headline workload 1..5 (default 5: the multi-branch tree, 128 seq x 32 heads)")
     ap.add_argument("--no-comparator", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample (headline)")
+    ap.add_argument("--cpu-seconds-per-config", type=float, default=4.0,
+                    help="target CPU time of the oracle sample of each other workload")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the headline workload (no per_config entries, no decode point)")
+    ap.add_argument("--no-decode", action="store_true", help="leave out the decode-progression point")
     ap.add_argument("--prefix-len", type=int, default=None,
                     help="instead of a numbered workload: --n-seq sequences x 32 heads with this shared prefix "
                          "length (any length, e.g. 1766) and --suffix-len private tokens each")
@@ -273,6 +288,53 @@ def decode_progression(torch, n_seq, n_shared, checkpoints, two_phase, flush, wi
     return res
 
 
+def decode_host_overlap(torch, n_seq, n_shared, n_steps, prebuild, heads=32, seed=11):
+    """Decode steps as a sampling loop runs them: after each ca_decode_step the
+    host waits for the GPU (the next token would come from that step's
+    output).  Per step: the host time of the call and the wall time from call
+    to finished step, split into structural steps (a chunk filled up: the
+    table changes shape and is uploaded), the steps just before them (which,
+    with the prebuild on, also build the next table after their launch,
+    while the GPU runs) and the other fill-only steps."""
+    from decode_attention_prefix_tree_amd import ChunkAttention, _capi
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    cap = (n_shared + 63) // 64 + n_seq * ((n_steps + 63) // 64 + 1) + 8
+    ca = ChunkAttention(heads, cap, device="cuda:0")
+    ca.set_option(_capi.CA_OPT_PREBUILD_PLAN, 1 if prebuild else 0)
+    ks = torch.randn((n_shared, heads, 128), generator=gen, device="cuda").half()
+    prompt = np.arange(n_shared, dtype=np.int32)
+    for i in range(n_seq):
+        ca.insert(i, prompt, ks, ks)
+    out = torch.empty((n_seq, heads, 128), dtype=torch.float16, device="cuda")
+    ca.ensure_workspace()
+    k = torch.randn((n_seq, heads, 128), generator=gen, device="cuda").half()
+    q = torch.randn((n_seq, heads, 128), generator=gen, device="cuda").half()
+    ca.attend(q, out)
+    torch.cuda.synchronize()
+    rows = []
+    toks = np.zeros(n_seq, np.int32)
+    for c in range(1, n_steps + 1):
+        toks[:] = c
+        t0 = time.perf_counter()
+        ca.decode_step(toks, k, k, q, out)
+        t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        # the prompt fills whole chunks, so every 64th append opens new chunks
+        kind = "structural" if (c - 1) % 64 == 0 else "before_structural" if c % 64 == 0 else "fill_only"
+        rows.append((kind, (t1 - t0) * 1e6, (t2 - t0) * 1e6))
+    st = ca.stats()
+    del ca
+    torch.cuda.synchronize()
+    res = {"prebuild": bool(prebuild), "steps": n_steps, "prebuilt_plans": st["prebuilt_plans"],
+           "table_uploads": st["table_uploads"]}
+    for name in ("structural", "before_structural", "fill_only"):
+        sel = [r for r in rows[1:] if r[0] == name]  # the first step warms up
+        res[name] = {"steps": len(sel), "call_us": float(np.mean([r[1] for r in sel])) if sel else None,
+                     "wall_us": float(np.mean([r[2] for r in sel])) if sel else None}
+    return res
+
+
 def decode_main(args, torch):
     flush = Flusher(torch)
     line = {"metric": "decode progression: generated tokens/s (ca_decode_step: one token per sequence "
@@ -309,6 +371,120 @@ def decode_main(args, torch):
     print(json.dumps(line), flush=True)
 
 
+def step_stats(ms):
+    """mean / p10 / p50 / p90 in microseconds of per-step event times (ms)."""
+    return {"mean": float(ms.mean()) * 1e3, "p10": float(np.percentile(ms, 10)) * 1e3,
+            "p50": float(np.median(ms)) * 1e3, "p90": float(np.percentile(ms, 90)) * 1e3}
+
+
+def comparator(torch, wl, q, steps, warmup, flush, t_ours, seg_cache, kind, **kw):
+    """The same step on another layout of the same workload, timed the same way."""
+    from decode_attention_prefix_tree_amd import ChunkAttention, load_workload, slots_needed
+    cmp_ca = ChunkAttention(wl.heads, slots_needed(wl, share=kw.get("share", True)) + 8, device="cuda:0", **kw)
+    load_workload(cmp_ca, wl, segments=seg_cache)
+    cmp_ca.ensure_workspace()
+    out2 = torch.empty_like(q)
+
+    def cstep():
+        cmp_ca.attend(q, out2)
+
+    for _ in range(warmup):
+        cstep()
+    cc = time_steps(torch, cstep, steps, flush)
+    tc = float(cc.mean()) * 1e-3
+    cst = cmp_ca.stats()
+    res = {"kind": kind, "ms_per_step": tc * 1e3, "attended_tokens_per_s": cst["attended_tokens"] / tc,
+           "stored_kv_gbps": cst["unique_kv_bytes"] / tc / 1e9,
+           # bytes the kernels ask for, counting every re-read of a shared chunk;
+           # caches (L2, Infinity Cache) serve many of them, so this is not HBM traffic
+           "logical_kv_read_gbps": (cst["sf_chunk_reads"] + cst["cf_chunk_reads"]) * 4 * 64 * wl.heads * 128
+           / tc / 1e9,
+           "speedup": tc / t_ours}
+    del cmp_ca
+    torch.cuda.synchronize()
+    return res
+
+
+def measure(torch, args, wl, flush, full, seg_cache, chunk=64, comparators=True, cpu_seconds=None):
+    """One workload: the step timed cold over args.steps steps (after
+    args.warmup untimed ones), its launches timed apart, the comparators and
+    the oracle on the host.  full: also warm steps and the phases alone."""
+    from decode_attention_prefix_tree_amd import ChunkAttention, _capi, load_workload, slots_needed
+    ca = ChunkAttention(wl.heads, slots_needed(wl, chunk=chunk) + 8, device="cuda:0", chunk_size=chunk)
+    load_workload(ca, wl, segments=seg_cache)
+    q = torch.from_numpy(wl.q).cuda()
+    out = torch.empty_like(q)
+    ca.ensure_workspace()
+    st = ca.stats()
+    torch.cuda.synchronize()
+
+    def step():
+        ca.attend(q, out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    cold = time_steps(torch, step, args.steps, flush)
+    wall = time.perf_counter() - wall0
+    one_launch = bool(st["one_launch_step"])
+    lt = time_launches(torch, ca, q, out, args.steps, flush, (_capi.CA_PHASE_PARTIALS, _capi.CA_PHASE_MERGE))
+    unique_b = st["unique_kv_bytes"]
+    t_mean = float(cold.mean()) * 1e-3
+    # The dominant kernel: the partials launch (chunk-first and sequence-first
+    # blocks in one grid), or, in the one-launch step, that launch with the
+    # merge blocks, which is the whole step.  Algorithmic bytes per launch: the
+    # unique KV bytes (each shared chunk once, each private chunk once).
+    dom_t = t_mean if one_launch else float(lt[:, 0].mean()) * 1e-3
+    res = {
+        "workload": wl.description, "n_seq": wl.n_seq, "heads": wl.heads, "chunk": chunk,
+        "launches_per_step": 1 if one_launch else 2,
+        "cf_chunks_per_task": st["cf_chunks_per_task"], "sf_chunks_per_task": st["sf_chunks_per_task"],
+        "step_us": step_stats(cold),
+        "attended_tokens_per_s": st["attended_tokens"] / t_mean,
+        "unique_kv_gbps": unique_b / t_mean / 1e9,
+        "frac": unique_b / t_mean / 1e9 / HBM_PEAK_GBPS,
+        "queries_per_s": wl.n_seq / t_mean,
+        "dominant_kernel": {"kernel": "partials_kernel" + (" (one-launch step, merge blocks included)"
+                                                           if one_launch else ""),
+                            "avg_launch_us": dom_t * 1e6, "gbps": unique_b / dom_t / 1e9,
+                            "frac": unique_b / dom_t / 1e9 / HBM_PEAK_GBPS},
+        "launch_us_two_launch_form": {"partials_kernel": float(lt[:, 0].mean()) * 1e3,
+                                      "merge_kernel": float(lt[:, 1].mean()) * 1e3},
+        "tokens": {"attended": st["attended_tokens"], "unique": st["unique_tokens"],
+                   "shared": st["shared_tokens"], "private": st["private_tokens"]},
+        "unique_kv_bytes": unique_b,
+        "timed_wall_s": wall,
+    }
+    if full:
+        per_tok = 4 * wl.heads * wl.head_dim
+        warm = time_steps(torch, step, args.steps)
+        ph = time_launches(torch, ca, q, out, args.steps, flush,
+                           (_capi.CA_PHASE_CHUNK_FIRST, _capi.CA_PHASE_SEQUENCE_FIRST))
+        res["warm_step_us"] = {"mean": float(warm.mean()) * 1e3, "p50": float(np.median(warm)) * 1e3,
+                               "unique_kv_gbps": unique_b / (float(warm.mean()) * 1e-3) / 1e9}
+        res["phase_alone_us"] = {"chunk_first": float(ph[:, 0].mean()) * 1e3,
+                                 "sequence_first": float(ph[:, 1].mean()) * 1e3,
+                                 "sequence_first_gbps": st["private_tokens"] * per_tok
+                                 / (float(ph[:, 1].mean()) * 1e-3) / 1e9}
+    del ca
+    torch.cuda.synchronize()
+    if comparators and not args.no_comparator:
+        log("  comparator: unshared paged layout")
+        res["comparator"] = comparator(
+            torch, wl, q, args.steps, args.warmup, flush, t_mean, seg_cache,
+            "unshared paged decode (own HIP kernel, every sequence keeps its own 64-token blocks)", share=False)
+        log("  comparator: shared pages, no chunk-first phase")
+        res["comparator_shared_pages"] = comparator(
+            torch, wl, q, args.steps, args.warmup, flush, t_mean, seg_cache,
+            "shared pages without two-phase partition (prefix stored once, every sequence streams its "
+            "whole path)", two_phase=False)
+    if cpu_seconds and not args.no_cpu_baseline:
+        log("  cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(wl, cpu_seconds)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -333,27 +509,26 @@ def main():
         wl = make_config(args.config)
         workload_name = CONFIG_NAMES[args.config]
     log(f"building workload {workload_name}")
-    ca = ChunkAttention(wl.heads, slots_needed(wl, chunk=args.chunk) + 8, device="cuda:0", chunk_size=args.chunk)
-    load_workload(ca, wl)
-    q = torch.from_numpy(wl.q).cuda()
-    out = torch.empty_like(q)
-    ca.ensure_workspace()
-    st = ca.stats()
-    torch.cuda.synchronize()
     flush = Flusher(torch)
 
-    def step():
-        ca.attend(q, out)
-
-    log("warmup")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    from decode_attention_prefix_tree_amd import _capi
-    step_launches = (_capi.CA_PHASE_PARTIALS, _capi.CA_PHASE_MERGE)
-    one_launch = bool(st["one_launch_step"])
     if args.profile_only:
+        from decode_attention_prefix_tree_amd import _capi
+        ca = ChunkAttention(wl.heads, slots_needed(wl, chunk=args.chunk) + 8, device="cuda:0",
+                            chunk_size=args.chunk)
+        load_workload(ca, wl)
+        q = torch.from_numpy(wl.q).cuda()
+        out = torch.empty_like(q)
+        ca.ensure_workspace()
+        st = ca.stats()
+        torch.cuda.synchronize()
+
+        def step():
+            ca.attend(q, out)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        one_launch = bool(st["one_launch_step"])
         if one_launch and not args.phases:
             # the step is one launch (merge blocks close the partials grid)
             names = ("partials_kernel (one-launch step)",)
@@ -364,7 +539,7 @@ def main():
                                (_capi.CA_PHASE_CHUNK_FIRST, _capi.CA_PHASE_SEQUENCE_FIRST, _capi.CA_PHASE_MERGE))
         else:
             names = ("partials_kernel", "merge_kernel")
-            lt = time_launches(torch, ca, q, out, args.steps, flush, step_launches)
+            lt = time_launches(torch, ca, q, out, args.steps, flush, (_capi.CA_PHASE_PARTIALS, _capi.CA_PHASE_MERGE))
         # Calibration for hardware byte counters: a plain device copy of a known
         # size (256 MiB read + 256 MiB written), cold like the steps.
         src = torch.ones(1 << 27, dtype=torch.float16, device="cuda")
@@ -379,41 +554,24 @@ def main():
                           "steps": args.steps, "config": args.config}), flush=True)
         return
 
-    log(f"timing {args.steps} cold steps")
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    cold = time_steps(torch, step, args.steps, flush)
-    wall = time.perf_counter() - wall0
-
-    log("timing warm steps")
-    warm = time_steps(torch, step, args.steps)
-    log("timing launches")
-    lt = time_launches(torch, ca, q, out, args.steps, flush, step_launches)
-    ph = time_launches(torch, ca, q, out, args.steps, flush,
-                       (_capi.CA_PHASE_CHUNK_FIRST, _capi.CA_PHASE_SEQUENCE_FIRST))
-
-    unique_b = st["unique_kv_bytes"]
-    per_tok = 4 * wl.heads * wl.head_dim
-    shared_b = st["shared_tokens"] * per_tok
-    private_b = st["private_tokens"] * per_tok
-    t_mean = float(cold.mean()) * 1e-3
-    value = st["attended_tokens"] / t_mean
-
-    # The dominant kernel: the partials launch of a step (chunk-first and
-    # sequence-first blocks in one grid; in the one-launch step it also holds
-    # the merge blocks, and the step is that launch).  Its algorithmic bytes
-    # are the unique KV bytes (each shared chunk once, each private chunk once).
-    dom_t = t_mean if one_launch else float(lt[:, 0].mean()) * 1e-3
-    roof = {"kernel": "partials_kernel" + (" (one-launch step, merge blocks included)" if one_launch else ""),
-            "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
-            "achieved": unique_b / dom_t / 1e9,
-            "traffic": recorded_traffic(args.config) if args.config and not one_launch else None,
-            "bytes_per_launch": unique_b, "avg_launch_us": dom_t * 1e6}
-    roof["frac"] = roof["achieved"] / HBM_PEAK_GBPS
-
+    log(f"headline: {workload_name}")
+    seg_cache = {}
+    head = measure(torch, args, wl, flush, True, seg_cache, chunk=args.chunk, cpu_seconds=args.cpu_seconds)
+    del seg_cache
+    dom = head["dominant_kernel"]
+    traffic = recorded_traffic(args.config) if args.config and args.chunk == 64 else None
+    roof = {"kernel": dom["kernel"], "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
+            "achieved": dom["gbps"], "frac": dom["gbps"] / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "traffic_source": (f"recorded: profiles/partials_kernel_workload{args.config}_traffic.md "
+                               "(FETCH_SIZE and WRITE_SIZE passes, per launch; its kernel source sha256 "
+                               "matches the sources built here)") if traffic else
+                              "none recorded for this workload and kernel source",
+            "bytes_per_launch": head["unique_kv_bytes"], "avg_launch_us": dom["avg_launch_us"]}
+    t_mean = head["step_us"]["mean"] * 1e-6
     result = {
         "metric": METRIC,
-        "value": value,
+        "value": head["attended_tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -426,61 +584,54 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_name, "n_seq": wl.n_seq, "heads": wl.heads,
                    "head_dim": wl.head_dim, "chunk": args.chunk, "cache": "cold (1 GiB read before each step)",
-                   "cf_chunks_per_task": st["cf_chunks_per_task"], "sf_chunks_per_task": st["sf_chunks_per_task"],
-                   "launches_per_step": 1 if one_launch else 2},
-        "unique_kv_gbps": unique_b / t_mean / 1e9,
-        "hbm_frac_unique": unique_b / t_mean / 1e9 / HBM_PEAK_GBPS,
-        "queries_per_s": wl.n_seq / t_mean,
-        "step_us": {"mean": t_mean * 1e6, "p10": float(np.percentile(cold, 10)) * 1e3,
-                    "p50": float(np.median(cold)) * 1e3, "p90": float(np.percentile(cold, 90)) * 1e3},
-        "warm_step_us": {"mean": float(warm.mean()) * 1e3, "p50": float(np.median(warm)) * 1e3,
-                         "unique_kv_gbps": unique_b / (float(warm.mean()) * 1e-3) / 1e9},
-        "launch_us": {"partials_kernel": float(lt[:, 0].mean()) * 1e3, "merge_kernel": float(lt[:, 1].mean()) * 1e3},
-        "phase_alone_us": {"chunk_first": float(ph[:, 0].mean()) * 1e3, "sequence_first": float(ph[:, 1].mean()) * 1e3,
-                           "sequence_first_gbps": private_b / (float(ph[:, 1].mean()) * 1e-3) / 1e9},
-        "tokens": {"attended": st["attended_tokens"], "unique": st["unique_tokens"],
-                   "shared": st["shared_tokens"], "private": st["private_tokens"]},
-        "timed_wall_s": wall,
+                   "cf_chunks_per_task": head["cf_chunks_per_task"],
+                   "sf_chunks_per_task": head["sf_chunks_per_task"],
+                   "launches_per_step": head["launches_per_step"]},
+        "unique_kv_gbps": head["unique_kv_gbps"],
+        "hbm_frac_unique": head["frac"],
+        "queries_per_s": head["queries_per_s"],
+        "step_us": head["step_us"],
         "roofline": roof,
     }
+    for key in ("warm_step_us", "launch_us_two_launch_form", "phase_alone_us", "tokens", "timed_wall_s",
+                "comparator", "comparator_shared_pages", "cpu_baseline"):
+        if key in head:
+            result[key] = head[key]
+    del wl
 
-    if not args.no_comparator:
-        def comparator(kind, **kw):
-            cmp_ca = ChunkAttention(wl.heads, slots_needed(wl, share=kw.get("share", True)) + 8,
-                                    device="cuda:0", **kw)
-            load_workload(cmp_ca, wl)
-            cmp_ca.ensure_workspace()
-            out2 = torch.empty_like(q)
-
-            def cstep():
-                cmp_ca.attend(q, out2)
-
-            for _ in range(args.warmup):
-                cstep()
-            cc = time_steps(torch, cstep, args.steps, flush)
-            tc = float(cc.mean()) * 1e-3
-            cst = cmp_ca.stats()
-            res = {"kind": kind, "ms_per_step": tc * 1e3, "attended_tokens_per_s": cst["attended_tokens"] / tc,
-                   "stored_kv_gbps": cst["unique_kv_bytes"] / tc / 1e9,
-                   "read_kv_gbps": (cst["sf_chunk_reads"] + cst["cf_chunk_reads"]) * 4 * 64 * wl.heads * 128
-                   / tc / 1e9,
-                   "speedup": tc / t_mean}
-            del cmp_ca
-            torch.cuda.synchronize()
-            return res
-
-        log("comparator: unshared paged layout")
-        result["comparator"] = comparator(
-            "unshared paged decode (own HIP kernel, every sequence keeps its own 64-token blocks)", share=False)
-        log("comparator: shared pages, no chunk-first phase")
-        result["comparator_shared_pages"] = comparator(
-            "shared pages without two-phase partition (prefix stored once, every sequence streams its "
-            "whole path)", two_phase=False)
-
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-
+    if not args.headline_only and args.prefix_len is None:
+        per = {}
+        cases = [(str(k), k, 64) for k in (1, 2, 3, 4, 5) if k != args.config]
+        cases += [("prefix1766", None, 64), ("2_chunk32", 2, 32), ("2_chunk128", 2, 128)]
+        for name, k, chunk in cases:
+            if k is None:
+                # the plugin system prompt of the pages (1,766 tokens) with 512-token suffixes
+                w = make_prefix_suffix(1766, [512] * 32, heads=32, seed=2000 + 1766)
+            else:
+                w = make_config(k)
+            log(f"per config: {name}: {w.description}, chunk {chunk}")
+            cache = {}
+            main_case = chunk == 64
+            per[str(name)] = measure(torch, args, w, flush, False, cache, chunk=chunk, comparators=main_case,
+                                     cpu_seconds=args.cpu_seconds_per_config if main_case else None)
+            del cache, w
+        result["per_config"] = per
+    if not args.headline_only and not args.no_decode:
+        log("decode progression: batch 32, n_s 2048, n_c 512")
+        dec = {}
+        for mode, two_phase, one_call in (("decode_step", True, True), ("append_then_attend", True, False),
+                                          ("shared_pages_no_chunk_first", False, False)):
+            dec[mode] = decode_progression(torch, 32, 2048, [512], two_phase, flush, one_call=one_call)[512]
+        dec["speedup_decode_step_vs_shared_pages"] = (
+            (dec["shared_pages_no_chunk_first"]["append_us"] + dec["shared_pages_no_chunk_first"]["attend_us"])
+            / (dec["decode_step"]["append_us"] + dec["decode_step"]["attend_us"]))
+        result["decode_point"] = {"workload": "32 sequences x 32 heads sharing a 2,048-token prompt, one token "
+                                              "appended per sequence per step, mean over the 16 cold steps "
+                                              "ending at n_c = 512 completion tokens", **dec}
+        log("decode host overlap: batch 32 and 96, 256 steps, waiting for each step")
+        result["decode_host_overlap"] = {
+            f"batch{b}": {("prebuild_on" if pb else "prebuild_off"): decode_host_overlap(torch, b, 2048, 256, pb)
+                          for pb in (True, False)} for b in (32, 96)}
     print(json.dumps(result), flush=True)
 
 

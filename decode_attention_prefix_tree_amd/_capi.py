@@ -21,6 +21,8 @@ CA_OPT_CF_CHUNKS_PER_TASK = 1
 CA_OPT_SF_CHUNKS_PER_TASK = 2
 CA_OPT_FUSED_MERGE = 3
 CA_OPT_MERGE_POLL_LIMIT = 4
+CA_OPT_FAIL_DEVICE_OPS = 5
+CA_OPT_PREBUILD_PLAN = 6
 CA_PHASE_CHUNK_FIRST = 1
 CA_PHASE_SEQUENCE_FIRST = 2
 CA_PHASE_MERGE = 3
@@ -66,6 +68,7 @@ class ca_stats_t(ctypes.Structure):
         ("cf_chunks_per_task", ctypes.c_int64),
         ("one_launch_step", ctypes.c_int64),
         ("sf_chunks_per_task", ctypes.c_int64),
+        ("prebuilt_plans", ctypes.c_int64),
     ]
 
 
@@ -78,6 +81,8 @@ _SIGS = {
     "ca_attach_pool": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64]),
     "ca_workspace_bytes": (_c.c_int, [_c.c_void_p, _c.POINTER(_c.c_size_t)]),
     "ca_attach_workspace": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t]),
+    "ca_staging_bytes": (_c.c_int, [_c.c_void_p, _c.POINTER(_c.c_size_t)]),
+    "ca_attach_staging": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t]),
     "ca_set_option": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int]),
     "ca_insert": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.POINTER(_c.c_int32), _c.c_int32, _c.c_void_p,
                              _c.c_void_p, _c.c_void_p, _c.POINTER(_c.c_int32)]),
@@ -94,6 +99,7 @@ _SIGS = {
     "ca_list_sequences": (_c.c_int, [_c.c_void_p, _c.POINTER(_c.c_int64), _c.c_int]),
     "ca_export_table": (_c.c_int, [_c.c_void_p, _c.POINTER(_c.c_int32), _c.c_int, _c.POINTER(_c.c_int64),
                                    _c.c_int, _c.POINTER(_c.c_int), _c.POINTER(_c.c_int)]),
+    "ca_export_plan": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.POINTER(_c.c_size_t)]),
     "ca_stats": (_c.c_int, [_c.c_void_p, _c.POINTER(ca_stats_t)]),
     "ca_last_error": (_c.c_char_p, [_c.c_void_p]),
 }

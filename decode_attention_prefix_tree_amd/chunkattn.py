@@ -56,6 +56,7 @@ class ChunkAttention:
         self.device = device
         self.pool = None
         self.ws = None
+        self.stage = None
         self._n_live = 0
         if device is None:
             check(self.ctx, self.lib.ca_attach_pool(self.ctx, None, capacity_slots))
@@ -65,6 +66,7 @@ class ChunkAttention:
             self.pool = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
             check(self.ctx, self.lib.ca_attach_pool(self.ctx, ctypes.c_void_p(self.pool.data_ptr()),
                                                    capacity_slots))
+            self._lend_staging(3 << 16)
 
     # -- lifetime -------------------------------------------------------------
     def close(self):
@@ -148,6 +150,14 @@ class ChunkAttention:
             order.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ns.value, ctypes.byref(nr), ctypes.byref(ns)))
         return rows[: nr.value], [int(x) for x in order[: ns.value]]
 
+    def export_plan(self) -> bytes:
+        """The device table image of the current plan (for bit-exact comparisons)."""
+        n = ctypes.c_size_t(0)
+        check(self.ctx, self.lib.ca_export_plan(self.ctx, None, 0, ctypes.byref(n)))
+        buf = ctypes.create_string_buffer(max(n.value, 1))
+        check(self.ctx, self.lib.ca_export_plan(self.ctx, buf, n.value, ctypes.byref(n)))
+        return buf.raw[: n.value]
+
     def stats(self) -> Dict[str, float]:
         s = _capi.ca_stats_t()
         check(self.ctx, self.lib.ca_stats(self.ctx, ctypes.byref(s)))
@@ -158,6 +168,21 @@ class ChunkAttention:
         check(self.ctx, self.lib.ca_workspace_bytes(self.ctx, ctypes.byref(n)))
         return int(n.value)
 
+    def staging_bytes(self) -> int:
+        n = ctypes.c_size_t(0)
+        check(self.ctx, self.lib.ca_staging_bytes(self.ctx, ctypes.byref(n)))
+        return int(n.value)
+
+    def _lend_staging(self, nbytes: int) -> None:
+        """Pinned host memory (a torch tensor) for the table uploads, cut to a
+        256-byte aligned start."""
+        import torch
+        buf = torch.empty(nbytes + 256, dtype=torch.uint8, pin_memory=True)
+        off = (-buf.data_ptr()) % 256
+        view = buf[off:off + nbytes]
+        check(self.ctx, self.lib.ca_attach_staging(self.ctx, ctypes.c_void_p(view.data_ptr()), nbytes))
+        self.stage = view  # the view keeps the whole buffer alive
+
     # -- step -----------------------------------------------------------------
     def ensure_workspace(self) -> None:
         import torch
@@ -166,6 +191,9 @@ class ChunkAttention:
             self.ws = torch.empty(max(need + need // 4, 4096), dtype=torch.uint8, device=self.pool.device)
             check(self.ctx, self.lib.ca_attach_workspace(self.ctx, ctypes.c_void_p(self.ws.data_ptr()),
                                                          self.ws.numel()))
+        stage = self.staging_bytes()
+        if self.stage is None or self.stage.numel() < stage:
+            self._lend_staging(max(stage + stage // 4, 3 << 16))
 
     def _qo(self, q, out):
         import torch
@@ -223,14 +251,35 @@ class ChunkAttention:
                                                  ctypes.c_void_p(out.data_ptr()), self._stream(stream)))
 
 
-def load_workload(ca: ChunkAttention, wl, device="cuda", stream=None) -> None:
-    """Insert every sequence of a seeded workload (ids 0..N-1) with its K/V."""
+def load_workload(ca: ChunkAttention, wl, device="cuda", stream=None, segments: Optional[dict] = None) -> None:
+    """Insert every sequence of a seeded workload (ids 0..N-1) with its K/V.
+
+    A workload built from segments has each segment's K/V copied to the device
+    once (kept in ``segments`` when given, so several contexts can share the
+    copies) and every sequence's K/V assembled on the device; other workloads
+    copy each sequence's rows."""
     import torch
+    segs = getattr(wl, "segments", None)
+    if segs is None:
+        for i in range(wl.n_seq):
+            k, v = wl.seq_kv(i)
+            kt = torch.from_numpy(np.ascontiguousarray(k)).to(device)
+            vt = torch.from_numpy(np.ascontiguousarray(v)).to(device)
+            ca.insert(i, wl.seq_tokens(i), kt, vt, stream=stream)
+        return
+    cache = segments if segments is not None else {}
     for i in range(wl.n_seq):
-        k, v = wl.seq_kv(i)
-        kt = torch.from_numpy(np.ascontiguousarray(k)).to(device)
-        vt = torch.from_numpy(np.ascontiguousarray(v)).to(device)
+        for j in wl.paths[i]:
+            if j not in cache:
+                cache[j] = (torch.from_numpy(segs[j].k).to(device), torch.from_numpy(segs[j].v).to(device))
+        parts = [cache[j] for j in wl.paths[i]]
+        kt = torch.cat([p[0] for p in parts]) if len(parts) > 1 else parts[0][0]
+        vt = torch.cat([p[1] for p in parts]) if len(parts) > 1 else parts[0][1]
         ca.insert(i, wl.seq_tokens(i), kt, vt, stream=stream)
+        if len(parts) > 1 and stream is not None:
+            # the copies read kt/vt on another stream than torch's: keep them
+            # alive until that stream is past them
+            stream.synchronize()
 
 
 def slots_needed(wl, chunk: int = CHUNK, share: bool = True) -> int:

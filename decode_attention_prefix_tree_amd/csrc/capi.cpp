@@ -7,6 +7,7 @@
 #include <cstddef>
 #include <cstring>
 #include <exception>
+#include <mutex>
 #include <string>
 
 #include "../../include/chunkattn.h"
@@ -15,6 +16,20 @@
 #include "manager.h"
 
 using chunkattn::Error;
+
+// The plan of the tree as it will be after the next append of one token to
+// every live sequence: built by the call that has just enqueued a step, after
+// its launch, so the host builds it while the GPU runs that step.
+struct Prebuild {
+  // the tree version it was built from and the sequences that append
+  uint64_t base_version = 0;
+  std::vector<int64_t> ids;
+  // the result
+  bool ok = false;
+  chunkattn::Plan plan;
+  int cf_auto = 0, plan_cf_group = 0;
+  double ms = 0.0;
+};
 
 struct ca_ctx {
   int heads = 0, head_dim = 0, chunk = 0, flags = 0;
@@ -28,14 +43,20 @@ struct ca_ctx {
   int plan_cf_group = 8;           // the group the current plan was built with
   int fused_merge = 2;              // CA_OPT_FUSED_MERGE: 0 two launches, 1 one launch, 2 chosen per plan
   int merge_poll_limit = 0;         // CA_OPT_MERGE_POLL_LIMIT (0: the kernels' own bound)
-  unsigned fuse_epoch = 0;          // one-launch steps since the last table upload
   unsigned decode_epoch = 0;        // ca_decode_step launches that grew chunks in the kernel
+  int fail_ops = 0;                 // CA_OPT_FAIL_DEVICE_OPS: device operations left to fail
+  bool prebuild_on = true;          // CA_OPT_PREBUILD_PLAN
+  Prebuild pre;
+  int64_t prebuilt_plans = 0;       // structural appends that found their plan built ahead
+  bool broken = false;              // a device operation after a tree change failed
 
   // plan cache: rebuilt after the tree changes, uploaded when stale
   chunkattn::Plan plan;
   bool plan_valid = false;
   bool fills_stale = false;  // plan structure current, chunk fills grew since
   int64_t fill_refreshes = 0, table_uploads = 0, patched_appends = 0;
+  // The device copy of the table: the workspace it was uploaded to and the
+  // tree version it holds.
   uint64_t version = 1, uploaded_version = 0;
   void* uploaded_ws = nullptr;
   size_t off_cf = 0, off_sf = 0, off_refs = 0, off_qrow = 0, off_seqparts = 0, off_partlist = 0;
@@ -46,13 +67,18 @@ struct ca_ctx {
 
   // pinned staging for the table upload, a ring of three buffers: each event
   // marks when the copy out of its buffer has finished, so a buffer is
-  // rewritten without waiting on the most recent uploads
+  // rewritten without waiting on the most recent uploads.  The buffers are
+  // three equal parts of the caller's pinned memory (ca_attach_staging) or,
+  // when the caller lent none, the library's own (allocated at the first
+  // upload that needs them).
   static constexpr int kStages = 3;
   void* stage[kStages] = {nullptr, nullptr, nullptr};
   size_t stage_bytes[kStages] = {0, 0, 0};
   hipEvent_t stage_done[kStages] = {nullptr, nullptr, nullptr};
   bool stage_pending[kStages] = {false, false, false};
   int stage_next = 0;
+  void* lent_stage = nullptr;       // the caller's pinned staging, or null
+  size_t lent_stage_bytes = 0;
 
   std::string err;
 
@@ -64,7 +90,7 @@ struct ca_ctx {
         if (stage_pending[b]) (void)hipEventSynchronize(stage_done[b]);
         (void)hipEventDestroy(stage_done[b]);
       }
-      if (stage[b]) (void)hipHostFree(stage[b]);
+      if (stage[b] && lent_stage == nullptr) (void)hipHostFree(stage[b]);
     }
   }
 };
@@ -99,7 +125,33 @@ void touch_after_append(ca_ctx* c) {
   }
 }
 
-bool device_table_current(const ca_ctx* c) { return c->uploaded_version == c->version && c->uploaded_ws == c->ws; }
+// The device table in workspace `ws` holds the current tree.
+bool table_current_in(const ca_ctx* c, const void* ws) {
+  return ws != nullptr && c->uploaded_version == c->version && c->uploaded_ws == ws;
+}
+
+// Some device table (at uploaded_ws) holds the current tree: appends can
+// patch fill counts there instead of forcing a new upload.
+bool device_table_current(const ca_ctx* c) { return table_current_in(c, c->uploaded_ws); }
+
+// After a failed device operation: the next step uploads the table again
+// (which also clears the arrival counters and the fill tags).
+void mark_table_stale(ca_ctx* c) { c->uploaded_version = 0; }
+
+// Test knob (CA_OPT_FAIL_DEVICE_OPS): the next device operation fails as a
+// HIP error would, before anything is enqueued.
+void device_op(ca_ctx* c, const char* what) {
+  if (c->fail_ops > 0) {
+    c->fail_ops -= 1;
+    throw Error(CA_E_HIP, std::string(what) + ": injected failure");
+  }
+}
+
+void require_usable(const ca_ctx* c) {
+  if (c->broken)
+    throw Error(CA_E_STATE, "a device operation failed after the tree had changed; the stored K/V no longer "
+                            "match the tree: destroy the context");
+}
 
 // with_fills: the host plan's fill counts are needed too (an upload, an
 // export, stats); a step whose device table is current does not need them.
@@ -142,6 +194,9 @@ int64_t sf_min_tasks(int heads) {
   return (kResidentBlocks * 5 / 2 + heads - 1) / heads;
 }
 
+void layout_plan(ca_ctx* c);
+int build_for(const ca_ctx* c, chunkattn::Plan* plan, const chunkattn::NextAppend* next);
+
 void ensure_plan(ca_ctx* c, bool with_fills = true) {
   if (c->plan_valid) {
     if (c->fills_stale && with_fills) {
@@ -155,18 +210,19 @@ void ensure_plan(ca_ctx* c, bool with_fills = true) {
     return;
   }
   auto t0 = std::chrono::steady_clock::now();
-  const bool two_phase = (c->flags & CA_CREATE_NO_CHUNK_FIRST) == 0;
-  const int g = c->cf_group ? c->cf_group : c->cf_auto;
-  const int64_t sf_min = sf_min_tasks(c->heads);
-  c->mgr.build_plan(g, c->sf_group, two_phase, &c->plan, sf_min);
-  if (c->cf_group == 0 && two_phase && c->plan.shared_chunks > 0) {
-    const int want = auto_cf_group(c->plan, c->heads, c->head_dim, c->chunk);
-    if (want != g) c->mgr.build_plan(want, c->sf_group, two_phase, &c->plan, sf_min);
-    c->cf_auto = want;
-  }
+  c->cf_auto = build_for(c, &c->plan, nullptr);
   c->plan_cf_group = c->cf_group ? c->cf_group : c->cf_auto;
   c->mgr.clear_structural();
   c->fills_stale = false;
+  layout_plan(c);
+  c->plan_valid = true;
+  c->rebuilds += 1;
+  c->last_rebuild_ms =
+      std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+}
+
+// Offsets of the plan's arrays in the workspace (and its total size).
+void layout_plan(ca_ctx* c) {
   const chunkattn::Plan& p = c->plan;
   size_t off = 0;
   c->off_cf = off;
@@ -191,10 +247,71 @@ void ensure_plan(ca_ctx* c, bool with_fills = true) {
   c->off_part_ms = off;
   off = align_up(off + static_cast<size_t>(p.n_parts) * c->heads * 2 * sizeof(float));
   c->total_bytes = off;
+}
+
+// The plan of a tree: the chunk-first group as given, or chosen for the
+// plan (built once with the last choice, again if the plan wants another).
+// `next`: the tree after those appends.  Returns the automatic choice.
+int build_for(const ca_ctx* c, chunkattn::Plan* plan, const chunkattn::NextAppend* next) {
+  const bool two_phase = (c->flags & CA_CREATE_NO_CHUNK_FIRST) == 0;
+  const int g = c->cf_group ? c->cf_group : c->cf_auto;
+  const int64_t sf_min = sf_min_tasks(c->heads);
+  c->mgr.build_plan(g, c->sf_group, two_phase, plan, sf_min, next);
+  int cf_auto = c->cf_auto;
+  if (c->cf_group == 0 && two_phase && plan->shared_chunks > 0) {
+    const int want = auto_cf_group(*plan, c->heads, c->head_dim, c->chunk);
+    if (want != g) c->mgr.build_plan(want, c->sf_group, two_phase, plan, sf_min, next);
+    cf_auto = want;
+  }
+  return cf_auto;
+}
+
+// After a batch of one-token appends over every live sequence (a decode
+// step) has been enqueued: if the next such batch will change the plan's
+// shape (a sequence's last chunk is full or shared, or a chunk of 128 opens
+// its second tile), build the plan of that tree now, while the GPU runs the
+// work just enqueued; the next batch then takes it instead of rebuilding.
+void prebuild_next(ca_ctx* c) {
+  Prebuild& p = c->pre;
+  if (!c->prebuild_on || c->mgr.live() == 0) return;
+  if (p.ok && p.base_version == c->version) return;  // already built for this tree
+  if (!c->mgr.next_append_structural()) return;
+  const auto t0 = std::chrono::steady_clock::now();
+  p.ok = false;
+  p.base_version = c->version;
+  p.ids = c->mgr.sequences();
+  chunkattn::NextAppend next;
+  if (c->mgr.predict_append_batch(p.ids.data(), static_cast<int32_t>(p.ids.size()), &next) && next.structural) {
+    p.cf_auto = build_for(c, &p.plan, &next);
+    p.plan_cf_group = c->cf_group ? c->cf_group : p.cf_auto;
+    p.ok = true;
+  }
+  p.ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+}
+
+// Before the appends of `ids` (one token each): whether the plan built ahead
+// is the plan of the tree they will make.
+bool prebuild_matches(const ca_ctx* c, const int64_t* ids, int32_t n) {
+  const Prebuild& p = c->pre;
+  if (!p.ok || p.base_version != c->version || static_cast<size_t>(n) != p.ids.size()) return false;
+  for (int32_t j = 0; j < n; ++j)
+    if (ids[j] != p.ids[j]) return false;
+  return true;
+}
+
+// After those appends changed the plan's shape: take the plan built ahead.
+void adopt_prebuild(ca_ctx* c) {
+  std::swap(c->plan, c->pre.plan);
+  c->pre.ok = false;
+  c->cf_auto = c->pre.cf_auto;
+  c->plan_cf_group = c->pre.plan_cf_group;
+  c->mgr.clear_structural();
+  c->fills_stale = false;
+  layout_plan(c);
   c->plan_valid = true;
   c->rebuilds += 1;
-  c->last_rebuild_ms =
-      std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+  c->prebuilt_plans += 1;
+  c->last_rebuild_ms = c->pre.ms;
 }
 
 template <typename T>
@@ -202,25 +319,9 @@ void put(char* base, size_t off, const std::vector<T>& v) {
   if (!v.empty()) std::memcpy(base + off, v.data(), v.size() * sizeof(T));
 }
 
-void upload(ca_ctx* c, void* stream) {
-  if (device_table_current(c)) return;
-  ensure_plan(c);
-  const int b = c->stage_next;
-  c->stage_next = (b + 1) % ca_ctx::kStages;
-  if (c->stage_pending[b]) {
-    hip_check(hipEventSynchronize(c->stage_done[b]), "hipEventSynchronize");
-    c->stage_pending[b] = false;
-  }
-  if (c->stage_bytes[b] < c->table_bytes) {
-    if (c->stage[b]) hip_check(hipHostFree(c->stage[b]), "hipHostFree");
-    c->stage[b] = nullptr;
-    size_t want = align_up(c->table_bytes * 2);
-    hip_check(hipHostMalloc(&c->stage[b], want, hipHostMallocDefault), "hipHostMalloc");
-    c->stage_bytes[b] = want;
-  }
-  if (!c->stage_done[b])
-    hip_check(hipEventCreateWithFlags(&c->stage_done[b], hipEventDisableTiming), "hipEventCreate");
-  char* s = static_cast<char*>(c->stage[b]);
+// The device table of the current plan (table_bytes): records, chunk refs,
+// row and partial lists, and zeroed arrival counters.
+void table_image(const ca_ctx* c, char* s) {
   const chunkattn::Plan& p = c->plan;
   std::memset(s, 0, c->table_bytes);
   put(s, c->off_cf, p.cf_units);
@@ -229,19 +330,60 @@ void upload(ca_ctx* c, void* stream) {
   put(s, c->off_qrow, p.dfs_qrow);
   put(s, c->off_seqparts, p.seq_parts);
   put(s, c->off_partlist, p.part_list);
-  hip_check(hipMemcpyAsync(c->ws, s, c->table_bytes, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)),
-            "hipMemcpyAsync(table)");
-  hip_check(hipEventRecord(c->stage_done[b], static_cast<hipStream_t>(stream)), "hipEventRecord");
-  c->stage_pending[b] = true;
-  c->table_uploads += 1;
-  c->fuse_epoch = 0;    // the upload zeroed the arrival counters
-  c->decode_epoch = 0;  // and wrote untagged fill counts
-  c->uploaded_version = c->version;
-  c->uploaded_ws = c->ws;
 }
 
-chunkattn::StepArgs step_args(ca_ctx* c, const void* q, void* out) {
-  char* w = static_cast<char*>(c->ws);
+// Staging bytes for the current table: three parts, each holding the table.
+size_t staging_need(const ca_ctx* c) { return ca_ctx::kStages * align_up(c->table_bytes); }
+
+void upload(ca_ctx* c, void* stream, void* ws) {
+  if (table_current_in(c, ws)) return;
+  // A graph would replay the copy from a staging buffer that later uploads
+  // rewrite (and waiting for the ring is no call for a capture): a step is
+  // captured only once its table is on the device.
+  hipStreamCaptureStatus capturing = hipStreamCaptureStatusNone;
+  hip_check(hipStreamIsCapturing(static_cast<hipStream_t>(stream), &capturing), "hipStreamIsCapturing");
+  if (capturing != hipStreamCaptureStatusNone)
+    throw Error(CA_E_STATE, "the chunk table must be uploaded first, which cannot be captured: run one step "
+                            "(or ca_prepare) on the tree as it is before capturing");
+  ensure_plan(c);
+  const int b = c->stage_next;
+  if (c->lent_stage != nullptr) {
+    if (c->lent_stage_bytes < staging_need(c))
+      throw Error(CA_E_WORKSPACE, "staging of " + std::to_string(staging_need(c)) + " bytes needed, " +
+                                      std::to_string(c->lent_stage_bytes) + " attached");
+  }
+  if (c->stage_pending[b]) {
+    hip_check(hipEventSynchronize(c->stage_done[b]), "hipEventSynchronize");
+    c->stage_pending[b] = false;
+  }
+  if (c->lent_stage == nullptr && c->stage_bytes[b] < c->table_bytes) {
+    if (c->stage[b]) hip_check(hipHostFree(c->stage[b]), "hipHostFree");
+    c->stage[b] = nullptr;
+    c->stage_bytes[b] = 0;
+    size_t want = align_up(c->table_bytes * 2);
+    hip_check(hipHostMalloc(&c->stage[b], want, hipHostMallocDefault), "hipHostMalloc");
+    c->stage_bytes[b] = want;
+  }
+  if (!c->stage_done[b])
+    hip_check(hipEventCreateWithFlags(&c->stage_done[b], hipEventDisableTiming), "hipEventCreate");
+  char* s = static_cast<char*>(c->stage[b]);
+  table_image(c, s);
+  // from here on the device copy may be half written: stale until done
+  mark_table_stale(c);
+  device_op(c, "table upload");
+  hip_check(hipMemcpyAsync(ws, s, c->table_bytes, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)),
+            "hipMemcpyAsync(table)");
+  c->stage_next = (b + 1) % ca_ctx::kStages;
+  c->stage_pending[b] = true;
+  hip_check(hipEventRecord(c->stage_done[b], static_cast<hipStream_t>(stream)), "hipEventRecord");
+  c->table_uploads += 1;
+  c->decode_epoch = 0;  // the upload wrote untagged fill counts
+  c->uploaded_version = c->version;
+  c->uploaded_ws = ws;
+}
+
+chunkattn::StepArgs step_args(ca_ctx* c, void* ws, const void* q, void* out) {
+  char* w = static_cast<char*>(ws);
   const chunkattn::Plan& p = c->plan;
   chunkattn::StepArgs a{};
   a.pool = c->pool;
@@ -271,14 +413,15 @@ chunkattn::StepArgs step_args(ca_ctx* c, const void* q, void* out) {
   return a;
 }
 
-void check_step(ca_ctx* c, const void* q, void* out) {
+// ws, ws_bytes: the workspace the step runs in.
+void check_step(ca_ctx* c, const void* q, void* out, const void* ws, size_t ws_bytes) {
   if (!c->pool_attached || c->pool == nullptr) throw Error(CA_E_NO_POOL, "no device pool attached");
   if (c->mgr.live() == 0) throw Error(CA_E_EMPTY, "no live sequence");
   if (q == nullptr || out == nullptr) throw Error(CA_E_INVALID_ARG, "q and out must be device pointers");
-  ensure_plan(c, !device_table_current(c));
-  if (c->ws == nullptr || c->ws_bytes < c->total_bytes)
+  ensure_plan(c, !table_current_in(c, ws));
+  if (ws == nullptr || ws_bytes < c->total_bytes)
     throw Error(CA_E_WORKSPACE, "workspace of " + std::to_string(c->total_bytes) + " bytes needed, " +
-                                    std::to_string(c->ws_bytes) + " attached");
+                                    std::to_string(ws_bytes) + " attached");
   // int32 indexing limits of the kernels
   if (static_cast<int64_t>(c->plan.cf_units.size()) * c->heads > INT32_MAX ||
       static_cast<int64_t>(c->plan.sf_tasks.size()) * c->heads > INT32_MAX ||
@@ -286,7 +429,12 @@ void check_step(ca_ctx* c, const void* q, void* out) {
     throw Error(CA_E_UNSUPPORTED, "step too large for one launch");
 }
 
-void launch(int e, const char* what) {
+// A kernel launch: the injected failure (if any) comes before anything is
+// enqueued; a HIP error is reported with its text.
+template <typename F>
+void launch(ca_ctx* c, const char* what, F&& go) {
+  device_op(c, what);
+  const int e = go();
   if (e != 0) throw Error(CA_E_HIP, std::string(what) + ": " + hipGetErrorString(static_cast<hipError_t>(e)));
 }
 
@@ -303,7 +451,7 @@ struct FillPatch {
 // otherwise.  out gets one entry per op.
 bool fill_patches(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, std::vector<FillPatch>* out) {
   out->clear();
-  if (!c->plan_valid || !c->mgr.fills_only() || c->ws == nullptr || !device_table_current(c)) return false;
+  if (!c->plan_valid || !c->mgr.fills_only() || !device_table_current(c)) return false;
   const chunkattn::Plan& p = c->plan;
   const int32_t refs = static_cast<int32_t>(c->off_refs / sizeof(int32_t));
   const int32_t tasks = static_cast<int32_t>(c->off_sf / sizeof(int32_t));
@@ -360,7 +508,8 @@ void run_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* 
   chunkattn::KvOpBatch batch{};
   chunkattn::TablePatches tp{};
   int n = 0;
-  int32_t* table = static_cast<int32_t*>(c->ws);
+  // fill patches go to the device table that holds the current tree
+  int32_t* table = static_cast<int32_t*>(c->uploaded_ws);
   for (size_t i = 0; i < pieces.size(); ++i) {
     batch.ops[n++] = pieces[i];
     if (patch_of[i] >= 0) {
@@ -373,10 +522,24 @@ void run_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* 
       }
     }
     if (n == chunkattn::kOpsPerLaunch || i + 1 == pieces.size()) {
-      launch(chunkattn::launch_kv_write(c->pool, c->heads, batch, n, k, v, table, tp, stream), "kv_write");
+      launch(c, "kv_write", [&] { return chunkattn::launch_kv_write(c->pool, c->heads, batch, n, k, v, table, tp, stream); });
       n = 0;
       tp.n = 0;
     }
+  }
+}
+
+// The K/V writes of appends that have already changed the tree.  If they
+// cannot be enqueued, the tree holds tokens that the pool does not: the
+// context refuses further work (CA_E_STATE) from then on.
+void store_appended(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* k, const void* v, void* stream,
+                    const std::vector<FillPatch>& patches = {}) {
+  try {
+    run_kv_ops(c, ops, k, v, stream, patches);
+  } catch (const Error&) {
+    c->broken = true;
+    mark_table_stale(c);
+    throw;
   }
 }
 
@@ -406,13 +569,26 @@ void touch_patched(ca_ctx* c) {
   c->uploaded_version = c->version;
 }
 
+// The step's launches.  After any failure the table is uploaded again before
+// the next step (which also clears the arrival counters).
 void launch_step(ca_ctx* c, const chunkattn::StepArgs& a, void* stream) {
-  if (one_launch(c)) {
-    launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, true, ++c->fuse_epoch, stream), "step");
-  } else {
-    launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, false, 0, stream), "partials");
-    launch(chunkattn::launch_merge(a, stream), "merge");
+  try {
+    if (one_launch(c)) {
+      launch(c, "step", [&] { return chunkattn::launch_partials(a, chunkattn::kPartsBoth, true, stream); });
+    } else {
+      launch(c, "partials", [&] { return chunkattn::launch_partials(a, chunkattn::kPartsBoth, false, stream); });
+      launch(c, "merge", [&] { return chunkattn::launch_merge(a, stream); });
+    }
+  } catch (const Error&) {
+    mark_table_stale(c);
+    throw;
   }
+}
+
+// One attend step in workspace ws (after check_step).
+void attend_in(ca_ctx* c, const void* q, void* out, void* stream, void* ws) {
+  upload(c, stream, ws);
+  launch_step(c, step_args(c, ws, q, out), stream);
 }
 
 #define CA_GUARD(ctx, ...)                                                    \
@@ -462,10 +638,14 @@ int ca_create(int heads, int head_dim, int chunk_size, ca_ctx** out) {
   return ca_create_ex(heads, head_dim, chunk_size, 0, out);
 }
 
-void ca_destroy(ca_ctx* ctx) { delete ctx; }
+void ca_destroy(ca_ctx* ctx) {
+  if (ctx == nullptr) return;
+  delete ctx;
+}
 
 int ca_attach_pool(ca_ctx* ctx, void* dev, int64_t capacity_slots) {
   CA_GUARD(ctx, {
+    require_usable(ctx);
     if (capacity_slots < 0) throw Error(CA_E_INVALID_ARG, "negative capacity");
     if (dev != nullptr && ctx->chunk != 32 && ctx->chunk != 64 && ctx->chunk != 128)
       throw Error(CA_E_UNSUPPORTED, "a device pool needs chunk size 32, 64 or 128");
@@ -494,8 +674,51 @@ int ca_attach_workspace(ca_ctx* ctx, void* dev, size_t bytes) {
   CA_GUARD(ctx, {
     if (dev != nullptr && (reinterpret_cast<uintptr_t>(dev) % kAlign) != 0)
       throw Error(CA_E_INVALID_ARG, "workspace must be 256-byte aligned");
+    // appends must not patch fill counts into a workspace the caller took back
+    if (ctx->uploaded_ws == ctx->ws && dev != ctx->ws) ctx->uploaded_ws = nullptr;
     ctx->ws = dev;
     ctx->ws_bytes = dev ? bytes : 0;
+    return CA_OK;
+  });
+}
+
+int ca_staging_bytes(ca_ctx* ctx, size_t* out) {
+  CA_GUARD(ctx, {
+    if (out == nullptr) throw Error(CA_E_INVALID_ARG, "out is NULL");
+    ensure_plan(ctx, false);
+    *out = staging_need(ctx);
+    return CA_OK;
+  });
+}
+
+int ca_attach_staging(ca_ctx* ctx, void* host, size_t bytes) {
+  CA_GUARD(ctx, {
+    if (host != nullptr && (reinterpret_cast<uintptr_t>(host) % kAlign) != 0)
+      throw Error(CA_E_INVALID_ARG, "staging must be 256-byte aligned");
+    // copies still reading the old buffers finish first: the caller may
+    // free them once this returns
+    for (int b = 0; b < ca_ctx::kStages; ++b) {
+      if (ctx->stage_pending[b]) {
+        hip_check(hipEventSynchronize(ctx->stage_done[b]), "hipEventSynchronize");
+        ctx->stage_pending[b] = false;
+      }
+      if (ctx->stage[b] && ctx->lent_stage == nullptr) hip_check(hipHostFree(ctx->stage[b]), "hipHostFree");
+      ctx->stage[b] = nullptr;
+      ctx->stage_bytes[b] = 0;
+    }
+    ctx->lent_stage = host;
+    ctx->lent_stage_bytes = host ? bytes : 0;
+    if (host != nullptr) {
+      const size_t part = bytes / ca_ctx::kStages / kAlign * kAlign;
+      for (int b = 0; b < ca_ctx::kStages; ++b) {
+        ctx->stage[b] = static_cast<char*>(host) + b * part;
+        ctx->stage_bytes[b] = part;
+        // the events are made here, so that steps never create any
+        if (!ctx->stage_done[b])
+          hip_check(hipEventCreateWithFlags(&ctx->stage_done[b], hipEventDisableTiming), "hipEventCreate");
+      }
+    }
+    ctx->stage_next = 0;
     return CA_OK;
   });
 }
@@ -514,6 +737,14 @@ int ca_set_option(ca_ctx* ctx, int option, int value) {
     } else if (option == CA_OPT_FUSED_MERGE) {
       if (value < 0 || value > 2) throw Error(CA_E_INVALID_ARG, "fused merge is 0, 1 or 2 (automatic)");
       ctx->fused_merge = value;
+    } else if (option == CA_OPT_PREBUILD_PLAN) {
+      if (value < 0 || value > 1) throw Error(CA_E_INVALID_ARG, "prebuild is 0 or 1");
+      ctx->prebuild_on = value != 0;
+      return CA_OK;  // the plan is unaffected
+    } else if (option == CA_OPT_FAIL_DEVICE_OPS) {
+      if (value < 0) throw Error(CA_E_INVALID_ARG, "failure count must be >= 0");
+      ctx->fail_ops = value;
+      return CA_OK;  // the plan is unaffected
     } else {
       throw Error(CA_E_UNSUPPORTED, "unknown option");
     }
@@ -525,16 +756,27 @@ int ca_set_option(ca_ctx* ctx, int option, int value) {
 int ca_insert(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n, const void* k_dev,
               const void* v_dev, void* stream, int32_t* n_matched) {
   CA_GUARD(ctx, {
+    require_usable(ctx);
     if (!ctx->pool_attached) throw Error(CA_E_NO_POOL, "attach a pool (or a NULL pool) first");
     if (n < 1 || tokens == nullptr) throw Error(CA_E_INVALID_ARG, "insert needs n >= 1 host tokens");
     const bool device = ctx->pool != nullptr;
     if (device && (k_dev == nullptr || v_dev == nullptr))
       throw Error(CA_E_INVALID_ARG, "k_dev and v_dev are required when a device pool is attached");
     std::vector<chunkattn::KvOp> ops;
+    // A failed copy puts the tree back as it was: the copies only write the
+    // slots this insert took (new chunks, a split's tail), which are free again.
+    chunkattn::Manager before = device ? ctx->mgr : chunkattn::Manager(ctx->chunk, true);
     int32_t matched = ctx->mgr.insert(seq_id, tokens, n, &ops);
     touch(ctx);
+    if (device) {
+      try {
+        run_kv_ops(ctx, ops, k_dev, v_dev, stream);
+      } catch (const Error&) {
+        ctx->mgr = std::move(before);
+        throw;
+      }
+    }
     if (n_matched) *n_matched = matched;
-    if (device) run_kv_ops(ctx, ops, k_dev, v_dev, stream);
     return CA_OK;
   });
 }
@@ -542,6 +784,7 @@ int ca_insert(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n, con
 int ca_append(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n, const void* k_dev,
               const void* v_dev, void* stream) {
   CA_GUARD(ctx, {
+    require_usable(ctx);
     if (!ctx->pool_attached) throw Error(CA_E_NO_POOL, "attach a pool (or a NULL pool) first");
     if (n < 1 || tokens == nullptr) throw Error(CA_E_INVALID_ARG, "append needs n >= 1 host tokens");
     const bool device = ctx->pool != nullptr;
@@ -554,7 +797,7 @@ int ca_append(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n, con
       touch_patched(ctx);
     else
       touch_after_append(ctx);
-    if (device) run_kv_ops(ctx, ops, k_dev, v_dev, stream, patches);
+    if (device) store_appended(ctx, ops, k_dev, v_dev, stream, patches);
     return CA_OK;
   });
 }
@@ -562,6 +805,7 @@ int ca_append(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n, con
 int ca_append_batch(ca_ctx* ctx, int32_t n, const int64_t* seq_ids, const int32_t* tokens, const void* k_dev,
                     const void* v_dev, void* stream) {
   CA_GUARD(ctx, {
+    require_usable(ctx);
     if (!ctx->pool_attached) throw Error(CA_E_NO_POOL, "attach a pool (or a NULL pool) first");
     if (n < 1 || seq_ids == nullptr || tokens == nullptr) throw Error(CA_E_INVALID_ARG, "append batch needs n >= 1");
     const bool device = ctx->pool != nullptr;
@@ -569,18 +813,23 @@ int ca_append_batch(ca_ctx* ctx, int32_t n, const int64_t* seq_ids, const int32_
       throw Error(CA_E_INVALID_ARG, "k_dev and v_dev are required when a device pool is attached");
     std::vector<chunkattn::KvOp> ops;
     std::vector<FillPatch> patches;
+    const bool prebuilt = prebuild_matches(ctx, seq_ids, n);
     ctx->mgr.append_batch(seq_ids, tokens, n, &ops);
-    if (device && fill_patches(ctx, ops, &patches))
+    if (device && fill_patches(ctx, ops, &patches)) {
       touch_patched(ctx);
-    else
+    } else {
       touch_after_append(ctx);
-    if (device) run_kv_ops(ctx, ops, k_dev, v_dev, stream, patches);
+      if (prebuilt && !ctx->plan_valid) adopt_prebuild(ctx);
+    }
+    if (device) store_appended(ctx, ops, k_dev, v_dev, stream, patches);
+    prebuild_next(ctx);
     return CA_OK;
   });
 }
 
 int ca_remove(ca_ctx* ctx, int64_t seq_id) {
   CA_GUARD(ctx, {
+    require_usable(ctx);
     ctx->mgr.remove(seq_id);
     touch(ctx);
     return CA_OK;
@@ -589,40 +838,45 @@ int ca_remove(ca_ctx* ctx, int64_t seq_id) {
 
 int ca_prepare(ca_ctx* ctx, void* stream) {
   CA_GUARD(ctx, {
+    require_usable(ctx);
     if (!ctx->pool_attached || ctx->pool == nullptr) throw Error(CA_E_NO_POOL, "no device pool attached");
     if (ctx->mgr.live() == 0) throw Error(CA_E_EMPTY, "no live sequence");
     ensure_plan(ctx, false);
     if (ctx->ws == nullptr || ctx->ws_bytes < ctx->total_bytes)
       throw Error(CA_E_WORKSPACE, "workspace too small");
-    upload(ctx, stream);
+    upload(ctx, stream, ctx->ws);
     return CA_OK;
   });
 }
 
 int ca_attend_phase(ca_ctx* ctx, int phase, const void* q_dev, void* out_dev, void* stream) {
   CA_GUARD(ctx, {
-    check_step(ctx, q_dev, out_dev);
-    upload(ctx, stream);
-    chunkattn::StepArgs a = step_args(ctx, q_dev, out_dev);
-    if (phase == CA_PHASE_CHUNK_FIRST)
-      launch(chunkattn::launch_partials(a, chunkattn::kPartsChunkFirst, false, 0, stream), "partials");
-    else if (phase == CA_PHASE_SEQUENCE_FIRST)
-      launch(chunkattn::launch_partials(a, chunkattn::kPartsSequenceFirst, false, 0, stream), "partials");
-    else if (phase == CA_PHASE_PARTIALS)
-      launch(chunkattn::launch_partials(a, chunkattn::kPartsBoth, false, 0, stream), "partials");
-    else if (phase == CA_PHASE_MERGE)
-      launch(chunkattn::launch_merge(a, stream), "merge");
-    else
-      throw Error(CA_E_INVALID_ARG, "unknown phase");
+    require_usable(ctx);
+    if (phase < CA_PHASE_CHUNK_FIRST || phase > CA_PHASE_PARTIALS) throw Error(CA_E_INVALID_ARG, "unknown phase");
+    check_step(ctx, q_dev, out_dev, ctx->ws, ctx->ws_bytes);
+    upload(ctx, stream, ctx->ws);
+    chunkattn::StepArgs a = step_args(ctx, ctx->ws, q_dev, out_dev);
+    const int part = phase == CA_PHASE_CHUNK_FIRST      ? chunkattn::kPartsChunkFirst
+                     : phase == CA_PHASE_SEQUENCE_FIRST ? chunkattn::kPartsSequenceFirst
+                                                        : chunkattn::kPartsBoth;
+    try {
+      if (phase == CA_PHASE_MERGE)
+        launch(ctx, "merge", [&] { return chunkattn::launch_merge(a, stream); });
+      else
+        launch(ctx, "partials", [&] { return chunkattn::launch_partials(a, part, false, stream); });
+    } catch (const Error&) {
+      mark_table_stale(ctx);
+      throw;
+    }
     return CA_OK;
   });
 }
 
 int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream) {
   CA_GUARD(ctx, {
-    check_step(ctx, q_dev, out_dev);
-    upload(ctx, stream);
-    launch_step(ctx, step_args(ctx, q_dev, out_dev), stream);
+    require_usable(ctx);
+    check_step(ctx, q_dev, out_dev, ctx->ws, ctx->ws_bytes);
+    attend_in(ctx, q_dev, out_dev, stream, ctx->ws);
     return CA_OK;
   });
 }
@@ -630,6 +884,7 @@ int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream) {
 int ca_decode_step(ca_ctx* ctx, const int32_t* tokens, const void* k_dev, const void* v_dev, const void* q_dev,
                    void* out_dev, void* stream) {
   CA_GUARD(ctx, {
+    require_usable(ctx);
     if (!ctx->pool_attached || ctx->pool == nullptr) throw Error(CA_E_NO_POOL, "no device pool attached");
     if (ctx->mgr.live() == 0) throw Error(CA_E_EMPTY, "no live sequence");
     if (tokens == nullptr || k_dev == nullptr || v_dev == nullptr)
@@ -638,36 +893,47 @@ int ca_decode_step(ca_ctx* ctx, const int32_t* tokens, const void* k_dev, const 
     const std::vector<int64_t> ids = ctx->mgr.sequences();
     std::vector<chunkattn::KvOp> ops;
     std::vector<FillPatch> patches;
+    const bool prebuilt = prebuild_matches(ctx, ids.data(), static_cast<int32_t>(ids.size()));
     ctx->mgr.append_batch(ids.data(), tokens, static_cast<int32_t>(ids.size()), &ops);
     // Every token grew its sequence's private last chunk in place and the
-    // device table is current: the step's own blocks write the tokens.  The
-    // epoch tags the fill counts they store; it restarts (with a clean table)
-    // before it would wrap.
-    const bool in_kernel = fill_patches(ctx, ops, &patches) && ctx->decode_epoch < chunkattn::kEpochMask;
+    // table in the step's workspace is current: the step's own blocks write
+    // the tokens.  The epoch tags the fill counts they store; it restarts
+    // (with a clean table) before it would wrap.
+    const bool in_kernel = fill_patches(ctx, ops, &patches) && ctx->uploaded_ws == ctx->ws &&
+                           ctx->decode_epoch < chunkattn::kEpochMask;
     if (in_kernel) {
       touch_patched(ctx);
       ctx->decode_epoch += 1;
     } else {
       touch_after_append(ctx);
-      run_kv_ops(ctx, ops, k_dev, v_dev, stream);
+      if (prebuilt && !ctx->plan_valid) adopt_prebuild(ctx);
+      store_appended(ctx, ops, k_dev, v_dev, stream);
     }
     try {
-      check_step(ctx, q_dev, out_dev);
+      check_step(ctx, q_dev, out_dev, ctx->ws, ctx->ws_bytes);
     } catch (const Error&) {
       // The step cannot run as it is (a larger workspace is needed, or it
       // exceeds the kernels' index range): store the tokens and their fill
       // counts now, as ca_append_batch does, so the tree and the device agree.
-      if (in_kernel) run_kv_ops(ctx, ops, k_dev, v_dev, stream, patches);
+      if (in_kernel) store_appended(ctx, ops, k_dev, v_dev, stream, patches);
       throw;
     }
-    upload(ctx, stream);
-    chunkattn::StepArgs a = step_args(ctx, q_dev, out_dev);
-    if (in_kernel) {
-      a.app_k = k_dev;
-      a.app_v = v_dev;
-      a.app_epoch = ctx->decode_epoch;
+    try {
+      upload(ctx, stream, ctx->ws);
+      chunkattn::StepArgs a = step_args(ctx, ctx->ws, q_dev, out_dev);
+      if (in_kernel) {
+        a.app_k = k_dev;
+        a.app_v = v_dev;
+        a.app_epoch = ctx->decode_epoch;
+      }
+      launch_step(ctx, a, stream);
+    } catch (const Error&) {
+      // The tokens were to be written by the step itself: store them with a
+      // write launch instead (if that fails too, the context is unusable).
+      if (in_kernel) store_appended(ctx, ops, k_dev, v_dev, stream, patches);
+      throw;
     }
-    launch_step(ctx, a, stream);
+    prebuild_next(ctx);
     return CA_OK;
   });
 }
@@ -694,6 +960,17 @@ int ca_export_table(ca_ctx* ctx, int32_t* rows, int cap_rows, int64_t* dfs_seq_o
       throw Error(CA_E_INVALID_ARG, "output capacity too small");
     if (nr) std::memcpy(rows, p.rows.data(), p.rows.size() * sizeof(int32_t));
     if (ns) std::memcpy(dfs_seq_order, p.dfs_seq.data(), p.dfs_seq.size() * sizeof(int64_t));
+    return CA_OK;
+  });
+}
+
+int ca_export_plan(ca_ctx* ctx, void* buf, size_t cap, size_t* bytes) {
+  CA_GUARD(ctx, {
+    ensure_plan(ctx);
+    if (bytes) *bytes = ctx->table_bytes;
+    if (buf == nullptr && cap == 0) return CA_OK;
+    if (buf == nullptr || cap < ctx->table_bytes) throw Error(CA_E_INVALID_ARG, "output capacity too small");
+    table_image(ctx, static_cast<char*>(buf));
     return CA_OK;
   });
 }
@@ -730,6 +1007,7 @@ int ca_stats(ca_ctx* ctx, ca_stats_t* out) {
     s.cf_chunks_per_task = ctx->plan_cf_group;
     s.sf_chunks_per_task = ctx->plan.sf_group;
     s.one_launch_step = one_launch(ctx) ? 1 : 0;
+    s.prebuilt_plans = ctx->prebuilt_plans;
     *out = s;
     return CA_OK;
   });

@@ -38,7 +38,7 @@ struct StepArgs {
   const int32_t* part_list;    // partial ids
   float* part_o;               // [n_parts][H][128]
   float* part_ms;              // [n_parts][H][2]: running max (log2 units), sum
-  unsigned* arrivals;          // [n_seq][H] partials written by one-launch steps since the upload
+  unsigned* arrivals;          // [n_seq][H] partials written so far in a one-launch step (zero between launches)
   int heads;
   int dense_parts;             // > 0: sequence i's j-th partial is i * dense_parts + j (j < count)
   int part_stride;             // partial id step between rows of a chunk-first unit
@@ -68,9 +68,8 @@ enum PartialsPart { kPartsBoth = 0, kPartsChunkFirst = 1, kPartsSequenceFirst = 
 // One grid with the chunk-first blocks first and the sequence-first blocks
 // after them; `part` restricts the launch to one side.  With fuse_merge (and
 // part == kPartsBoth) merge blocks close the grid and write out: the whole
-// step in one launch; epoch counts the one-launch steps since the table (with
-// its arrival counters) was uploaded, this one included.
-int launch_partials(const StepArgs& a, int part, bool fuse_merge, unsigned epoch, void* stream);
+// step in one launch, whose arrival counters are zero again when it ends.
+int launch_partials(const StepArgs& a, int part, bool fuse_merge, void* stream);
 int launch_merge(const StepArgs& a, void* stream);
 
 }  // namespace chunkattn

@@ -100,11 +100,16 @@ __device__ __forceinline__ h2 lo2(h8 v, int j) {
 
 // Step-local communication between blocks (the one-launch step).  Partials
 // are written with agent-scope relaxed atomic stores and read back with
-// agent-scope atomic loads: both are coherent across the XCDs by themselves
-// (global_store/global_load with sc1), so no cache-wide write-back or
-// invalidate is needed.  A writer waits for its stores to complete before it
-// counts its arrival, so a merger that sees the full count reads complete
-// data.
+// agent-scope atomic loads: on gfx950 both are device-scope accesses (sc1)
+// that write through and read past the XCD's L2, so they are coherent across
+// the XCDs by themselves.  A writer waits for its stores to be acknowledged
+// (s_waitcnt vmcnt(0), then its block's barrier) before it counts its
+// arrival; a merger issues its partial loads only after its poll has
+// returned the full count.  The memory model's own release/acquire at agent
+// scope would add a write-back of the whole L2 to every arrival and an
+// invalidate of the whole L2 to every merge: measured, that doubles the
+// multi-branch step (201 -> 420 us), so the ordering rests on these two
+// hardware facts instead.
 __device__ __forceinline__ void store_agent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -184,10 +189,10 @@ __device__ __forceinline__ void merge_one(const StepArgs& a, int pos, int head, 
   *reinterpret_cast<h2*>(out) = res;
 }
 
-// One more partial of (pos, head) is written (called once the caller's
-// partial stores have completed).  The counters only grow: every one-launch
-// step adds each sequence's partial count, and they restart from zero when the
-// table is uploaded.
+// One more partial of (pos, head) is written.  Each counter is zero when a
+// launch starts (the table upload clears them, and every merge returns its
+// counter to zero): the producers of a (sequence, head) add one each, its
+// merge waits for the count and then takes it off again.
 __device__ __forceinline__ void arrive(const StepArgs& a, int pos, int head) {
   __hip_atomic_fetch_add(a.arrivals + pos * a.heads + head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -252,20 +257,25 @@ constexpr int kMaxPolls = 1 << 20;
 // block in the grid, so they are dispatched last, into the step's tail, and
 // only ever wait for blocks dispatched before them.  Wave w of merge block mb
 // merges item mb*4 + w = (DFS position, head), once the item's counter has
-// reached epoch * count (epoch = one-launch steps since the table upload).
-__device__ __forceinline__ void merge_block(const StepArgs& a, int mb, unsigned epoch) {
+// reached the sequence's partial count; then it subtracts that count, so the
+// counter is zero again when every producer has arrived.  Nothing carries
+// over from one launch to the next, so a step can be captured in a graph and
+// replayed.  A wave that gives up subtracts the count too: producers always
+// arrive, and the late ones bring the counter back to zero by the end of the
+// launch.
+__device__ __forceinline__ void merge_block(const StepArgs& a, int mb) {
   const int item = mb * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (item >= a.n_seq * a.heads) return;
   const int pos = item / a.heads, head = item - pos * a.heads;
   const int cnt = a.seq_parts[2 * pos + 1];
   const int qrow = a.dfs_qrow[pos];
   unsigned* ctr = a.arrivals + item;
-  const unsigned target = epoch * static_cast<unsigned>(cnt);
+  const unsigned target = static_cast<unsigned>(cnt);
   // the first poll goes out with the loads of cnt and qrow
   unsigned seen = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   bool ok = true;
   const int limit = a.max_polls > 0 ? a.max_polls : kMaxPolls;
-  for (int tries = 0; static_cast<int>(seen - target) < 0; ++tries) {
+  for (int tries = 0; seen < target; ++tries) {
     if (tries == limit) {
       ok = false;
       break;
@@ -273,17 +283,17 @@ __device__ __forceinline__ void merge_block(const StepArgs& a, int mb, unsigned 
     __builtin_amdgcn_s_sleep(2);
     seen = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   }
-  // keep the partial loads after the poll
+  // keep the partial loads after the poll (the compiler must not hoist them)
   asm volatile("" ::: "memory");
   if (!ok) {
     _Float16* out = static_cast<_Float16*>(a.out) + (static_cast<size_t>(qrow) * a.heads + head) * D + 2 * lane;
     *reinterpret_cast<h2*>(out) = h2{static_cast<_Float16>(NAN), static_cast<_Float16>(NAN)};
-    return;
-  }
-  if (a.dense_parts > 0)
+  } else if (a.dense_parts > 0) {
     merge_dense<true>(a, pos, head, lane, cnt, qrow);
-  else
+  } else {
     merge_one<true>(a, pos, head, lane);
+  }
+  if (lane == 0) __hip_atomic_fetch_sub(ctr, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -782,11 +792,10 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
 // n_cf, n_sf: chunk-first and sequence-first blocks of the step; first:
 // index of this launch's first block in the step's grid (0, or n_cf to launch
 // only the sequence-first part).  kFuse: the one-launch step, whose grid ends
-// with the merge blocks (epoch: see merge_block).  kAppend: a decode step
+// with the merge blocks.  kAppend: a decode step
 // with in-kernel appends (StepArgs::app_k set).
 template <bool kFuse, bool kAppend, bool kHalf>
-__global__ __launch_bounds__(256, 3) void partials_kernel(StepArgs a, int n_cf, int n_sf, int first,
-                                                          unsigned epoch) {
+__global__ __launch_bounds__(256, 3) void partials_kernel(StepArgs a, int n_cf, int n_sf, int first) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   const int b = blockIdx.x + first;
   if (b < n_cf) {
@@ -803,7 +812,7 @@ __global__ __launch_bounds__(256, 3) void partials_kernel(StepArgs a, int n_cf, 
       sequence_first_block<kFuse, true, kAppend, kHalf>(a, logical, smem);
   }
   else if constexpr (kFuse)
-    merge_block(a, b - n_cf - n_sf, epoch);
+    merge_block(a, b - n_cf - n_sf);
 }
 
 // Merge of every (sequence, head), four per block (the unfused step).
@@ -819,7 +828,7 @@ __global__ __launch_bounds__(256) void merge_kernel(StepArgs a) {
 
 }  // namespace
 
-int launch_partials(const StepArgs& a, int part, bool fuse_merge, unsigned epoch, void* stream) {
+int launch_partials(const StepArgs& a, int part, bool fuse_merge, void* stream) {
   const int n_cf = a.n_cf_units * a.heads, n_sf = a.n_sf_tasks * a.heads;
   const bool fuse = fuse_merge && part == kPartsBoth;
   const int n_merge = fuse ? (a.n_seq * a.heads + 3) / 4 : 0;
@@ -829,7 +838,7 @@ int launch_partials(const StepArgs& a, int part, bool fuse_merge, unsigned epoch
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool append = a.app_k != nullptr;
   const dim3 grid(count), block(256);
-#define CA_LAUNCH(F, A, HT) hipLaunchKernelGGL((partials_kernel<F, A, HT>), grid, block, 0, st, a, n_cf, n_sf, first, epoch)
+#define CA_LAUNCH(F, A, HT) hipLaunchKernelGGL((partials_kernel<F, A, HT>), grid, block, 0, st, a, n_cf, n_sf, first)
   if (a.half_tiles) {
     if (fuse && append) CA_LAUNCH(true, true, true);
     else if (fuse) CA_LAUNCH(true, false, true);

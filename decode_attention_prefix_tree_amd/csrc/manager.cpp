@@ -193,6 +193,61 @@ void Manager::append_batch(const int64_t* seqs, const int32_t* tokens, int32_t n
   for (int32_t j = 0; j < n; ++j) append(seqs[j], tokens + j, 1, ops, j);
 }
 
+bool Manager::next_append_structural() const {
+  for (const auto& kv : end_) {
+    const Node& nd = nodes_[kv.second];
+    const int32_t fill = static_cast<int32_t>(nd.tokens.size());
+    if (nd.ref != 1 || fill >= C_ || tiles_of(fill + 1) != tiles_of(fill)) return true;
+  }
+  return false;
+}
+
+bool Manager::predict_append_batch(const int64_t* seqs, int32_t n, NextAppend* out) const {
+  NextAppend& x = *out;
+  x.grow.clear();
+  x.add.clear();
+  x.structural = false;
+  x.n_nodes = nodes_.size();
+  if (n < 1 || seqs == nullptr) return false;
+  std::vector<int64_t> sorted(seqs, seqs + n);
+  std::sort(sorted.begin(), sorted.end());
+  if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) return false;
+  // new chunks take node indices from the reuse list (last first), then the
+  // end of the node array, and the lowest free slots in order: the k smallest
+  // entries of the min-heap, by a best-first walk over it
+  size_t reuse = free_nodes_.size();
+  const std::vector<int32_t>& heap = free_.heap();
+  std::priority_queue<std::pair<int32_t, size_t>, std::vector<std::pair<int32_t, size_t>>,
+                      std::greater<std::pair<int32_t, size_t>>>
+      frontier;
+  if (!heap.empty()) frontier.push({heap[0], 0});
+  for (int32_t j = 0; j < n; ++j) {
+    auto it = end_.find(seqs[j]);
+    if (it == end_.end()) return false;
+    const int32_t e = it->second;
+    const Node& nd = nodes_[e];
+    const int32_t fill = static_cast<int32_t>(nd.tokens.size());
+    if (nd.ref == 1 && fill < C_) {
+      x.grow.push_back(e);
+      if (tiles_of(fill + 1) != tiles_of(fill)) x.structural = true;
+      continue;
+    }
+    if (frontier.empty()) return false;  // out of slots
+    const auto [slot, h] = frontier.top();
+    frontier.pop();
+    for (size_t c = 2 * h + 1; c <= 2 * h + 2 && c < heap.size(); ++c) frontier.push({heap[c], c});
+    int32_t idx;
+    if (reuse > 0) {
+      idx = free_nodes_[--reuse];
+    } else {
+      idx = static_cast<int32_t>(x.n_nodes++);
+    }
+    x.add.push_back({e, idx, next_id_ + static_cast<int32_t>(x.add.size()), slot, nd.start + fill, seqs[j]});
+    x.structural = true;
+  }
+  return true;
+}
+
 void Manager::remove(int64_t seq) {
   auto it = end_.find(seq);
   if (it == end_.end()) throw Error(kUnknownSeq, "sequence id not live");
@@ -249,9 +304,64 @@ void Plan::clear() {
   cf_chunk_reads = sf_chunk_reads = shared_chunks = shared_tokens = unique_tokens = attended_tokens = 0;
 }
 
-void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan, int64_t sf_min_tasks) const {
+void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan, int64_t sf_min_tasks,
+                         const NextAppend* next) const {
   Plan& P = *plan;
   P.clear();
+
+  // The nodes as the plan sees them: the tree as it is, or with `next`'s
+  // tokens appended (a grown chunk holds one token more; a new chunk, one
+  // token, is its parent's last child and holds the sequence that moved to it).
+  const size_t n_nodes = next ? next->n_nodes : nodes_.size();
+  std::vector<int32_t> grown, virt, vchild_head, vchild_next;
+  if (next) {
+    grown.assign(n_nodes, 0);
+    for (int32_t g : next->grow) grown[g] = 1;
+    virt.assign(n_nodes, -1);
+    vchild_head.assign(n_nodes, -1);
+    vchild_next.assign(next->add.size(), -1);
+    std::vector<int32_t> tail(n_nodes, -1);
+    for (size_t k = 0; k < next->add.size(); ++k) {
+      const NextAppend::Add& a = next->add[k];
+      virt[a.idx] = static_cast<int32_t>(k);
+      if (tail[a.parent] < 0)
+        vchild_head[a.parent] = static_cast<int32_t>(k);
+      else
+        vchild_next[tail[a.parent]] = static_cast<int32_t>(k);
+      tail[a.parent] = static_cast<int32_t>(k);
+    }
+  }
+  auto added = [&](int32_t n) -> const NextAppend::Add* {
+    return next && virt[n] >= 0 ? &next->add[virt[n]] : nullptr;
+  };
+  auto fill_of = [&](int32_t n) -> int32_t {
+    if (added(n)) return 1;
+    return static_cast<int32_t>(nodes_[n].tokens.size()) + (next ? grown[n] : 0);
+  };
+  auto ref_of = [&](int32_t n) -> int32_t { return added(n) ? 1 : nodes_[n].ref; };
+  std::vector<int32_t> kids;
+  auto children_of = [&](int32_t n) -> const std::vector<int32_t>& {
+    if (!next) return nodes_[n].children;
+    kids.clear();
+    if (!added(n)) kids = nodes_[n].children;
+    for (int32_t k = vchild_head[n]; k >= 0; k = vchild_next[k]) kids.push_back(next->add[k].idx);
+    return kids;
+  };
+  std::vector<int64_t> ends;
+  auto ended_of = [&](int32_t n) -> const std::vector<int64_t>& {
+    if (!next) return nodes_[n].ended;
+    ends.clear();
+    if (const NextAppend::Add* a = added(n)) {
+      ends.push_back(a->seq);
+      return ends;
+    }
+    for (int64_t s : nodes_[n].ended) {
+      bool moved = false;
+      for (int32_t k = vchild_head[n]; k >= 0 && !moved; k = vchild_next[k]) moved = next->add[k].seq == s;
+      if (!moved) ends.push_back(s);
+    }
+    return ends;
+  };
 
   // Caller row of each sequence: rank in ascending id order.
   std::map<int64_t, int32_t> qrow;
@@ -266,8 +376,10 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
   std::vector<int32_t> end_row;           // per DFS position
   struct Frame { int32_t node, parent_row; bool closing; int32_t row; };
   std::vector<Frame> stack;
-  const auto& rc = nodes_[0].children;
-  for (auto it = rc.rbegin(); it != rc.rend(); ++it) stack.push_back({*it, -1, false, -1});
+  {
+    const std::vector<int32_t>& rc = children_of(0);
+    for (auto it = rc.rbegin(); it != rc.rend(); ++it) stack.push_back({*it, -1, false, -1});
+  }
   while (!stack.empty()) {
     Frame f = stack.back();
     stack.pop_back();
@@ -275,19 +387,24 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
       P.rows[static_cast<size_t>(f.row) * 7 + 5] = static_cast<int32_t>(P.dfs_seq.size());
       continue;
     }
-    const Node& nd = nodes_[f.node];
+    const NextAppend::Add* a = added(f.node);
     int32_t r = static_cast<int32_t>(row_node.size());
     row_node.push_back(f.node);
-    P.rows.insert(P.rows.end(), {nd.id, f.parent_row, nd.start, static_cast<int32_t>(nd.tokens.size()),
-                                 static_cast<int32_t>(P.dfs_seq.size()), -1, nd.slot});
+    if (a)
+      P.rows.insert(P.rows.end(), {a->id, f.parent_row, a->start, 1, static_cast<int32_t>(P.dfs_seq.size()), -1,
+                                   a->slot});
+    else
+      P.rows.insert(P.rows.end(), {nodes_[f.node].id, f.parent_row, nodes_[f.node].start, fill_of(f.node),
+                                   static_cast<int32_t>(P.dfs_seq.size()), -1, nodes_[f.node].slot});
     P.row_node.push_back(f.node);
-    for (int64_t s : nd.ended) {
+    for (int64_t s : ended_of(f.node)) {
       P.dfs_seq.push_back(s);
       P.dfs_qrow.push_back(qrow.at(s));
       end_row.push_back(r);
     }
     stack.push_back({f.node, f.parent_row, true, r});
-    for (auto it = nd.children.rbegin(); it != nd.children.rend(); ++it) stack.push_back({*it, r, false, -1});
+    const std::vector<int32_t>& ch = children_of(f.node);
+    for (auto it = ch.rbegin(); it != ch.rend(); ++it) stack.push_back({*it, r, false, -1});
   }
   const int32_t n_rows = static_cast<int32_t>(row_node.size());
   const int32_t n_seq = static_cast<int32_t>(P.dfs_seq.size());
@@ -496,16 +613,15 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
   // where each chunk ref lives, so a fill change can be patched in place
   P.ref_task.assign(P.ref_node.size(), -1);
   P.ref_pos.assign(P.ref_node.size(), -1);
-  P.private_ref.assign(nodes_.size(), -1);
+  P.private_ref.assign(n_nodes, -1);
   for (size_t t = 0; t < P.sf_tasks.size(); ++t)
     for (int c = 0; c < P.sf_tasks[t].n_chunks; ++c) {
       const int32_t k = P.sf_tasks[t].chunk_begin + c;
       P.ref_task[k] = static_cast<int32_t>(t);
       P.ref_pos[k] = c;
-      const Node& nd = nodes_[P.ref_node[k]];
+      const int32_t node = P.ref_node[k];
       // a private chunk's appends go to its last tile
-      if (nd.ref == 1 && P.ref_sub[k] + 1 == tiles_of(static_cast<int32_t>(nd.tokens.size())))
-        P.private_ref[P.ref_node[k]] = k;
+      if (ref_of(node) == 1 && P.ref_sub[k] + 1 == tiles_of(fill_of(node))) P.private_ref[node] = k;
     }
 }
 

@@ -130,6 +130,21 @@ struct Plan {
   void clear();
 };
 
+// The tree after one more token for each of a batch of sequences, as a plan
+// sees it, without changing the tree: which chunks grow in place and which
+// new chunks would be made (node index, id, slot, position, in the order
+// append_batch allocates them).  Token values play no part in a plan.
+struct NextAppend {
+  struct Add {
+    int32_t parent, idx, id, slot, start;
+    int64_t seq;
+  };
+  std::vector<int32_t> grow;  // nodes that take their sequence's token in place
+  std::vector<Add> add;       // new chunks
+  size_t n_nodes = 0;         // size of the node array afterwards
+  bool structural = false;    // the appends change the plan's shape
+};
+
 class Manager {
  public:
   Manager(int chunk, bool share);
@@ -158,6 +173,13 @@ class Manager {
   // before anything changes (unknown or repeated id, too few free slots).
   void append_batch(const int64_t* seqs, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops);
 
+  // What append_batch(seqs, n) would do, one token each (see NextAppend);
+  // false if it would fail.
+  bool predict_append_batch(const int64_t* seqs, int32_t n, NextAppend* out) const;
+  // Whether one more token for every live sequence would change the plan's
+  // shape (a last chunk full or shared, or a chunk opening another tile).
+  bool next_append_structural() const;
+
   // True when the last mutations only grew chunks in place (no chunk created
   // or freed, no sequence joined or left) since the last clear_structural().
   bool fills_only() const { return !structural_; }
@@ -173,7 +195,10 @@ class Manager {
   // sequence-first tasks (physically shared pages, no chunk-first phase).
   // sf_group <= 0: chosen per plan, the largest of 16, 8, 4 that gives at
   // least sf_min_tasks sequence-first tasks (Plan::sf_group says which).
-  void build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan, int64_t sf_min_tasks = 0) const;
+  // With `next`, the plan of the tree after those appends (the same plan
+  // that build_plan gives once they are made).
+  void build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan, int64_t sf_min_tasks = 0,
+                  const NextAppend* next = nullptr) const;
   // Bring a plan built for the current structure up to date with chunk fills
   // that grew since: fill counts in the table, the chunk refs and the refs
   // carried inline by task records, and the token totals.
@@ -205,7 +230,12 @@ class Manager {
   int64_t n_nodes_ = 0;
   std::vector<Node> nodes_;                 // nodes_[0] is the root
   std::vector<int32_t> free_nodes_;         // reusable indices in nodes_
-  std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_;
+  // free slots, a min-heap whose array the prediction of appends reads
+  struct FreeSlots : std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> {
+    using priority_queue::priority_queue;
+    const std::vector<int32_t>& heap() const { return c; }
+  };
+  FreeSlots free_;
   std::map<int64_t, int32_t> end_;          // seq -> node index where it ends
   std::map<int64_t, int32_t> len_;          // seq -> length
 };

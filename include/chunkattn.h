@@ -23,6 +23,17 @@
  *    the caller's stream only and is asynchronous: errors inside kernels
  *    surface through the stream.  Host-side tables are built on the calling
  *    thread.
+ *  - Chunk-table uploads copy from pinned host staging: the caller's
+ *    (ca_attach_staging), or, if the caller lends none, pinned memory the
+ *    library allocates at the first upload that needs it and frees in
+ *    ca_destroy.  That is the library's only allocation.
+ *  - CA_E_HIP from a call that only reads the tree (ca_attend,
+ *    ca_attend_phase, ca_prepare) leaves the context usable; the next step
+ *    uploads the table again.  ca_insert puts the tree back as it was.  After
+ *    appends (ca_append, ca_append_batch, ca_decode_step) have changed the
+ *    tree, a failure to enqueue their K/V writes leaves tokens in the tree
+ *    that the pool does not hold: every later call that changes the tree or
+ *    runs device work then returns CA_E_STATE (destroy the context).
  *  - A context is not thread-safe.  Calls that enqueue device work on
  *    different streams must be ordered by the caller.
  *  - Element types: K, V, Q and the output are IEEE binary16 (fp16); the
@@ -93,11 +104,26 @@ enum {
                                     (sequence, head) pairs, else two (measured crossover on
                                     MI355X).  All give the same bits; ca_stats reports the
                                     choice for the current tree. */
-  CA_OPT_MERGE_POLL_LIMIT = 4    /* one-launch step: how many times a merge wave checks that
+  CA_OPT_MERGE_POLL_LIMIT = 4,   /* one-launch step: how many times a merge wave checks that
                                     its partials have arrived before it gives up and writes
                                     NaN for its (sequence, head); 0 (default): the library's
                                     own bound (about 0.1 s, never reached in practice).  For
                                     exercising that failure path. */
+  CA_OPT_FAIL_DEVICE_OPS = 5,    /* for tests of failure handling: the next `value` device
+                                    operations of the context (table uploads, kernel
+                                    launches) fail with CA_E_HIP before anything is
+                                    enqueued; 0 (default) turns it off.  Does not touch the
+                                    chunk table. */
+  CA_OPT_PREBUILD_PLAN = 6       /* 1 (default): when ca_decode_step, or ca_append_batch over
+                                    every live sequence in ascending id order, has enqueued its
+                                    work and the next such append will change the table's shape
+                                    (a last chunk is full or shared, or a chunk of 128 opens
+                                    its second tile), the call also builds the table of that
+                                    tree before it returns, while the GPU runs the work just
+                                    enqueued (the summary's section 3.3: context generation
+                                    on the CPU overlapped with the GPU); that next append then
+                                    takes it instead of rebuilding.  0: every table is built
+                                    in the call that needs it. */
 };
 
 /* ca_attend_phase phases.  A step is CA_PHASE_PARTIALS (one launch holding
@@ -141,6 +167,7 @@ typedef struct ca_stats_t {
   int64_t cf_chunks_per_task; /* chunk-first group of the current plan */
   int64_t one_launch_step;    /* 1 if ca_attend runs the step as one launch */
   int64_t sf_chunks_per_task; /* sequence-first group of the current plan */
+  int64_t prebuilt_plans;     /* tables built ahead, by the call before the one that needed them */
 } ca_stats_t;
 
 /* Bytes of one chunk slot: K and V, all heads, fp16 = 4 * heads * chunk_size
@@ -177,6 +204,19 @@ int ca_workspace_bytes(ca_ctx* ctx, size_t* out);
  * stay alive while enqueued steps use it. */
 int ca_attach_workspace(ca_ctx* ctx, void* dev, size_t bytes);
 
+/* Pinned host staging for chunk-table uploads (the plan is cached and copied
+ * to the device only after the tree changed shape: summary section 3.3):
+ * ca_staging_bytes gives the size the current tree needs (three parts, each
+ * one table, so an upload never waits for the last two).  ca_attach_staging
+ * lends `bytes` of pinned host memory (hipHostMalloc, or a pinned torch
+ * tensor), 256-byte aligned; the caller owns it and keeps it alive until it
+ * attaches another or destroys the context.  It first waits for copies still
+ * reading earlier staging, so that memory may be freed once it returns.
+ * host NULL: back to library-owned staging.  A step whose table must be
+ * uploaded and does not fit the attached staging returns CA_E_WORKSPACE. */
+int ca_staging_bytes(ca_ctx* ctx, size_t* out);
+int ca_attach_staging(ca_ctx* ctx, void* host, size_t bytes);
+
 /* Tuning knobs (CA_OPT_*).  Takes effect at the next table rebuild. */
 int ca_set_option(ca_ctx* ctx, int option, int value);
 
@@ -188,7 +228,8 @@ int ca_set_option(ca_ctx* ctx, int option, int value);
  * passes this call.  A divergence inside a stored chunk splits that chunk.
  * *n_matched (may be NULL) receives the number of leading tokens already
  * stored.  Errors: CA_E_DUP_SEQ, CA_E_INVALID_ARG (n < 1, NULL pointers),
- * CA_E_NO_CAPACITY.  A failed call changes nothing. */
+ * CA_E_NO_CAPACITY, CA_E_HIP (the copy could not be enqueued).  A failed call
+ * changes nothing (after CA_E_HIP the tree is put back as it was). */
 int ca_insert(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n,
               const void* k_dev, const void* v_dev, void* stream, int32_t* n_matched);
 
@@ -198,7 +239,9 @@ int ca_insert(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n,
  * grows new private chunks.  k_dev, v_dev: fp16 [n][heads][head_dim].
  * An append that lands wholly in place keeps the table's shape, as in
  * ca_append_batch (fill counts stored on the device by the write launch).
- * Errors: CA_E_UNKNOWN_SEQ, CA_E_INVALID_ARG, CA_E_NO_CAPACITY. */
+ * Errors: CA_E_UNKNOWN_SEQ, CA_E_INVALID_ARG, CA_E_NO_CAPACITY (nothing
+ * changes); CA_E_HIP (the tree changed but the K/V could not be written: the
+ * context is unusable, see the conventions above). */
 int ca_append(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n,
               const void* k_dev, const void* v_dev, void* stream);
 
@@ -213,7 +256,8 @@ int ca_append(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n,
  * stores are ordered on `stream` like the K/V writes: enqueue appends and
  * steps of one context on one stream (or order them with events).
  * Errors: CA_E_UNKNOWN_SEQ, CA_E_INVALID_ARG (an id repeated in the batch),
- * CA_E_NO_CAPACITY; all are detected before anything changes. */
+ * CA_E_NO_CAPACITY; all are detected before anything changes.  CA_E_HIP: as
+ * for ca_append. */
 int ca_append_batch(ca_ctx* ctx, int32_t n, const int64_t* seq_ids, const int32_t* tokens,
                     const void* k_dev, const void* v_dev, void* stream);
 
@@ -236,7 +280,13 @@ int ca_remove(ca_ctx* ctx, int64_t seq_id);
  * fixed order, so the result does not depend on block timing.  Steps of one
  * context must not overlap (they share the workspace and its arrival
  * counters).  No host synchronisation.
- * Errors: CA_E_EMPTY, CA_E_WORKSPACE, CA_E_NO_POOL, CA_E_HIP. */
+ * HIP graphs: a step whose table is already on the device (a step or
+ * ca_prepare ran since the tree last changed shape) enqueues kernel launches
+ * only, and can be captured; the graph replays the step with the pointers
+ * and the tree shape of the capture (appends that only grow chunks in place
+ * keep it valid: they store the fill counts on the device).  A step that
+ * would upload the table while its stream is capturing returns CA_E_STATE.
+ * Errors: CA_E_EMPTY, CA_E_WORKSPACE, CA_E_NO_POOL, CA_E_HIP, CA_E_STATE. */
 int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream);
 
 /* One decode step of the whole batch (summary section 3.1: decoding appends
@@ -256,7 +306,9 @@ int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream);
  * CA_E_WORKSPACE (a step that grew new chunks can need a larger workspace)
  * and CA_E_UNSUPPORTED (a step beyond the kernels' index range) come after
  * the tokens were stored: attach a workspace of ca_workspace_bytes and finish
- * with ca_attend. */
+ * with ca_attend.  CA_E_HIP from the step's launch also comes after the
+ * tokens were stored (by a write launch in its place); if they cannot be
+ * stored either, the context is unusable (see the conventions above). */
 int ca_decode_step(ca_ctx* ctx, const int32_t* tokens, const void* k_dev, const void* v_dev,
                    const void* q_dev, void* out_dev, void* stream);
 
@@ -280,6 +332,13 @@ int ca_list_sequences(ca_ctx* ctx, int64_t* ids, int cap);
  * Pointers may be NULL with capacity 0 to query sizes. */
 int ca_export_table(ca_ctx* ctx, int32_t* rows, int cap_rows, int64_t* dfs_seq_order,
                     int cap_seqs, int* n_rows, int* n_seqs);
+
+/* The device table of the current plan as it is uploaded (records, chunk
+ * refs, row and partial lists, zeroed arrival counters; its layout is
+ * private to the library): *bytes receives its size; buf may be NULL with
+ * cap 0 to query it.  For bit-exact comparison of plans in tests.
+ * CA_E_INVALID_ARG if cap is too small (nothing written). */
+int ca_export_plan(ca_ctx* ctx, void* buf, size_t cap, size_t* bytes);
 
 int ca_stats(ca_ctx* ctx, ca_stats_t* out);
 const char* ca_last_error(ca_ctx* ctx);

@@ -542,3 +542,127 @@ def test_tiny_chunks_random_ops_bit_exact_against_model(chunk):
                 got = e.name
             assert got == want, (chunk, trial, step, kind)
             model_and_lib_agree(m, ca)
+
+
+def test_staging_size_and_attach_checks():
+    """ca_staging_bytes is three 256-byte aligned parts, each holding the
+    table (the table alone is what ca_workspace_bytes holds besides the
+    partials); a misaligned staging pointer is refused; NULL detaches."""
+    lib = _capi.load()
+    ca = ChunkAttention(8, 64, device=None)
+    for i in range(5):
+        ca.insert(i, list(range(100)) + [1000 + i] * (10 + 30 * i))
+    need = ctypes.c_size_t(0)
+    assert lib.ca_staging_bytes(ca.ctx, ctypes.byref(need)) == 0
+    assert need.value > 0 and need.value % (3 * 256) == 0
+    assert need.value // 3 < ca.workspace_bytes()
+    assert lib.ca_staging_bytes(ca.ctx, None) == -1
+    assert lib.ca_attach_staging(ca.ctx, ctypes.c_void_p(4096 + 8), 1 << 16) == -1
+    assert lib.ca_attach_staging(ca.ctx, None, 0) == 0
+
+
+def test_failure_injection_option():
+    lib = _capi.load()
+    ca = ChunkAttention(2, 16, device=None)
+    assert lib.ca_set_option(ca.ctx, _capi.CA_OPT_FAIL_DEVICE_OPS, -1) == -1
+    assert lib.ca_set_option(ca.ctx, _capi.CA_OPT_FAIL_DEVICE_OPS, 3) == 0
+    # a host-only context runs no device operation: inserts are unaffected
+    ca.insert(1, list(range(70)))
+    assert ca.sequences() == [1]
+
+
+def test_insert_with_failed_copy_changes_nothing():
+    """An insert whose K/V copy cannot be enqueued (injected failure, before any
+    HIP call) returns CA_E_HIP and leaves the tree as it was."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.device_count() > 0:
+        pytest.skip("uses a stand-in pool address: only where no GPU is visible")
+    lib = _capi.load()
+    ctx = ctypes.c_void_p()
+    assert lib.ca_create(2, 128, 64, ctypes.byref(ctx)) == 0
+    try:
+        assert lib.ca_attach_pool(ctx, ctypes.c_void_p(1 << 20), 32) == 0
+        assert lib.ca_set_option(ctx, _capi.CA_OPT_FAIL_DEVICE_OPS, 1 << 20) == 0
+        toks = (ctypes.c_int32 * 150)(*range(150))
+        matched = ctypes.c_int32(-7)
+        rc = lib.ca_insert(ctx, 5, toks, 150, ctypes.c_void_p(1 << 21), ctypes.c_void_p(1 << 22), None,
+                           ctypes.byref(matched))
+        assert rc == -8 and b"injected" in lib.ca_last_error(ctx)
+        assert matched.value == -7
+        assert lib.ca_list_sequences(ctx, None, 0) == 0
+        st = _capi.ca_stats_t()
+        assert lib.ca_stats(ctx, ctypes.byref(st)) == 0
+        assert st.free_slots == 32 and st.chunks == 0 and st.unique_tokens == 0
+        # the same id can be tried again (it was not left half inserted)
+        rc = lib.ca_insert(ctx, 5, toks, 150, ctypes.c_void_p(1 << 21), ctypes.c_void_p(1 << 22), None, None)
+        assert rc == -8 and lib.ca_list_sequences(ctx, None, 0) == 0
+    finally:
+        lib.ca_destroy(ctx)
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 128])
+def test_prebuilt_plans_equal_fresh_builds(chunk):
+    """Two host contexts run the same script, one building the next table
+    ahead of structural decode steps (in the call before), one building every
+    table in the call that needs it: after every call their chunk tables,
+    device table images and plan statistics are equal byte for byte, and the
+    first one did take prebuilt tables.  The script decodes one token per
+    live sequence (so last chunks fill up, chunks of 128 open their second
+    tile, shared last chunks get private children) with inserts that share
+    and split chunks, duplicates, removals and partial batches mixed in."""
+    rng = np.random.default_rng(700 + chunk)
+    a = ChunkAttention(3, 6000, device=None, chunk_size=chunk)
+    b = ChunkAttention(3, 6000, device=None, chunk_size=chunk)
+    b.set_option(_capi.CA_OPT_PREBUILD_PLAN, 0)
+    live = {}
+    next_id = [0]
+    keys = ("chunks", "shared_chunks", "unique_tokens", "attended_tokens", "cf_tasks", "cf_units", "sf_tasks",
+            "partials", "cf_chunks_per_task", "sf_chunks_per_task", "free_slots")
+
+    def insert(toks):
+        sid = next_id[0]
+        next_id[0] += 1
+        for ca in (a, b):
+            ca.insert(sid, toks)
+        live[sid] = list(toks)
+
+    base = [int(x) for x in rng.integers(0, 1000, size=int(rng.integers(chunk, 3 * chunk)))]
+    for i in range(6):
+        insert(base + [5000 + i] * int(rng.integers(0, chunk + 5)))
+    insert(list(live[2]))  # a duplicate: its last chunk is shared
+    step = 0
+    for it in range(260):
+        u = rng.random()
+        ids = sorted(live)
+        if u < 0.82:
+            toks = [int(x) for x in rng.integers(0, 1000, size=len(ids))]
+            for ca in (a, b):
+                ca.append_batch(ids, toks)
+            for s_, t in zip(ids, toks):
+                live[s_].append(t)
+            step += 1
+        elif u < 0.88:
+            src = live[ids[int(rng.integers(0, len(ids)))]]
+            cut = int(rng.integers(1, len(src) + 1))
+            insert(src[:cut] + ([int(rng.integers(2000, 3000))] if rng.random() < 0.7 else []))
+        elif u < 0.93 and len(ids) > 3:
+            victim = ids[int(rng.integers(0, len(ids)))]
+            for ca in (a, b):
+                ca.remove(victim)
+            del live[victim]
+        else:
+            sub = sorted(rng.choice(ids, size=max(1, len(ids) // 2), replace=False).tolist())
+            toks = [int(x) for x in rng.integers(0, 1000, size=len(sub))]
+            for ca in (a, b):
+                ca.append_batch(sub, toks)
+            for s_, t in zip(sub, toks):
+                live[s_].append(t)
+        ra, oa = a.export_table()
+        rb, ob = b.export_table()
+        assert np.array_equal(ra, rb) and oa == ob, it
+        assert a.export_plan() == b.export_plan(), it
+        sa, sb = a.stats(), b.stats()
+        for k in keys:
+            assert sa[k] == sb[k], (it, k)
+    assert a.stats()["prebuilt_plans"] >= 3, a.stats()["prebuilt_plans"]
+    assert b.stats()["prebuilt_plans"] == 0

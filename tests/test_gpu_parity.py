@@ -862,3 +862,77 @@ def test_workspace_too_small():
     kv = [[np.concatenate([a, b[i:i + 1]]) for a, b in zip(wl.seq_kv(i), (k, v))] for i in range(n)]
     assert_parity(out.cpu().numpy(), A.decode_step(q2, kv), "after growing the workspace")
     ca.ws = big  # keep it alive with the context
+
+
+@pytest.mark.parametrize("fused", [0, 1])
+def test_captured_step_replays_equal_eager_steps(fused):
+    """A step captured in a HIP graph (torch.cuda.graph around ca_attend) and
+    replayed with new queries copied into the captured q: every replay equals
+    an eager step on the same q bit for bit and matches the oracle, with eager
+    steps and host syncs between replays; tokens appended in place between
+    replays (fill counts stored on the device) are seen by the replays.  In
+    the one-launch step nothing carries over between replays (arrival
+    counters return to zero).  A step that would upload the table while the
+    stream captures is refused (CA_E_STATE)."""
+    _say(f"graph capture, fused={fused}")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import CaError, _capi
+    rng = np.random.default_rng(400 + fused)
+    wl = make_prefix_suffix(200, [int(x) for x in rng.integers(5, 50, size=24)], heads=4, seed=401)
+    ca = build_ca(wl, capacity=80)
+    ca.set_option(_capi.CA_OPT_FUSED_MERGE, fused)
+    twin = build_ca(wl, capacity=80)
+    n, H = wl.n_seq, wl.heads
+    q = torch.from_numpy(wl.q).cuda()
+    out = torch.empty_like(q)
+    ca.ensure_workspace()
+    ca.attend(q, out)  # the table is on the device: the step only launches kernels
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ca.attend(q, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ca.attend(q, out)
+    torch.cuda.synchronize()
+    kv = [[x.copy() for x in wl.seq_kv(i)] for i in range(n)]
+    for rep in range(6):
+        if rep in (2, 4):
+            # one token per sequence, in place (every last chunk has room)
+            k = rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+            v = rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+            kt, vt = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+            toks = np.full(n, 9000 + rep, np.int32)
+            ca.append_batch(list(range(n)), toks, kt, vt)
+            twin.append_batch(list(range(n)), toks, kt, vt)
+            for i in range(n):
+                kv[i] = [np.concatenate([a, b[i:i + 1]]) for a, b in zip(kv[i], (k, v))]
+        qn = rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+        q.copy_(torch.from_numpy(qn).cuda())
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        eager = run_step(twin, qn)
+        assert np.array_equal(got.view(np.uint16), eager.view(np.uint16)), rep
+        assert_parity(got, A.decode_step(qn, kv), f"graph replay {rep}")
+    assert ca.stats()["table_uploads"] == 1
+    # a structural change: the next step must upload, which a capture refuses
+    ca.insert(n, list(range(40)), torch.zeros((40, H, 128), dtype=torch.float16, device="cuda:0"),
+              torch.zeros((40, H, 128), dtype=torch.float16, device="cuda:0"))
+    q2 = torch.zeros((n + 1, H, 128), dtype=torch.float16, device="cuda:0")
+    out2 = torch.empty_like(q2)
+    ca.ensure_workspace()
+    g2 = torch.cuda.CUDAGraph()
+    with pytest.raises(CaError) as ei:
+        with torch.cuda.graph(g2):
+            ca.attend(q2, out2)
+    assert ei.value.name == "state"
+    torch.cuda.synchronize()
+    ca.attend(q2, out2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out2).all()
