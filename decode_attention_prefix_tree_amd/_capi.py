@@ -23,6 +23,7 @@ CA_OPT_FUSED_MERGE = 3
 CA_OPT_MERGE_POLL_LIMIT = 4
 CA_OPT_FAIL_DEVICE_OPS = 5
 CA_OPT_PREBUILD_PLAN = 6
+CA_NOALLOC_SCRATCH_BYTES = 16 << 20
 CA_PHASE_CHUNK_FIRST = 1
 CA_PHASE_SEQUENCE_FIRST = 2
 CA_PHASE_MERGE = 3
@@ -92,6 +93,7 @@ _SIGS = {
                                    _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "ca_remove": (_c.c_int, [_c.c_void_p, _c.c_int64]),
     "ca_attend": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "ca_attend_noalloc": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "ca_decode_step": (_c.c_int, [_c.c_void_p, _c.POINTER(_c.c_int32), _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                   _c.c_void_p, _c.c_void_p]),
     "ca_prepare": (_c.c_int, [_c.c_void_p, _c.c_void_p]),

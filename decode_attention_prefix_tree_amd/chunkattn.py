@@ -222,6 +222,19 @@ class ChunkAttention:
         check(self.ctx, rc)
         return out
 
+    def attend_noalloc(self, q, out, stream=None):
+        """attend() with the step's workspace in the library's static device
+        scratch (ca_attend_noalloc): no allocation by the library or here;
+        out must be given."""
+        if self.device is None:
+            raise CaError(-9, "host-only context")
+        if out is None:
+            raise ValueError("attend_noalloc writes into a caller-provided out")
+        q, out = self._qo(q, out)
+        check(self.ctx, self.lib.ca_attend_noalloc(self.ctx, ctypes.c_void_p(q.data_ptr()),
+                                                   ctypes.c_void_p(out.data_ptr()), self._stream(stream)))
+        return out
+
     def decode_step(self, tokens, k, v, q, out=None, stream=None):
         """Append tokens[r] with K/V row r to the r-th live sequence (ascending
         id), then attend with q; returns out (ca_decode_step)."""

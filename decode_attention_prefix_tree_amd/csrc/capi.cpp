@@ -31,6 +31,8 @@ struct Prebuild {
   double ms = 0.0;
 };
 
+static_assert(CA_NOALLOC_SCRATCH_BYTES == chunkattn::kStaticScratchBytes, "the header states the scratch size");
+
 struct ca_ctx {
   int heads = 0, head_dim = 0, chunk = 0, flags = 0;
   chunkattn::Manager mgr;
@@ -55,10 +57,11 @@ struct ca_ctx {
   bool plan_valid = false;
   bool fills_stale = false;  // plan structure current, chunk fills grew since
   int64_t fill_refreshes = 0, table_uploads = 0, patched_appends = 0;
-  // The device copy of the table: the workspace it was uploaded to and the
-  // tree version it holds.
+  // The device copy of the table: the workspace it was uploaded to (the
+  // caller's, or a device's static scratch) and the tree version it holds.
   uint64_t version = 1, uploaded_version = 0;
   void* uploaded_ws = nullptr;
+  int scratch_dev = -1;             // device whose static scratch uploaded_ws is, or -1
   size_t off_cf = 0, off_sf = 0, off_refs = 0, off_qrow = 0, off_seqparts = 0, off_partlist = 0;
   size_t off_arrivals = 0;
   size_t table_bytes = 0, off_part_o = 0, off_part_ms = 0, total_bytes = 0;
@@ -125,9 +128,21 @@ void touch_after_append(ca_ctx* c) {
   }
 }
 
+// Which context's table each device's static scratch holds (the last one
+// uploaded there); a context that finds another owner uploads again.
+std::mutex g_scratch_mu;
+const ca_ctx* g_scratch_owner[chunkattn::kMaxScratchDevices] = {};
+
+bool scratch_owned_by(const ca_ctx* c) {
+  if (c->scratch_dev < 0) return false;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_owner[c->scratch_dev] == c;
+}
+
 // The device table in workspace `ws` holds the current tree.
 bool table_current_in(const ca_ctx* c, const void* ws) {
-  return ws != nullptr && c->uploaded_version == c->version && c->uploaded_ws == ws;
+  if (ws == nullptr || c->uploaded_version != c->version || c->uploaded_ws != ws) return false;
+  return c->scratch_dev < 0 || scratch_owned_by(c);
 }
 
 // Some device table (at uploaded_ws) holds the current tree: appends can
@@ -335,7 +350,9 @@ void table_image(const ca_ctx* c, char* s) {
 // Staging bytes for the current table: three parts, each holding the table.
 size_t staging_need(const ca_ctx* c) { return ca_ctx::kStages * align_up(c->table_bytes); }
 
-void upload(ca_ctx* c, void* stream, void* ws) {
+// scratch_dev: the device whose static scratch ws is, or -1 for the caller's
+// workspace.
+void upload(ca_ctx* c, void* stream, void* ws, int scratch_dev = -1) {
   if (table_current_in(c, ws)) return;
   // A graph would replay the copy from a staging buffer that later uploads
   // rewrite (and waiting for the ring is no call for a capture): a step is
@@ -380,6 +397,11 @@ void upload(ca_ctx* c, void* stream, void* ws) {
   c->decode_epoch = 0;  // the upload wrote untagged fill counts
   c->uploaded_version = c->version;
   c->uploaded_ws = ws;
+  c->scratch_dev = scratch_dev;
+  if (scratch_dev >= 0) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    g_scratch_owner[scratch_dev] = c;
+  }
 }
 
 chunkattn::StepArgs step_args(ca_ctx* c, void* ws, const void* q, void* out) {
@@ -413,12 +435,16 @@ chunkattn::StepArgs step_args(ca_ctx* c, void* ws, const void* q, void* out) {
   return a;
 }
 
-// ws, ws_bytes: the workspace the step runs in.
-void check_step(ca_ctx* c, const void* q, void* out, const void* ws, size_t ws_bytes) {
+// ws, ws_bytes: the workspace the step runs in (the caller's, or the static
+// scratch of the allocation-free step, whose size is fixed).
+void check_step(ca_ctx* c, const void* q, void* out, const void* ws, size_t ws_bytes, bool fixed_ws = false) {
   if (!c->pool_attached || c->pool == nullptr) throw Error(CA_E_NO_POOL, "no device pool attached");
   if (c->mgr.live() == 0) throw Error(CA_E_EMPTY, "no live sequence");
   if (q == nullptr || out == nullptr) throw Error(CA_E_INVALID_ARG, "q and out must be device pointers");
   ensure_plan(c, !table_current_in(c, ws));
+  if (fixed_ws && ws_bytes < c->total_bytes)
+    throw Error(CA_E_WORKSPACE, "this step needs a workspace of " + std::to_string(c->total_bytes) +
+                                    " bytes; the static scratch holds " + std::to_string(ws_bytes));
   if (ws == nullptr || ws_bytes < c->total_bytes)
     throw Error(CA_E_WORKSPACE, "workspace of " + std::to_string(c->total_bytes) + " bytes needed, " +
                                     std::to_string(ws_bytes) + " attached");
@@ -585,9 +611,19 @@ void launch_step(ca_ctx* c, const chunkattn::StepArgs& a, void* stream) {
   }
 }
 
+// The static scratch of the allocation-free step on the current device
+// (its address is looked up at the first use on that device and kept).
+void* static_scratch_ws(int* dev) {
+  void* p = nullptr;
+  const int e = chunkattn::static_scratch(&p, dev);
+  if (e != 0) throw Error(CA_E_HIP, std::string("hipGetSymbolAddress(scratch): ") +
+                                        hipGetErrorString(static_cast<hipError_t>(e)));
+  return p;
+}
+
 // One attend step in workspace ws (after check_step).
-void attend_in(ca_ctx* c, const void* q, void* out, void* stream, void* ws) {
-  upload(c, stream, ws);
+void attend_in(ca_ctx* c, const void* q, void* out, void* stream, void* ws, int scratch_dev = -1) {
+  upload(c, stream, ws, scratch_dev);
   launch_step(c, step_args(c, ws, q, out), stream);
 }
 
@@ -640,6 +676,11 @@ int ca_create(int heads, int head_dim, int chunk_size, ca_ctx** out) {
 
 void ca_destroy(ca_ctx* ctx) {
   if (ctx == nullptr) return;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    for (const ca_ctx*& o : g_scratch_owner)
+      if (o == ctx) o = nullptr;
+  }
   delete ctx;
 }
 
@@ -675,7 +716,7 @@ int ca_attach_workspace(ca_ctx* ctx, void* dev, size_t bytes) {
     if (dev != nullptr && (reinterpret_cast<uintptr_t>(dev) % kAlign) != 0)
       throw Error(CA_E_INVALID_ARG, "workspace must be 256-byte aligned");
     // appends must not patch fill counts into a workspace the caller took back
-    if (ctx->uploaded_ws == ctx->ws && dev != ctx->ws) ctx->uploaded_ws = nullptr;
+    if (ctx->uploaded_ws == ctx->ws && ctx->scratch_dev < 0 && dev != ctx->ws) ctx->uploaded_ws = nullptr;
     ctx->ws = dev;
     ctx->ws_bytes = dev ? bytes : 0;
     return CA_OK;
@@ -877,6 +918,19 @@ int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream) {
     require_usable(ctx);
     check_step(ctx, q_dev, out_dev, ctx->ws, ctx->ws_bytes);
     attend_in(ctx, q_dev, out_dev, stream, ctx->ws);
+    return CA_OK;
+  });
+}
+
+int ca_attend_noalloc(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream) {
+  CA_GUARD(ctx, {
+    require_usable(ctx);
+    int dev = -1;
+    void* ws = static_scratch_ws(&dev);
+    check_step(ctx, q_dev, out_dev, ws, chunkattn::kStaticScratchBytes, true);
+    if (!table_current_in(ctx, ws) && ctx->lent_stage == nullptr)
+      throw Error(CA_E_STATE, "the chunk table must be uploaded: attach a staging buffer (ca_attach_staging) first");
+    attend_in(ctx, q_dev, out_dev, stream, ws, dev);
     return CA_OK;
   });
 }

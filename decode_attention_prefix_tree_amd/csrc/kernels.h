@@ -72,4 +72,12 @@ enum PartialsPart { kPartsBoth = 0, kPartsChunkFirst = 1, kPartsSequenceFirst = 
 int launch_partials(const StepArgs& a, int part, bool fuse_merge, void* stream);
 int launch_merge(const StepArgs& a, void* stream);
 
+// Device scratch for steps whose caller cannot allocate: a file-scope array
+// of the kernels' module, one copy per device, held until the process ends.
+// static_scratch() returns its device address on the current device (looked
+// up once per device and kept) and that device's index; a hipError_t value.
+constexpr size_t kStaticScratchBytes = size_t{16} << 20;  // CA_NOALLOC_SCRATCH_BYTES
+constexpr int kMaxScratchDevices = 64;
+int static_scratch(void** ptr, int* device);
+
 }  // namespace chunkattn

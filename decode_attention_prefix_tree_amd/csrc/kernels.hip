@@ -15,6 +15,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "kernels.h"
 #include "tile_layout.h"
@@ -859,6 +860,31 @@ int launch_merge(const StepArgs& a, void* stream) {
   dim3 grid((a.n_seq * a.heads + 3) / 4);
   hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
+}
+
+// The workspace of the allocation-free step: chunk table, arrival counters
+// and partial results of one step, at most kStaticScratchBytes.  On the host
+// the name stands for a host-side shadow, never for the device memory: host
+// code uses only the address that hipGetSymbolAddress returns per device.
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+int static_scratch(void** ptr, int* device) {
+  static std::mutex mu;
+  static void* addr[kMaxScratchDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (dev < 0 || dev >= kMaxScratchDevices) return static_cast<int>(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return static_cast<int>(e);
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *device = dev;
+  return 0;
 }
 
 }  // namespace chunkattn

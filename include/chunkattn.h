@@ -289,6 +289,26 @@ int ca_remove(ca_ctx* ctx, int64_t seq_id);
  * Errors: CA_E_EMPTY, CA_E_WORKSPACE, CA_E_NO_POOL, CA_E_HIP, CA_E_STATE. */
 int ca_attend(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, serving
+ * loops or harnesses that forbid allocation): ca_attend with the step's
+ * workspace (chunk table, arrival counters, partial results) in a static
+ * device array of the library instead of the caller's workspace.  The array
+ * holds 16 MiB (CA_NOALLOC_SCRATCH_BYTES); a step whose ca_workspace_bytes is
+ * larger returns CA_E_WORKSPACE.  There is one array per device, in the
+ * library's code object, held until the process ends; the current device
+ * (hipGetDevice) is the one used, and must hold the pool, q, out and the
+ * stream.  Its address is looked up (hipGetSymbolAddress) at the first call
+ * on each device.  The call allocates nothing: when the table must be
+ * uploaded it copies from staging the caller attached (ca_attach_staging;
+ * CA_E_STATE without), and the arrival counters start at zero with each
+ * upload.  Every context on a device shares that device's array: a context
+ * whose table another context has replaced there uploads it again, so calls
+ * of different contexts can alternate, but calls that overlap on one device
+ * (different streams or threads, without ordering) race.  Same arguments,
+ * results and other errors as ca_attend. */
+#define CA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int ca_attend_noalloc(ca_ctx* ctx, const void* q_dev, void* out_dev, void* stream);
+
 /* One decode step of the whole batch (summary section 3.1: decoding appends
  * to leaf chunks; section 2.2: one query token per sequence): token tokens[r]
  * with K/V row r of k_dev, v_dev (fp16 [n_live][heads][head_dim]) is appended
