@@ -77,6 +77,9 @@ def parse():
     ap.add_argument("--decode-only", default=None, metavar="MODE:BATCH:NC",
                     help="with --decode: one run only, e.g. decode_step:32:512 (modes decode_step, two_phase, "
                          "shared_pages_no_chunk_first), for profiling one configuration")
+    ap.add_argument("--row-appends", type=int, default=1, choices=(0, 1),
+                    help="with --decode: chunks made by appends stored row-major (1, the library default) or "
+                         "as tiles (0)")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the per-kernel timing loop (for rocprofv3 runs); prints its event means")
     ap.add_argument("--phases", action="store_true",
@@ -223,18 +226,19 @@ def cpu_baseline(wl, seconds_target):
 
 
 def decode_progression(torch, n_seq, n_shared, checkpoints, two_phase, flush, window=16, heads=32, seed=7,
-                       one_call=False):
+                       one_call=False, row_appends=1):
     """Decode steps from a fully shared prompt: each step appends one token per
     sequence and attends, either as ca_append_batch + ca_attend or, with
     one_call, as ca_decode_step.  Returns, per checkpoint n_c (the completion
     length reached), the mean cold GPU time of the append and the attend (or
     of the whole step) over the `window` steps ending there, and the host time
     per step."""
-    from decode_attention_prefix_tree_amd import ChunkAttention
+    from decode_attention_prefix_tree_amd import ChunkAttention, _capi
     gen = torch.Generator(device="cuda").manual_seed(seed)
     max_c = max(checkpoints)
     cap = (n_shared + 63) // 64 + n_seq * ((max_c + 63) // 64 + 1) + 8
     ca = ChunkAttention(heads, cap, device="cuda:0", two_phase=two_phase)
+    ca.set_option(_capi.CA_OPT_ROW_APPENDS, row_appends)
     ks = torch.randn((n_shared, heads, 128), generator=gen, device="cuda").half()
     vs = torch.randn((n_shared, heads, 128), generator=gen, device="cuda").half()
     prompt = np.arange(n_shared, dtype=np.int32)
@@ -346,8 +350,9 @@ def decode_main(args, torch):
     if args.decode_only:
         mode, batch, nc = args.decode_only.split(":")
         two_phase, one_call = {m[0]: m[1:] for m in modes}[mode]
-        line["config"].update({"mode": mode, "batch": int(batch), "n_c": int(nc)})
-        r = decode_progression(torch, int(batch), 2048, [int(nc)], two_phase, flush, one_call=one_call)[int(nc)]
+        line["config"].update({"mode": mode, "batch": int(batch), "n_c": int(nc), "row_appends": args.row_appends})
+        r = decode_progression(torch, int(batch), 2048, [int(nc)], two_phase, flush, one_call=one_call,
+                               row_appends=args.row_appends)[int(nc)]
         line.update(r)
         line["value"] = r["generated_tokens_per_s"]
         print(json.dumps(line), flush=True)

@@ -23,6 +23,7 @@ CA_OPT_FUSED_MERGE = 3
 CA_OPT_MERGE_POLL_LIMIT = 4
 CA_OPT_FAIL_DEVICE_OPS = 5
 CA_OPT_PREBUILD_PLAN = 6
+CA_OPT_ROW_APPENDS = 7
 CA_NOALLOC_SCRATCH_BYTES = 16 << 20
 CA_PHASE_CHUNK_FIRST = 1
 CA_PHASE_SEQUENCE_FIRST = 2
@@ -70,6 +71,7 @@ class ca_stats_t(ctypes.Structure):
         ("one_launch_step", ctypes.c_int64),
         ("sf_chunks_per_task", ctypes.c_int64),
         ("prebuilt_plans", ctypes.c_int64),
+        ("row_chunks", ctypes.c_int64),
     ]
 
 

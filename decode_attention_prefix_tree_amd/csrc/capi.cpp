@@ -432,6 +432,7 @@ chunkattn::StepArgs step_args(ca_ctx* c, void* ws, const void* q, void* out) {
   a.app_epoch = 0;
   a.half_tiles = c->chunk < chunkattn::kTileKeys ? 1 : 0;
   a.max_polls = c->merge_poll_limit;
+  a.row_chunks = p.row_refs > 0 ? 1 : 0;
   return a;
 }
 
@@ -491,7 +492,8 @@ bool fill_patches(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, std::vecto
     }
     const int32_t task_off =
         p.ref_pos[k] < chunkattn::kSfInline ? tasks + p.ref_task[k] * kTaskInts + kFillField + p.ref_pos[k] : -1;
-    out->push_back(FillPatch{refs + 2 * k + 1, task_off, c->mgr.tile_fill(o.dst_key0 + o.n_rows, p.ref_sub[k])});
+    const int32_t row = c->mgr.row(o.node) ? chunkattn::kRowBit : 0;
+    out->push_back(FillPatch{refs + 2 * k + 1, task_off, c->mgr.tile_fill(o.dst_key0 + o.n_rows, p.ref_sub[k]) | row});
   }
   return true;
 }
@@ -504,26 +506,60 @@ bool fill_patches(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, std::vecto
 // never share a 16-byte unit.  Keys are written in increasing order, so a
 // piece that starts a chunk's part of a tile is that part's first write
 // since the slot was allocated: it clears the part's other keys (unwritten V
-// columns must be finite, they meet zero probabilities).
+// columns must be finite, they meet zero probabilities).  A row-major chunk
+// needs no clearing (its readers never touch rows past the fill).  A
+// conversion to tiles is one piece per tile holding the chunk's keys: the
+// chunk's part of the tile and how many of its keys are filled.
 void tile_pieces(const chunkattn::KvOp& o, int C, std::vector<chunkattn::KvOpDev>* out) {
   constexpr int32_t T = chunkattn::kTileKeys;
   const int32_t part = std::min<int32_t>(C, T);  // keys of one chunk in one tile
+  if (o.mode == chunkattn::kOpConvert) {
+    for (int32_t done = 0; done < o.n_rows; done += part) {
+      const int64_t dg = static_cast<int64_t>(o.dst_slot) * C + done;
+      const int32_t key0 = static_cast<int32_t>(dg % T);
+      out->push_back(chunkattn::KvOpDev{static_cast<int32_t>(dg / T), key0, std::min(part, o.n_rows - done), 0, 0,
+                                        key0, key0 + part, chunkattn::kKvToTiles});
+    }
+    return;
+  }
+  const bool rows = o.mode == chunkattn::kOpRows;
   for (int32_t done = 0; done < o.n_rows;) {
     const int64_t dg = static_cast<int64_t>(o.dst_slot) * C + o.dst_key0 + done;
     const int32_t key0 = static_cast<int32_t>(dg % T);
     const int32_t n = std::min<int32_t>(o.n_rows - done, T - key0);
     const int32_t src0 = o.from_pool ? o.src_slot * C + o.src_row0 + done : o.src_row0 + done;
-    const bool first = dg % part == 0;
+    const bool first = !rows && dg % part == 0;
     out->push_back(chunkattn::KvOpDev{static_cast<int32_t>(dg / T), key0, n, src0, o.from_pool,
-                                      first ? key0 : 0, first ? key0 + part : 0, 0});
+                                      first ? key0 : 0, first ? key0 + part : 0,
+                                      rows ? chunkattn::kKvRowWrite : chunkattn::kKvTileWrite});
     done += n;
   }
 }
 
 // Launch the copies, kOpsPerLaunch tile pieces at a time; the patches of an
 // op (if any) ride with the launch that writes its last piece.
+void launch_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* k, const void* v, void* stream,
+                   const std::vector<FillPatch>& patches);
+
 void run_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* k, const void* v, void* stream,
                 const std::vector<FillPatch>& patches = {}) {
+  // Conversions to tiles first, in launches of their own: the copies of the
+  // same mutation may read the converted chunks (a split's tail).
+  std::vector<chunkattn::KvOp> converts, rest;
+  for (const chunkattn::KvOp& o : ops) (o.mode == chunkattn::kOpConvert ? converts : rest).push_back(o);
+  if (converts.empty()) {
+    launch_kv_ops(c, ops, k, v, stream, patches);
+    return;
+  }
+  if (!patches.empty()) throw Error(CA_E_INTERNAL, "fill patches with conversions");
+  launch_kv_ops(c, converts, k, v, stream, {});
+  if (!rest.empty()) launch_kv_ops(c, rest, k, v, stream, {});
+}
+
+// The launches of a list of copies (no conversion after another copy of the
+// same list: conversions come in lists of their own).
+void launch_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* k, const void* v, void* stream,
+                   const std::vector<FillPatch>& patches) {
   std::vector<chunkattn::KvOpDev> pieces;
   std::vector<int32_t> patch_of;  // per piece: index into patches, or -1
   for (size_t i = 0; i < ops.size(); ++i) {
@@ -778,6 +814,10 @@ int ca_set_option(ca_ctx* ctx, int option, int value) {
     } else if (option == CA_OPT_FUSED_MERGE) {
       if (value < 0 || value > 2) throw Error(CA_E_INVALID_ARG, "fused merge is 0, 1 or 2 (automatic)");
       ctx->fused_merge = value;
+    } else if (option == CA_OPT_ROW_APPENDS) {
+      if (value < 0 || value > 1) throw Error(CA_E_INVALID_ARG, "row appends is 0 or 1");
+      ctx->mgr.set_row_appends(value != 0);
+      return CA_OK;  // chunks made from now on
     } else if (option == CA_OPT_PREBUILD_PLAN) {
       if (value < 0 || value > 1) throw Error(CA_E_INVALID_ARG, "prebuild is 0 or 1");
       ctx->prebuild_on = value != 0;
@@ -1062,6 +1102,7 @@ int ca_stats(ca_ctx* ctx, ca_stats_t* out) {
     s.sf_chunks_per_task = ctx->plan.sf_group;
     s.one_launch_step = one_launch(ctx) ? 1 : 0;
     s.prebuilt_plans = ctx->prebuilt_plans;
+    s.row_chunks = ctx->mgr.row_chunks();
     *out = s;
     return CA_OK;
   });

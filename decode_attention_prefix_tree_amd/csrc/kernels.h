@@ -20,8 +20,11 @@ constexpr int kSfReuseField = 5;
 constexpr int kSfAppendField = 6;
 // Fill counts (at most 64) in the device table may carry, above bit 8, the
 // epoch of the decode step that last grew them in the kernel; readers mask.
+// Bit 7 marks a chunk stored row-major (chunks grown by appends: see
+// tile_layout.h); it rides along with the count wherever the count goes.
 constexpr int kFillBits = 8;
-constexpr int kFillMask = (1 << kFillBits) - 1;
+constexpr int kRowBit = 1 << 7;
+constexpr int kFillMask = kRowBit - 1;
 constexpr unsigned kEpochMask = (1u << (32 - kFillBits)) - 1;
 constexpr int kDenseParts = 16; // most partials per sequence for the dense partial layout
 
@@ -59,6 +62,9 @@ struct StepArgs {
   // One-launch step: polls a merge wave makes before it gives up and writes
   // NaN (0: the built-in bound, about 0.1 s).
   int max_polls;
+  // Some chunk of the plan is stored row-major (kRowBit in its fill count):
+  // the launch takes the kernel instance that reads both layouts.
+  int row_chunks;
 };
 
 // Which blocks of the partials kernel to launch.

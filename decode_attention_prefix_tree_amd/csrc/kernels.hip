@@ -585,8 +585,12 @@ __device__ __forceinline__ void chunk_first_block(const StepArgs& a, int logical
 // 64-entry LDS row of its wave.  Three waves per SIMD keep about 384 KiB of
 // loads in flight per CU.  kAppend: a decode step whose blocks also write the
 // new tokens; the attend-only kernel has no stores into the pool or the
-// table, so its table reads stay scalar loads.
-template <bool kFuse, bool kNT, bool kAppend, bool kHalf>
+// table, so its table reads stay scalar loads.  kRow: some chunks are stored
+// row-major (tile_layout.h); a wave reads such a chunk by rows: lane group
+// g = lane / 16 takes rows 4j + g, each lane 8 dims of them (every load is
+// 1 KiB of contiguous rows), scores are summed across the group's 16 lanes,
+// and the chunk's output rows join the tile-layout accumulators through LDS.
+template <bool kFuse, bool kNT, bool kAppend, bool kHalf, bool kRow>
 __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logical, char* smem) {
   // heads vary fastest: blocks that run together read neighbouring 32 KiB
   // tiles of the same slots, which keeps HBM accesses close to sequential
@@ -643,24 +647,36 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
       const int cslot = ac < kSfInline ? t[8 + ac] : a.chunk_refs[2 * (chunk_begin + ac)];
       // key p of a 32-token chunk is key 32 * (slot % 2) + p of its tile
       const int slot = kHalf ? cslot >> 1 : cslot;
-      if (kHalf) p += (cslot & 1) * 32;
       _Float16* kw = const_cast<_Float16*>(pool) + tile_base(slot, head, H, 0);
       _Float16* vw = kw + TILE;
-      // K: load (p/32)*8 + j, lanes (half, p%32): dims 16j + 8half .. +8
-      if (i == (p & 31)) {
+      if (kRow && (fill & kRowBit)) {
+        // row layout: one K row and one V row, written by the lanes that
+        // read row p in the loop below (group p % 4, 16 bytes each)
+        const int key = (kHalf ? (cslot & 1) * 32 : 0) + p;
+        if ((lane >> 4) == (p & 3)) {
+          const int sub = lane & 15;
+          *reinterpret_cast<h8*>(kw + k_row_off(key) + sub * 8) = *reinterpret_cast<const h8*>(new_lds + sub * 8);
+          *reinterpret_cast<h8*>(vw + v_row_off(key) + sub * 8) =
+              *reinterpret_cast<const h8*>(new_lds + D + sub * 8);
+        }
+      } else {
+        if (kHalf) p += (cslot & 1) * 32;
+        // K: load (p/32)*8 + j, lanes (half, p%32): dims 16j + 8half .. +8
+        if (i == (p & 31)) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          *reinterpret_cast<h8*>(kw + (((p >> 5) * 8 + j) * 64 + lane) * 8) =
-              *reinterpret_cast<const h8*>(new_lds + j * 16 + half * 8);
-      }
-      // V: load 4nb + p/16, lanes (half (p/4)%2, i): dim 32nb + i, key p at element e
-      if (half == ((p >> 2) & 1)) {
-        const int e = (p & 3) | (((p >> 3) & 1) << 2);
+          for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<h8*>(kw + (((p >> 5) * 8 + j) * 64 + lane) * 8) =
+                *reinterpret_cast<const h8*>(new_lds + j * 16 + half * 8);
+        }
+        // V: load 4nb + p/16, lanes (half (p/4)%2, i): dim 32nb + i, key p at element e
+        if (half == ((p >> 2) & 1)) {
+          const int e = (p & 3) | (((p >> 3) & 1) << 2);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) vw[((nb * 4 + (p >> 4)) * 64 + lane) * 8 + e] = new_lds[D + nb * 32 + i];
+          for (int nb = 0; nb < 4; ++nb) vw[((nb * 4 + (p >> 4)) * 64 + lane) * 8 + e] = new_lds[D + nb * 32 + i];
+        }
       }
       if (lane == 0) {
-        const int tagged = append_fill | static_cast<int>(a.app_epoch << kFillBits);
+        const int tagged = append_fill | (fill & kRowBit) | static_cast<int>(a.app_epoch << kFillBits);
         const_cast<int32_t*>(a.chunk_refs)[2 * (chunk_begin + ac) + 1] = tagged;
         if (ac < kSfInline) const_cast<int*>(t)[12 + ac] = tagged;
       }
@@ -677,6 +693,78 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
     const _Float16* kt = pool + tile_base(tile, head, H, 0) + hh * 8 * 512;
     const _Float16* vt = pool + tile_base(tile, head, H, 1) + hh * 2 * 512;
     if (kAppend && c == append_at) nvalid = append_fill;
+    if (kRow && (fill & kRowBit)) {
+      // Row layout.  Loads j of K and V bring rows 4j .. 4j+3 of the chunk
+      // (1 KiB each); a load past the fill reads rows 0..3 again (its rows
+      // get zero weight).  Lane (g, sub) holds dims 8 sub .. 8 sub + 7 of row
+      // 4j + g.
+      constexpr int kJ = kHalf ? 8 : 16;
+      const int g = lane >> 4, sub = lane & 15;
+      const int key0 = kHalf ? hh * 32 : 0;
+      const _Float16* kr = pool + tile_base(tile, head, H, 0) + sub * 8;
+      const _Float16* vr = pool + tile_base(tile, head, H, 1) + sub * 8;
+      h8 kq[kJ], vq[kJ];
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const int r = key0 + (4 * j < nvalid ? 4 * j : 0) + g;
+        kq[j] = ld_tile<kNT>(kr + k_row_off(r));
+        vq[j] = ld_tile<kNT>(vr + v_row_off(r));
+      }
+      const h8 qv = *reinterpret_cast<const h8*>(q_lds + sub * 8);
+      float x[kJ];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        float d = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) d = __builtin_amdgcn_fdot2(lo2(kq[j], jj), lo2(qv, jj), d, false);
+        // the row's 16 pieces are in the 16 lanes of the group
+        d += dpp<kQuadXor1>(d);
+        d += dpp<kQuadXor2>(d);
+        d += dpp<kRowHalfMirror>(d);
+        d += dpp<kRowMirror>(d);
+        x[j] = 4 * j + g < nvalid ? d * a.scale_log2e : -INFINITY;
+        mx = fmaxf(mx, x[j]);
+      }
+      mx = max_halves(fmaxf(mx, swap16(mx)));
+      const float mnew = fmaxf(m, mx);  // finite: row 0 of a chunk is always filled
+      const float alpha = exp2f(m - mnew);
+      float psum = 0.f;
+      float o8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const float pr = exp2f(x[j] - mnew);
+        psum += pr;
+        // rows past the fill hold anything: they add nothing
+        const bool live = 4 * j + g < nvalid;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o8[e] = fmaf(pr, live ? static_cast<float>(vq[j][e]) : 0.f, o8[e]);
+      }
+      // each row's weight is in all 16 lanes of its group: count it once
+      l = l * alpha + (sub == 0 ? psum : 0.f);
+      m = mnew;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o8[e] = sum_halves(o8[e] + swap16(o8[e]));
+      // into the tile-layout accumulators (dim 32 nb + i at lane (half, i))
+      // through the wave's output row in LDS; half 1 adds nothing
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[nb] *= alpha;
+      if (lane < 16) {
+        *reinterpret_cast<f4*>(&w_o[wave][8 * sub]) = f4{o8[0], o8[1], o8[2], o8[3]};
+        *reinterpret_cast<f4*>(&w_o[wave][8 * sub + 4]) = f4{o8[4], o8[5], o8[6], o8[7]};
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (half == 0) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[nb] += w_o[wave][32 * nb + i];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      continue;
+    }
     // Keys past the fill get zero weight, so the tile blocks that hold only
     // such keys are not fetched from memory: a K load block covers 32 keys,
     // a V block 16, and a block wholly past the fill reads the chunk's first
@@ -795,7 +883,7 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
 // only the sequence-first part).  kFuse: the one-launch step, whose grid ends
 // with the merge blocks.  kAppend: a decode step
 // with in-kernel appends (StepArgs::app_k set).
-template <bool kFuse, bool kAppend, bool kHalf>
+template <bool kFuse, bool kAppend, bool kHalf, bool kRow>
 __global__ __launch_bounds__(256, 3) void partials_kernel(StepArgs a, int n_cf, int n_sf, int first) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   const int b = blockIdx.x + first;
@@ -808,9 +896,9 @@ __global__ __launch_bounds__(256, 3) void partials_kernel(StepArgs a, int n_cf, 
   } else if (b < n_cf + n_sf) {
     const int logical = b - n_cf;
     if (a.sf_tasks[(logical / a.heads) * 16 + kSfReuseField])
-      sequence_first_block<kFuse, false, kAppend, kHalf>(a, logical, smem);
+      sequence_first_block<kFuse, false, kAppend, kHalf, kRow>(a, logical, smem);
     else
-      sequence_first_block<kFuse, true, kAppend, kHalf>(a, logical, smem);
+      sequence_first_block<kFuse, true, kAppend, kHalf, kRow>(a, logical, smem);
   }
   else if constexpr (kFuse)
     merge_block(a, b - n_cf - n_sf);
@@ -839,18 +927,19 @@ int launch_partials(const StepArgs& a, int part, bool fuse_merge, void* stream) 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool append = a.app_k != nullptr;
   const dim3 grid(count), block(256);
-#define CA_LAUNCH(F, A, HT) hipLaunchKernelGGL((partials_kernel<F, A, HT>), grid, block, 0, st, a, n_cf, n_sf, first)
+#define CA_LAUNCH(F, A, HT, R) \
+  hipLaunchKernelGGL((partials_kernel<F, A, HT, R>), grid, block, 0, st, a, n_cf, n_sf, first)
+#define CA_LAUNCH_FA(HT, R)                 \
+  if (fuse && append) CA_LAUNCH(true, true, HT, R);   \
+  else if (fuse) CA_LAUNCH(true, false, HT, R);       \
+  else if (append) CA_LAUNCH(false, true, HT, R);     \
+  else CA_LAUNCH(false, false, HT, R);
   if (a.half_tiles) {
-    if (fuse && append) CA_LAUNCH(true, true, true);
-    else if (fuse) CA_LAUNCH(true, false, true);
-    else if (append) CA_LAUNCH(false, true, true);
-    else CA_LAUNCH(false, false, true);
+    if (a.row_chunks) { CA_LAUNCH_FA(true, true) } else { CA_LAUNCH_FA(true, false) }
   } else {
-    if (fuse && append) CA_LAUNCH(true, true, false);
-    else if (fuse) CA_LAUNCH(true, false, false);
-    else if (append) CA_LAUNCH(false, true, false);
-    else CA_LAUNCH(false, false, false);
+    if (a.row_chunks) { CA_LAUNCH_FA(false, true) } else { CA_LAUNCH_FA(false, false) }
   }
+#undef CA_LAUNCH_FA
 #undef CA_LAUNCH
   return static_cast<int>(hipGetLastError());
 }

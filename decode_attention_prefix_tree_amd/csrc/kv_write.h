@@ -17,8 +17,16 @@ constexpr int kOpsPerLaunch = 64;  // 2 KiB of kernel arguments
 // come from two tiles.  Keys in [zero_lo, zero_hi) that are not written
 // become zeros (a chunk's first write clears the chunk's part of the tile);
 // every other key keeps its value.
+// mode kKvRowWrite: the chunk is stored row-major (tile_layout.h): the caller
+// rows go to their key rows, nothing else is written (rows past a chunk's
+// fill are never read).  mode kKvToTiles: the chunk's part of the tile,
+// keys [zero_lo, zero_hi), is rewritten from the row layout to the tile
+// layout: keys below zero_lo + n_rows keep their values, the rest become
+// zeros (the chunk becomes shared, or is split, and the chunk-first path and
+// pool-to-pool copies read tiles).
+enum { kKvTileWrite = 0, kKvRowWrite = 1, kKvToTiles = 2 };
 struct KvOpDev {
-  int32_t dst_tile, dst_key0, n_rows, src0, from_pool, zero_lo, zero_hi, pad;
+  int32_t dst_tile, dst_key0, n_rows, src0, from_pool, zero_lo, zero_hi, mode;
 };
 
 struct KvOpBatch {

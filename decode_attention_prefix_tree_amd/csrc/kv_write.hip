@@ -31,6 +31,45 @@ __global__ __launch_bounds__(256) void kv_write_kernel(_Float16* pool, int heads
   const int head = blockIdx.y, kv = blockIdx.z;
   _Float16* dst = pool + tile_base(op.dst_tile, head, heads, kv);
   const _Float16* src = kv ? v_src : k_src;
+  if (op.mode == kKvRowWrite) {
+    // 16 units of 16 bytes per row
+    for (int w = threadIdx.x; w < op.n_rows * 16; w += 256) {
+      const int r = w >> 4, u = w & 15, key = op.dst_key0 + r;
+      *reinterpret_cast<h8*>(dst + (kv == 0 ? k_row_off(key) : v_row_off(key)) + u * 8) =
+          *reinterpret_cast<const h8*>(src + (static_cast<size_t>(op.src0 + r) * heads + head) * D + u * 8);
+    }
+    return;
+  }
+  if (op.mode == kKvToTiles) {
+    // every unit of the chunk's part is read (from rows) before any is
+    // written, since both layouts share the same memory
+    h8 val[4];
+    int units[4], n = 0;
+    for (int u = threadIdx.x; u < TILE / 8; u += 256) {
+      const int L = u >> 6, lane = u & 63, half = lane >> 5, i = lane & 31;
+      const int first = kv == 0 ? (L >> 3) * 32 + i : (L & 3) * 16 + half * 4;  // a key of the unit
+      if (first < op.zero_lo || first >= op.zero_hi) continue;
+      h8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int key, dim;
+        if (kv == 0) {
+          key = first;
+          dim = (L & 7) * 16 + half * 8 + e;
+        } else {
+          key = first + (e & 3) + ((e >> 2) << 3);
+          dim = (L >> 2) * 32 + i;
+        }
+        x[e] = key < op.zero_lo + op.n_rows ? dst[(kv == 0 ? k_row_off(key) : v_row_off(key)) + dim]
+                                             : static_cast<_Float16>(0.0f);
+      }
+      val[n] = x;
+      units[n++] = u;
+    }
+    __syncthreads();
+    for (int j = 0; j < n; ++j) *reinterpret_cast<h8*>(dst + units[j] * 8) = val[j];
+    return;
+  }
   const int lo = op.dst_key0, hi = op.dst_key0 + op.n_rows;  // written keys [lo, hi)
   const int zlo = op.zero_lo, zhi = op.zero_hi;                // cleared keys [zlo, zhi)
   const bool whole = zlo == 0 && zhi == C;  // every unit rewritten, none read

@@ -74,6 +74,7 @@ int32_t Manager::insert(int64_t seq, const int32_t* tokens, int32_t n, std::vect
 
   // Walk from the root without touching anything.
   int32_t cur = 0, pos = 0, split_node = -1, split_at = 0;
+  std::vector<int32_t> path;  // matched chunks (the split one included)
   while (share_ && pos < n) {
     int32_t next = -1;
     for (int32_t c : nodes_[cur].children) {
@@ -84,6 +85,7 @@ int32_t Manager::insert(int64_t seq, const int32_t* tokens, int32_t n, std::vect
     int32_t lim = std::min<int32_t>(static_cast<int32_t>(t.size()), n - pos), k = 0;
     while (k < lim && t[k] == tokens[pos + k]) ++k;
     pos += k;
+    path.push_back(next);
     if (k < static_cast<int32_t>(t.size())) { split_node = next; split_at = k; break; }
     cur = next;
   }
@@ -92,6 +94,15 @@ int32_t Manager::insert(int64_t seq, const int32_t* tokens, int32_t n, std::vect
     throw Error(kNoCapacity, "need " + std::to_string(need) + " chunk slots, " +
                                  std::to_string(free_slots()) + " free");
   const int32_t matched = pos;
+
+  // Matched chunks become shared (or are split): the chunk-first path and
+  // pool-to-pool copies read tiles, so row-major ones are converted first.
+  for (int32_t x : path) {
+    Node& nd = nodes_[x];
+    if (!nd.row) continue;
+    if (ops) ops->push_back(KvOp{nd.slot, 0, static_cast<int32_t>(nd.tokens.size()), 0, -1, 0, x, kOpConvert});
+    nd.row = false;
+  }
 
   if (split_node >= 0) {
     int32_t tail = new_node(split_node, nodes_[split_node].start + split_at);
@@ -142,7 +153,7 @@ void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<
   if (take > 0) {
     Node& nd = nodes_[e];
     nd.tokens.insert(nd.tokens.end(), tokens, tokens + take);
-    if (ops) ops->push_back(KvOp{nd.slot, fill, take, src_base, -1, 0, e});
+    if (ops) ops->push_back(KvOp{nd.slot, fill, take, src_base, -1, 0, e, nd.row ? kOpRows : kOpTiles});
     // growing into another 64-key tile adds a tile ref to the plan
     if (tiles_of(fill + take) != tiles_of(fill)) structural_ = true;
   }
@@ -158,8 +169,9 @@ void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<
     Node& nd = nodes_[idx];
     nd.tokens.assign(tokens + i, tokens + i + piece);
     nd.ref = 1;
+    nd.row = row_appends_;
     nodes_[cur].children.push_back(idx);
-    if (ops) ops->push_back(KvOp{nd.slot, 0, piece, src_base + i, -1, 0});
+    if (ops) ops->push_back(KvOp{nd.slot, 0, piece, src_base + i, -1, 0, idx, nd.row ? kOpRows : kOpTiles});
     cur = idx;
     pos += piece;
     i += piece;
@@ -191,6 +203,12 @@ void Manager::append_batch(const int64_t* seqs, const int32_t* tokens, int32_t n
     throw Error(kNoCapacity, "need " + std::to_string(need) + " chunk slots, " +
                                  std::to_string(free_slots()) + " free");
   for (int32_t j = 0; j < n; ++j) append(seqs[j], tokens + j, 1, ops, j);
+}
+
+int64_t Manager::row_chunks() const {
+  int64_t n = 0;
+  for (size_t i = 1; i < nodes_.size(); ++i) n += nodes_[i].alive && nodes_[i].row ? 1 : 0;
+  return n;
 }
 
 bool Manager::next_append_structural() const {
@@ -302,6 +320,7 @@ void Plan::clear() {
   dense_parts = 0;
   part_stride = 1;
   cf_chunk_reads = sf_chunk_reads = shared_chunks = shared_tokens = unique_tokens = attended_tokens = 0;
+  row_refs = 0;
 }
 
 void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan, int64_t sf_min_tasks,
@@ -339,6 +358,7 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
     return static_cast<int32_t>(nodes_[n].tokens.size()) + (next ? grown[n] : 0);
   };
   auto ref_of = [&](int32_t n) -> int32_t { return added(n) ? 1 : nodes_[n].ref; };
+  auto row_of = [&](int32_t n) -> bool { return added(n) ? row_appends_ : nodes_[n].row; };
   std::vector<int32_t> kids;
   auto children_of = [&](int32_t n) -> const std::vector<int32_t>& {
     if (!next) return nodes_[n].children;
@@ -447,6 +467,7 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
       tasks[t].chunk_begin = static_cast<int32_t>(P.chunk_refs.size() / 2);
       for (int32_t r : task_rows[t])
         for (int32_t k = 0; k < tiles_of(R(r, 3)); ++k) {
+          if (row_of(row_node[r])) throw Error(kInternal, "plan: a shared chunk is stored row-major");
           P.chunk_refs.push_back(tile_slot(R(r, 6), k));
           P.chunk_refs.push_back(tile_fill(R(r, 3), k));
           P.ref_node.push_back(row_node[r]);
@@ -535,7 +556,9 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
       for (int32_t q = j; q < stop; ++q) {
         const int c = q - j;
         const int32_t r = priv[q].first, k = priv[q].second;
-        const int32_t slot = tile_slot(R(r, 6), k), fill = tile_fill(R(r, 3), k);
+        const bool row = row_of(row_node[r]);
+        const int32_t slot = tile_slot(R(r, 6), k), fill = tile_fill(R(r, 3), k) | (row ? kRowBit : 0);
+        P.row_refs += row ? 1 : 0;
         // the last tile of the chunk where the sequence ends takes its next
         // decoded token
         if (r == end_row[i] && k + 1 == tiles_of(R(r, 3))) st.append_at = c;
@@ -637,8 +660,11 @@ void Manager::refresh_fills(Plan* plan) const {
     P.attended_tokens += static_cast<int64_t>(fill) * (row[5] - row[4]);
     if (row[5] - row[4] >= 2) P.shared_tokens += fill;
   }
-  for (size_t k = 0; k < P.ref_node.size(); ++k)
-    P.chunk_refs[2 * k + 1] = tile_fill(static_cast<int32_t>(nodes_[P.ref_node[k]].tokens.size()), P.ref_sub[k]);
+  for (size_t k = 0; k < P.ref_node.size(); ++k) {
+    const Node& nd = nodes_[P.ref_node[k]];
+    P.chunk_refs[2 * k + 1] =
+        tile_fill(static_cast<int32_t>(nd.tokens.size()), P.ref_sub[k]) | (nd.row ? kRowBit : 0);
+  }
   for (CfUnit& u : P.cf_units)
     for (int c = 0; c < kCfInline && c < u.n_chunks; ++c) u.n_valid[c] = P.chunk_refs[2 * (u.chunk_begin + c) + 1];
   for (SfTask& t : P.sf_tasks)

@@ -51,6 +51,12 @@ struct Error : std::runtime_error {
 // write that starts at key 0 is the chunk's first since its slot was
 // allocated (keys are written in order), so the chunk's other keys are
 // cleared with it.
+// mode: how the chunk is stored.  kOpTiles writes into the tile layout;
+// kOpRows writes rows of a chunk kept row-major (a chunk grown by appends);
+// kOpConvert rewrites such a chunk's first n_rows keys into the tile layout
+// (it is about to be shared or split), and must run before the other copies
+// of the same mutation.
+enum KvOpMode : int32_t { kOpTiles = 0, kOpRows = 1, kOpConvert = 2 };
 struct KvOp {
   int32_t dst_slot;
   int32_t dst_key0;
@@ -59,6 +65,7 @@ struct KvOp {
   int32_t src_slot;   // only for from_pool
   int32_t from_pool;
   int32_t node = -1;  // manager node written (host bookkeeping only)
+  int32_t mode = kOpTiles;
 };
 
 // Per-step work plan built from the DFS order.  All ids are int32 so the
@@ -124,6 +131,7 @@ struct Plan {
   int64_t shared_tokens = 0;
   int64_t unique_tokens = 0;
   int64_t attended_tokens = 0;
+  int64_t row_refs = 0;             // chunk refs of row-major chunks (kRowBit set)
 
   // Empty every list but keep its storage (plans are rebuilt often while
   // decoding, at about the same size).
@@ -153,6 +161,13 @@ class Manager {
   int64_t capacity() const { return capacity_; }
   int64_t free_slots() const { return static_cast<int64_t>(free_.size()); }
   int chunk() const { return C_; }
+  // Chunks made by appends from now on are stored row-major (default), or
+  // in the tile layout like inserted ones.
+  void set_row_appends(bool on) { row_appends_ = on; }
+  bool row_appends() const { return row_appends_; }
+  // Whether a live chunk node is stored row-major.
+  bool row(int32_t node) const { return nodes_[node].row; }
+  int64_t row_chunks() const;
   // The kernels read 64-key tiles: a chunk of C > 64 tokens is C / 64 tiles
   // (slot s owns tiles s * C / 64 ...), of which the plan lists those that
   // hold tokens; a chunk of 32 is half of tile s / 2 and its ref carries s
@@ -212,6 +227,7 @@ class Manager {
     int32_t start = 0;     // position of the first token in the sequence
     int32_t ref = 0;       // live sequences through or ending at this node
     bool alive = false;
+    bool row = false;      // stored row-major (made by an append, never shared since)
     std::vector<int32_t> tokens;
     std::vector<int32_t> children;  // indices, creation order
     std::vector<int64_t> ended;     // sequences ending here, arrival order
@@ -225,6 +241,7 @@ class Manager {
   int C_;
   bool share_;
   bool structural_ = true;
+  bool row_appends_ = true;
   int64_t capacity_ = 0;
   int32_t next_id_ = 0;
   int64_t n_nodes_ = 0;

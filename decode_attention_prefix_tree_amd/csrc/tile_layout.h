@@ -15,6 +15,16 @@
 //    That key order is the order in which the S^T accumulators of a lane
 //    hold P^T, so P goes from the first product to the second without any
 //    lane exchange.
+//
+// Row layout.  A chunk grown by decode appends keeps its keys row-major in
+// the same 16 KiB K and V regions, so one token is one 256-byte K row and one
+// 256-byte V row per head instead of pieces of two dozen lines of the tile
+// layout.  Key k of the tile: K row at k * 128 halves; V row at
+// (4 * ((k % 32) / 8) + 2 * (k / 32)) * 512 + (k % 8) * 128 halves.  Both keep
+// keys 0..31 and 32..63 inside the units the tile layout gives those halves
+// (K load blocks 0..7 and 8..15; V load blocks 4nb + 0, 1 and 4nb + 2, 3), so
+// two 32-token chunks that share a tile never overlap in either layout, and
+// rows 4j .. 4j + 3 are always 1 KiB of contiguous memory.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,6 +50,12 @@ __device__ __forceinline__ size_t tile_base(int tile, int head, int heads, int k
 
 __device__ __forceinline__ int k_off(int key, int dim) {
   return ((((key >> 5) * 8 + (dim >> 4)) * 2 + ((dim >> 3) & 1)) * 32 + (key & 31)) * 8 + (dim & 7);
+}
+
+__device__ __forceinline__ int k_row_off(int key) { return key * D; }
+
+__device__ __forceinline__ int v_row_off(int key) {
+  return (4 * ((key & 31) >> 3) + 2 * (key >> 5)) * 512 + (key & 7) * D;
 }
 
 __device__ __forceinline__ int v_off(int key, int dim) {

@@ -114,7 +114,7 @@ enum {
                                     launches) fail with CA_E_HIP before anything is
                                     enqueued; 0 (default) turns it off.  Does not touch the
                                     chunk table. */
-  CA_OPT_PREBUILD_PLAN = 6       /* 1 (default): when ca_decode_step, or ca_append_batch over
+  CA_OPT_PREBUILD_PLAN = 6,      /* 1 (default): when ca_decode_step, or ca_append_batch over
                                     every live sequence in ascending id order, has enqueued its
                                     work and the next such append will change the table's shape
                                     (a last chunk is full or shared, or a chunk of 128 opens
@@ -124,6 +124,14 @@ enum {
                                     on the CPU overlapped with the GPU); that next append then
                                     takes it instead of rebuilding.  0: every table is built
                                     in the call that needs it. */
+  CA_OPT_ROW_APPENDS = 7         /* 1 (default): chunks that appends create keep their keys
+                                    row-major in their slot (one K row and one V row per
+                                    token and head: a decoded token is two contiguous 256-byte
+                                    writes per head), and the sequence-first phase reads them
+                                    by rows; an insert that makes such a chunk shared, or
+                                    splits it, first rewrites it in the tile layout.  0:
+                                    chunks made from now on use the tile layout (one token's
+                                    K and V then land in pieces of two dozen lines). */
 };
 
 /* ca_attend_phase phases.  A step is CA_PHASE_PARTIALS (one launch holding
@@ -168,6 +176,7 @@ typedef struct ca_stats_t {
   int64_t one_launch_step;    /* 1 if ca_attend runs the step as one launch */
   int64_t sf_chunks_per_task; /* sequence-first group of the current plan */
   int64_t prebuilt_plans;     /* tables built ahead, by the call before the one that needed them */
+  int64_t row_chunks;         /* chunks stored row-major (made by appends, never shared) */
 } ca_stats_t;
 
 /* Bytes of one chunk slot: K and V, all heads, fp16 = 4 * heads * chunk_size

@@ -671,6 +671,172 @@ def test_pool_holds_each_chunks_kv(name, chunk):
     assert n_keys == sum(int(r[3]) for r in rows)
 
 
+def _k_row_off(key, dim):
+    """Position of K[key][dim] of a row-major chunk in its 64-key tile."""
+    return key * 128 + dim
+
+
+def _v_row_off(key, dim):
+    """Position of V[key][dim] of a row-major chunk in its 64-key tile: rows
+    of keys 0..31 and 32..63 stay inside the V units of their tile half."""
+    return (4 * ((key & 31) >> 3) + 2 * (key >> 5)) * 512 + (key & 7) * 128 + dim
+
+
+def _check_pool(ca, heads, chunk, kv_of, row_rows):
+    """Every key of every table row against the K/V the caller supplied:
+    table rows in row_rows are read in the row layout, the others in the tile
+    layout."""
+    torch = _torch()
+    rows, order = ca.export_table()
+    flat = ca.pool.view(torch.float16).cpu().numpy()
+    tile_halves = heads * 2 * 64 * 128
+    pool = flat[:flat.size // tile_halves * tile_halves].reshape(-1, heads, 2, 64 * 128)
+    keys = np.arange(64)[:, None]
+    dims = np.arange(128)[None, :]
+    offs = {False: (_k_off(keys, dims), _v_off(keys, dims)), True: (_k_row_off(keys, dims), _v_row_off(keys, dims))}
+    n_keys = 0
+    for ri, r in enumerate(rows):
+        start, n, sb, slot = int(r[2]), int(r[3]), int(r[4]), int(r[6])
+        k, v = kv_of(order[sb])
+        koff, voff = offs[ri in row_rows]
+        for j in range(n):
+            t, kk = divmod(slot * chunk + j, 64)
+            assert np.array_equal(pool[t][:, 0][:, koff[kk]], k[start + j]), (ri, r, j)
+            assert np.array_equal(pool[t][:, 1][:, voff[kk]], v[start + j]), (ri, r, j)
+            n_keys += 1
+    assert n_keys == sum(int(r[3]) for r in rows)
+    return rows, order
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 128])
+def test_pool_rows_of_appended_chunks_and_their_conversion(chunk):
+    """Chunks made by appends hold their keys row-major (ca_stats counts
+    them), chunks made by inserts hold tiles; an insert that shares a
+    sequence's appended chunks, and one that diverges inside one of them,
+    first rewrite those chunks as tiles.  Every key is compared with the
+    caller's K/V bit for bit after each stage, and each step with the
+    oracle."""
+    _say(f"row chunks and conversions, chunk {chunk}")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import ChunkAttention
+    rng = np.random.default_rng(500 + chunk)
+    H = 2
+    ca = ChunkAttention(H, 64, device="cuda:0", chunk_size=chunk)
+    toks, kvs = {}, {}
+
+    def rnd_kv(n):
+        return [rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16) for _ in range(2)]
+
+    def put(sid, t, k, v):
+        ca.insert(sid, t, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+        toks[sid], kvs[sid] = list(t), [k, v]
+
+    base = [int(x) for x in rng.integers(0, 50, size=2 * chunk)]
+    kb, vb = rnd_kv(2 * chunk)
+    put(0, base, kb, vb)
+    k1, v1 = rnd_kv(chunk)
+    put(1, base[:chunk] + [777] * chunk, np.concatenate([kb[:chunk], k1]), np.concatenate([vb[:chunk], v1]))
+    inserted = {0: 2 * chunk, 1: 2 * chunk}
+    # appends: single tokens and a multi-token append, crossing chunk ends
+    for step in range(chunk + 7):
+        for sid in (0, 1):
+            n = 3 if step == 5 else 1
+            k, v = rnd_kv(n)
+            t = [1000 + step * 10 + j for j in range(n)]
+            ca.append(sid, t, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+            toks[sid] += t
+            kvs[sid] = [np.concatenate([kvs[sid][0], k]), np.concatenate([kvs[sid][1], v])]
+    torch.cuda.synchronize()
+    st = ca.stats()
+    assert st["row_chunks"] >= 4, st["row_chunks"]
+
+    def rows_in_row_layout(rows, order, row_seqs):
+        # chunks that only appends made: past the inserted length of a sequence in row_seqs
+        out = set()
+        for ri, r in enumerate(rows):
+            if r[5] - r[4] == 1 and order[r[4]] in row_seqs and r[2] >= inserted[order[r[4]]]:
+                out.add(ri)
+        return out
+
+    def check(row_seqs, label):
+        rows, order = ca.export_table()
+        rr = rows_in_row_layout(rows, order, row_seqs)
+        _check_pool(ca, H, chunk, lambda s: kvs[s], rr)
+        q = rng.standard_normal((len(toks), H, 128), dtype=np.float32).astype(np.float16)
+        got = run_step(ca, q)
+        ids = sorted(toks)
+        assert_parity(got, A.decode_step(q, [kvs[s] for s in ids]), label)
+        return len(rr)
+
+    assert check({0, 1}, "appended chunks in rows") == st["row_chunks"]
+    # sequence 2 shares all of sequence 0 (its appended chunks become shared)
+    put(2, list(toks[0]), *[x.copy() for x in kvs[0]])
+    assert ca.stats()["row_chunks"] < st["row_chunks"]
+    check({1}, "after sharing sequence 0's chunks")
+    # sequence 3 diverges inside sequence 1's last appended chunk
+    cut = len(toks[1]) - 3
+    k3, v3 = rnd_kv(5)
+    put(3, toks[1][:cut] + [4242] * 5, np.concatenate([kvs[1][0][:cut], k3]), np.concatenate([kvs[1][1][:cut], v3]))
+    check(set(), "after splitting sequence 1's last chunk")
+    assert ca.stats()["row_chunks"] == 0
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 128])
+@pytest.mark.parametrize("rows_on", [1, 0])
+def test_decode_with_inserts_into_decoded_chunks(chunk, rows_on):
+    """Decode steps (ca_decode_step) interleaved with inserts of sequences
+    that copy a prefix of a decoding sequence, cut anywhere (sharing its
+    appended chunks, or splitting one), and removals; every step against the
+    oracle, with row-major appended chunks on and off."""
+    _say(f"decode with inserts, chunk {chunk}, rows {rows_on}")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import ChunkAttention, _capi
+    rng = np.random.default_rng(600 + chunk + rows_on)
+    H = 2
+    ca = ChunkAttention(H, 400, device="cuda:0", chunk_size=chunk)
+    ca.set_option(_capi.CA_OPT_ROW_APPENDS, rows_on)
+    live = {}
+    nid = [0]
+
+    def rnd(n):
+        return rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+
+    def insert(t, k, v):
+        sid = nid[0]
+        nid[0] += 1
+        ca.insert(sid, t, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+        live[sid] = (list(t), k, v)
+
+    pre = [int(x) for x in rng.integers(0, 30, size=100)]
+    kp, vp = rnd(100), rnd(100)
+    for i in range(3):
+        n = int(rng.integers(1, 70))
+        insert(pre + [900 + i] * n, np.concatenate([kp, rnd(n)]), np.concatenate([vp, rnd(n)]))
+    for step in range(150):
+        ids = sorted(live)
+        k, v, q = rnd(len(ids)), rnd(len(ids)), rnd(len(ids))
+        t = [int(x) for x in rng.integers(0, 30, size=len(ids))]
+        out = ca.decode_step(np.array(t, np.int32), torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                             torch.from_numpy(q).cuda())
+        for j, s_ in enumerate(ids):
+            tt, kk, vv = live[s_]
+            live[s_] = (tt + [t[j]], np.concatenate([kk, k[j:j + 1]]), np.concatenate([vv, v[j:j + 1]]))
+        if step % 10 == 0 or step == 149:
+            torch.cuda.synchronize()
+            assert_parity(out.cpu().numpy(), A.decode_step(q, [live[s_][1:] for s_ in ids]), f"decode {step}")
+        if step % 17 == 8:
+            src = live[ids[int(rng.integers(0, len(ids)))]]
+            cut = int(rng.integers(1, len(src[0]) + 1))
+            extra = int(rng.integers(0, 4))
+            insert(src[0][:cut] + [5000 + step] * extra, np.concatenate([src[1][:cut], rnd(extra)]),
+                   np.concatenate([src[2][:cut], rnd(extra)]))
+        if step % 29 == 20 and len(live) > 2:
+            victim = ids[int(rng.integers(0, len(ids)))]
+            ca.remove(victim)
+            del live[victim]
+    assert (ca.stats()["row_chunks"] > 0) == bool(rows_on)
+
+
 def test_one_sequence_of_65536_tokens():
     """The longest single context here: one private sequence of 65,536 tokens
     (1,024 chunks, 256 sequence-first tasks per head, 256 partials merged
