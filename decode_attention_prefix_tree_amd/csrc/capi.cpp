@@ -29,9 +29,20 @@ struct Prebuild {
   chunkattn::Plan plan;
   int cf_auto = 0, plan_cf_group = 0;
   double ms = 0.0;
+  // the workspace the plan's table was copied into, after the step that
+  // built it (null: not copied, or overwritten since)
+  void* uploaded_ws = nullptr;
 };
 
 static_assert(CA_NOALLOC_SCRATCH_BYTES == chunkattn::kStaticScratchBytes, "the header states the scratch size");
+
+// Byte offsets of a plan's arrays in the workspace: the device table
+// (records, chunk refs, row and partial lists, arrival counters), then the
+// partial results; table_bytes is what an upload copies, total the size.
+struct Layout {
+  size_t cf = 0, sf = 0, refs = 0, qrow = 0, seqparts = 0, partlist = 0, arrivals = 0;
+  size_t table_bytes = 0, part_o = 0, part_ms = 0, total = 0;
+};
 
 struct ca_ctx {
   int heads = 0, head_dim = 0, chunk = 0, flags = 0;
@@ -62,9 +73,7 @@ struct ca_ctx {
   uint64_t version = 1, uploaded_version = 0;
   void* uploaded_ws = nullptr;
   int scratch_dev = -1;             // device whose static scratch uploaded_ws is, or -1
-  size_t off_cf = 0, off_sf = 0, off_refs = 0, off_qrow = 0, off_seqparts = 0, off_partlist = 0;
-  size_t off_arrivals = 0;
-  size_t table_bytes = 0, off_part_o = 0, off_part_ms = 0, total_bytes = 0;
+  Layout lay;                       // where the plan's arrays sit in the workspace
   int64_t rebuilds = 0;
   double last_rebuild_ms = 0.0;
 
@@ -236,33 +245,36 @@ void ensure_plan(ca_ctx* c, bool with_fills = true) {
       std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
 }
 
-// Offsets of the plan's arrays in the workspace (and its total size).
-void layout_plan(ca_ctx* c) {
-  const chunkattn::Plan& p = c->plan;
+// Offsets of a plan's arrays in the workspace (and its total size).
+Layout layout_of(const chunkattn::Plan& p, int heads, int head_dim) {
+  Layout l;
   size_t off = 0;
-  c->off_cf = off;
+  l.cf = off;
   off = align_up(off + p.cf_units.size() * sizeof(chunkattn::CfUnit));
-  c->off_sf = off;
+  l.sf = off;
   off = align_up(off + p.sf_tasks.size() * sizeof(chunkattn::SfTask));
-  c->off_refs = off;
+  l.refs = off;
   off = align_up(off + p.chunk_refs.size() * sizeof(int32_t));
-  c->off_qrow = off;
+  l.qrow = off;
   off = align_up(off + p.dfs_qrow.size() * sizeof(int32_t));
-  c->off_seqparts = off;
+  l.seqparts = off;
   off = align_up(off + p.seq_parts.size() * sizeof(int32_t));
-  c->off_partlist = off;
+  l.partlist = off;
   off = align_up(off + p.part_list.size() * sizeof(int32_t));
   // arrival counters of the fused merge: uploaded as zeros with the table,
   // and every step leaves them at zero again
-  c->off_arrivals = off;
-  off = align_up(off + p.dfs_seq.size() * static_cast<size_t>(c->heads) * sizeof(int32_t));
-  c->table_bytes = off;
-  c->off_part_o = off;
-  off = align_up(off + static_cast<size_t>(p.n_parts) * c->heads * c->head_dim * sizeof(float));
-  c->off_part_ms = off;
-  off = align_up(off + static_cast<size_t>(p.n_parts) * c->heads * 2 * sizeof(float));
-  c->total_bytes = off;
+  l.arrivals = off;
+  off = align_up(off + p.dfs_seq.size() * static_cast<size_t>(heads) * sizeof(int32_t));
+  l.table_bytes = off;
+  l.part_o = off;
+  off = align_up(off + static_cast<size_t>(p.n_parts) * heads * head_dim * sizeof(float));
+  l.part_ms = off;
+  off = align_up(off + static_cast<size_t>(p.n_parts) * heads * 2 * sizeof(float));
+  l.total = off;
+  return l;
 }
+
+void layout_plan(ca_ctx* c) { c->lay = layout_of(c->plan, c->heads, c->head_dim); }
 
 // The plan of a tree: the chunk-first group as given, or chosen for the
 // plan (built once with the last choice, again if the plan wants another).
@@ -281,18 +293,24 @@ int build_for(const ca_ctx* c, chunkattn::Plan* plan, const chunkattn::NextAppen
   return cf_auto;
 }
 
+void copy_table(ca_ctx* c, void* stream, void* ws, const chunkattn::Plan& p, const Layout& l);
+void note_upload(ca_ctx* c, void* ws, int scratch_dev);
+
 // After a batch of one-token appends over every live sequence (a decode
 // step) has been enqueued: if the next such batch will change the plan's
 // shape (a sequence's last chunk is full or shared, or a chunk of 128 opens
 // its second tile), build the plan of that tree now, while the GPU runs the
 // work just enqueued; the next batch then takes it instead of rebuilding.
-void prebuild_next(ca_ctx* c) {
+// upload: the step that reads the current table is enqueued already (a
+// decode step), so the new table may go to the workspace now.
+void prebuild_next(ca_ctx* c, void* stream, bool upload) {
   Prebuild& p = c->pre;
   if (!c->prebuild_on || c->mgr.live() == 0) return;
   if (p.ok && p.base_version == c->version) return;  // already built for this tree
   if (!c->mgr.next_append_structural()) return;
   const auto t0 = std::chrono::steady_clock::now();
   p.ok = false;
+  p.uploaded_ws = nullptr;
   p.base_version = c->version;
   p.ids = c->mgr.sequences();
   chunkattn::NextAppend next;
@@ -300,6 +318,18 @@ void prebuild_next(ca_ctx* c) {
     p.cf_auto = build_for(c, &p.plan, &next);
     p.plan_cf_group = c->cf_group ? c->cf_group : p.cf_auto;
     p.ok = true;
+    // Its table goes to the caller's workspace too, ordered after the work
+    // just enqueued, when it fits (else the step that needs it uploads it).
+    // The device table then no longer holds the current tree.
+    const Layout l = layout_of(p.plan, c->heads, c->head_dim);
+    if (upload && c->pool != nullptr && c->ws != nullptr && c->ws_bytes >= l.total && c->fail_ops == 0) {
+      try {
+        copy_table(c, stream, c->ws, p.plan, l);
+        p.uploaded_ws = c->ws;
+      } catch (const Error&) {
+        mark_table_stale(c);
+      }
+    }
   }
   p.ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
 }
@@ -327,6 +357,10 @@ void adopt_prebuild(ca_ctx* c) {
   c->rebuilds += 1;
   c->prebuilt_plans += 1;
   c->last_rebuild_ms = c->pre.ms;
+  // its table is already in the workspace, unless something was uploaded there since
+  if (c->pre.uploaded_ws != nullptr && c->pre.uploaded_ws == c->ws && c->ws_bytes >= c->lay.total)
+    note_upload(c, c->ws, -1);
+  c->pre.uploaded_ws = nullptr;
 }
 
 template <typename T>
@@ -334,26 +368,26 @@ void put(char* base, size_t off, const std::vector<T>& v) {
   if (!v.empty()) std::memcpy(base + off, v.data(), v.size() * sizeof(T));
 }
 
-// The device table of the current plan (table_bytes): records, chunk refs,
-// row and partial lists, and zeroed arrival counters.
-void table_image(const ca_ctx* c, char* s) {
-  const chunkattn::Plan& p = c->plan;
-  std::memset(s, 0, c->table_bytes);
-  put(s, c->off_cf, p.cf_units);
-  put(s, c->off_sf, p.sf_tasks);
-  put(s, c->off_refs, p.chunk_refs);
-  put(s, c->off_qrow, p.dfs_qrow);
-  put(s, c->off_seqparts, p.seq_parts);
-  put(s, c->off_partlist, p.part_list);
+// The device table of a plan (table_bytes): records, chunk refs, row and
+// partial lists, and zeroed arrival counters.
+void table_image(const chunkattn::Plan& p, const Layout& l, char* s) {
+  std::memset(s, 0, l.table_bytes);
+  put(s, l.cf, p.cf_units);
+  put(s, l.sf, p.sf_tasks);
+  put(s, l.refs, p.chunk_refs);
+  put(s, l.qrow, p.dfs_qrow);
+  put(s, l.seqparts, p.seq_parts);
+  put(s, l.partlist, p.part_list);
 }
 
 // Staging bytes for the current table: three parts, each holding the table.
-size_t staging_need(const ca_ctx* c) { return ca_ctx::kStages * align_up(c->table_bytes); }
+size_t staging_need(const ca_ctx* c) { return ca_ctx::kStages * align_up(c->lay.table_bytes); }
 
-// scratch_dev: the device whose static scratch ws is, or -1 for the caller's
-// workspace.
-void upload(ca_ctx* c, void* stream, void* ws, int scratch_dev = -1) {
-  if (table_current_in(c, ws)) return;
+
+// Copy a plan's device table into workspace ws on the stream, through the
+// next staging buffer of the ring.  Throws before enqueueing anything if the
+// stream captures or the lent staging is too small.
+void copy_table(ca_ctx* c, void* stream, void* ws, const chunkattn::Plan& p, const Layout& l) {
   // A graph would replay the copy from a staging buffer that later uploads
   // rewrite (and waiting for the ring is no call for a capture): a step is
   // captured only once its table is on the device.
@@ -362,39 +396,43 @@ void upload(ca_ctx* c, void* stream, void* ws, int scratch_dev = -1) {
   if (capturing != hipStreamCaptureStatusNone)
     throw Error(CA_E_STATE, "the chunk table must be uploaded first, which cannot be captured: run one step "
                             "(or ca_prepare) on the tree as it is before capturing");
-  ensure_plan(c);
   const int b = c->stage_next;
-  if (c->lent_stage != nullptr) {
-    if (c->lent_stage_bytes < staging_need(c))
-      throw Error(CA_E_WORKSPACE, "staging of " + std::to_string(staging_need(c)) + " bytes needed, " +
-                                      std::to_string(c->lent_stage_bytes) + " attached");
-  }
+  const size_t need = ca_ctx::kStages * align_up(l.table_bytes);
+  if (c->lent_stage != nullptr && c->lent_stage_bytes < need)
+    throw Error(CA_E_WORKSPACE, "staging of " + std::to_string(need) + " bytes needed, " +
+                                    std::to_string(c->lent_stage_bytes) + " attached");
   if (c->stage_pending[b]) {
     hip_check(hipEventSynchronize(c->stage_done[b]), "hipEventSynchronize");
     c->stage_pending[b] = false;
   }
-  if (c->lent_stage == nullptr && c->stage_bytes[b] < c->table_bytes) {
+  if (c->lent_stage == nullptr && c->stage_bytes[b] < l.table_bytes) {
     if (c->stage[b]) hip_check(hipHostFree(c->stage[b]), "hipHostFree");
     c->stage[b] = nullptr;
     c->stage_bytes[b] = 0;
-    size_t want = align_up(c->table_bytes * 2);
+    size_t want = align_up(l.table_bytes * 2);
     hip_check(hipHostMalloc(&c->stage[b], want, hipHostMallocDefault), "hipHostMalloc");
     c->stage_bytes[b] = want;
   }
   if (!c->stage_done[b])
     hip_check(hipEventCreateWithFlags(&c->stage_done[b], hipEventDisableTiming), "hipEventCreate");
   char* s = static_cast<char*>(c->stage[b]);
-  table_image(c, s);
+  table_image(p, l, s);
   // from here on the device copy may be half written: stale until done
   mark_table_stale(c);
+  if (ws == c->pre.uploaded_ws) c->pre.uploaded_ws = nullptr;
   device_op(c, "table upload");
-  hip_check(hipMemcpyAsync(ws, s, c->table_bytes, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)),
+  hip_check(hipMemcpyAsync(ws, s, l.table_bytes, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)),
             "hipMemcpyAsync(table)");
   c->stage_next = (b + 1) % ca_ctx::kStages;
   c->stage_pending[b] = true;
   hip_check(hipEventRecord(c->stage_done[b], static_cast<hipStream_t>(stream)), "hipEventRecord");
   c->table_uploads += 1;
-  c->decode_epoch = 0;  // the upload wrote untagged fill counts
+}
+
+// After a table copy into ws holding the current plan: the device table is
+// current (untagged fill counts, cleared arrival counters).
+void note_upload(ca_ctx* c, void* ws, int scratch_dev) {
+  c->decode_epoch = 0;
   c->uploaded_version = c->version;
   c->uploaded_ws = ws;
   c->scratch_dev = scratch_dev;
@@ -404,6 +442,15 @@ void upload(ca_ctx* c, void* stream, void* ws, int scratch_dev = -1) {
   }
 }
 
+// scratch_dev: the device whose static scratch ws is, or -1 for the caller's
+// workspace.
+void upload(ca_ctx* c, void* stream, void* ws, int scratch_dev = -1) {
+  if (table_current_in(c, ws)) return;
+  ensure_plan(c);
+  copy_table(c, stream, ws, c->plan, c->lay);
+  note_upload(c, ws, scratch_dev);
+}
+
 chunkattn::StepArgs step_args(ca_ctx* c, void* ws, const void* q, void* out) {
   char* w = static_cast<char*>(ws);
   const chunkattn::Plan& p = c->plan;
@@ -411,15 +458,15 @@ chunkattn::StepArgs step_args(ca_ctx* c, void* ws, const void* q, void* out) {
   a.pool = c->pool;
   a.q = q;
   a.out = out;
-  a.cf_units = reinterpret_cast<const int32_t*>(w + c->off_cf);
-  a.sf_tasks = reinterpret_cast<const int32_t*>(w + c->off_sf);
-  a.chunk_refs = reinterpret_cast<const int32_t*>(w + c->off_refs);
-  a.dfs_qrow = reinterpret_cast<const int32_t*>(w + c->off_qrow);
-  a.seq_parts = reinterpret_cast<const int32_t*>(w + c->off_seqparts);
-  a.part_list = reinterpret_cast<const int32_t*>(w + c->off_partlist);
-  a.part_o = reinterpret_cast<float*>(w + c->off_part_o);
-  a.part_ms = reinterpret_cast<float*>(w + c->off_part_ms);
-  a.arrivals = reinterpret_cast<unsigned*>(w + c->off_arrivals);
+  a.cf_units = reinterpret_cast<const int32_t*>(w + c->lay.cf);
+  a.sf_tasks = reinterpret_cast<const int32_t*>(w + c->lay.sf);
+  a.chunk_refs = reinterpret_cast<const int32_t*>(w + c->lay.refs);
+  a.dfs_qrow = reinterpret_cast<const int32_t*>(w + c->lay.qrow);
+  a.seq_parts = reinterpret_cast<const int32_t*>(w + c->lay.seqparts);
+  a.part_list = reinterpret_cast<const int32_t*>(w + c->lay.partlist);
+  a.part_o = reinterpret_cast<float*>(w + c->lay.part_o);
+  a.part_ms = reinterpret_cast<float*>(w + c->lay.part_ms);
+  a.arrivals = reinterpret_cast<unsigned*>(w + c->lay.arrivals);
   a.heads = c->heads;
   a.dense_parts = p.dense_parts;
   a.part_stride = p.part_stride;
@@ -443,11 +490,11 @@ void check_step(ca_ctx* c, const void* q, void* out, const void* ws, size_t ws_b
   if (c->mgr.live() == 0) throw Error(CA_E_EMPTY, "no live sequence");
   if (q == nullptr || out == nullptr) throw Error(CA_E_INVALID_ARG, "q and out must be device pointers");
   ensure_plan(c, !table_current_in(c, ws));
-  if (fixed_ws && ws_bytes < c->total_bytes)
-    throw Error(CA_E_WORKSPACE, "this step needs a workspace of " + std::to_string(c->total_bytes) +
+  if (fixed_ws && ws_bytes < c->lay.total)
+    throw Error(CA_E_WORKSPACE, "this step needs a workspace of " + std::to_string(c->lay.total) +
                                     " bytes; the static scratch holds " + std::to_string(ws_bytes));
-  if (ws == nullptr || ws_bytes < c->total_bytes)
-    throw Error(CA_E_WORKSPACE, "workspace of " + std::to_string(c->total_bytes) + " bytes needed, " +
+  if (ws == nullptr || ws_bytes < c->lay.total)
+    throw Error(CA_E_WORKSPACE, "workspace of " + std::to_string(c->lay.total) + " bytes needed, " +
                                     std::to_string(ws_bytes) + " attached");
   // int32 indexing limits of the kernels
   if (static_cast<int64_t>(c->plan.cf_units.size()) * c->heads > INT32_MAX ||
@@ -480,8 +527,8 @@ bool fill_patches(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, std::vecto
   out->clear();
   if (!c->plan_valid || !c->mgr.fills_only() || !device_table_current(c)) return false;
   const chunkattn::Plan& p = c->plan;
-  const int32_t refs = static_cast<int32_t>(c->off_refs / sizeof(int32_t));
-  const int32_t tasks = static_cast<int32_t>(c->off_sf / sizeof(int32_t));
+  const int32_t refs = static_cast<int32_t>(c->lay.refs / sizeof(int32_t));
+  const int32_t tasks = static_cast<int32_t>(c->lay.sf / sizeof(int32_t));
   constexpr int32_t kTaskInts = sizeof(chunkattn::SfTask) / sizeof(int32_t);
   constexpr int32_t kFillField = offsetof(chunkattn::SfTask, n_valid) / sizeof(int32_t);
   for (const chunkattn::KvOp& o : ops) {
@@ -742,7 +789,7 @@ int ca_workspace_bytes(ca_ctx* ctx, size_t* out) {
   CA_GUARD(ctx, {
     if (out == nullptr) throw Error(CA_E_INVALID_ARG, "out is NULL");
     ensure_plan(ctx, false);
-    *out = ctx->total_bytes;
+    *out = ctx->lay.total;
     return CA_OK;
   });
 }
@@ -903,7 +950,9 @@ int ca_append_batch(ca_ctx* ctx, int32_t n, const int64_t* seq_ids, const int32_
       if (prebuilt && !ctx->plan_valid) adopt_prebuild(ctx);
     }
     if (device) store_appended(ctx, ops, k_dev, v_dev, stream, patches);
-    prebuild_next(ctx);
+    // the attention of this step is still to come (ca_attend): build ahead,
+    // but leave the table on the device as it is
+    prebuild_next(ctx, stream, false);
     return CA_OK;
   });
 }
@@ -923,7 +972,7 @@ int ca_prepare(ca_ctx* ctx, void* stream) {
     if (!ctx->pool_attached || ctx->pool == nullptr) throw Error(CA_E_NO_POOL, "no device pool attached");
     if (ctx->mgr.live() == 0) throw Error(CA_E_EMPTY, "no live sequence");
     ensure_plan(ctx, false);
-    if (ctx->ws == nullptr || ctx->ws_bytes < ctx->total_bytes)
+    if (ctx->ws == nullptr || ctx->ws_bytes < ctx->lay.total)
       throw Error(CA_E_WORKSPACE, "workspace too small");
     upload(ctx, stream, ctx->ws);
     return CA_OK;
@@ -1027,7 +1076,7 @@ int ca_decode_step(ca_ctx* ctx, const int32_t* tokens, const void* k_dev, const 
       if (in_kernel) store_appended(ctx, ops, k_dev, v_dev, stream, patches);
       throw;
     }
-    prebuild_next(ctx);
+    prebuild_next(ctx, stream, true);
     return CA_OK;
   });
 }
@@ -1061,10 +1110,10 @@ int ca_export_table(ca_ctx* ctx, int32_t* rows, int cap_rows, int64_t* dfs_seq_o
 int ca_export_plan(ca_ctx* ctx, void* buf, size_t cap, size_t* bytes) {
   CA_GUARD(ctx, {
     ensure_plan(ctx);
-    if (bytes) *bytes = ctx->table_bytes;
+    if (bytes) *bytes = ctx->lay.table_bytes;
     if (buf == nullptr && cap == 0) return CA_OK;
-    if (buf == nullptr || cap < ctx->table_bytes) throw Error(CA_E_INVALID_ARG, "output capacity too small");
-    table_image(ctx, static_cast<char*>(buf));
+    if (buf == nullptr || cap < ctx->lay.table_bytes) throw Error(CA_E_INVALID_ARG, "output capacity too small");
+    table_image(ctx->plan, ctx->lay, static_cast<char*>(buf));
     return CA_OK;
   });
 }

@@ -122,8 +122,11 @@ enum {
                                     tree before it returns, while the GPU runs the work just
                                     enqueued (the summary's section 3.3: context generation
                                     on the CPU overlapped with the GPU); that next append then
-                                    takes it instead of rebuilding.  0: every table is built
-                                    in the call that needs it. */
+                                    takes it instead of rebuilding.  ca_decode_step also
+                                    copies that table into the workspace after its own step
+                                    (a call in between that needs the current table uploads
+                                    it again).  0: every table is built and uploaded in the
+                                    call that needs it. */
   CA_OPT_ROW_APPENDS = 7         /* 1 (default): chunks that appends create keep their keys
                                     row-major in their slot (one K row and one V row per
                                     token and head: a decoded token is two contiguous 256-byte

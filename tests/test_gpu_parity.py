@@ -1102,3 +1102,60 @@ def test_captured_step_replays_equal_eager_steps(fused):
     ca.attend(q2, out2)
     torch.cuda.synchronize()
     assert torch.isfinite(out2).all()
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 128])
+def test_tables_built_and_uploaded_ahead(chunk):
+    """Decode steps with tables built ahead (and copied into the workspace
+    after the step that built them) against a twin context that builds and
+    uploads every table in the step that needs it: bit for bit at every step,
+    through structural steps (last chunks fill up at different steps), an
+    insert that makes a prediction stale, and extra ca_attend calls between
+    steps that upload the current table over the one copied ahead; the
+    oracle every few steps."""
+    _say(f"tables built ahead, chunk {chunk}")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import ChunkAttention, _capi
+    rng = np.random.default_rng(800 + chunk)
+    H = 2
+    cas = [ChunkAttention(H, 300, device="cuda:0", chunk_size=chunk) for _ in range(2)]
+    cas[1].set_option(_capi.CA_OPT_PREBUILD_PLAN, 0)
+    live = {}
+
+    def rnd(n):
+        return rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+
+    def insert(sid, t, k, v):
+        for ca in cas:
+            ca.insert(sid, t, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+        live[sid] = (list(t), k, v)
+
+    pre = list(range(3 * chunk))
+    kp, vp = rnd(3 * chunk), rnd(3 * chunk)
+    for i, n in enumerate((0, 5, chunk - 1, chunk // 2)):
+        insert(i, pre + [700 + i] * n, np.concatenate([kp, rnd(n)]), np.concatenate([vp, rnd(n)]))
+    for step in range(3 * chunk + 10):
+        ids = sorted(live)
+        k, v, q = rnd(len(ids)), rnd(len(ids)), rnd(len(ids))
+        t = np.array([int(x) for x in rng.integers(0, 40, size=len(ids))], np.int32)
+        outs = [ca.decode_step(t, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                               torch.from_numpy(q).cuda()).cpu().numpy() for ca in cas]
+        assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16)), step
+        for j, s_ in enumerate(ids):
+            tt, kk, vv = live[s_]
+            live[s_] = (tt + [int(t[j])], np.concatenate([kk, k[j:j + 1]]), np.concatenate([vv, v[j:j + 1]]))
+        if step % 23 == 0:
+            assert_parity(outs[0], A.decode_step(q, [live[s_][1:] for s_ in ids]), f"ahead {step}")
+        if step % 31 == 7:
+            # a step of attention alone: it uploads the current table (over a
+            # table copied ahead for the next tree, if any)
+            q2 = rnd(len(ids))
+            o2 = [ca.attend(torch.from_numpy(q2).cuda()).cpu().numpy() for ca in cas]
+            assert np.array_equal(o2[0].view(np.uint16), o2[1].view(np.uint16)), step
+        if step == 2 * chunk:
+            src = live[1]
+            insert(9, src[0][:chunk + 3] + [4321], np.concatenate([src[1][:chunk + 3], rnd(1)]),
+                   np.concatenate([src[2][:chunk + 3], rnd(1)]))
+    st = cas[0].stats()
+    assert st["prebuilt_plans"] >= 3 and cas[1].stats()["prebuilt_plans"] == 0
+    assert st["table_uploads"] < cas[1].stats()["table_uploads"] + 4
