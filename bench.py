@@ -23,8 +23,10 @@ the multi-branch tree: 128 sequences x 32 heads, a 1,024-token root, four
   comparator_shared_pages  the prefix stored once but no chunk-first phase
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
 per_config holds the same figures for the other workloads (and the 1,766-token
-prefix, and chunk sizes 32 and 128), decode_point one decode-progression
-point (batch 32, 2,048 shared prompt tokens, 512 completion tokens).
+prefix, and chunk sizes 32 and 128); ns_sweep_batch32 the shared-prompt sweep
+(0..4096 shared tokens, batch 32); decode_progression the decode sweeps over
+completion length and batch (2,048 shared prompt tokens); decode_host_overlap
+the host time of structural and fill-only decode steps.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5] [--headline-only]
 """
@@ -81,7 +83,8 @@ def parse():
                     help="with --decode: chunks made by appends stored row-major (1, the library default) or "
                          "as tiles (0)")
     ap.add_argument("--profile-only", action="store_true",
-                    help="only the per-kernel timing loop (for rocprofv3 runs); prints its event means")
+                    help="only the step timing loop (for rocprofv3 runs): warmup steps, then cold steps as "
+                         "ca_attend runs them; prints the event mean")
     ap.add_argument("--phases", action="store_true",
                     help="with --profile-only: launch the chunk-first and sequence-first parts of the partials "
                          "kernel separately (then the merge), so counters can be read per phase")
@@ -335,7 +338,9 @@ def decode_host_overlap(torch, n_seq, n_shared, n_steps, prebuild, heads=32, see
     for name in ("structural", "before_structural", "fill_only"):
         sel = [r for r in rows[1:] if r[0] == name]  # the first step warms up
         res[name] = {"steps": len(sel), "call_us": float(np.mean([r[1] for r in sel])) if sel else None,
-                     "wall_us": float(np.mean([r[2] for r in sel])) if sel else None}
+                     "wall_us": float(np.mean([r[2] for r in sel])) if sel else None,
+                     "call_us_p50": float(np.median([r[1] for r in sel])) if sel else None,
+                     "wall_us_p50": float(np.median([r[2] for r in sel])) if sel else None}
     return res
 
 
@@ -534,17 +539,16 @@ def main():
             step()
         torch.cuda.synchronize()
         one_launch = bool(st["one_launch_step"])
-        if one_launch and not args.phases:
-            # the step is one launch (merge blocks close the partials grid)
-            names = ("partials_kernel (one-launch step)",)
+        if not args.phases:
+            # the real step (ca_attend): one launch whose grid ends with the
+            # merge blocks, or the partials launch and the merge launch
+            names = ("step (partials_kernel, merge blocks included)" if one_launch
+                     else "step (partials_kernel + merge_kernel)",)
             lt = time_steps(torch, step, args.steps, flush)[:, None]
         elif args.phases:
             names = ("chunk_first", "sequence_first", "merge_kernel")
             lt = time_launches(torch, ca, q, out, args.steps, flush,
                                (_capi.CA_PHASE_CHUNK_FIRST, _capi.CA_PHASE_SEQUENCE_FIRST, _capi.CA_PHASE_MERGE))
-        else:
-            names = ("partials_kernel", "merge_kernel")
-            lt = time_launches(torch, ca, q, out, args.steps, flush, (_capi.CA_PHASE_PARTIALS, _capi.CA_PHASE_MERGE))
         # Calibration for hardware byte counters: a plain device copy of a known
         # size (256 MiB read + 256 MiB written), cold like the steps.
         src = torch.ones(1 << 27, dtype=torch.float16, device="cuda")
@@ -621,21 +625,57 @@ def main():
                                      cpu_seconds=args.cpu_seconds_per_config if main_case else None)
             del cache, w
         result["per_config"] = per
+    if not args.headline_only and args.prefix_len is None:
+        # The pages' shared-prompt sweep (summary section 4.1, Table 3: chunk 64,
+        # batch 32, shared tokens 0..4096), here with 512 private tokens each,
+        # against shared pages without the chunk-first phase and the unshared
+        # paged layout.
+        log("shared-prompt sweep: 32 seq x 32 heads, n_s 0 / 1024 / 2048 / 4096 + 512 private")
+        sweep = {}
+        for ns in (0, 1024, 2048, 4096):
+            w = make_prefix_suffix(ns, [512] * 32, heads=32, seed=3000 + ns)
+            cache = {}
+            r = measure(torch, args, w, flush, False, cache, cpu_seconds=None)
+            sweep[str(ns)] = {"step_us": r["step_us"]["mean"], "unique_kv_gbps": r["unique_kv_gbps"], "frac": r["frac"],
+                              "attended_tokens_per_s": r["attended_tokens_per_s"],
+                              "shared_pages_step_us": r["comparator_shared_pages"]["ms_per_step"] * 1e3,
+                              "unshared_step_us": r["comparator"]["ms_per_step"] * 1e3,
+                              "speedup_vs_shared_pages": r["comparator_shared_pages"]["speedup"],
+                              "speedup_vs_unshared": r["comparator"]["speedup"]}
+            del cache, w
+        result["ns_sweep_batch32"] = sweep
     if not args.headline_only and not args.no_decode:
-        log("decode progression: batch 32, n_s 2048, n_c 512")
-        dec = {}
-        for mode, two_phase, one_call in (("decode_step", True, True), ("append_then_attend", True, False),
-                                          ("shared_pages_no_chunk_first", False, False)):
-            dec[mode] = decode_progression(torch, 32, 2048, [512], two_phase, flush, one_call=one_call)[512]
-        dec["speedup_decode_step_vs_shared_pages"] = (
-            (dec["shared_pages_no_chunk_first"]["append_us"] + dec["shared_pages_no_chunk_first"]["attend_us"])
-            / (dec["decode_step"]["append_us"] + dec["decode_step"]["attend_us"]))
-        result["decode_point"] = {"workload": "32 sequences x 32 heads sharing a 2,048-token prompt, one token "
-                                              "appended per sequence per step, mean over the 16 cold steps "
-                                              "ending at n_c = 512 completion tokens", **dec}
-        log("decode host overlap: batch 32 and 96, 256 steps, waiting for each step")
+        # The decode progression (Figures 3 and 4): 2,048 shared prompt tokens,
+        # one token per sequence per step; completion lengths 512..2048 at batch
+        # 32 and batches 16..96 at 512 completion tokens.
+        log("decode progression: n_c 512 / 1024 / 2048 at batch 32, batch 16 / 32 / 64 / 96 at n_c 512")
+        modes = (("decode_step", True, True), ("append_then_attend", True, False),
+                 ("shared_pages_no_chunk_first", False, False))
+        nc_sweep = {m: decode_progression(torch, 32, 2048, [512, 1024, 2048], tp, flush, one_call=oc)
+                    for m, tp, oc in modes}
+        batch_sweep = {m: {b: (nc_sweep[m][512] if b == 32 else
+                               decode_progression(torch, b, 2048, [512], tp, flush, one_call=oc)[512])
+                           for b in (16, 32, 64, 96)} for m, tp, oc in modes}
+
+        def step_us(r):
+            return r["append_us"] + r["attend_us"]
+
+        result["decode_progression"] = {
+            "workload": "32 heads, a 2,048-token prompt shared by every sequence, one token appended per sequence "
+                        "per step; each point the mean of the 16 cold steps ending at that completion length",
+            "nc_sweep_batch32": nc_sweep,
+            "batch_sweep_nc512": batch_sweep,
+            "generated_tokens_per_s_decode_step": {
+                "nc": {nc: nc_sweep["decode_step"][nc]["generated_tokens_per_s"] for nc in (512, 1024, 2048)},
+                "batch": {b: batch_sweep["decode_step"][b]["generated_tokens_per_s"] for b in (16, 32, 64, 96)}},
+            "speedup_decode_step_vs_shared_pages": {
+                "nc": {nc: step_us(nc_sweep["shared_pages_no_chunk_first"][nc]) / step_us(nc_sweep["decode_step"][nc])
+                       for nc in (512, 1024, 2048)},
+                "batch": {b: step_us(batch_sweep["shared_pages_no_chunk_first"][b]) /
+                          step_us(batch_sweep["decode_step"][b]) for b in (16, 32, 64, 96)}}}
+        log("decode host overlap: batch 32 and 96, 1024 steps, waiting for each step")
         result["decode_host_overlap"] = {
-            f"batch{b}": {("prebuild_on" if pb else "prebuild_off"): decode_host_overlap(torch, b, 2048, 256, pb)
+            f"batch{b}": {("prebuild_on" if pb else "prebuild_off"): decode_host_overlap(torch, b, 2048, 1024, pb)
                           for pb in (True, False)} for b in (32, 96)}
     print(json.dumps(result), flush=True)
 
