@@ -30,7 +30,10 @@ struct Prebuild {
   int cf_auto = 0, plan_cf_group = 0;
   double ms = 0.0;
   // the workspace the plan's table was copied into, after the step that
-  // built it (null: not copied, or overwritten since)
+  // built it (null: not copied, or overwritten since).  That copy holds each
+  // sequence's last chunk at its fill count before the appends, so it
+  // becomes the current table once their fill counts are stored (by the
+  // step's own blocks, or with the K/V writes).
   void* uploaded_ws = nullptr;
 };
 
@@ -293,7 +296,8 @@ int build_for(const ca_ctx* c, chunkattn::Plan* plan, const chunkattn::NextAppen
   return cf_auto;
 }
 
-void copy_table(ca_ctx* c, void* stream, void* ws, const chunkattn::Plan& p, const Layout& l);
+void copy_table(ca_ctx* c, void* stream, void* ws, const chunkattn::Plan& p, const Layout& l,
+                bool before_appends = false);
 void note_upload(ca_ctx* c, void* ws, int scratch_dev);
 
 // After a batch of one-token appends over every live sequence (a decode
@@ -324,7 +328,7 @@ void prebuild_next(ca_ctx* c, void* stream, bool upload) {
     const Layout l = layout_of(p.plan, c->heads, c->head_dim);
     if (upload && c->pool != nullptr && c->ws != nullptr && c->ws_bytes >= l.total && c->fail_ops == 0) {
       try {
-        copy_table(c, stream, c->ws, p.plan, l);
+        copy_table(c, stream, c->ws, p.plan, l, true);
         p.uploaded_ws = c->ws;
       } catch (const Error&) {
         mark_table_stale(c);
@@ -345,7 +349,11 @@ bool prebuild_matches(const ca_ctx* c, const int64_t* ids, int32_t n) {
 }
 
 // After those appends changed the plan's shape: take the plan built ahead.
-void adopt_prebuild(ca_ctx* c) {
+// Returns whether its table is in the workspace already (copied ahead, and
+// nothing uploaded there since): the device table is then noted as current,
+// and the caller must store the appends' fill counts into it (fill_patches)
+// or mark it stale.
+bool adopt_prebuild(ca_ctx* c) {
   std::swap(c->plan, c->pre.plan);
   c->pre.ok = false;
   c->cf_auto = c->pre.cf_auto;
@@ -357,10 +365,10 @@ void adopt_prebuild(ca_ctx* c) {
   c->rebuilds += 1;
   c->prebuilt_plans += 1;
   c->last_rebuild_ms = c->pre.ms;
-  // its table is already in the workspace, unless something was uploaded there since
-  if (c->pre.uploaded_ws != nullptr && c->pre.uploaded_ws == c->ws && c->ws_bytes >= c->lay.total)
-    note_upload(c, c->ws, -1);
+  const bool ahead = c->pre.uploaded_ws != nullptr && c->pre.uploaded_ws == c->ws && c->ws_bytes >= c->lay.total;
+  if (ahead) note_upload(c, c->ws, -1);
   c->pre.uploaded_ws = nullptr;
+  return ahead;
 }
 
 template <typename T>
@@ -369,8 +377,11 @@ void put(char* base, size_t off, const std::vector<T>& v) {
 }
 
 // The device table of a plan (table_bytes): records, chunk refs, row and
-// partial lists, and zeroed arrival counters.
-void table_image(const chunkattn::Plan& p, const Layout& l, char* s) {
+// partial lists, and zeroed arrival counters.  before_appends: the plan is
+// of the tree after one token is appended to every sequence; the chunk ref
+// that takes each sequence's token (its task's append field) keeps the fill
+// count from before that token.
+void table_image(const chunkattn::Plan& p, const Layout& l, char* s, bool before_appends = false) {
   std::memset(s, 0, l.table_bytes);
   put(s, l.cf, p.cf_units);
   put(s, l.sf, p.sf_tasks);
@@ -378,6 +389,16 @@ void table_image(const chunkattn::Plan& p, const Layout& l, char* s) {
   put(s, l.qrow, p.dfs_qrow);
   put(s, l.seqparts, p.seq_parts);
   put(s, l.partlist, p.part_list);
+  if (!before_appends) return;
+  auto* tasks = reinterpret_cast<chunkattn::SfTask*>(s + l.sf);
+  auto* refs = reinterpret_cast<int32_t*>(s + l.refs);
+  for (size_t t = 0; t < p.sf_tasks.size(); ++t) {
+    const int32_t at = tasks[t].append_at;
+    if (at < 0) continue;
+    // the fill is at least 1 after the append; the row bit stays
+    refs[2 * (tasks[t].chunk_begin + at) + 1] -= 1;
+    if (at < chunkattn::kSfInline) tasks[t].n_valid[at] -= 1;
+  }
 }
 
 // Staging bytes for the current table: three parts, each holding the table.
@@ -387,7 +408,8 @@ size_t staging_need(const ca_ctx* c) { return ca_ctx::kStages * align_up(c->lay.
 // Copy a plan's device table into workspace ws on the stream, through the
 // next staging buffer of the ring.  Throws before enqueueing anything if the
 // stream captures or the lent staging is too small.
-void copy_table(ca_ctx* c, void* stream, void* ws, const chunkattn::Plan& p, const Layout& l) {
+void copy_table(ca_ctx* c, void* stream, void* ws, const chunkattn::Plan& p, const Layout& l,
+                bool before_appends) {
   // A graph would replay the copy from a staging buffer that later uploads
   // rewrite (and waiting for the ring is no call for a capture): a step is
   // captured only once its table is on the device.
@@ -416,7 +438,7 @@ void copy_table(ca_ctx* c, void* stream, void* ws, const chunkattn::Plan& p, con
   if (!c->stage_done[b])
     hip_check(hipEventCreateWithFlags(&c->stage_done[b], hipEventDisableTiming), "hipEventCreate");
   char* s = static_cast<char*>(c->stage[b]);
-  table_image(p, l, s);
+  table_image(p, l, s, before_appends);
   // from here on the device copy may be half written: stale until done
   mark_table_stale(c);
   if (ws == c->pre.uploaded_ws) c->pre.uploaded_ws = nullptr;
@@ -541,6 +563,33 @@ bool fill_patches(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, std::vecto
         p.ref_pos[k] < chunkattn::kSfInline ? tasks + p.ref_task[k] * kTaskInts + kFillField + p.ref_pos[k] : -1;
     const int32_t row = c->mgr.row(o.node) ? chunkattn::kRowBit : 0;
     out->push_back(FillPatch{refs + 2 * k + 1, task_off, c->mgr.tile_fill(o.dst_key0 + o.n_rows, p.ref_sub[k]) | row});
+  }
+  return true;
+}
+
+// After appends that changed the plan's shape and match the plan built
+// ahead: take that plan.  If its table was copied ahead into the workspace,
+// the appends' fill counts go into it (patches, one per op) and it is current
+// once they are stored; if they cannot be patched there, the table is
+// uploaded again before the next step.  Returns whether patches were made.
+bool take_prebuild(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, std::vector<FillPatch>* patches) {
+  patches->clear();
+  if (!adopt_prebuild(c)) return false;
+  if (fill_patches(c, ops, patches)) return true;
+  mark_table_stale(c);
+  return false;
+}
+
+// Whether the step's own blocks can store these appends: one token per op
+// from the caller's rows, into a row-major chunk or into a tile part that
+// already holds keys (a tile part's first write also clears its other keys,
+// which only the write launch does).
+bool kernel_can_store(const ca_ctx* c, const std::vector<chunkattn::KvOp>& ops) {
+  const int64_t part = std::min<int64_t>(c->chunk, chunkattn::kTileKeys);
+  for (const chunkattn::KvOp& o : ops) {
+    if (o.n_rows != 1 || o.from_pool || o.mode == chunkattn::kOpConvert) return false;
+    if (o.mode == chunkattn::kOpTiles && (static_cast<int64_t>(o.dst_slot) * c->chunk + o.dst_key0) % part == 0)
+      return false;
   }
   return true;
 }
@@ -947,7 +996,8 @@ int ca_append_batch(ca_ctx* ctx, int32_t n, const int64_t* seq_ids, const int32_
       touch_patched(ctx);
     } else {
       touch_after_append(ctx);
-      if (prebuilt && !ctx->plan_valid) adopt_prebuild(ctx);
+      // a table copied ahead takes these fill counts with the K/V writes
+      if (prebuilt && !ctx->plan_valid && take_prebuild(ctx, ops, &patches)) touch_patched(ctx);
     }
     if (device) store_appended(ctx, ops, k_dev, v_dev, stream, patches);
     // the attention of this step is still to come (ca_attend): build ahead,
@@ -1038,20 +1088,27 @@ int ca_decode_step(ca_ctx* ctx, const int32_t* tokens, const void* k_dev, const 
     std::vector<FillPatch> patches;
     const bool prebuilt = prebuild_matches(ctx, ids.data(), static_cast<int32_t>(ids.size()));
     ctx->mgr.append_batch(ids.data(), tokens, static_cast<int32_t>(ids.size()), &ops);
-    // Every token grew its sequence's private last chunk in place and the
-    // table in the step's workspace is current: the step's own blocks write
-    // the tokens.  The epoch tags the fill counts they store; it restarts
-    // (with a clean table) before it would wrap.
-    const bool in_kernel = fill_patches(ctx, ops, &patches) && ctx->uploaded_ws == ctx->ws &&
-                           ctx->decode_epoch < chunkattn::kEpochMask;
-    if (in_kernel) {
-      touch_patched(ctx);
-      ctx->decode_epoch += 1;
-    } else {
+    // The table in the step's workspace holds the tree up to these appends'
+    // fill counts: the current table (every token grew its sequence's
+    // private last chunk in place), or the one copied ahead for the chunks
+    // these appends open.  The fill counts are then stored into it: by the
+    // step's own blocks, which also write the tokens, tagging the counts with
+    // the epoch (it restarts, with a clean table, before it would wrap), or
+    // by the write launch where a token opens a tile part that must be
+    // cleared first.
+    bool patched = ctx->decode_epoch < chunkattn::kEpochMask && fill_patches(ctx, ops, &patches) &&
+                   ctx->uploaded_ws == ctx->ws;
+    if (!patched) {
+      patches.clear();
       touch_after_append(ctx);
-      if (prebuilt && !ctx->plan_valid) adopt_prebuild(ctx);
-      store_appended(ctx, ops, k_dev, v_dev, stream);
+      patched = prebuilt && !ctx->plan_valid && take_prebuild(ctx, ops, &patches);
     }
+    const bool in_kernel = patched && kernel_can_store(ctx, ops);
+    if (patched) touch_patched(ctx);
+    if (in_kernel)
+      ctx->decode_epoch += 1;
+    else
+      store_appended(ctx, ops, k_dev, v_dev, stream, patches);
     try {
       check_step(ctx, q_dev, out_dev, ctx->ws, ctx->ws_bytes);
     } catch (const Error&) {

@@ -125,8 +125,12 @@ enum {
                                     takes it instead of rebuilding.  ca_decode_step also
                                     copies that table into the workspace after its own step
                                     (a call in between that needs the current table uploads
-                                    it again).  0: every table is built and uploaded in the
-                                    call that needs it. */
+                                    it again), with each sequence's last chunk at its fill
+                                    before the next token: the next decode step then stores
+                                    the tokens of the chunks it opens itself (row-major
+                                    chunks, CA_OPT_ROW_APPENDS) and uploads nothing.
+                                    0: every table is built and uploaded in the call that
+                                    needs it. */
   CA_OPT_ROW_APPENDS = 7         /* 1 (default): chunks that appends create keep their keys
                                     row-major in their slot (one K row and one V row per
                                     token and head: a decoded token is two contiguous 256-byte
@@ -173,8 +177,9 @@ typedef struct ca_stats_t {
   int64_t private_tokens;    /* tokens held in chunks with one reference */
   int64_t fill_refreshes;    /* plan updates that only refreshed chunk fills */
   int64_t table_uploads;     /* host-to-device copies of the chunk table */
-  int64_t patched_appends;   /* appends whose fill counts the write launch
-                                stored into the device table itself */
+  int64_t patched_appends;   /* appends whose fill counts went into the device
+                                table in place (stored by the write launch or by
+                                the decode step's own blocks), with no upload */
   int64_t cf_chunks_per_task; /* chunk-first group of the current plan */
   int64_t one_launch_step;    /* 1 if ca_attend runs the step as one launch */
   int64_t sf_chunks_per_task; /* sequence-first group of the current plan */

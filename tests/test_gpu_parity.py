@@ -1105,22 +1105,28 @@ def test_captured_step_replays_equal_eager_steps(fused):
 
 
 @pytest.mark.parametrize("chunk", [32, 64, 128])
-def test_tables_built_and_uploaded_ahead(chunk):
+@pytest.mark.parametrize("rows_on", [1, 0])
+def test_tables_built_and_uploaded_ahead(chunk, rows_on):
     """Decode steps with tables built ahead (and copied into the workspace
-    after the step that built them) against a twin context that builds and
+    after the step that built them, with each sequence's last chunk at its
+    fill before the next token) against a twin context that builds and
     uploads every table in the step that needs it: bit for bit at every step,
-    through structural steps (last chunks fill up at different steps), an
-    insert that makes a prediction stale, and extra ca_attend calls between
-    steps that upload the current table over the one copied ahead; the
-    oracle every few steps."""
-    _say(f"tables built ahead, chunk {chunk}")
+    through structural steps (last chunks fill up at different steps; the
+    step's own blocks store the tokens of the chunks they open when those are
+    row-major, the write launch otherwise), an insert that makes a prediction
+    stale, and extra ca_attend calls between steps that upload the current
+    table over the one copied ahead; the oracle every few steps, and every
+    stored key against the caller's K/V at the end."""
+    _say(f"tables built ahead, chunk {chunk}, rows {rows_on}")
     torch = _torch()
     from decode_attention_prefix_tree_amd import ChunkAttention, _capi
     rng = np.random.default_rng(800 + chunk)
     H = 2
     cas = [ChunkAttention(H, 300, device="cuda:0", chunk_size=chunk) for _ in range(2)]
     cas[1].set_option(_capi.CA_OPT_PREBUILD_PLAN, 0)
-    live = {}
+    for ca in cas:
+        ca.set_option(_capi.CA_OPT_ROW_APPENDS, rows_on)
+    live, inserted = {}, {}
 
     def rnd(n):
         return rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
@@ -1129,6 +1135,7 @@ def test_tables_built_and_uploaded_ahead(chunk):
         for ca in cas:
             ca.insert(sid, t, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
         live[sid] = (list(t), k, v)
+        inserted[sid] = len(t)
 
     pre = list(range(3 * chunk))
     kp, vp = rnd(3 * chunk), rnd(3 * chunk)
@@ -1156,6 +1163,15 @@ def test_tables_built_and_uploaded_ahead(chunk):
             src = live[1]
             insert(9, src[0][:chunk + 3] + [4321], np.concatenate([src[1][:chunk + 3], rnd(1)]),
                    np.concatenate([src[2][:chunk + 3], rnd(1)]))
-    st = cas[0].stats()
-    assert st["prebuilt_plans"] >= 3 and cas[1].stats()["prebuilt_plans"] == 0
-    assert st["table_uploads"] < cas[1].stats()["table_uploads"] + 4
+    st, st1 = cas[0].stats(), cas[1].stats()
+    assert st["prebuilt_plans"] >= 3 and st1["prebuilt_plans"] == 0
+    assert st["table_uploads"] < st1["table_uploads"] + 4
+    # the structural steps that found their table in place stored their
+    # fill counts there instead of uploading a new table
+    assert st["patched_appends"] >= st1["patched_appends"] + 3, (st["patched_appends"], st1["patched_appends"])
+    for ca in cas:
+        rows, order = ca.export_table()
+        # chunks that appends opened: private, past the sequence's inserted length
+        rr = {ri for ri, r in enumerate(rows)
+              if rows_on and r[5] - r[4] == 1 and r[2] >= inserted[order[r[4]]]}
+        _check_pool(ca, H, chunk, lambda s_: live[s_][1:], rr)
