@@ -281,9 +281,12 @@ def decode_progression(torch, n_seq, n_shared, checkpoints, two_phase, flush, wi
             app = float(np.mean([r[0] for r in rows])) * 1e3
             att = float(np.mean([r[1] for r in rows])) * 1e3
             host = float(np.mean([r[2] for r in rows])) * 1e6
+            host_p50 = float(np.median([r[2] for r in rows])) * 1e6
+            host_max = float(np.max([r[2] for r in rows])) * 1e6
             st = ca.stats()
             # with one_call the append column is 0 and attend is the whole step
             res[c] = {"append_us": app, "attend_us": att, "host_us_per_step": host,
+                      "host_us_p50": host_p50, "host_us_max": host_max,
                       "generated_tokens_per_s": n_seq / ((app + att) * 1e-6),
                       "attended_tokens_per_s": st["attended_tokens"] / (att * 1e-6),
                       "unique_kv_gbps": st["unique_kv_bytes"] / (att * 1e-6) / 1e9,

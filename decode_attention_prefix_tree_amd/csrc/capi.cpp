@@ -319,6 +319,7 @@ void prebuild_next(ca_ctx* c, void* stream, bool upload) {
   p.ids = c->mgr.sequences();
   chunkattn::NextAppend next;
   if (c->mgr.predict_append_batch(p.ids.data(), static_cast<int32_t>(p.ids.size()), &next) && next.structural) {
+    c->mgr.stock_for_append(next);
     p.cf_auto = build_for(c, &p.plan, &next);
     p.plan_cf_group = c->cf_group ? c->cf_group : p.cf_auto;
     p.ok = true;

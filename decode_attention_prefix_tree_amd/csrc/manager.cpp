@@ -25,27 +25,32 @@ void Manager::set_capacity(int64_t capacity) {
   if (!end_.empty()) throw Error(kState, "pool can only change while no sequence is live");
   if (capacity < 0 || capacity > INT32_MAX) throw Error(kInvalidArg, "capacity out of range");
   capacity_ = capacity;
-  free_ = decltype(free_)();
-  std::vector<int32_t> all(static_cast<size_t>(capacity));
-  for (int32_t i = 0; i < capacity; ++i) all[i] = i;
-  free_ = decltype(free_)(std::greater<int32_t>(), std::move(all));
+  free_.reset(capacity);
 }
 
-int32_t Manager::alloc_slot() {
-  int32_t s = free_.top();
-  free_.pop();
-  return s;
-}
+int32_t Manager::alloc_slot() { return free_.take(); }
 
 int32_t Manager::new_node(int32_t parent, int32_t start) {
   int32_t idx;
   if (!free_nodes_.empty()) {
+    // a freed node: its lists are empty and keep their room
     idx = free_nodes_.back();
     free_nodes_.pop_back();
-    nodes_[idx] = Node();
+    Node& r = nodes_[idx];
+    r.ref = 0;
+    r.row = false;
   } else {
     idx = static_cast<int32_t>(nodes_.size());
     nodes_.emplace_back();
+    Node& f = nodes_[idx];
+    if (!spare_tokens_.empty()) {
+      f.tokens.swap(spare_tokens_.back());
+      spare_tokens_.pop_back();
+    }
+    if (!spare_ended_.empty()) {
+      f.ended.swap(spare_ended_.back());
+      spare_ended_.pop_back();
+    }
   }
   Node& n = nodes_[idx];
   n.id = next_id_++;
@@ -59,7 +64,7 @@ int32_t Manager::new_node(int32_t parent, int32_t start) {
 
 void Manager::free_node(int32_t idx) {
   Node& n = nodes_[idx];
-  free_.push(n.slot);
+  free_.give(n.slot);
   n.alive = false;
   n.tokens.clear();
   n.children.clear();
@@ -220,6 +225,25 @@ bool Manager::next_append_structural() const {
   return false;
 }
 
+void Manager::stock_for_append(const NextAppend& next) {
+  size_t fresh = 0;
+  for (const NextAppend::Add& a : next.add) {
+    if (static_cast<size_t>(a.idx) >= nodes_.size()) ++fresh;
+    std::vector<int32_t>& ch = nodes_[a.parent].children;
+    ch.reserve(ch.size() + 1);
+  }
+  // geometric growth: an exact reserve would move every node at every call
+  if (nodes_.capacity() < next.n_nodes) nodes_.reserve(std::max(next.n_nodes, 2 * nodes_.capacity()));
+  while (spare_tokens_.size() < fresh) {
+    spare_tokens_.emplace_back();
+    spare_tokens_.back().reserve(C_);
+  }
+  while (spare_ended_.size() < fresh) {
+    spare_ended_.emplace_back();
+    spare_ended_.back().reserve(1);
+  }
+}
+
 bool Manager::predict_append_batch(const int64_t* seqs, int32_t n, NextAppend* out) const {
   NextAppend& x = *out;
   x.grow.clear();
@@ -231,14 +255,9 @@ bool Manager::predict_append_batch(const int64_t* seqs, int32_t n, NextAppend* o
   std::sort(sorted.begin(), sorted.end());
   if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) return false;
   // new chunks take node indices from the reuse list (last first), then the
-  // end of the node array, and the lowest free slots in order: the k smallest
-  // entries of the min-heap, by a best-first walk over it
+  // end of the node array, and the lowest free slots in increasing order
   size_t reuse = free_nodes_.size();
-  const std::vector<int32_t>& heap = free_.heap();
-  std::priority_queue<std::pair<int32_t, size_t>, std::vector<std::pair<int32_t, size_t>>,
-                      std::greater<std::pair<int32_t, size_t>>>
-      frontier;
-  if (!heap.empty()) frontier.push({heap[0], 0});
+  FreeSlots::Walk slots(free_);
   for (int32_t j = 0; j < n; ++j) {
     auto it = end_.find(seqs[j]);
     if (it == end_.end()) return false;
@@ -250,10 +269,8 @@ bool Manager::predict_append_batch(const int64_t* seqs, int32_t n, NextAppend* o
       if (tiles_of(fill + 1) != tiles_of(fill)) x.structural = true;
       continue;
     }
-    if (frontier.empty()) return false;  // out of slots
-    const auto [slot, h] = frontier.top();
-    frontier.pop();
-    for (size_t c = 2 * h + 1; c <= 2 * h + 2 && c < heap.size(); ++c) frontier.push({heap[c], c});
+    const int32_t slot = slots.next();
+    if (slot < 0) return false;  // out of slots
     int32_t idx;
     if (reuse > 0) {
       idx = free_nodes_[--reuse];

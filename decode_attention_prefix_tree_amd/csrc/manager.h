@@ -30,7 +30,6 @@
 #include <cstdint>
 #include <functional>
 #include <map>
-#include <queue>
 #include <stdexcept>
 #include <string>
 #include <vector>
@@ -194,6 +193,11 @@ class Manager {
   // Whether one more token for every live sequence would change the plan's
   // shape (a last chunk full or shared, or a chunk opening another tile).
   bool next_append_structural() const;
+  // Memory for the chunks a predicted append will open (node array room,
+  // token and sequence lists, the parents' child lists), allocated now so
+  // that the append itself allocates nothing: the host can do this while
+  // the GPU still runs the previous step.
+  void stock_for_append(const NextAppend& next);
 
   // True when the last mutations only grew chunks in place (no chunk created
   // or freed, no sequence joined or left) since the last clear_structural().
@@ -247,10 +251,59 @@ class Manager {
   int64_t n_nodes_ = 0;
   std::vector<Node> nodes_;                 // nodes_[0] is the root
   std::vector<int32_t> free_nodes_;         // reusable indices in nodes_
-  // free slots, a min-heap whose array the prediction of appends reads
-  struct FreeSlots : std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> {
-    using priority_queue::priority_queue;
-    const std::vector<int32_t>& heap() const { return c; }
+  // empty lists with room reserved, taken by new nodes (stock_for_append)
+  std::vector<std::vector<int32_t>> spare_tokens_;
+  std::vector<std::vector<int64_t>> spare_ended_;
+  // Free chunk slots, lowest first: one bit per slot (set = free) and the
+  // index of the first word that may hold a free slot (every word below it
+  // is all taken), so taking the lowest free slot costs a few word reads.
+  class FreeSlots {
+   public:
+    void reset(int64_t capacity) {
+      bits_.assign(static_cast<size_t>((capacity + 63) / 64), ~uint64_t{0});
+      if (capacity % 64) bits_.back() = (uint64_t{1} << (capacity % 64)) - 1;
+      n_ = capacity;
+      first_ = 0;
+    }
+    int64_t size() const { return n_; }
+    // the lowest free slot (there must be one)
+    int32_t take() {
+      while (bits_[first_] == 0) ++first_;
+      uint64_t& w = bits_[first_];
+      const int32_t s = static_cast<int32_t>(first_ * 64 + static_cast<size_t>(__builtin_ctzll(w)));
+      w &= w - 1;
+      --n_;
+      return s;
+    }
+    void give(int32_t s) {
+      bits_[static_cast<size_t>(s) >> 6] |= uint64_t{1} << (s & 63);
+      ++n_;
+      first_ = std::min(first_, static_cast<size_t>(s) >> 6);
+    }
+    // The free slots in increasing order, without taking them.
+    class Walk {
+     public:
+      explicit Walk(const FreeSlots& f) : f_(f), word_(f.first_), left_(word_ < f.bits_.size() ? f.bits_[word_] : 0) {}
+      // the next free slot, or -1 when none is left
+      int32_t next() {
+        while (left_ == 0) {
+          if (++word_ >= f_.bits_.size()) return -1;
+          left_ = f_.bits_[word_];
+        }
+        const int32_t s = static_cast<int32_t>(word_ * 64 + static_cast<size_t>(__builtin_ctzll(left_)));
+        left_ &= left_ - 1;
+        return s;
+      }
+     private:
+      const FreeSlots& f_;
+      size_t word_;
+      uint64_t left_;
+    };
+
+   private:
+    std::vector<uint64_t> bits_;
+    int64_t n_ = 0;
+    size_t first_ = 0;
   };
   FreeSlots free_;
   std::map<int64_t, int32_t> end_;          // seq -> node index where it ends

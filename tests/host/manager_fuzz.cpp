@@ -4,8 +4,9 @@
 // manager's own error (never an internal one), at chunk sizes 2 to 128, with
 // chunks made by appends stored row-major or not.  Before every batched
 // append over all live sequences, the plan predicted for the tree after it
-// must equal the plan built once it is made, and the prediction must fail
-// exactly when the append does.
+// must equal the plan built once it is made (with or without the new chunks'
+// memory reserved ahead), and the prediction must fail exactly when the
+// append does.
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -66,6 +67,8 @@ int main(int argc, char** argv) {
           NextAppend next;
           Plan pred, fresh;
           const bool can = m.predict_append_batch(ids.data(), (int32_t)ids.size(), &next);
+          // memory for the new chunks reserved ahead changes nothing else
+          if (can && rng() % 2) m.stock_for_append(next);
           if (can) m.build_plan(cfg, sfg, two_phase, &pred, min_tasks, &next);
           bool done = false;
           try {
