@@ -174,6 +174,22 @@ void device_op(ca_ctx* c, const char* what) {
   }
 }
 
+// Calls that change the tree update host state that a graph replay would
+// not: with a device pool they refuse a capturing stream, before anything
+// changes.  A stream the runtime cannot query is not capturing; the error
+// is cleared here and the call's own device work reports it.
+void refuse_capture(const ca_ctx* c, void* stream, const char* what) {
+  if (c->pool == nullptr) return;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &st) != hipSuccess) {
+    (void)hipGetLastError();
+    return;
+  }
+  if (st != hipStreamCaptureStatusNone)
+    throw Error(CA_E_STATE, std::string(what) + " changes the tree on the host, which a graph replay would not "
+                                                "repeat: call it outside the capture (ca_attend can be captured)");
+}
+
 void require_usable(const ca_ctx* c) {
   if (c->broken)
     throw Error(CA_E_STATE, "a device operation failed after the tree had changed; the stored K/V no longer "
@@ -940,6 +956,7 @@ int ca_insert(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n, con
     const bool device = ctx->pool != nullptr;
     if (device && (k_dev == nullptr || v_dev == nullptr))
       throw Error(CA_E_INVALID_ARG, "k_dev and v_dev are required when a device pool is attached");
+    refuse_capture(ctx, stream, "ca_insert");
     std::vector<chunkattn::KvOp> ops;
     // A failed copy puts the tree back as it was: the copies only write the
     // slots this insert took (new chunks, a split's tail), which are free again.
@@ -968,6 +985,7 @@ int ca_append(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n, con
     const bool device = ctx->pool != nullptr;
     if (device && (k_dev == nullptr || v_dev == nullptr))
       throw Error(CA_E_INVALID_ARG, "k_dev and v_dev are required when a device pool is attached");
+    refuse_capture(ctx, stream, "ca_append");
     std::vector<chunkattn::KvOp> ops;
     std::vector<FillPatch> patches;
     ctx->mgr.append(seq_id, tokens, n, &ops);
@@ -989,6 +1007,7 @@ int ca_append_batch(ca_ctx* ctx, int32_t n, const int64_t* seq_ids, const int32_
     const bool device = ctx->pool != nullptr;
     if (device && (k_dev == nullptr || v_dev == nullptr))
       throw Error(CA_E_INVALID_ARG, "k_dev and v_dev are required when a device pool is attached");
+    refuse_capture(ctx, stream, "ca_append_batch");
     std::vector<chunkattn::KvOp> ops;
     std::vector<FillPatch> patches;
     const bool prebuilt = prebuild_matches(ctx, seq_ids, n);
@@ -1084,6 +1103,7 @@ int ca_decode_step(ca_ctx* ctx, const int32_t* tokens, const void* k_dev, const 
     if (tokens == nullptr || k_dev == nullptr || v_dev == nullptr)
       throw Error(CA_E_INVALID_ARG, "tokens, k_dev and v_dev are required");
     if (q_dev == nullptr || out_dev == nullptr) throw Error(CA_E_INVALID_ARG, "q and out must be device pointers");
+    refuse_capture(ctx, stream, "ca_decode_step");
     const std::vector<int64_t> ids = ctx->mgr.sequences();
     std::vector<chunkattn::KvOp> ops;
     std::vector<FillPatch> patches;

@@ -36,6 +36,10 @@
  *    runs device work then returns CA_E_STATE (destroy the context).
  *  - A context is not thread-safe.  Calls that enqueue device work on
  *    different streams must be ordered by the caller.
+ *  - Calls that change the tree (ca_insert, ca_append, ca_append_batch,
+ *    ca_decode_step) return CA_E_STATE, changing nothing, when a device pool
+ *    is attached and `stream` is capturing a HIP graph: a replay would repeat
+ *    their device writes but not the host's tree update.  Capture ca_attend.
  *  - Element types: K, V, Q and the output are IEEE binary16 (fp16); the
  *    kernels accumulate in fp32.  Token ids are int32.
  *  - head_dim 128; chunk_size 64 (the chunk size of the summary's Table 3,

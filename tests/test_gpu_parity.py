@@ -1039,7 +1039,8 @@ def test_captured_step_replays_equal_eager_steps(fused):
     replays (fill counts stored on the device) are seen by the replays.  In
     the one-launch step nothing carries over between replays (arrival
     counters return to zero).  A step that would upload the table while the
-    stream captures is refused (CA_E_STATE)."""
+    stream captures is refused (CA_E_STATE), and so is every call that
+    changes the tree, which then stays as it was."""
     _say(f"graph capture, fused={fused}")
     torch = _torch()
     from decode_attention_prefix_tree_amd import CaError, _capi
@@ -1100,6 +1101,25 @@ def test_captured_step_replays_equal_eager_steps(fused):
     assert ei.value.name == "state"
     torch.cuda.synchronize()
     ca.attend(q2, out2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out2).all()
+    # calls that change the tree refuse a capturing stream and change nothing
+    table = ca.export_table()
+    kz = torch.zeros((n + 1, H, 128), dtype=torch.float16, device="cuda:0")
+    attempts = [lambda: ca.decode_step(np.zeros(n + 1, np.int32), kz, kz, q2, out2),
+                lambda: ca.append_batch(list(range(n + 1)), np.zeros(n + 1, np.int32), kz, kz),
+                lambda: ca.append(0, [5], kz[:1], kz[:1]),
+                lambda: ca.insert(n + 7, [1, 2, 3], kz[:3], kz[:3])]
+    for call in attempts:
+        g3 = torch.cuda.CUDAGraph()
+        with pytest.raises(CaError) as ei:
+            with torch.cuda.graph(g3):
+                call()
+        assert ei.value.name == "state"
+        torch.cuda.synchronize()
+        after = ca.export_table()
+        assert all(np.array_equal(x, y) for x, y in zip(table, after))
+    ca.decode_step(np.zeros(n + 1, np.int32), kz, kz, q2, out2)
     torch.cuda.synchronize()
     assert torch.isfinite(out2).all()
 
