@@ -864,8 +864,12 @@ int ca_attach_workspace(ca_ctx* ctx, void* dev, size_t bytes) {
   CA_GUARD(ctx, {
     if (dev != nullptr && (reinterpret_cast<uintptr_t>(dev) % kAlign) != 0)
       throw Error(CA_E_INVALID_ARG, "workspace must be 256-byte aligned");
-    // appends must not patch fill counts into a workspace the caller took back
-    if (ctx->uploaded_ws == ctx->ws && ctx->scratch_dev < 0 && dev != ctx->ws) ctx->uploaded_ws = nullptr;
+    // appends must not patch fill counts into a workspace the caller took
+    // back, nor take a table copied ahead into it
+    if (dev != ctx->ws) {
+      if (ctx->uploaded_ws == ctx->ws && ctx->scratch_dev < 0) ctx->uploaded_ws = nullptr;
+      ctx->pre.uploaded_ws = nullptr;
+    }
     ctx->ws = dev;
     ctx->ws_bytes = dev ? bytes : 0;
     return CA_OK;

@@ -1195,3 +1195,54 @@ def test_tables_built_and_uploaded_ahead(chunk, rows_on):
         rr = {ri for ri, r in enumerate(rows)
               if rows_on and r[5] - r[4] == 1 and r[2] >= inserted[order[r[4]]]}
         _check_pool(ca, H, chunk, lambda s_: live[s_][1:], rr)
+
+
+def test_workspace_swapped_after_a_table_was_copied_ahead():
+    """A table copied ahead into the workspace is forgotten once the caller
+    attaches another workspace, also when it later attaches the first buffer
+    again (whose contents are then the caller's, here zeros): the structural
+    step uploads its own table and matches a twin without tables built ahead
+    bit for bit, and the oracle."""
+    _say("workspace swapped after a copy ahead")
+    import ctypes
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import ChunkAttention, _capi
+    rng = np.random.default_rng(901)
+    H, n = 2, 3
+    cas = [ChunkAttention(H, 32, device="cuda:0") for _ in range(2)]
+    cas[1].set_option(_capi.CA_OPT_PREBUILD_PLAN, 0)
+    kv = []
+    for i in range(n):
+        k, v = [rng.standard_normal((63, H, 128), dtype=np.float32).astype(np.float16) for _ in range(2)]
+        for ca in cas:
+            ca.insert(i, [1000 * i + j for j in range(63)], torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+        kv.append([k, v])
+
+    def step():
+        k, v, q = [rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16) for _ in range(3)]
+        t = np.arange(n, dtype=np.int32) + 7
+        outs = [ca.decode_step(t, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                               torch.from_numpy(q).cuda()).cpu().numpy() for ca in cas]
+        for i in range(n):
+            kv[i] = [np.concatenate([kv[i][0], k[i:i + 1]]), np.concatenate([kv[i][1], v[i:i + 1]])]
+        assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16))
+        assert_parity(outs[0], A.decode_step(q, kv), "swapped workspace")
+
+    for ca in cas:
+        ca.ensure_workspace()
+    up0 = cas[0].stats()["table_uploads"]
+    step()  # every last chunk is full now: the next step's table was copied ahead
+    torch.cuda.synchronize()
+    st = cas[0].stats()
+    assert st["prebuilt_plans"] == 0 and st["table_uploads"] == up0 + 2  # this step's table, the one ahead
+    ca = cas[0]
+    first = ca.ws
+    other = torch.empty_like(first)
+    assert ca.lib.ca_attach_workspace(ca.ctx, ctypes.c_void_p(other.data_ptr()), other.numel()) == 0
+    first.zero_()
+    assert ca.lib.ca_attach_workspace(ca.ctx, ctypes.c_void_p(first.data_ptr()), first.numel()) == 0
+    uploads = ca.stats()["table_uploads"]
+    step()  # structural: every sequence opens a chunk
+    torch.cuda.synchronize()
+    assert ca.stats()["prebuilt_plans"] == 1 and ca.stats()["table_uploads"] == uploads + 1
+    step()
