@@ -213,8 +213,9 @@ void ca_destroy(ca_ctx* ctx);
  * slots are used in pairs: an odd last slot is left out of the capacity.
  * dev may be NULL: the context then manages the tree and tables on the host
  * only and every call that needs the device returns CA_E_NO_POOL.  A device
- * pool needs chunk_size 32, 64 or 128 (CA_E_UNSUPPORTED otherwise).  Allowed only while no sequence is
- * live (CA_E_STATE otherwise).  The caller keeps the memory alive and owns it. */
+ * pool needs chunk_size 32, 64 or 128 (CA_E_UNSUPPORTED otherwise).  Allowed
+ * only while no sequence is live (CA_E_STATE otherwise).  The caller keeps
+ * the memory alive and owns it. */
 int ca_attach_pool(ca_ctx* ctx, void* dev, int64_t capacity_slots);
 
 /* Device workspace needed by ca_attend for the current tree: the chunk table
@@ -222,7 +223,11 @@ int ca_attach_pool(ca_ctx* ctx, void* dev, int64_t capacity_slots);
 int ca_workspace_bytes(ca_ctx* ctx, size_t* out);
 
 /* Lend a device workspace (256-byte aligned).  The caller owns it; it must
- * stay alive while enqueued steps use it. */
+ * stay alive while enqueued steps use it, and the library keeps the chunk
+ * table there from one call to the next: the caller does not write into it
+ * while it is attached.  Attaching another buffer (or NULL) makes the next
+ * step upload the table again, also if the first buffer is attached again
+ * later. */
 int ca_attach_workspace(ca_ctx* ctx, void* dev, size_t bytes);
 
 /* Pinned host staging for chunk-table uploads (the plan is cached and copied
