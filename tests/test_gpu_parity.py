@@ -708,6 +708,35 @@ def _check_pool(ca, heads, chunk, kv_of, row_rows):
     return rows, order
 
 
+def _check_pool_either_layout(ca, heads, chunk, kv_of):
+    """Every key of every table row against the caller's K/V, reading each
+    chunk in the layout (row-major or tiles) in which all its keys match:
+    after removals the layout of a chunk is not known from the table alone,
+    and a chunk whose keys match in neither fails."""
+    torch = _torch()
+    rows, order = ca.export_table()
+    flat = ca.pool.view(torch.float16).cpu().numpy()
+    tile_halves = heads * 2 * 64 * 128
+    pool = flat[:flat.size // tile_halves * tile_halves].reshape(-1, heads, 2, 64 * 128)
+    keys = np.arange(64)[:, None]
+    dims = np.arange(128)[None, :]
+    layouts = [(_k_off(keys, dims), _v_off(keys, dims)), (_k_row_off(keys, dims), _v_row_off(keys, dims))]
+    for r in rows:
+        start, n, sb, slot = int(r[2]), int(r[3]), int(r[4]), int(r[6])
+        k, v = kv_of(order[sb])
+        ok = False
+        for koff, voff in layouts:
+            good = True
+            for j in range(n):
+                t, kk = divmod(slot * chunk + j, 64)
+                if not (np.array_equal(pool[t][:, 0][:, koff[kk]], k[start + j]) and
+                        np.array_equal(pool[t][:, 1][:, voff[kk]], v[start + j])):
+                    good = False
+                    break
+            ok = ok or good
+        assert ok, r
+
+
 @pytest.mark.parametrize("chunk", [32, 64, 128])
 def test_pool_rows_of_appended_chunks_and_their_conversion(chunk):
     """Chunks made by appends hold their keys row-major (ca_stats counts
@@ -815,7 +844,9 @@ def test_decode_with_inserts_into_decoded_chunks(chunk, rows_on):
     for step in range(150):
         ids = sorted(live)
         k, v, q = rnd(len(ids)), rnd(len(ids)), rnd(len(ids))
-        t = [int(x) for x in rng.integers(0, 30, size=len(ids))]
+        # distinct token ids per (step, sequence), so an insert that copies a
+        # prefix follows its source's path and carries the same K/V
+        t = [100_000 + 64 * step + j for j in range(len(ids))]
         out = ca.decode_step(np.array(t, np.int32), torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
                              torch.from_numpy(q).cuda())
         for j, s_ in enumerate(ids):
@@ -1195,6 +1226,93 @@ def test_tables_built_and_uploaded_ahead(chunk, rows_on):
         rr = {ri for ri, r in enumerate(rows)
               if rows_on and r[5] - r[4] == 1 and r[2] >= inserted[order[r[4]]]}
         _check_pool(ca, H, chunk, lambda s_: live[s_][1:], rr)
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 128])
+def test_decode_loop_with_churn_matches_a_twin_without_tables_ahead(chunk):
+    """A randomized serving loop on two contexts, one building (and copying)
+    tables ahead and one not: decode steps, append_batch + attend steps,
+    attention alone, inserts that share a decoding sequence's prefix cut
+    anywhere, and removals, in random order over 260 steps.  Both contexts
+    must give the same output bit for bit at every step and the same chunk
+    table; the oracle checks every 20th step, and every stored key is
+    compared with the caller's K/V at the end."""
+    _say(f"serving loop with churn, chunk {chunk}")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import ChunkAttention, _capi
+    rng = np.random.default_rng(1200 + chunk)
+    H = 2
+    cas = [ChunkAttention(H, 500, device="cuda:0", chunk_size=chunk) for _ in range(2)]
+    cas[1].set_option(_capi.CA_OPT_PREBUILD_PLAN, 0)
+    live = {}
+    nid = [0]
+
+    def rnd(n):
+        return rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+
+    def insert(t, k, v):
+        sid = nid[0]
+        nid[0] += 1
+        kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+        for ca in cas:
+            ca.insert(sid, t, kd, vd)
+        live[sid] = (list(t), k, v)
+
+    def same(outs, label):
+        assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16)), label
+
+    pre = [int(x) for x in rng.integers(0, 30, size=2 * chunk + 5)]
+    kp, vp = rnd(len(pre)), rnd(len(pre))
+    for i in range(5):
+        n = int(rng.integers(1, 2 * chunk))
+        insert(pre + [900 + i] * n, np.concatenate([kp, rnd(n)]), np.concatenate([vp, rnd(n)]))
+    prebuilt_seen = 0
+    for step in range(260):
+        ids = sorted(live)
+        q = rnd(len(ids))
+        qd = torch.from_numpy(q).cuda()
+        op = rng.random()
+        if op < 0.85:
+            k, v = rnd(len(ids)), rnd(len(ids))
+            # a token id per (step, sequence): an insert that copies a prefix
+            # then matches exactly its source's path (two sequences whose
+            # tokens agree but whose K/V do not would share the first one's
+            # K/V, which the oracle of the second would not see)
+            t = [100_000 + 64 * step + j for j in range(len(ids))]
+            kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+            if op < 0.7:
+                outs = [ca.decode_step(np.array(t, np.int32), kd, vd, qd).cpu().numpy() for ca in cas]
+            else:
+                outs = []
+                for ca in cas:
+                    ca.append_batch(ids, np.array(t, np.int32), kd, vd)
+                    outs.append(ca.attend(qd).cpu().numpy())
+            for j, s_ in enumerate(ids):
+                tt, kk, vv = live[s_]
+                live[s_] = (tt + [t[j]], np.concatenate([kk, k[j:j + 1]]), np.concatenate([vv, v[j:j + 1]]))
+        else:
+            outs = [ca.attend(qd).cpu().numpy() for ca in cas]
+        same(outs, step)
+        if step % 20 == 0:
+            assert_parity(outs[0], A.decode_step(q, [live[s_][1:] for s_ in ids]), f"churn {step}")
+        prebuilt_seen = cas[0].stats()["prebuilt_plans"]
+        r = rng.random()
+        if r < 0.05:
+            src = live[ids[int(rng.integers(0, len(ids)))]]
+            cut = int(rng.integers(1, len(src[0]) + 1))
+            extra = int(rng.integers(0, 4))
+            insert(src[0][:cut] + [5000 + step] * extra, np.concatenate([src[1][:cut], rnd(extra)]),
+                   np.concatenate([src[2][:cut], rnd(extra)]))
+        elif r < 0.08 and len(live) > 2:
+            victim = ids[int(rng.integers(0, len(ids)))]
+            for ca in cas:
+                ca.remove(victim)
+            del live[victim]
+    assert prebuilt_seen >= 3 and cas[1].stats()["prebuilt_plans"] == 0
+    tables = [ca.export_table() for ca in cas]
+    assert np.array_equal(tables[0][0], tables[1][0]) and tables[0][1] == tables[1][1]
+    for ca in cas:
+        _check_pool_either_layout(ca, H, chunk, lambda s_: live[s_][1:])
 
 
 def test_workspace_swapped_after_a_table_was_copied_ahead():
