@@ -24,6 +24,7 @@ CA_OPT_MERGE_POLL_LIMIT = 4
 CA_OPT_FAIL_DEVICE_OPS = 5
 CA_OPT_PREBUILD_PLAN = 6
 CA_OPT_ROW_APPENDS = 7
+CA_OPT_FAIL_AFTER_DEVICE_OPS = 8
 CA_NOALLOC_SCRATCH_BYTES = 16 << 20
 CA_PHASE_CHUNK_FIRST = 1
 CA_PHASE_SEQUENCE_FIRST = 2

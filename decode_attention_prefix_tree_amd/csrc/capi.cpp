@@ -61,6 +61,7 @@ struct ca_ctx {
   int merge_poll_limit = 0;         // CA_OPT_MERGE_POLL_LIMIT (0: the kernels' own bound)
   unsigned decode_epoch = 0;        // ca_decode_step launches that grew chunks in the kernel
   int fail_ops = 0;                 // CA_OPT_FAIL_DEVICE_OPS: device operations left to fail
+  int fail_after = 0;               // CA_OPT_FAIL_AFTER_DEVICE_OPS: ones that succeed first
   bool prebuild_on = true;          // CA_OPT_PREBUILD_PLAN
   Prebuild pre;
   int64_t prebuilt_plans = 0;       // structural appends that found their plan built ahead
@@ -165,10 +166,15 @@ bool device_table_current(const ca_ctx* c) { return table_current_in(c, c->uploa
 // (which also clears the arrival counters and the fill tags).
 void mark_table_stale(ca_ctx* c) { c->uploaded_version = 0; }
 
-// Test knob (CA_OPT_FAIL_DEVICE_OPS): the next device operation fails as a
-// HIP error would, before anything is enqueued.
+// Test knobs (CA_OPT_FAIL_DEVICE_OPS, CA_OPT_FAIL_AFTER_DEVICE_OPS): once
+// fail_after more device operations have gone out, the next fail_ops fail as
+// a HIP error would, before anything is enqueued.
 void device_op(ca_ctx* c, const char* what) {
   if (c->fail_ops > 0) {
+    if (c->fail_after > 0) {
+      c->fail_after -= 1;
+      return;
+    }
     c->fail_ops -= 1;
     throw Error(CA_E_HIP, std::string(what) + ": injected failure");
   }
@@ -597,6 +603,16 @@ bool take_prebuild(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, std::vect
   return false;
 }
 
+bool same_ops(const std::vector<chunkattn::KvOp>& a, const std::vector<chunkattn::KvOp>& b) {
+  if (a.size() != b.size()) return false;
+  for (size_t i = 0; i < a.size(); ++i)
+    if (a[i].dst_slot != b[i].dst_slot || a[i].dst_key0 != b[i].dst_key0 || a[i].n_rows != b[i].n_rows ||
+        a[i].src_row0 != b[i].src_row0 || a[i].src_slot != b[i].src_slot || a[i].from_pool != b[i].from_pool ||
+        a[i].mode != b[i].mode)
+      return false;
+  return true;
+}
+
 // Whether the step's own blocks can store these appends: one token per op
 // from the caller's rows, into a row-major chunk or into a tile part that
 // already holds keys (a tile part's first write also clears its other keys,
@@ -649,10 +665,12 @@ void tile_pieces(const chunkattn::KvOp& o, int C, std::vector<chunkattn::KvOpDev
   }
 }
 
-// Launch the copies, kOpsPerLaunch tile pieces at a time; the patches of an
-// op (if any) ride with the launch that writes its last piece.
+// Launch the copies, at most kOpsPerLaunch tile pieces at a time and never
+// one op's pieces (at most two: an op writes one chunk) over two launches; an
+// op's patches (if any) ride with its launch.  ops_done (if given) counts the
+// ops whose launch has gone out, also when a later launch fails.
 void launch_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* k, const void* v, void* stream,
-                   const std::vector<FillPatch>& patches);
+                   const std::vector<FillPatch>& patches, size_t* ops_done = nullptr);
 
 void run_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* k, const void* v, void* stream,
                 const std::vector<FillPatch>& patches = {}) {
@@ -672,23 +690,29 @@ void run_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* 
 // The launches of a list of copies (no conversion after another copy of the
 // same list: conversions come in lists of their own).
 void launch_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const void* k, const void* v, void* stream,
-                   const std::vector<FillPatch>& patches) {
-  std::vector<chunkattn::KvOpDev> pieces;
-  std::vector<int32_t> patch_of;  // per piece: index into patches, or -1
-  for (size_t i = 0; i < ops.size(); ++i) {
-    tile_pieces(ops[i], c->chunk, &pieces);
-    patch_of.resize(pieces.size(), -1);
-    if (!patches.empty() && !pieces.empty()) patch_of.back() = static_cast<int32_t>(i);
-  }
+                   const std::vector<FillPatch>& patches, size_t* ops_done) {
   chunkattn::KvOpBatch batch{};
   chunkattn::TablePatches tp{};
   int n = 0;
+  size_t in_batch = 0;  // ops before this index are in a launch or in the batch
+  if (ops_done) *ops_done = 0;
   // fill patches go to the device table that holds the current tree
   int32_t* table = static_cast<int32_t*>(c->uploaded_ws);
-  for (size_t i = 0; i < pieces.size(); ++i) {
-    batch.ops[n++] = pieces[i];
-    if (patch_of[i] >= 0) {
-      const FillPatch& f = patches[patch_of[i]];
+  auto flush = [&] {
+    if (n == 0) return;
+    launch(c, "kv_write", [&] { return chunkattn::launch_kv_write(c->pool, c->heads, batch, n, k, v, table, tp, stream); });
+    if (ops_done) *ops_done = in_batch;
+    n = 0;
+    tp.n = 0;
+  };
+  std::vector<chunkattn::KvOpDev> pieces;
+  for (size_t i = 0; i < ops.size(); ++i) {
+    pieces.clear();
+    tile_pieces(ops[i], c->chunk, &pieces);
+    if (n + static_cast<int>(pieces.size()) > chunkattn::kOpsPerLaunch) flush();
+    for (const chunkattn::KvOpDev& pc : pieces) batch.ops[n++] = pc;
+    if (!patches.empty() && !pieces.empty()) {
+      const FillPatch& f = patches[i];
       tp.off[tp.n] = f.ref_off;
       tp.val[tp.n++] = f.val;
       if (f.task_off >= 0) {
@@ -696,12 +720,9 @@ void launch_kv_ops(ca_ctx* c, const std::vector<chunkattn::KvOp>& ops, const voi
         tp.val[tp.n++] = f.val;
       }
     }
-    if (n == chunkattn::kOpsPerLaunch || i + 1 == pieces.size()) {
-      launch(c, "kv_write", [&] { return chunkattn::launch_kv_write(c->pool, c->heads, batch, n, k, v, table, tp, stream); });
-      n = 0;
-      tp.n = 0;
-    }
+    in_batch = i + 1;
   }
+  flush();
 }
 
 // The K/V writes of appends that have already changed the tree.  If they
@@ -943,6 +964,10 @@ int ca_set_option(ca_ctx* ctx, int option, int value) {
       if (value < 0) throw Error(CA_E_INVALID_ARG, "failure count must be >= 0");
       ctx->fail_ops = value;
       return CA_OK;  // the plan is unaffected
+    } else if (option == CA_OPT_FAIL_AFTER_DEVICE_OPS) {
+      if (value < 0) throw Error(CA_E_INVALID_ARG, "operation count must be >= 0");
+      ctx->fail_after = value;
+      return CA_OK;
     } else {
       throw Error(CA_E_UNSUPPORTED, "unknown option");
     }
@@ -961,20 +986,38 @@ int ca_insert(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n, con
     if (device && (k_dev == nullptr || v_dev == nullptr))
       throw Error(CA_E_INVALID_ARG, "k_dev and v_dev are required when a device pool is attached");
     refuse_capture(ctx, stream, "ca_insert");
-    std::vector<chunkattn::KvOp> ops;
-    // A failed copy puts the tree back as it was: the copies only write the
-    // slots this insert took (new chunks, a split's tail), which are free again.
-    chunkattn::Manager before = device ? ctx->mgr : chunkattn::Manager(ctx->chunk, true);
-    int32_t matched = ctx->mgr.insert(seq_id, tokens, n, &ops);
-    touch(ctx);
-    if (device) {
+    int32_t matched = 0;
+    if (!device) {
+      matched = ctx->mgr.insert(seq_id, tokens, n, nullptr);
+    } else {
+      // The copies go out before the tree changes, so a copy that cannot be
+      // enqueued leaves the tree as it was.  Conversions of row-major chunks
+      // to tiles (chunks this insert shares or splits) come first, in
+      // launches of their own; if some went out and a later launch fails,
+      // the tree records those chunks' new layout (same tokens, same K/V)
+      // and nothing else.
+      std::vector<chunkattn::KvOp> ops, converts, rest, done;
+      matched = ctx->mgr.insert_ops(seq_id, tokens, n, &ops);
+      for (const chunkattn::KvOp& o : ops) (o.mode == chunkattn::kOpConvert ? converts : rest).push_back(o);
+      size_t converted = 0;
       try {
-        run_kv_ops(ctx, ops, k_dev, v_dev, stream);
+        if (!converts.empty()) launch_kv_ops(ctx, converts, k_dev, v_dev, stream, {}, &converted);
+        if (!rest.empty()) launch_kv_ops(ctx, rest, k_dev, v_dev, stream, {});
       } catch (const Error&) {
-        ctx->mgr = std::move(before);
+        if (converted > 0) {
+          ctx->mgr.mark_tiles(std::vector<chunkattn::KvOp>(converts.begin(), converts.begin() + converted));
+          touch(ctx);
+        }
         throw;
       }
+      ctx->mgr.insert(seq_id, tokens, n, &done);
+      if (!same_ops(done, ops)) {
+        ctx->broken = true;
+        touch(ctx);
+        throw Error(CA_E_INTERNAL, "insert: the tree took other slots than its copies wrote");
+      }
     }
+    touch(ctx);
     if (n_matched) *n_matched = matched;
     return CA_OK;
   });

@@ -73,13 +73,12 @@ void Manager::free_node(int32_t idx) {
   --n_nodes_;
 }
 
-int32_t Manager::insert(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops) {
+void Manager::walk_insert(int64_t seq, const int32_t* tokens, int32_t n, InsertWalk* w) const {
   if (n < 1 || tokens == nullptr) throw Error(kInvalidArg, "insert needs at least one token");
   if (end_.count(seq)) throw Error(kDupSeq, "sequence id already live");
-
   // Walk from the root without touching anything.
   int32_t cur = 0, pos = 0, split_node = -1, split_at = 0;
-  std::vector<int32_t> path;  // matched chunks (the split one included)
+  w->path.clear();  // matched chunks (the split one included)
   while (share_ && pos < n) {
     int32_t next = -1;
     for (int32_t c : nodes_[cur].children) {
@@ -90,7 +89,7 @@ int32_t Manager::insert(int64_t seq, const int32_t* tokens, int32_t n, std::vect
     int32_t lim = std::min<int32_t>(static_cast<int32_t>(t.size()), n - pos), k = 0;
     while (k < lim && t[k] == tokens[pos + k]) ++k;
     pos += k;
-    path.push_back(next);
+    w->path.push_back(next);
     if (k < static_cast<int32_t>(t.size())) { split_node = next; split_at = k; break; }
     cur = next;
   }
@@ -98,6 +97,46 @@ int32_t Manager::insert(int64_t seq, const int32_t* tokens, int32_t n, std::vect
   if (need > free_slots())
     throw Error(kNoCapacity, "need " + std::to_string(need) + " chunk slots, " +
                                  std::to_string(free_slots()) + " free");
+  w->cur = cur;
+  w->pos = pos;
+  w->split_node = split_node;
+  w->split_at = split_at;
+}
+
+int32_t Manager::insert_ops(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops) const {
+  InsertWalk w;
+  walk_insert(seq, tokens, n, &w);
+  for (int32_t x : w.path)
+    if (nodes_[x].row)
+      ops->push_back(KvOp{nodes_[x].slot, 0, static_cast<int32_t>(nodes_[x].tokens.size()), 0, -1, 0, x, kOpConvert});
+  // the new chunks take the lowest free slots, the split's tail first
+  FreeSlots::Walk slots(free_);
+  int32_t pos = w.pos;
+  if (w.split_node >= 0) {
+    const Node& head = nodes_[w.split_node];
+    ops->push_back(KvOp{slots.next(), 0, static_cast<int32_t>(head.tokens.size()) - w.split_at, w.split_at,
+                        head.slot, 1});
+  }
+  while (pos < n) {
+    const int32_t take = std::min<int32_t>(C_, n - pos);
+    ops->push_back(KvOp{slots.next(), 0, take, pos, -1, 0});
+    pos += take;
+  }
+  return w.pos;
+}
+
+void Manager::mark_tiles(const std::vector<KvOp>& converts) {
+  for (const KvOp& o : converts)
+    if (o.mode == kOpConvert && o.node >= 0) nodes_[o.node].row = false;
+  structural_ = true;
+}
+
+int32_t Manager::insert(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops) {
+  InsertWalk w;
+  walk_insert(seq, tokens, n, &w);
+  const std::vector<int32_t>& path = w.path;
+  int32_t cur = w.cur, pos = w.pos;
+  const int32_t split_node = w.split_node, split_at = w.split_at;
   const int32_t matched = pos;
 
   // Matched chunks become shared (or are split): the chunk-first path and

@@ -181,6 +181,13 @@ class Manager {
 
   // Mutations return the device copies they need (possibly none).
   int32_t insert(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops);
+  // The copies insert(seq, tokens, n) would return, in the same order and to
+  // the same slots, without changing anything (same errors as insert): the
+  // caller can enqueue them first and change the tree only once they are.
+  int32_t insert_ops(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops) const;
+  // After conversions to tiles (kOpConvert ops) went to the device but the
+  // insert that needed them did not happen: the tree records the new layout.
+  void mark_tiles(const std::vector<KvOp>& converts);
   // src_base: row of the caller's K/V that holds the first appended token.
   void append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops, int32_t src_base = 0);
   // One token for each of n sequences (token j, K/V row j).  All checks run
@@ -237,6 +244,13 @@ class Manager {
     std::vector<int64_t> ended;     // sequences ending here, arrival order
   };
 
+  // An insert's walk from the root: the matched chunks, where the match
+  // ends (the node and token position), and the chunk it splits, if any.
+  struct InsertWalk {
+    std::vector<int32_t> path;
+    int32_t cur = 0, pos = 0, split_node = -1, split_at = 0;
+  };
+  void walk_insert(int64_t seq, const int32_t* tokens, int32_t n, InsertWalk* w) const;
   int32_t new_node(int32_t parent, int32_t start);
   void free_node(int32_t idx);
   int32_t alloc_slot();

@@ -29,7 +29,8 @@
  *    ca_destroy.  That is the library's only allocation.
  *  - CA_E_HIP from a call that only reads the tree (ca_attend,
  *    ca_attend_phase, ca_prepare) leaves the context usable; the next step
- *    uploads the table again.  ca_insert puts the tree back as it was.  After
+ *    uploads the table again.  ca_insert enqueues its copies before it
+ *    changes the tree, so after CA_E_HIP the tree is as it was.  After
  *    appends (ca_append, ca_append_batch, ca_decode_step) have changed the
  *    tree, a failure to enqueue their K/V writes leaves tokens in the tree
  *    that the pool does not hold: every later call that changes the tree or
@@ -135,7 +136,7 @@ enum {
                                     chunks, CA_OPT_ROW_APPENDS) and uploads nothing.
                                     0: every table is built and uploaded in the call that
                                     needs it. */
-  CA_OPT_ROW_APPENDS = 7         /* 1 (default): chunks that appends create keep their keys
+  CA_OPT_ROW_APPENDS = 7,        /* 1 (default): chunks that appends create keep their keys
                                     row-major in their slot (one K row and one V row per
                                     token and head: a decoded token is two contiguous 256-byte
                                     writes per head), and the sequence-first phase reads them
@@ -143,6 +144,9 @@ enum {
                                     splits it, first rewrites it in the tile layout.  0:
                                     chunks made from now on use the tile layout (one token's
                                     K and V then land in pieces of two dozen lines). */
+  CA_OPT_FAIL_AFTER_DEVICE_OPS = 8 /* for tests of failure handling: this many device
+                                    operations of the context succeed before the failures
+                                    of CA_OPT_FAIL_DEVICE_OPS begin (default 0). */
 };
 
 /* ca_attend_phase phases.  A step is CA_PHASE_PARTIALS (one launch holding
@@ -255,7 +259,11 @@ int ca_set_option(ca_ctx* ctx, int option, int value);
  * *n_matched (may be NULL) receives the number of leading tokens already
  * stored.  Errors: CA_E_DUP_SEQ, CA_E_INVALID_ARG (n < 1, NULL pointers),
  * CA_E_NO_CAPACITY, CA_E_HIP (the copy could not be enqueued).  A failed call
- * changes nothing (after CA_E_HIP the tree is put back as it was). */
+ * changes nothing: the copies are enqueued before the tree changes.  One
+ * exception is internal: chunks stored row-major (CA_OPT_ROW_APPENDS) that
+ * the insert shares or splits are first rewritten as tiles in a launch of
+ * their own; if that launch went out and a later one fails, they stay tiles
+ * (same tokens, same K/V, the same results). */
 int ca_insert(ca_ctx* ctx, int64_t seq_id, const int32_t* tokens, int32_t n,
               const void* k_dev, const void* v_dev, void* stream, int32_t* n_matched);
 

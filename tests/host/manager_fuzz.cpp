@@ -6,7 +6,8 @@
 // append over all live sequences, the plan predicted for the tree after it
 // must equal the plan built once it is made (with or without the new chunks'
 // memory reserved ahead), and the prediction must fail exactly when the
-// append does.
+// append does.  Before every insert, the copies announced for it
+// (insert_ops) must be the ones it returns, and fail exactly when it does.
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -18,6 +19,16 @@ using namespace chunkattn;
 template <typename T>
 static bool same(const std::vector<T>& a, const std::vector<T>& b) {
   return a.size() == b.size() && (a.empty() || std::memcmp(a.data(), b.data(), a.size() * sizeof(T)) == 0);
+}
+
+static bool same_ops(const std::vector<KvOp>& a, const std::vector<KvOp>& b) {
+  if (a.size() != b.size()) return false;
+  for (size_t i = 0; i < a.size(); ++i)
+    if (a[i].dst_slot != b[i].dst_slot || a[i].dst_key0 != b[i].dst_key0 || a[i].n_rows != b[i].n_rows ||
+        a[i].src_row0 != b[i].src_row0 || a[i].src_slot != b[i].src_slot || a[i].from_pool != b[i].from_pool ||
+        a[i].mode != b[i].mode || a[i].node != b[i].node)
+      return false;
+  return true;
 }
 
 static bool same_plan(const Plan& a, const Plan& b) {
@@ -50,7 +61,27 @@ int main(int argc, char** argv) {
           int64_t id = rng() % 60;
           std::vector<int32_t> toks(1 + rng() % (C < 8 ? 20 : 400));
           for (auto& x : toks) x = rng() % 3;
-          m.insert(id, toks.data(), (int32_t)toks.size(), &ops);
+          // the copies announced ahead are the ones the insert returns, and
+          // announcing fails exactly when the insert does
+          std::vector<KvOp> ahead;
+          bool ahead_ok = true;
+          try {
+            m.insert_ops(id, toks.data(), (int32_t)toks.size(), &ahead);
+          } catch (const Error& e) {
+            if (e.code == -11) throw;
+            ahead_ok = false;
+          }
+          bool done = false;
+          try {
+            m.insert(id, toks.data(), (int32_t)toks.size(), &ops);
+            done = true;
+          } catch (const Error& e) {
+            if (ahead_ok || e.code == -11) throw;
+          }
+          if (done != ahead_ok || (done && !same_ops(ahead, ops))) {
+            printf("FAIL: copies announced ahead differ from the insert's (trial %d step %d, C %d)\n", t, s, C);
+            return 1;
+          }
           live.push_back(id);
         } else if (r < 60) {
           int64_t id = live[rng() % live.size()];

@@ -566,6 +566,8 @@ def test_failure_injection_option():
     ca = ChunkAttention(2, 16, device=None)
     assert lib.ca_set_option(ca.ctx, _capi.CA_OPT_FAIL_DEVICE_OPS, -1) == -1
     assert lib.ca_set_option(ca.ctx, _capi.CA_OPT_FAIL_DEVICE_OPS, 3) == 0
+    assert lib.ca_set_option(ca.ctx, _capi.CA_OPT_FAIL_AFTER_DEVICE_OPS, -1) == -1
+    assert lib.ca_set_option(ca.ctx, _capi.CA_OPT_FAIL_AFTER_DEVICE_OPS, 2) == 0
     # a host-only context runs no device operation: inserts are unaffected
     ca.insert(1, list(range(70)))
     assert ca.sequences() == [1]

@@ -102,6 +102,66 @@ def test_failed_insert_changes_nothing():
     _parity(_step(ca, q), A.decode_step(q, kv), "after the insert")
 
 
+@pytest.mark.parametrize("succeed_first", [0, 1])
+def test_failed_insert_into_decoded_chunks(succeed_first):
+    """An insert that shares a decoded sequence's row-major chunks (so they
+    are first rewritten as tiles, in a launch of their own), splits one and
+    adds new chunks fails at a copy.  When the conversion launch itself fails
+    (succeed_first 0) nothing changes; when it went out and the copies failed
+    (succeed_first 1), the table and sequences are still those from before and
+    only the converted chunks' layout changed.  Either way the steps then
+    match the oracle, and the same insert then succeeds."""
+    _say(f"failed insert into decoded chunks, {succeed_first} operation(s) first")
+    import torch
+    from decode_attention_prefix_tree_amd import CaError, ChunkAttention, _capi
+    rng = np.random.default_rng(310 + succeed_first)
+    H = 2
+    ca = ChunkAttention(H, 64, device="cuda:0")
+
+    def rnd(n):
+        return rng.standard_normal((n, H, 128), dtype=np.float32).astype(np.float16)
+
+    toks = [int(x) for x in range(40)]
+    kv = [rnd(40), rnd(40)]
+    ca.insert(0, toks, torch.from_numpy(kv[0]).cuda(), torch.from_numpy(kv[1]).cuda())
+    for step in range(100):  # 100 decoded tokens: one full appended chunk and part of another
+        k, v = rnd(1), rnd(1)
+        q = rnd(1)
+        ca.decode_step(np.array([1000 + step], np.int32), torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                       torch.from_numpy(q).cuda())
+        toks.append(1000 + step)
+        kv = [np.concatenate([kv[0], k]), np.concatenate([kv[1], v])]
+    torch.cuda.synchronize()
+    rows0, order0 = ca.export_table()
+    st0 = ca.stats()
+    assert st0["row_chunks"] >= 2
+    cut = 40 + 64 + 20  # inside the second appended chunk
+    new_k, new_v = rnd(80), rnd(80)
+    t9 = toks[:cut] + list(range(7000, 7080))
+    k9 = np.concatenate([kv[0][:cut], new_k])
+    v9 = np.concatenate([kv[1][:cut], new_v])
+    k9t, v9t = torch.from_numpy(k9).cuda(), torch.from_numpy(v9).cuda()
+    ca.set_option(_capi.CA_OPT_FAIL_AFTER_DEVICE_OPS, succeed_first)
+    ca.set_option(_capi.CA_OPT_FAIL_DEVICE_OPS, 1)
+    with pytest.raises(CaError) as ei:
+        ca.insert(9, t9, k9t, v9t)
+    assert ei.value.name == "hip"
+    rows1, order1 = ca.export_table()
+    assert np.array_equal(rows0, rows1) and order0 == order1
+    st1 = ca.stats()
+    for key in ("live_sequences", "chunks", "free_slots", "unique_tokens"):
+        assert st1[key] == st0[key], key
+    if succeed_first:
+        assert st1["row_chunks"] < st0["row_chunks"]
+    else:
+        assert st1["row_chunks"] == st0["row_chunks"]
+    q = rnd(1)
+    _parity(_step(ca, q), A.decode_step(q, [kv]), "after the failed insert")
+    assert ca.insert(9, t9, k9t, v9t) == cut
+    q = rnd(2)
+    _parity(_step(ca, q), A.decode_step(q, [kv, [k9, v9]]), "after the insert")
+
+
 def test_decode_step_whose_launch_fails_stores_the_tokens():
     """ca_decode_step with in-kernel appends whose launch fails: the tokens go
     to the pool by a write launch, the call returns CA_E_HIP, and the next
