@@ -97,7 +97,8 @@ _SIGS = {
     "ca_remove": (_c.c_int, [_c.c_void_p, _c.c_int64]),
     "ca_attend": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "ca_attend_noalloc": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
-    "ca_decode_step": (_c.c_int, [_c.c_void_p, _c.POINTER(_c.c_int32), _c.c_void_p, _c.c_void_p, _c.c_void_p,
+    # tokens as an address: the binding passes the array's data pointer
+    "ca_decode_step": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                   _c.c_void_p, _c.c_void_p]),
     "ca_prepare": (_c.c_int, [_c.c_void_p, _c.c_void_p]),
     "ca_attend_phase": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p]),

@@ -24,8 +24,9 @@ def slot_bytes(heads: int, head_dim: int = HEAD_DIM, chunk: int = CHUNK) -> int:
 
 
 def _tokens(tokens) -> np.ndarray:
-    t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
-    return t
+    if type(tokens) is np.ndarray and tokens.dtype == np.int32 and tokens.ndim == 1 and tokens.flags.c_contiguous:
+        return tokens
+    return np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
 
 
 def _ptr_i32(a: np.ndarray):
@@ -64,6 +65,12 @@ class ChunkAttention:
             import torch
             nbytes = capacity_slots * slot_bytes(heads, head_dim, chunk_size)
             self.pool = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            # what the per-step argument checks use, looked up once
+            self._torch, self._f16 = torch, torch.float16
+            raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+            index = self.pool.device.index
+            self._current_stream = (lambda: raw(index)) if raw is not None else (
+                lambda: torch.cuda.current_stream(index).cuda_stream)
             check(self.ctx, self.lib.ca_attach_pool(self.ctx, ctypes.c_void_p(self.pool.data_ptr()),
                                                    capacity_slots))
             self._lend_staging(3 << 16)
@@ -82,24 +89,29 @@ class ChunkAttention:
 
     # -- helpers --------------------------------------------------------------
     def _stream(self, stream=None):
+        """The hipStream_t of `stream`, else of the pool device's current stream."""
         if self.device is None:
             return None
-        import torch
-        s = stream if stream is not None else torch.cuda.current_stream(self.pool.device)
-        return ctypes.c_void_p(s.cuda_stream)
+        return stream.cuda_stream if stream is not None else self._current_stream()
+
+    def _f16_ptr(self, name: str, x, shape):
+        """Device address of a contiguous fp16 CUDA tensor of the given shape."""
+        try:
+            if x.dtype is self._f16 and x.is_cuda and x.shape == shape and x.is_contiguous():
+                return x.data_ptr()
+        except AttributeError:
+            pass
+        if not isinstance(x, self._torch.Tensor) or x.dtype != self._f16 or not x.is_cuda:
+            raise TypeError(f"{name} must be a float16 CUDA tensor")
+        raise ValueError(f"{name} must be contiguous {list(shape)}")
 
     def _kv(self, k, v, n: int):
         if self.device is None:
             if k is not None or v is not None:
                 raise ValueError("a host-only context takes no K/V")
             return None, None
-        import torch
-        for name, x in (("k", k), ("v", v)):
-            if not isinstance(x, torch.Tensor) or x.dtype != torch.float16 or not x.is_cuda:
-                raise TypeError(f"{name} must be a float16 CUDA tensor")
-            if tuple(x.shape) != (n, self.heads, self.head_dim) or not x.is_contiguous():
-                raise ValueError(f"{name} must be contiguous [{n}, {self.heads}, {self.head_dim}]")
-        return ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr())
+        shape = (n, self.heads, self.head_dim)
+        return self._f16_ptr("k", k, shape), self._f16_ptr("v", v, shape)
 
     # -- tree -----------------------------------------------------------------
     def insert(self, seq_id: int, tokens, k=None, v=None, stream=None) -> int:
@@ -196,24 +208,26 @@ class ChunkAttention:
             self._lend_staging(max(stage + stage // 4, 3 << 16))
 
     def _qo(self, q, out):
-        import torch
+        """q and out (made like q when None) checked; returns out and both addresses."""
         shape = (self._n_live, self.heads, self.head_dim)
-        if not isinstance(q, torch.Tensor) or q.dtype != torch.float16 or not q.is_cuda:
-            raise TypeError("q must be a float16 CUDA tensor")
-        if tuple(q.shape) != shape or not q.is_contiguous():
-            raise ValueError(f"q must be contiguous {list(shape)} (rows in ascending seq id)")
+        qp = self._f16_ptr("q (rows in ascending seq id)", q, shape)
         if out is None:
-            out = torch.empty_like(q)
-        elif tuple(out.shape) != shape or out.dtype != torch.float16 or not out.is_contiguous():
-            raise ValueError("out must match q")
-        return q, out
+            out = self._torch.empty_like(q)
+        else:
+            try:
+                ok = out.dtype is self._f16 and out.shape == shape and out.is_contiguous()
+            except AttributeError:
+                ok = False
+            if not ok:
+                raise ValueError("out must match q")
+        return out, qp, out.data_ptr()
 
     def attend(self, q, out=None, stream=None):
         """out[r] = softmax(q[r] K_r^T / sqrt(d)) V_r for the r-th live sequence."""
         if self.device is None:
             raise CaError(-9, "host-only context")
-        q, out = self._qo(q, out)
-        args = (self.ctx, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(out.data_ptr()), self._stream(stream))
+        out, qp, op = self._qo(q, out)
+        args = (self.ctx, qp, op, self._stream(stream))
         rc = self.lib.ca_attend(*args)
         if rc == -7:
             # the tree outgrew the workspace (nothing was launched): grow it
@@ -230,9 +244,8 @@ class ChunkAttention:
             raise CaError(-9, "host-only context")
         if out is None:
             raise ValueError("attend_noalloc writes into a caller-provided out")
-        q, out = self._qo(q, out)
-        check(self.ctx, self.lib.ca_attend_noalloc(self.ctx, ctypes.c_void_p(q.data_ptr()),
-                                                   ctypes.c_void_p(out.data_ptr()), self._stream(stream)))
+        out, qp, op = self._qo(q, out)
+        check(self.ctx, self.lib.ca_attend_noalloc(self.ctx, qp, op, self._stream(stream)))
         return out
 
     def decode_step(self, tokens, k, v, q, out=None, stream=None):
@@ -244,9 +257,8 @@ class ChunkAttention:
         if len(t) != self._n_live:
             raise ValueError("one token per live sequence")
         kp, vp = self._kv(k, v, len(t))
-        q, out = self._qo(q, out)
-        rc = self.lib.ca_decode_step(self.ctx, _ptr_i32(t), kp, vp, ctypes.c_void_p(q.data_ptr()),
-                                     ctypes.c_void_p(out.data_ptr()), self._stream(stream))
+        out, qp, op = self._qo(q, out)
+        rc = self.lib.ca_decode_step(self.ctx, t.ctypes.data, kp, vp, qp, op, self._stream(stream))
         if rc == -7:
             # the tokens are stored; the tree outgrew the workspace: grow it
             # and run the step's attention

@@ -1315,6 +1315,51 @@ def test_decode_loop_with_churn_matches_a_twin_without_tables_ahead(chunk):
         _check_pool_either_layout(ca, H, chunk, lambda s_: live[s_][1:])
 
 
+def test_binding_rejects_bad_tensors():
+    """The binding's argument checks (a fast path, then the detailed one for
+    the message): wrong dtype or device raise TypeError, wrong shape or a
+    non-contiguous tensor ValueError, for q, out and the decode step's K/V;
+    nothing is launched and the context stays usable."""
+    _say("binding argument checks")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import ChunkAttention
+    H, n = 2, 3
+    ca = ChunkAttention(H, 16, device="cuda:0")
+    kv = torch.zeros((10, H, 128), dtype=torch.float16, device="cuda:0")
+    for i in range(n):
+        ca.insert(i, [100 * i + j for j in range(10)], kv, kv)
+    good = torch.zeros((n, H, 128), dtype=torch.float16, device="cuda:0")
+    toks = np.arange(n, dtype=np.int32)
+    bad_type = [good.float(), good.cpu(), good.numpy(force=True) if hasattr(good, "numpy") else None]
+    bad_value = [good[:2], torch.zeros((n, H, 64), dtype=torch.float16, device="cuda:0"),
+                 torch.zeros((n, 128, H), dtype=torch.float16, device="cuda:0").transpose(1, 2)]
+    for b in bad_type:
+        if b is None:
+            continue
+        with pytest.raises(TypeError):
+            ca.attend(b)
+        with pytest.raises(TypeError):
+            ca.decode_step(toks, b, good, good)
+    for b in bad_value:
+        with pytest.raises(ValueError):
+            ca.attend(b)
+        with pytest.raises(ValueError):
+            ca.attend(good, b)
+        with pytest.raises(ValueError):
+            ca.decode_step(toks, good, b, good)
+    with pytest.raises(ValueError):
+        ca.decode_step(toks[:2], good, good, good)
+    assert ca.stats()["unique_tokens"] == 10 * n
+    out = ca.attend(good)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    # tokens given as a list, a wider integer array or a strided view are converted
+    for t in ([5, 6, 7], np.arange(3, dtype=np.int64), np.arange(6, dtype=np.int32)[::2]):
+        ca.decode_step(t, good, good, good)
+    torch.cuda.synchronize()
+    assert ca.stats()["unique_tokens"] == 13 * n
+
+
 def test_workspace_swapped_after_a_table_was_copied_ahead():
     """A table copied ahead into the workspace is forgotten once the caller
     attaches another workspace, also when it later attaches the first buffer
