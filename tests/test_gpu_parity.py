@@ -1228,21 +1228,24 @@ def test_tables_built_and_uploaded_ahead(chunk, rows_on):
         _check_pool(ca, H, chunk, lambda s_: live[s_][1:], rr)
 
 
-@pytest.mark.parametrize("chunk", [32, 64, 128])
-def test_decode_loop_with_churn_matches_a_twin_without_tables_ahead(chunk):
+@pytest.mark.parametrize("chunk,mode", [(32, "tree"), (64, "tree"), (128, "tree"), (64, "unshared"),
+                                        (64, "no_chunk_first")])
+def test_decode_loop_with_churn_matches_a_twin_without_tables_ahead(chunk, mode):
     """A randomized serving loop on two contexts, one building (and copying)
     tables ahead and one not: decode steps, append_batch + attend steps,
     attention alone, inserts that share a decoding sequence's prefix cut
     anywhere, and removals, in random order over 260 steps.  Both contexts
     must give the same output bit for bit at every step and the same chunk
     table; the oracle checks every 20th step, and every stored key is
-    compared with the caller's K/V at the end."""
-    _say(f"serving loop with churn, chunk {chunk}")
+    compared with the caller's K/V at the end.  Also with the unshared layout
+    and with the prefix tree but no chunk-first phase."""
+    _say(f"serving loop with churn, chunk {chunk}, {mode}")
     torch = _torch()
     from decode_attention_prefix_tree_amd import ChunkAttention, _capi
     rng = np.random.default_rng(1200 + chunk)
     H = 2
-    cas = [ChunkAttention(H, 500, device="cuda:0", chunk_size=chunk) for _ in range(2)]
+    cas = [ChunkAttention(H, 500 if mode != "unshared" else 900, device="cuda:0", chunk_size=chunk,
+                          share=mode != "unshared", two_phase=mode != "no_chunk_first") for _ in range(2)]
     cas[1].set_option(_capi.CA_OPT_PREBUILD_PLAN, 0)
     live = {}
     nid = [0]
