@@ -22,7 +22,7 @@ Manager::Manager(int chunk, bool share) : C_(chunk), share_(share) {
 }
 
 void Manager::set_capacity(int64_t capacity) {
-  if (!end_.empty()) throw Error(kState, "pool can only change while no sequence is live");
+  if (!live_.empty()) throw Error(kState, "pool can only change while no sequence is live");
   if (capacity < 0 || capacity > INT32_MAX) throw Error(kInvalidArg, "capacity out of range");
   capacity_ = capacity;
   free_.reset(capacity);
@@ -75,7 +75,7 @@ void Manager::free_node(int32_t idx) {
 
 void Manager::walk_insert(int64_t seq, const int32_t* tokens, int32_t n, InsertWalk* w) const {
   if (n < 1 || tokens == nullptr) throw Error(kInvalidArg, "insert needs at least one token");
-  if (end_.count(seq)) throw Error(kDupSeq, "sequence id already live");
+  if (live_.count(seq)) throw Error(kDupSeq, "sequence id already live");
   // Walk from the root without touching anything.
   int32_t cur = 0, pos = 0, split_node = -1, split_at = 0;
   w->path.clear();  // matched chunks (the split one included)
@@ -158,7 +158,7 @@ int32_t Manager::insert(int64_t seq, const int32_t* tokens, int32_t n, std::vect
     for (int32_t c : t.children) nodes_[c].parent = tail;
     head.children.push_back(tail);
     t.ended.swap(head.ended);
-    for (int64_t s : t.ended) end_[s] = tail;
+    for (int64_t s : t.ended) live_.find(s)->second.end = tail;
     t.ref = head.ref;
     if (ops)
       ops->push_back(KvOp{t.slot, 0, static_cast<int32_t>(t.tokens.size()), split_at, head.slot, 1});
@@ -175,18 +175,23 @@ int32_t Manager::insert(int64_t seq, const int32_t* tokens, int32_t n, std::vect
     pos += take;
   }
   nodes_[cur].ended.push_back(seq);
-  end_[seq] = cur;
-  len_[seq] = n;
+  live_.emplace(seq, Live{cur, n});
   for (int32_t x = cur; x != 0; x = nodes_[x].parent) nodes_[x].ref += 1;
   structural_ = true;
   return matched;
 }
 
 void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops, int32_t src_base) {
-  auto it = end_.find(seq);
-  if (it == end_.end()) throw Error(kUnknownSeq, "sequence id not live");
+  auto it = live_.find(seq);
+  if (it == live_.end()) throw Error(kUnknownSeq, "sequence id not live");
   if (n < 1 || tokens == nullptr) throw Error(kInvalidArg, "append needs at least one token");
-  int32_t e = it->second;
+  append_to(it, tokens, n, ops, src_base);
+}
+
+void Manager::append_to(std::map<int64_t, Live>::iterator it, const int32_t* tokens, int32_t n,
+                        std::vector<KvOp>* ops, int32_t src_base) {
+  const int64_t seq = it->first;
+  int32_t e = it->second.end;
   const int32_t fill = static_cast<int32_t>(nodes_[e].tokens.size());
   const int32_t room = nodes_[e].ref == 1 ? C_ - fill : 0;
   const int32_t take = std::min(room, n);
@@ -201,7 +206,7 @@ void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<
     // growing into another 64-key tile adds a tile ref to the plan
     if (tiles_of(fill + take) != tiles_of(fill)) structural_ = true;
   }
-  len_[seq] += n;
+  it->second.len += n;
   if (take == n) return;
   std::vector<int64_t>& ended = nodes_[e].ended;
   ended.erase(std::find(ended.begin(), ended.end(), seq));
@@ -221,7 +226,7 @@ void Manager::append(int64_t seq, const int32_t* tokens, int32_t n, std::vector<
     i += piece;
   }
   nodes_[cur].ended.push_back(seq);
-  end_[seq] = cur;
+  it->second.end = cur;
   structural_ = true;
 }
 
@@ -236,17 +241,19 @@ void Manager::append_batch(const int64_t* seqs, const int32_t* tokens, int32_t n
   for (int32_t j = 1; j < n; ++j)
     if (order[j].first == order[j - 1].first) first_repeat = std::min(first_repeat, order[j].second);
   int64_t need = 0;
+  std::vector<std::map<int64_t, Live>::iterator> at(static_cast<size_t>(n));
   for (int32_t j = 0; j < n; ++j) {
-    auto it = end_.find(seqs[j]);
-    if (it == end_.end()) throw Error(kUnknownSeq, "sequence id not live: " + std::to_string(seqs[j]));
+    auto it = live_.find(seqs[j]);
+    if (it == live_.end()) throw Error(kUnknownSeq, "sequence id not live: " + std::to_string(seqs[j]));
     if (j == first_repeat) throw Error(kInvalidArg, "sequence id repeated in a batch");
-    const Node& e = nodes_[it->second];
+    const Node& e = nodes_[it->second.end];
     if (!(e.ref == 1 && static_cast<int32_t>(e.tokens.size()) < C_)) ++need;
+    at[j] = it;
   }
   if (need > free_slots())
     throw Error(kNoCapacity, "need " + std::to_string(need) + " chunk slots, " +
                                  std::to_string(free_slots()) + " free");
-  for (int32_t j = 0; j < n; ++j) append(seqs[j], tokens + j, 1, ops, j);
+  for (int32_t j = 0; j < n; ++j) append_to(at[j], tokens + j, 1, ops, j);
 }
 
 int64_t Manager::row_chunks() const {
@@ -256,8 +263,8 @@ int64_t Manager::row_chunks() const {
 }
 
 bool Manager::next_append_structural() const {
-  for (const auto& kv : end_) {
-    const Node& nd = nodes_[kv.second];
+  for (const auto& kv : live_) {
+    const Node& nd = nodes_[kv.second.end];
     const int32_t fill = static_cast<int32_t>(nd.tokens.size());
     if (nd.ref != 1 || fill >= C_ || tiles_of(fill + 1) != tiles_of(fill)) return true;
   }
@@ -298,9 +305,9 @@ bool Manager::predict_append_batch(const int64_t* seqs, int32_t n, NextAppend* o
   size_t reuse = free_nodes_.size();
   FreeSlots::Walk slots(free_);
   for (int32_t j = 0; j < n; ++j) {
-    auto it = end_.find(seqs[j]);
-    if (it == end_.end()) return false;
-    const int32_t e = it->second;
+    auto it = live_.find(seqs[j]);
+    if (it == live_.end()) return false;
+    const int32_t e = it->second.end;
     const Node& nd = nodes_[e];
     const int32_t fill = static_cast<int32_t>(nd.tokens.size());
     if (nd.ref == 1 && fill < C_) {
@@ -323,12 +330,11 @@ bool Manager::predict_append_batch(const int64_t* seqs, int32_t n, NextAppend* o
 }
 
 void Manager::remove(int64_t seq) {
-  auto it = end_.find(seq);
-  if (it == end_.end()) throw Error(kUnknownSeq, "sequence id not live");
+  auto it = live_.find(seq);
+  if (it == live_.end()) throw Error(kUnknownSeq, "sequence id not live");
   structural_ = true;
-  int32_t e = it->second;
-  end_.erase(it);
-  len_.erase(seq);
+  int32_t e = it->second.end;
+  live_.erase(it);
   std::vector<int64_t>& ended = nodes_[e].ended;
   ended.erase(std::find(ended.begin(), ended.end(), seq));
   for (int32_t x = e; x != 0;) {
@@ -344,15 +350,15 @@ void Manager::remove(int64_t seq) {
 
 std::vector<int64_t> Manager::sequences() const {
   std::vector<int64_t> out;
-  out.reserve(end_.size());
-  for (const auto& kv : end_) out.push_back(kv.first);
+  out.reserve(live_.size());
+  for (const auto& kv : live_) out.push_back(kv.first);
   return out;
 }
 
 int32_t Manager::seq_len(int64_t seq) const {
-  auto it = len_.find(seq);
-  if (it == len_.end()) throw Error(kUnknownSeq, "sequence id not live");
-  return it->second;
+  auto it = live_.find(seq);
+  if (it == live_.end()) throw Error(kUnknownSeq, "sequence id not live");
+  return it->second.len;
 }
 
 void Plan::clear() {
@@ -440,11 +446,12 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
   };
 
   // Caller row of each sequence: rank in ascending id order.
-  std::map<int64_t, int32_t> qrow;
-  {
-    int32_t r = 0;
-    for (const auto& kv : end_) qrow[kv.first] = r++;
-  }
+  std::vector<int64_t> ids;
+  ids.reserve(live_.size());
+  for (const auto& kv : live_) ids.push_back(kv.first);
+  auto qrow_of = [&](int64_t s) {
+    return static_cast<int32_t>(std::lower_bound(ids.begin(), ids.end(), s) - ids.begin());
+  };
 
   // Pass 1: DFS pre-order -> canonical rows, DFS order, row of each node,
   // the row where each DFS position's sequence ends.
@@ -475,7 +482,7 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
     P.row_node.push_back(f.node);
     for (int64_t s : ended_of(f.node)) {
       P.dfs_seq.push_back(s);
-      P.dfs_qrow.push_back(qrow.at(s));
+      P.dfs_qrow.push_back(qrow_of(s));
       end_row.push_back(r);
     }
     stack.push_back({f.node, f.parent_row, true, r});

@@ -176,7 +176,7 @@ class Manager {
   int32_t tile_fill(int32_t fill, int32_t t) const {
     return C_ > kTileKeys ? std::min(kTileKeys, fill - t * kTileKeys) : fill;
   }
-  size_t live() const { return end_.size(); }
+  size_t live() const { return live_.size(); }
   int64_t nodes() const { return n_nodes_; }
 
   // Mutations return the device copies they need (possibly none).
@@ -251,6 +251,13 @@ class Manager {
     int32_t cur = 0, pos = 0, split_node = -1, split_at = 0;
   };
   void walk_insert(int64_t seq, const int32_t* tokens, int32_t n, InsertWalk* w) const;
+  struct Live {
+    int32_t end;  // node index where the sequence ends
+    int32_t len;  // its length in tokens
+  };
+  // append() once its sequence is found
+  void append_to(std::map<int64_t, Live>::iterator it, const int32_t* tokens, int32_t n, std::vector<KvOp>* ops,
+                 int32_t src_base);
   int32_t new_node(int32_t parent, int32_t start);
   void free_node(int32_t idx);
   int32_t alloc_slot();
@@ -320,8 +327,7 @@ class Manager {
     size_t first_ = 0;
   };
   FreeSlots free_;
-  std::map<int64_t, int32_t> end_;          // seq -> node index where it ends
-  std::map<int64_t, int32_t> len_;          // seq -> length
+  std::map<int64_t, Live> live_;           // live sequences by id
 };
 
 }  // namespace chunkattn
