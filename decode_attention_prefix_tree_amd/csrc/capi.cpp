@@ -202,8 +202,6 @@ void require_usable(const ca_ctx* c) {
                             "match the tree: destroy the context");
 }
 
-// with_fills: the host plan's fill counts are needed too (an upload, an
-// export, stats); a step whose device table is current does not need them.
 // Chunk refs per chunk-first task when the caller leaves it open.  A
 // chunk-first wave walks its chunks one 32-key half after another, each half
 // one dependent round trip to memory (all 16 KiB of its tile loads in flight
@@ -246,6 +244,9 @@ int64_t sf_min_tasks(int heads) {
 void layout_plan(ca_ctx* c);
 int build_for(const ca_ctx* c, chunkattn::Plan* plan, const chunkattn::NextAppend* next);
 
+// The host plan of the current tree, rebuilt if the tree changed shape.
+// with_fills: the host plan's fill counts are needed too (an upload, an
+// export, stats); a step whose device table is current does not need them.
 void ensure_plan(ca_ctx* c, bool with_fills = true) {
   if (c->plan_valid) {
     if (c->fills_stale && with_fills) {

@@ -693,9 +693,17 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
     P.seq_parts[2 * i + 1] = ent_first[i + 1] - ent_first[i];
   }
   // Longest sequence-first tasks first: they start earliest, and the four
-  // waves of a block get tasks of about the same length.
-  std::stable_sort(P.sf_tasks.begin(), P.sf_tasks.end(),
-                   [](const SfTask& x, const SfTask& y) { return x.n_chunks > y.n_chunks; });
+  // waves of a block get tasks of about the same length.  Among tasks of one
+  // length, in the order of their first chunk's slot: blocks that run at the
+  // same time then read slots close together also where decoding has
+  // interleaved the sequences' chunks in the pool (one new chunk per
+  // sequence per round); measured on MI355X, 32 sequences with 2,048 shared
+  // and 496 private tokens grown that way take 55.1 us per step in sequence
+  // order, 54.0 us in slot order, 52.7 us when inserted whole.
+  std::stable_sort(P.sf_tasks.begin(), P.sf_tasks.end(), [&P](const SfTask& x, const SfTask& y) {
+    if (x.n_chunks != y.n_chunks) return x.n_chunks > y.n_chunks;
+    return P.chunk_refs[2 * x.chunk_begin] < P.chunk_refs[2 * y.chunk_begin];
+  });
   // where each chunk ref lives, so a fill change can be patched in place
   P.ref_task.assign(P.ref_node.size(), -1);
   P.ref_pos.assign(P.ref_node.size(), -1);
