@@ -821,7 +821,9 @@ extern "C" {
 
 size_t ca_slot_bytes(int heads, int head_dim, int chunk_size) {
   if (heads <= 0 || head_dim <= 0 || chunk_size <= 0) return 0;
-  return static_cast<size_t>(4) * heads * chunk_size * head_dim;
+  // a 64-key tile (pool_tile_halves at head_dim 128) per 64 tokens
+  const size_t tile_heads = chunkattn::pool_tile_halves(heads) / (2 * chunkattn::kTileKeys * chunkattn::kHeadDim);
+  return static_cast<size_t>(4) * tile_heads * chunk_size * head_dim;
 }
 
 int ca_create_ex(int heads, int head_dim, int chunk_size, int flags, ca_ctx** out) {

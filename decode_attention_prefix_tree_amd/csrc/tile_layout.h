@@ -1,9 +1,11 @@
 // Device-side layout of the chunk pool, shared by the decode-step kernels
 // and the KV write kernel.
 //
-// Tile layout.  The pool is a sequence of 64-key tiles; tile t, head h: K
-// tile at ((t*H + h)*2 + 0) * 8192 halves, V tile right after it (a chunk
-// slot of 64 tokens is one tile, of 128 two, two slots of 32 share one).
+// Tile layout.  The pool is a sequence of 64-key tiles, pool_tile_halves(H)
+// apart (every head's K and V tile, one head's more when H is a power of
+// two); tile t, head h: K tile at t * pool_tile_halves(H) + (2h + 0) * 8192
+// halves, V tile right after it (a chunk slot of 64 tokens is one tile, of
+// 128 two, two slots of 32 share one).
 // Within a tile the 64 x 128 fp16 elements
 // are ordered so that every MFMA operand fetch is one contiguous 1 KB wave
 // load (64 lanes x 16 bytes):
@@ -45,7 +47,7 @@ constexpr int C = kChunk;
 constexpr int TILE = C * D;  // halves per tile
 
 __device__ __forceinline__ size_t tile_base(int tile, int head, int heads, int kv) {
-  return ((static_cast<size_t>(tile) * heads + head) * 2 + kv) * TILE;
+  return static_cast<size_t>(tile) * static_cast<size_t>(pool_tile_halves(heads)) + (static_cast<size_t>(head) * 2 + kv) * TILE;
 }
 
 __device__ __forceinline__ int k_off(int key, int dim) {

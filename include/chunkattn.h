@@ -195,8 +195,13 @@ typedef struct ca_stats_t {
   int64_t row_chunks;         /* chunks stored row-major (made by appends, never shared) */
 } ca_stats_t;
 
-/* Bytes of one chunk slot: K and V, all heads, fp16 = 4 * heads * chunk_size
- * * head_dim.  Returns 0 for non-positive arguments. */
+/* Bytes of one chunk slot: K and V of every head in fp16, 4 * heads *
+ * chunk_size * head_dim, and of one head more when heads is a power of two
+ * (4 * (heads + 1) * chunk_size * head_dim): the pool's 64-key tiles are then
+ * not a power of two apart (at 32 heads a tile would be exactly 1 MiB), which
+ * streams faster on MI355X where decoding has spread a batch's chunks over
+ * tiles allocated a power of two apart.  Returns 0 for non-positive
+ * arguments. */
 size_t ca_slot_bytes(int heads, int head_dim, int chunk_size);
 
 /* Create a context.  heads >= 1; head_dim must be 128 and chunk_size 1..64 or
@@ -211,9 +216,11 @@ void ca_destroy(ca_ctx* ctx);
 
 /* Lend the context a device pool of capacity_slots slots, each
  * ca_slot_bytes() long, 256-byte aligned.  Layout inside the pool: 64-key
- * tiles, tile-major, then head, then K tile and V tile of 64 x 128 fp16 each
- * (tile element order is private to the library); a slot of 64 tokens is one
- * tile, of 128 two, and two slots of 32 share one.  With chunk_size 32 the
+ * tiles, tile-major (ca_slot_bytes(heads, 128, 64) bytes apart), then head,
+ * then K tile and V tile of 64 x 128 fp16 each (tile element order is private
+ * to the library; the extra head's room at the end of a tile is never
+ * touched); a slot of 64 tokens is one tile, of 128 two, and two slots of 32
+ * share one.  With chunk_size 32 the
  * slots are used in pairs: an odd last slot is left out of the capacity.
  * dev may be NULL: the context then manages the tree and tables on the host
  * only and every call that needs the device returns CA_E_NO_POOL.  A device

@@ -641,6 +641,19 @@ def _v_off(key, dim):
         ((key & 3) | (((key >> 3) & 1) << 2))
 
 
+def _pool_tiles(ca, heads):
+    """The pool as [tile][head][K|V][64 x 128 halves]: tiles lie
+    ca_slot_bytes(heads, 128, 64) apart (one head's pair more when the head
+    count is a power of two), heads and K/V contiguous inside a tile."""
+    from decode_attention_prefix_tree_amd import slot_bytes
+    torch = _torch()
+    flat = ca.pool.view(torch.float16).cpu().numpy()
+    stride = slot_bytes(heads, 128, 64) // 2
+    used = heads * 2 * 64 * 128
+    assert stride >= used
+    return flat[:flat.size // stride * stride].reshape(-1, stride)[:, :used].reshape(-1, heads, 2, 64 * 128)
+
+
 @pytest.mark.parametrize("chunk", [32, 64, 128])
 @pytest.mark.parametrize("name", ["deep_random", "interior_and_dups"])
 def test_pool_holds_each_chunks_kv(name, chunk):
@@ -649,13 +662,10 @@ def test_pool_holds_each_chunks_kv(name, chunk):
     j of every table row sits at global pool key slot * chunk + j, in tile
     order, bit for bit equal to the caller's K and V of that token."""
     _say(f"pool contents {name} chunk {chunk}")
-    torch = _torch()
     wl = from_token_lists(tiny_tree_cases()[name], heads=3, seed=9)
     ca = build_ca(wl, chunk=chunk)
     rows, order = ca.export_table()
-    flat = ca.pool.view(torch.float16).cpu().numpy()
-    tile_halves = wl.heads * 2 * 64 * 128  # one 64-key tile, every head, K and V
-    pool = flat[:flat.size // tile_halves * tile_halves].reshape(-1, wl.heads, 2, 64 * 128)
+    pool = _pool_tiles(ca, wl.heads)
     keys = np.arange(64)[:, None]
     dims = np.arange(128)[None, :]
     koff, voff = _k_off(keys, dims), _v_off(keys, dims)
@@ -686,11 +696,8 @@ def _check_pool(ca, heads, chunk, kv_of, row_rows):
     """Every key of every table row against the K/V the caller supplied:
     table rows in row_rows are read in the row layout, the others in the tile
     layout."""
-    torch = _torch()
     rows, order = ca.export_table()
-    flat = ca.pool.view(torch.float16).cpu().numpy()
-    tile_halves = heads * 2 * 64 * 128
-    pool = flat[:flat.size // tile_halves * tile_halves].reshape(-1, heads, 2, 64 * 128)
+    pool = _pool_tiles(ca, heads)
     keys = np.arange(64)[:, None]
     dims = np.arange(128)[None, :]
     offs = {False: (_k_off(keys, dims), _v_off(keys, dims)), True: (_k_row_off(keys, dims), _v_row_off(keys, dims))}
@@ -713,11 +720,8 @@ def _check_pool_either_layout(ca, heads, chunk, kv_of):
     chunk in the layout (row-major or tiles) in which all its keys match:
     after removals the layout of a chunk is not known from the table alone,
     and a chunk whose keys match in neither fails."""
-    torch = _torch()
     rows, order = ca.export_table()
-    flat = ca.pool.view(torch.float16).cpu().numpy()
-    tile_halves = heads * 2 * 64 * 128
-    pool = flat[:flat.size // tile_halves * tile_halves].reshape(-1, heads, 2, 64 * 128)
+    pool = _pool_tiles(ca, heads)
     keys = np.arange(64)[:, None]
     dims = np.arange(128)[None, :]
     layouts = [(_k_off(keys, dims), _v_off(keys, dims)), (_k_row_off(keys, dims), _v_row_off(keys, dims))]
