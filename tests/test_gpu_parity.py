@@ -681,6 +681,70 @@ def test_pool_holds_each_chunks_kv(name, chunk):
     assert n_keys == sum(int(r[3]) for r in rows)
 
 
+@pytest.mark.parametrize("chunk", [32, 64, 128])
+def test_pool_room_past_the_heads_is_never_written(chunk):
+    """With a power-of-two head count each pool tile has one head's K/V room
+    more than its heads use.  Inserts (splits, pool-to-pool copies), decode
+    steps (tokens stored by the step, chunks opened), an insert that shares
+    decoded chunks (their conversion to tiles) and a removal leave that room
+    as it was, and the output still matches the oracle."""
+    _say(f"pool room past the heads, chunk {chunk}")
+    torch = _torch()
+    from decode_attention_prefix_tree_amd import ChunkAttention, load_workload, slot_bytes, slots_needed
+    H = 4
+    rng = np.random.default_rng(700 + chunk)
+    shared = list(range(150))
+    seqs = [shared + [9000 + i] + [int(x) for x in rng.integers(0, 9, size=n)] for i, n in enumerate((3, 40, 77))]
+    seqs.append(shared[:70])
+    wl = from_token_lists(seqs, heads=H, seed=701)
+    cap = slots_needed(wl, chunk=chunk) + 40
+    ca = ChunkAttention(H, cap, device="cuda:0", chunk_size=chunk)
+    sentinel = 0x5A5A
+    ca.pool.view(torch.int16).fill_(sentinel)
+    load_workload(ca, wl, device="cuda:0")
+    toks = {i: [int(t) for t in wl.seq_tokens(i)] for i in range(wl.n_seq)}
+    kv = {i: [x.copy() for x in wl.seq_kv(i)] for i in range(wl.n_seq)}
+    ids = list(range(wl.n_seq))
+
+    def steps(n_steps, base):
+        q = None
+        for step in range(n_steps):
+            t = (base + step * 100 + np.arange(len(ids))).astype(np.int32)
+            k = rng.standard_normal((len(ids), H, 128), dtype=np.float32).astype(np.float16)
+            v = rng.standard_normal((len(ids), H, 128), dtype=np.float32).astype(np.float16)
+            q = rng.standard_normal((len(ids), H, 128), dtype=np.float32).astype(np.float16)
+            out = ca.decode_step(t, *(torch.from_numpy(x).cuda() for x in (k, v, q)))
+            for r, i in enumerate(ids):
+                toks[i].append(int(t[r]))
+                kv[i][0] = np.concatenate([kv[i][0], k[r:r + 1]])
+                kv[i][1] = np.concatenate([kv[i][1], v[r:r + 1]])
+        torch.cuda.synchronize()
+        return q, out.cpu().numpy()
+
+    steps(70, 10**6)
+    # a new sequence that shares sequence 1's decoded tokens up to the middle
+    # of a grown chunk, then diverges
+    cut = len(toks[1]) - 23
+    new_tok = toks[1][:cut] + [777000 + j for j in range(9)]
+    nk = rng.standard_normal((9, H, 128), dtype=np.float32).astype(np.float16)
+    nv = rng.standard_normal((9, H, 128), dtype=np.float32).astype(np.float16)
+    k_new = np.concatenate([kv[1][0][:cut], nk])
+    v_new = np.concatenate([kv[1][1][:cut], nv])
+    ca.insert(10, np.asarray(new_tok, np.int32), torch.from_numpy(k_new).cuda(), torch.from_numpy(v_new).cuda())
+    toks[10] = new_tok
+    kv[10] = [k_new, v_new]
+    ca.remove(2)
+    ids = [0, 1, 3, 10]
+    q, got = steps(40, 2 * 10**6)
+    assert_parity(got, A.decode_step(q, [kv[i] for i in ids]), f"pool room chunk {chunk}")
+    flat = ca.pool.view(torch.int16).cpu().numpy()
+    stride = slot_bytes(H, 128, 64) // 2
+    used = H * 2 * 64 * 128
+    assert stride == (H + 1) * 2 * 64 * 128
+    tiles = flat[:flat.size // stride * stride].reshape(-1, stride)
+    assert (tiles[:, used:] == sentinel).all(), np.argwhere(tiles[:, used:] != sentinel)[:4]
+
+
 def _k_row_off(key, dim):
     """Position of K[key][dim] of a row-major chunk in its 64-key tile."""
     return key * 128 + dim
