@@ -208,19 +208,23 @@ void require_usable(const ca_ctx* c) {
 // together).  The longest such chain should stay within half of the step's
 // own streaming time (unique KV bytes at about 6 TB/s), or the chunk-first
 // blocks become the step's tail; within that bound larger groups mean fewer
-// partials.  The per-half cost (2.5 us under full load) is calibrated on
-// MI355X: 16 chunks per task (8 halves per wave) are the fastest choice from
-// about 40 us of streaming up (1024 and 4096 shared tokens, 32 sequences;
-// the multi-branch tree), while 32 or 64 make the chains the tail at 4096
-// shared tokens (65.9 and 89.0 us against 59.3 us).
-// The group counts chunk refs: a 64-key tile (two halves) at C >= 64, one
-// half at C = 32, so 32-token chunks take twice as many refs per chain.
+// blocks and partials.  The per-half cost (2.5 us under full load) is
+// calibrated on MI355X: 16 tiles per task (8 halves per wave) are the fastest
+// choice at 285-335 MB (1024 and 4096 shared tokens, 32 sequences), while 32
+// or 64 make the chains the tail at 4096 shared tokens (65.9 and 89.0 us
+// against 59.3 us); from about 80 us of streaming, 32 wins (a 2048-token
+// prompt shared by 64 or 96 decoding sequences: 95.2 against 98.4 us and
+// 138.6 against 141.9 us; 2048 completion tokens at batch 32: 176.8 against
+// 180.4 us).  The group counts chunk refs: a 64-key tile (two halves) at
+// C >= 64, one half at C = 32, so 32-token chunks take twice as many refs per
+// chain, up to the 64 refs an explicit setting allows.
 int auto_cf_group(const chunkattn::Plan& p, int heads, int head_dim, int chunk) {
   const double kernel_us = static_cast<double>(p.unique_tokens) * 4.0 * heads * head_dim / 6.0e6;
   const int halves_per_ref = chunk < chunkattn::kTileKeys ? 1 : 2;
   const int refs_per_tile = 2 / halves_per_ref;
-  for (int g : {16, 8}) {
+  for (int g : {64, 32, 16, 8}) {
     const int refs = g * refs_per_tile;
+    if (refs > 64) continue;
     const int halves = halves_per_ref * ((refs + 3) / 4);
     if (halves * 2.5 <= 0.5 * kernel_us) return refs;
   }

@@ -92,8 +92,8 @@ enum {
 /* ca_set_option keys. */
 enum {
   CA_OPT_CF_CHUNKS_PER_TASK = 1, /* chunk refs of one shared run per chunk-first task (1..64), or
-                                    0 (default): chosen per plan, 4, 8 or 16 (8, 16 or 32 with
-                                    32-token chunks), so that a chunk-first wave's chain of
+                                    0 (default): chosen per plan, 4, 8, 16, 32 or 64 (8 to 64
+                                    with 32-token chunks), so that a chunk-first wave's chain of
                                     dependent tile loads stays well inside the step's streaming
                                     time (ca_stats reports the choice).  A ref is a 64-key tile
                                     (a chunk of 128 is two), or half a tile with chunks of 32. */

@@ -255,22 +255,27 @@ def test_non_aligned_prefix_at_scale():
 
 
 @pytest.mark.parametrize("chunk", [32, 64, 128])
-@pytest.mark.parametrize("case,want", [("w1", 4), ("p1024x256", 8), ("w2", 16), ("w3", 16), ("w5", 16)])
+@pytest.mark.parametrize("case,want", [("w1", 4), ("p1024x256", 8), ("w2", 16), ("w3", 16),
+                                       ("p2048x96", 32), ("w5", 64)])
 def test_automatic_chunk_first_group(case, want, chunk):
     """With the group left open, the longest chunk-first chain (2 halves per
     chunk of a wave, about 2.5 us each) must fit in half of the step's
     streaming time at 6 TB/s (32 heads): the tiny workload (6.3 MB) allows one
-    chunk per wave, 1024 shared + 32 x 256 private tokens (151 MB) two, 285 MB
-    and up four.  At 32-token chunks a ref is half a tile, so the same
-    chains take twice the refs.  An explicit setting wins."""
+    chunk per wave, 1024 shared + 32 x 256 private tokens (151 MB) two,
+    285-335 MB four, 2048 shared + 96 x 512 private (839 MB) eight and the
+    multi-branch tree (1.26 GB) sixteen.  At 32-token chunks a ref is half a
+    tile, so the same chains take twice the refs, at most 64.  An explicit
+    setting wins."""
     if case.startswith("w"):
         wl = make_config(int(case[1:]), heads=1)
+    elif case == "p2048x96":
+        wl = make_prefix_suffix(2048, [512] * 96, heads=1, seed=6)
     else:
         wl = make_prefix_suffix(1024, [256] * 32, heads=1, seed=5)
     ca = ChunkAttention(32, 20_000, device=None, chunk_size=chunk)
     for i in range(wl.n_seq):
         ca.insert(i, wl.seq_tokens(i))
-    want *= 2 if chunk == 32 else 1
+    want = min(64, want * 2) if chunk == 32 else want
     assert ca.stats()["cf_chunks_per_task"] == want
     ca.set_option(_capi.CA_OPT_CF_CHUNKS_PER_TASK, 8)
     assert ca.stats()["cf_chunks_per_task"] == 8

@@ -84,6 +84,24 @@ def test_workload_full(k):
         assert np.array_equal(run_step(ca, wl.q).view(np.uint16), got.view(np.uint16))
 
 
+@pytest.mark.parametrize("case", ["w3_cf32", "w3_cf64", "p2048x96_cf32"])
+def test_long_chunk_first_tasks(case):
+    """Chunk-first tasks of 32 and 64 chunks (the automatic choice once a
+    step streams for about 80 us or more): workload 3's 64-chunk prompt as
+    two tasks or one per head, and a 2,048-token prompt under 96 sequences
+    (three 32-row blocks of 32-chunk tasks); every output row against the
+    oracle."""
+    _say(f"long chunk-first tasks {case}")
+    if case.startswith("w3"):
+        wl = cached_config(3)
+    else:
+        wl = make_prefix_suffix(2048, [512] * 96, heads=8, seed=2048)
+    group = int(case.split("cf")[1])
+    ca = build_ca(wl, cf_group=group)
+    assert ca.stats()["cf_chunks_per_task"] == group
+    assert_parity(run_step(ca, wl.q), A.decode_workload(wl), case)
+
+
 @pytest.mark.parametrize("two_phase", [True, False])
 def test_non_aligned_prefix_full(two_phase):
     """A 1,766-token shared prefix (not a multiple of 64) with 512-token
