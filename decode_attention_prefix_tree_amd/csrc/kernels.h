@@ -12,12 +12,14 @@ constexpr int kTileKeys = kChunk;  // keys per K/V tile read by the kernels
 
 // Pool stride from one 64-key tile to the next, in fp16 elements: the K and
 // V tile of every head, and of one head more when the head count is a power
-// of two.  A tile of 32 heads would otherwise span exactly 1 MiB, so the same
-// head's tiles in tiles that decoding has allocated 32 (or 64, ...) apart lie
-// a power-of-two distance apart; on MI355X blocks streaming such tiles
-// together run slower (the batch-32 decode step 57.5 against 55.0 us).
+// of two from 16 up (the extra head then costs at most 1/16 of the pool).  A
+// tile of 32 heads would otherwise span exactly 1 MiB, so the same head's
+// tiles in tiles that decoding has allocated 32 (or 64, ...) apart lie a
+// power-of-two distance apart; on MI355X blocks streaming such tiles together
+// run slower (the batch-32 decode step 57.5 against 55.0 us).
+constexpr bool pool_pads_tiles(int heads) { return heads >= 16 && (heads & (heads - 1)) == 0; }
 constexpr int64_t pool_tile_halves(int heads) {
-  return static_cast<int64_t>(heads + ((heads & (heads - 1)) == 0 ? 1 : 0)) * 2 * kTileKeys * kHeadDim;
+  return static_cast<int64_t>(heads + (pool_pads_tiles(heads) ? 1 : 0)) * 2 * kTileKeys * kHeadDim;
 }
 constexpr int kCfInline = 8;   // chunk refs carried by a chunk-first unit record
 constexpr int kSfInline = 4;   // chunk refs carried by a sequence-first task record

@@ -3,7 +3,7 @@
 //
 // Tile layout.  The pool is a sequence of 64-key tiles, pool_tile_halves(H)
 // apart (every head's K and V tile, one head's more when H is a power of
-// two); tile t, head h: K tile at t * pool_tile_halves(H) + (2h + 0) * 8192
+// two from 16 up); tile t, head h: K tile at t * pool_tile_halves(H) + (2h + 0) * 8192
 // halves, V tile right after it (a chunk slot of 64 tokens is one tile, of
 // 128 two, two slots of 32 share one).
 // Within a tile the 64 x 128 fp16 elements

@@ -197,11 +197,11 @@ typedef struct ca_stats_t {
 
 /* Bytes of one chunk slot: K and V of every head in fp16, 4 * heads *
  * chunk_size * head_dim, and of one head more when heads is a power of two
- * (4 * (heads + 1) * chunk_size * head_dim): the pool's 64-key tiles are then
- * not a power of two apart (at 32 heads a tile would be exactly 1 MiB), which
- * streams faster on MI355X where decoding has spread a batch's chunks over
- * tiles allocated a power of two apart.  Returns 0 for non-positive
- * arguments. */
+ * from 16 up (4 * (heads + 1) * chunk_size * head_dim): the pool's 64-key
+ * tiles are then not a power of two apart (at 32 heads a tile would be
+ * exactly 1 MiB), which streams faster on MI355X where decoding has spread a
+ * batch's chunks over tiles allocated a power of two apart.  Returns 0 for
+ * non-positive arguments. */
 size_t ca_slot_bytes(int heads, int head_dim, int chunk_size);
 
 /* Create a context.  heads >= 1; head_dim must be 128 and chunk_size 1..64 or

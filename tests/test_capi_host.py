@@ -44,11 +44,11 @@ def test_create_rejects_unsupported_shapes():
 
 def test_slot_bytes_pad_power_of_two_head_counts():
     """A slot holds K and V of every head (4 * H * C * d bytes), and of one
-    head more when H is a power of two, so that tiles of one head in tiles
-    allocated a power of two apart do not lie a power of two apart; slots of
-    32 tokens are half a tile and of 128 two."""
+    head more when H is a power of two from 16 up, so that tiles of one head
+    in tiles allocated a power of two apart do not lie a power of two apart;
+    slots of 32 tokens are half a tile and of 128 two."""
     lib = _capi.load()
-    for heads, stored in ((32, 33), (16, 17), (8, 9), (1, 2), (3, 3), (24, 24), (40, 40)):
+    for heads, stored in ((32, 33), (16, 17), (64, 65), (8, 8), (4, 4), (1, 1), (3, 3), (24, 24), (40, 40)):
         for chunk in (32, 64, 128):
             assert lib.ca_slot_bytes(heads, 128, chunk) == 4 * stored * chunk * 128, (heads, chunk)
     assert lib.ca_slot_bytes(0, 128, 64) == 0 and lib.ca_slot_bytes(8, 128, 0) == 0

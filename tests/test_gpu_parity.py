@@ -662,7 +662,8 @@ def _v_off(key, dim):
 def _pool_tiles(ca, heads):
     """The pool as [tile][head][K|V][64 x 128 halves]: tiles lie
     ca_slot_bytes(heads, 128, 64) apart (one head's pair more when the head
-    count is a power of two), heads and K/V contiguous inside a tile."""
+    count is a power of two from 16 up), heads and K/V contiguous inside a
+    tile."""
     from decode_attention_prefix_tree_amd import slot_bytes
     torch = _torch()
     flat = ca.pool.view(torch.float16).cpu().numpy()
@@ -701,15 +702,15 @@ def test_pool_holds_each_chunks_kv(name, chunk):
 
 @pytest.mark.parametrize("chunk", [32, 64, 128])
 def test_pool_room_past_the_heads_is_never_written(chunk):
-    """With a power-of-two head count each pool tile has one head's K/V room
-    more than its heads use.  Inserts (splits, pool-to-pool copies), decode
+    """With a power-of-two head count from 16 up each pool tile has one
+    head's K/V room more than its heads use.  Inserts (splits, pool-to-pool copies), decode
     steps (tokens stored by the step, chunks opened), an insert that shares
     decoded chunks (their conversion to tiles) and a removal leave that room
     as it was, and the output still matches the oracle."""
     _say(f"pool room past the heads, chunk {chunk}")
     torch = _torch()
     from decode_attention_prefix_tree_amd import ChunkAttention, load_workload, slot_bytes, slots_needed
-    H = 4
+    H = 16
     rng = np.random.default_rng(700 + chunk)
     shared = list(range(150))
     seqs = [shared + [9000 + i] + [int(x) for x in rng.integers(0, 9, size=n)] for i, n in enumerate((3, 40, 77))]
