@@ -685,3 +685,49 @@ def test_prebuilt_plans_equal_fresh_builds(chunk):
             assert sa[k] == sb[k], (it, k)
     assert a.stats()["prebuilt_plans"] >= 3, a.stats()["prebuilt_plans"]
     assert b.stats()["prebuilt_plans"] == 0
+
+
+def _sf_records(ca):
+    """The sequence-first task records of the plan's device table: after the
+    chunk-first records (128 bytes each), at the next 256-byte boundary, 16
+    int32 each (chunk refs begin, count, DFS position, partial id, caller row,
+    reuse, append index, pad, 4 inline slots, 4 inline fill counts)."""
+    img = np.frombuffer(ca.export_plan(), dtype=np.int32)
+    st = ca.stats()
+    off = (int(st["cf_units"]) * 128 + 255) // 256 * 256 // 4
+    n = int(st["sf_tasks"])
+    return img[off:off + 16 * n].reshape(n, 16)
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 128])
+def test_sequence_first_tasks_longest_first_then_by_slot(chunk):
+    """Decoding gives every sequence one new chunk per chunk_size tokens, so
+    the sequences' chunks interleave in the pool.  The plan lists the
+    sequence-first tasks longest first and, among tasks of one length, by
+    the slot of their first chunk (not by sequence), so that blocks running
+    together read slots close together; every private chunk ref is in exactly
+    one task."""
+    ca = ChunkAttention(8, 4000, device=None, chunk_size=chunk)
+    ca.set_option(_capi.CA_OPT_SF_CHUNKS_PER_TASK, 4)
+    prompt = list(range(3 * chunk))
+    n = 12
+    for i in range(n):
+        ca.insert(i, prompt + [10_000 + i])
+    rng = np.random.default_rng(3)
+    for step in range(9 * chunk + 5):
+        ids = list(range(n)) if step < 6 * chunk else list(range(0, n, 2))
+        ca.append_batch(ids, [int(x) for x in 20_000 + step * 100 + np.arange(len(ids))])
+    recs = _sf_records(ca)
+    counts, first_slot = recs[:, 1], recs[:, 8]
+    assert (np.diff(counts) <= 0).all()
+    for c in np.unique(counts):
+        sl = first_slot[counts == c]
+        assert (np.diff(sl) > 0).all(), (c, sl)
+    # the tasks of one sequence (DFS position) cover its private refs once
+    refs = sorted(int(b) + k for b, cnt in zip(recs[:, 0], counts) for k in range(int(cnt)))
+    assert refs == list(range(min(refs), min(refs) + len(refs)))
+    # interleaved: some task's first slot lies below a task of a sequence
+    # that comes earlier in DFS order
+    pos = recs[:, 2]
+    assert any(pos[j] > pos[k] and first_slot[j] < first_slot[k]
+               for j in range(len(pos)) for k in range(len(pos)) if counts[j] == counts[k])
