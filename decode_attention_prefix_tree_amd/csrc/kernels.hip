@@ -90,6 +90,20 @@ __device__ __forceinline__ h8 ld_tile(const _Float16* p) {
   return *reinterpret_cast<const h8*>(p);
 }
 
+// A chunk-table entry read by a decode step that also grows fill counts in
+// the table (kAppend: its blocks store into the table, so the compiler would
+// read every entry with a vector load waited for at once).  Through the
+// constant address space the load is a scalar one and leaves the vector
+// memory counter to the tile loads.  Every entry holds its value for the
+// whole step except the growing chunks' fill counts, which a block may read
+// before or after another head's block tags them: both give the same key
+// (see the epoch test of the sequence-first block).
+template <bool kScalar>
+__device__ __forceinline__ int ld_table(const int* p) {
+  if constexpr (kScalar) return *(const __attribute__((address_space(4))) int*)p;
+  return *p;
+}
+
 __device__ __forceinline__ h2 lo2(h8 v, int j) {
   switch (j) {
     case 0: return __builtin_shufflevector(v, v, 0, 1);
@@ -596,7 +610,8 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
   // tiles of the same slots, which keeps HBM accesses close to sequential
   const int task = logical / a.heads, head = logical % a.heads;
   const int* t = a.sf_tasks + task * 16;
-  const int chunk_begin = t[0], n_chunks = t[1], dfs_pos = t[2], part_id = t[3], qrow = t[4];
+  const int chunk_begin = ld_table<kAppend>(t), n_chunks = ld_table<kAppend>(t + 1),
+            dfs_pos = ld_table<kAppend>(t + 2), part_id = ld_table<kAppend>(t + 3), qrow = ld_table<kAppend>(t + 4);
   // wave index in an SGPR: chunk lookups and tile bases stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, half = lane >> 5, i = lane & 31;
@@ -615,7 +630,7 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
   _Float16* new_lds = reinterpret_cast<_Float16*>(smem + kSfA);  // appended token: K row, then V row
   // In a decode step with in-kernel appends, the chunk (index in the task)
   // that takes this sequence's new token.
-  const int append_at = kAppend ? t[kSfAppendField] : -1;
+  const int append_at = kAppend ? ld_table<kAppend>(t + kSfAppendField) : -1;
   if (threadIdx.x < D / 8) {
     const _Float16* qp = static_cast<const _Float16*>(a.q) + (static_cast<size_t>(qrow) * H + head) * D;
     *reinterpret_cast<h8*>(q_lds + threadIdx.x * 8) = *reinterpret_cast<const h8*>(qp + threadIdx.x * 8);
@@ -640,11 +655,11 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
   int append_fill = 0;
   if (kAppend && append_at >= 0) {
     const int ac = append_at;
-    const int fill = ac < kSfInline ? t[12 + ac] : a.chunk_refs[2 * (chunk_begin + ac) + 1];
+    const int fill = ld_table<kAppend>(ac < kSfInline ? t + 12 + ac : a.chunk_refs + 2 * (chunk_begin + ac) + 1);
     int p = (static_cast<unsigned>(fill) >> kFillBits) == a.app_epoch ? (fill & kFillMask) - 1 : fill & kFillMask;
     append_fill = p + 1;
     if ((ac & 3) == wave) {
-      const int cslot = ac < kSfInline ? t[8 + ac] : a.chunk_refs[2 * (chunk_begin + ac)];
+      const int cslot = ld_table<kAppend>(ac < kSfInline ? t + 8 + ac : a.chunk_refs + 2 * (chunk_begin + ac));
       // key p of a 32-token chunk is key 32 * (slot % 2) + p of its tile
       const int slot = kHalf ? cslot >> 1 : cslot;
       _Float16* kw = const_cast<_Float16*>(pool) + tile_base(slot, head, H, 0);
@@ -684,8 +699,8 @@ __device__ __forceinline__ void sequence_first_block(const StepArgs& a, int logi
   }
 
   for (int c = wave; c < n_chunks; c += 4) {
-    const int slot = c < kSfInline ? t[8 + c] : a.chunk_refs[2 * (chunk_begin + c)];
-    const int fill = c < kSfInline ? t[12 + c] : a.chunk_refs[2 * (chunk_begin + c) + 1];
+    const int slot = ld_table<kAppend>(c < kSfInline ? t + 8 + c : a.chunk_refs + 2 * (chunk_begin + c));
+    const int fill = ld_table<kAppend>(c < kSfInline ? t + 12 + c : a.chunk_refs + 2 * (chunk_begin + c) + 1);
     int nvalid = fill & kFillMask;
     // a 32-token chunk is one half of its tile: its K blocks 8h .. 8h+7 and
     // V blocks 4nb + 2h, +1 land where keys 0..31 of a whole tile would
