@@ -44,7 +44,17 @@ int main(void) {
     printf("row %d %d %d %d %d %d %d\n", rows[7 * r], rows[7 * r + 1], rows[7 * r + 2], rows[7 * r + 3],
            rows[7 * r + 4], rows[7 * r + 5], rows[7 * r + 6]);
   printf("slot_bytes %zu\n", ca_slot_bytes(32, 128, 64));
+  ca_stats_t st;
+  if (ca_stats(c, &st) != CA_OK) return 20;
+  printf("stats %lld %lld %lld %lld %lld\n", (long long)st.live_sequences, (long long)st.chunks,
+         (long long)st.shared_chunks, (long long)st.unique_tokens, (long long)st.attended_tokens);
+  if (ca_set_option(c, CA_OPT_CF_CHUNKS_PER_TASK, 65) != CA_E_INVALID_ARG) return 21;
+  if (ca_set_option(c, 12345, 0) != CA_E_UNSUPPORTED) return 22;
+  if (ca_set_option(c, CA_OPT_SF_CHUNKS_PER_TASK, 1) != CA_OK) return 23;
+  if (ca_stats(c, &st) != CA_OK || st.sf_chunks_per_task != 1) return 24;
+  if (ca_remove(c, 7) != CA_OK || ca_stats(c, &st) != CA_OK || st.live_sequences != 1) return 25;
   ca_destroy(c);
+  ca_destroy(NULL);
   return 0;
 }
 """
@@ -80,3 +90,5 @@ def test_c_program_drives_a_host_only_context(tmp_path):
     fills = [int(line.split()[4]) for line in lines[1:4]]
     assert fills == [64, 6, 30], res.stdout
     assert lines[4] == f"slot_bytes {4 * 33 * 64 * 128}", res.stdout
+    # two sequences, three chunks (two shared), 100 unique tokens, 170 attended
+    assert lines[5] == "stats 2 3 2 100 170", res.stdout
