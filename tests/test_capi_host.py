@@ -731,3 +731,32 @@ def test_sequence_first_tasks_longest_first_then_by_slot(chunk):
     pos = recs[:, 2]
     assert any(pos[j] > pos[k] and first_slot[j] < first_slot[k]
                for j in range(len(pos)) for k in range(len(pos)) if counts[j] == counts[k])
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 128])
+def test_large_three_level_tree_matches_model(chunk):
+    """512 sequences in a three-level tree (a 1,000-token root, 8 branches of
+    500 tokens, suffixes of 1..300 tokens, so every level ends inside a
+    chunk), then removals of every third sequence and 200 decode rounds that
+    grow the survivors: the library's table, slot use and DFS order equal the
+    independent tree model's after each phase."""
+    rng = np.random.default_rng(900 + chunk)
+    root = [int(x) for x in 100_000 + np.arange(1000)]
+    branches = [[int(x) for x in 200_000 + 1000 * b + np.arange(500)] for b in range(8)]
+    m = PrefixTreeModel(chunk, 60_000)
+    ca = ChunkAttention(32, 60_000, device=None, chunk_size=chunk)
+    for i in range(512):
+        toks = root + branches[i % 8] + [int(x) for x in 300_000 + 1000 * i + np.arange(int(rng.integers(1, 301)))]
+        assert ca.insert(i, toks) == m.insert(i, toks)
+    model_and_lib_agree(m, ca)
+    for i in range(0, 512, 3):
+        ca.remove(i)
+        m.remove(i)
+    model_and_lib_agree(m, ca)
+    ids = m.sequences()
+    for step in range(200):
+        toks = [int(x) for x in 10_000_000 + 1000 * step + np.arange(len(ids))]
+        ca.append_batch(ids, toks)
+        for s_, t in zip(ids, toks):
+            m.append(s_, [t])
+    model_and_lib_agree(m, ca)
