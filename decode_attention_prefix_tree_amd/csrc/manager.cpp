@@ -589,12 +589,17 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
     // Left open: the largest of 16, 8 and 4 refs per task that still makes
     // at least sf_min_tasks tasks, so that the last round of blocks on the
     // chip stays well filled; longer tasks mean fewer partials to write and
-    // merge.
+    // merge.  Where chunk-first units share the launch the bar is 8/5 of
+    // that: their long blocks hold slots through the first rounds, and the
+    // sequence-first tail needs more, shorter blocks to even out behind them
+    // (1024 shared + 1024 private tokens at 64 and 72 sequences, 32 heads:
+    // group 8 in 170.4 and 190.1 us where 16 took 174.2 and 193.4).
     sf_group = 4;
+    const int64_t target = P.cf_units.empty() ? sf_min_tasks : (sf_min_tasks * 8 + 4) / 5;
     for (int g : {16, 8}) {
       int64_t tasks = 0;
       for (int32_t i = 0; i < n_seq; ++i) tasks += (priv_first[i + 1] - priv_first[i] + g - 1) / g;
-      if (tasks >= sf_min_tasks) {
+      if (tasks >= target) {
         sf_group = g;
         break;
       }

@@ -220,7 +220,8 @@ class Manager {
   // chunk on a sequence's path, shared or not, goes to that sequence's
   // sequence-first tasks (physically shared pages, no chunk-first phase).
   // sf_group <= 0: chosen per plan, the largest of 16, 8, 4 that gives at
-  // least sf_min_tasks sequence-first tasks (Plan::sf_group says which).
+  // least sf_min_tasks sequence-first tasks, 8/5 of that when the plan has
+  // chunk-first units (Plan::sf_group says which).
   // With `next`, the plan of the tree after those appends (the same plan
   // that build_plan gives once they are made).
   void build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan, int64_t sf_min_tasks = 0,

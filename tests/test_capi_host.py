@@ -512,6 +512,21 @@ def test_automatic_sequence_first_group(case, want):
         ca.set_option(_capi.CA_OPT_SF_CHUNKS_PER_TASK, 257)
 
 
+@pytest.mark.parametrize("shared,want", [(1024, 8), (0, 16)])
+def test_sequence_first_group_with_chunk_first_units(shared, want):
+    """The automatic sequence-first group asks for 8/5 as many tasks when
+    chunk-first units share the launch: 64 sequences of 16 private chunks at
+    32 heads make 64 tasks with 16 refs each, enough alone (60) but short of
+    96 behind a 1024-token shared prefix, where 8 refs each (128 tasks) win."""
+    ca = ChunkAttention(32, 10_000, device=None)
+    for i in range(64):
+        ca.insert(i, list(range(shared)) + [100_000 + 2000 * i + j for j in range(1024)])
+    st = ca.stats()
+    assert (st["cf_chunk_reads"] > 0) == (shared > 0)
+    assert st["sf_chunks_per_task"] == want
+    assert st["sf_tasks"] == 64 * 16 // want
+
+
 @pytest.mark.parametrize("chunk", [2, 3, 4])
 def test_tiny_chunks_random_ops_bit_exact_against_model(chunk):
     """Chunks of 2, 3 and 4 tokens, a vocabulary of 2 or 3 and sequences of at
