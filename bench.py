@@ -235,7 +235,8 @@ def decode_progression(torch, n_seq, n_shared, checkpoints, two_phase, flush, wi
     one_call, as ca_decode_step.  Returns, per checkpoint n_c (the completion
     length reached), the mean cold GPU time of the append and the attend (or
     of the whole step) over the `window` steps ending there, and the host time
-    per step."""
+    per step (each timed call is made with only the flush ahead of it on the
+    stream)."""
     from decode_attention_prefix_tree_amd import ChunkAttention, _capi
     gen = torch.Generator(device="cuda").manual_seed(seed)
     max_c = max(checkpoints)
@@ -257,6 +258,10 @@ def decode_progression(torch, n_seq, n_shared, checkpoints, two_phase, flush, wi
         timed = any(cp - window < c <= cp for cp in checkpoints)
         toks = np.full(n_seq, c, np.int32)
         if timed:
+            # untimed steps let the host run far ahead of the GPU; drain the
+            # queue first so that the call's host time is its own work and not
+            # a wait for queue space or a staging buffer the GPU still reads
+            torch.cuda.synchronize()
             flush()
             e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             h0 = time.perf_counter()

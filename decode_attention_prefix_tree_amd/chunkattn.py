@@ -23,6 +23,25 @@ def slot_bytes(heads: int, head_dim: int = HEAD_DIM, chunk: int = CHUNK) -> int:
     return int(load().ca_slot_bytes(heads, head_dim, chunk))
 
 
+_copy_path_warm = False
+
+
+def _warm_copy_path(torch, dev_buf) -> None:
+    """Make one pinned host-to-device copy of more than 16 KiB, once per
+    process.  The HIP runtime sets up its path for such copies at the first
+    one (about 6 ms on MI355X, most of it CPU time; later copies take a few
+    microseconds), and a table upload that is the first would pay it inside a
+    decode step."""
+    global _copy_path_warm
+    n = min(dev_buf.numel(), 64 << 10)
+    if _copy_path_warm or n <= 16 << 10:
+        return
+    src = torch.zeros(n, dtype=torch.uint8, pin_memory=True)
+    dev_buf[:n].copy_(src, non_blocking=True)
+    torch.cuda.current_stream(dev_buf.device).synchronize()
+    _copy_path_warm = True
+
+
 def _tokens(tokens) -> np.ndarray:
     if type(tokens) is np.ndarray and tokens.dtype == np.int32 and tokens.ndim == 1 and tokens.flags.c_contiguous:
         return tokens
@@ -65,6 +84,8 @@ class ChunkAttention:
             import torch
             nbytes = capacity_slots * slot_bytes(heads, head_dim, chunk_size)
             self.pool = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            # before the pool is attached, while its contents mean nothing
+            _warm_copy_path(torch, self.pool)
             # what the per-step argument checks use, looked up once
             self._torch, self._f16 = torch, torch.float16
             raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)

@@ -2,6 +2,7 @@
 // stores a message and returns a status code (declared in include/chunkattn.h).
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <chrono>
 #include <cmath>
 #include <cstddef>
@@ -85,9 +86,13 @@ struct ca_ctx {
   // marks when the copy out of its buffer has finished, so a buffer is
   // rewritten without waiting on the most recent uploads.  The buffers are
   // three equal parts of the caller's pinned memory (ca_attach_staging) or,
-  // when the caller lent none, the library's own (allocated at the first
-  // upload that needs them).
+  // when the caller lent none, the library's own: allocated at the first
+  // upload, at least kMinStageBytes each and twice the table, so that a tree
+  // growing in a decode loop rarely meets a pinned allocation (hipHostFree
+  // and hipHostMalloc took 5-6 ms in one such step on MI355X, where the
+  // step's kernels take 0.1 ms).
   static constexpr int kStages = 3;
+  static constexpr size_t kMinStageBytes = size_t{1} << 20;
   void* stage[kStages] = {nullptr, nullptr, nullptr};
   size_t stage_bytes[kStages] = {0, 0, 0};
   hipEvent_t stage_done[kStages] = {nullptr, nullptr, nullptr};
@@ -459,7 +464,7 @@ void copy_table(ca_ctx* c, void* stream, void* ws, const chunkattn::Plan& p, con
     if (c->stage[b]) hip_check(hipHostFree(c->stage[b]), "hipHostFree");
     c->stage[b] = nullptr;
     c->stage_bytes[b] = 0;
-    size_t want = align_up(l.table_bytes * 2);
+    size_t want = align_up(std::max(l.table_bytes * 2, ca_ctx::kMinStageBytes));
     hip_check(hipHostMalloc(&c->stage[b], want, hipHostMallocDefault), "hipHostMalloc");
     c->stage_bytes[b] = want;
   }

@@ -25,8 +25,9 @@
  *    thread.
  *  - Chunk-table uploads copy from pinned host staging: the caller's
  *    (ca_attach_staging), or, if the caller lends none, pinned memory the
- *    library allocates at the first upload that needs it and frees in
- *    ca_destroy.  That is the library's only allocation.
+ *    library allocates at the first upload (three buffers of at least 1 MiB
+ *    each, and of twice the table; a larger table reallocates one) and frees
+ *    in ca_destroy.  That is the library's only allocation.
  *  - CA_E_HIP from a call that only reads the tree (ca_attend,
  *    ca_attend_phase, ca_prepare) leaves the context usable; the next step
  *    uploads the table again.  ca_insert enqueues its copies before it
@@ -251,7 +252,11 @@ int ca_attach_workspace(ca_ctx* ctx, void* dev, size_t bytes);
  * attaches another or destroys the context.  It first waits for copies still
  * reading earlier staging, so that memory may be freed once it returns.
  * host NULL: back to library-owned staging.  A step whose table must be
- * uploaded and does not fit the attached staging returns CA_E_WORKSPACE. */
+ * uploaded and does not fit the attached staging returns CA_E_WORKSPACE.
+ * The first pinned host-to-device copy of more than 16 KiB in a process
+ * costs about 6 ms in the HIP runtime on MI355X, once; a caller whose decode
+ * loop must not meet it makes such a copy at start-up (the Python binding
+ * does when it allocates a pool). */
 int ca_staging_bytes(ca_ctx* ctx, size_t* out);
 int ca_attach_staging(ca_ctx* ctx, void* host, size_t bytes);
 
