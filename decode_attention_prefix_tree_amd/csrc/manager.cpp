@@ -586,10 +586,10 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
   run_first[n_seq] = static_cast<int32_t>(runs.size());
   priv_first[n_seq] = static_cast<int32_t>(priv.size());
   if (sf_group <= 0) {
-    // Left open: the largest of 16, 8 and 4 refs per task that still makes
-    // at least sf_min_tasks tasks, so that the last round of blocks on the
-    // chip stays well filled; longer tasks mean fewer partials to write and
-    // merge.  Where chunk-first units share the launch the bar is 8/5 of
+    // Left open: the largest of 16, 8 and 4 (or 3, below) refs per task
+    // that still makes at least sf_min_tasks tasks, so that the last round of
+    // blocks on the chip stays well filled; longer tasks mean fewer partials
+    // to write and merge.  Where chunk-first units share the launch the bar is 8/5 of
     // that: their long blocks hold slots through the first rounds, and the
     // sequence-first tail needs more, shorter blocks to even out behind them
     // (1024 shared + 1024 private tokens at 64 and 72 sequences, 32 heads:
@@ -603,6 +603,22 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
         sf_group = g;
         break;
       }
+    }
+    // Falling back to 4 behind chunk-first units: 3 when that makes more
+    // tasks and no sequence is left a one-chunk remainder (8 private chunks
+    // become 3 + 3 + 2).  4,096 shared + 512 private tokens, 32 sequences:
+    // 57.9-58.2 us against 58.9; 2,048 + 512 at 48 sequences 72.5 against
+    // 73.1-73.3 us.  4 chunks (3 + 1) measured slower with 3 and stay at 4.
+    if (sf_group == 4 && !P.cf_units.empty()) {
+      bool no_single = true;
+      int64_t t3 = 0, t4 = 0;
+      for (int32_t i = 0; i < n_seq; ++i) {
+        const int32_t n = priv_first[i + 1] - priv_first[i];
+        if (n > 1 && n % 3 == 1) no_single = false;
+        t3 += (n + 2) / 3;
+        t4 += (n + 3) / 4;
+      }
+      if (no_single && t3 > t4) sf_group = 3;
     }
   }
   P.sf_group = sf_group;

@@ -221,7 +221,8 @@ class Manager {
   // sequence-first tasks (physically shared pages, no chunk-first phase).
   // sf_group <= 0: chosen per plan, the largest of 16, 8, 4 that gives at
   // least sf_min_tasks sequence-first tasks, 8/5 of that when the plan has
-  // chunk-first units (Plan::sf_group says which).
+  // chunk-first units, where 3 replaces 4 if it makes more tasks and leaves
+  // no sequence a one-chunk remainder (Plan::sf_group says which).
   // With `next`, the plan of the tree after those appends (the same plan
   // that build_plan gives once they are made).
   void build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan, int64_t sf_min_tasks = 0,

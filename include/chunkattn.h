@@ -102,7 +102,9 @@ enum {
                                     (default): chosen per plan, the largest of 16, 8 and 4 that
                                     still gives the step about 2.5 rounds of blocks over the
                                     chip's resident block slots, 4 rounds when chunk-first
-                                    blocks share the launch (ca_stats reports the choice) */
+                                    blocks share the launch (there 3 instead of 4 where it
+                                    makes more tasks and no one-chunk remainder; ca_stats
+                                    reports the choice) */
   CA_OPT_FUSED_MERGE = 3,        /* 0: a step is a partials launch and a merge launch.
                                     1: one launch whose grid ends with merge blocks; each waits
                                     until the partials of its (sequence, head) are written (all

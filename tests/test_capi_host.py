@@ -488,13 +488,15 @@ def test_chunk32_capacity_in_pairs_and_plan():
     assert (st["cf_chunk_reads"], st["sf_chunk_reads"]) == (cf, sf)
 
 
-@pytest.mark.parametrize("case,want", [("w1", 4), ("w2", 4), ("w3", 4), ("w4", 16), ("w5", 16)])
+@pytest.mark.parametrize("case,want", [("w1", 4), ("w2", 3), ("w3", 3), ("w4", 16), ("w5", 16)])
 def test_automatic_sequence_first_group(case, want):
     """With the group left open, the largest of 16, 8 and 4 private refs per
     task that still gives 1920 / heads tasks (about 2.5 rounds of blocks over
-    3 x 256 resident block slots): 32 sequences with 8 private chunks each
-    stay at 4 (2048 blocks at 32 heads); 32 chunks each (workload 4) and the
-    multi-branch tree's ragged suffixes reach 16.  An explicit setting wins."""
+    3 x 256 resident block slots; 8/5 of that behind chunk-first units):
+    32 sequences with 8 private chunks each under a shared prefix fall back
+    to 3 (3 + 3 + 2 chunks: 3072 blocks at 32 heads); 32 chunks each
+    (workload 4) and the multi-branch tree's ragged suffixes reach 16.  An
+    explicit setting wins."""
     wl = make_config(int(case[1:]), heads=1)
     ca = ChunkAttention(32, 10_000, device=None)
     for i in range(wl.n_seq):
@@ -503,13 +505,29 @@ def test_automatic_sequence_first_group(case, want):
     assert st["sf_chunks_per_task"] == want
     # every sequence's private refs cut into tasks of that size
     rows, _ = ca.export_table()
-    assert st["sf_tasks"] >= 1920 // 32 or want == 4
+    assert st["sf_tasks"] >= 1920 // 32 or want in (3, 4)
     ca.set_option(_capi.CA_OPT_SF_CHUNKS_PER_TASK, 2)
     assert ca.stats()["sf_chunks_per_task"] == 2
     ca.set_option(_capi.CA_OPT_SF_CHUNKS_PER_TASK, 0)
     assert ca.stats()["sf_chunks_per_task"] == want
     with pytest.raises(CaError):
         ca.set_option(_capi.CA_OPT_SF_CHUNKS_PER_TASK, 257)
+
+
+@pytest.mark.parametrize("private,want", [(512, 3), (704, 3), (320, 4), (256, 4), (448, 4)])
+def test_sequence_first_fallback_three_without_single_chunk_tasks(private, want):
+    """Behind chunk-first units, where neither 16 nor 8 refs per task reach
+    the task target, 3 replaces 4 when it makes more tasks and no sequence
+    is left a one-chunk remainder: 8 and 11 private chunks take 3 (3 + 3 + 2,
+    3 + 3 + 3 + 2); 5 stays at 4 (two tasks either way), 4 and 7 too (3 + 1
+    and 3 + 3 + 1 would leave one)."""
+    ca = ChunkAttention(32, 10_000, device=None)
+    for i in range(32):
+        ca.insert(i, list(range(1024)) + [100_000 + 1000 * i + j for j in range(private)])
+    st = ca.stats()
+    assert st["sf_chunks_per_task"] == want
+    n = -(-private // 64)
+    assert st["sf_tasks"] == 32 * -(-n // want)
 
 
 @pytest.mark.parametrize("shared,want", [(1024, 8), (0, 16)])
