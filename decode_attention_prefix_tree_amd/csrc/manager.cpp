@@ -495,7 +495,12 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
 
   // Pass 2: runs of shared chunks (range >= 2).  A child with the same range
   // as its parent continues the parent's run (a chain: one child, nobody
-  // ends at the parent); a run holds at most cf_group chunks.
+  // ends at the parent); a run holds at most cf_group chunks, and a chain
+  // longer than that is cut into as few runs as the limit allows, of equal
+  // length to within one row: no run is left with a stub of a chain, whose
+  // units would hold block slots for little work (2,112 shared + 512
+  // private tokens, 32 sequences: runs of 11 + 11 + 11 chunks instead of
+  // 16 + 16 + 1, 53.0-53.1 against 53.8 us).
   std::vector<int32_t> task_of_row(n_rows, -1);
   struct Task { int32_t b, e, chunk_begin, n_chunks, last_row; };
   std::vector<Task> tasks;
@@ -510,8 +515,7 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
     int32_t t = p >= 0 ? task_of_row[p] : -1;
     // n_chunks counts the tile refs of the run (one per chunk of 64)
     const int32_t nt = tiles_of(R(r, 3));
-    if (t >= 0 && tasks[t].b == b && tasks[t].e == e && tasks[t].last_row == p &&
-        tasks[t].n_chunks + nt <= cf_group) {
+    if (t >= 0 && tasks[t].b == b && tasks[t].e == e && tasks[t].last_row == p) {
       tasks[t].n_chunks += nt;
       tasks[t].last_row = r;
     } else {
@@ -519,6 +523,31 @@ void Manager::build_plan(int cf_group, int sf_group, bool two_phase, Plan* plan,
       tasks.push_back({b, e, -1, nt, r});
     }
     task_of_row[r] = t;
+  }
+  {
+    // cut the chains: each run takes rows up to ceil(left / runs left) tiles
+    std::vector<std::vector<int32_t>> chain_rows(tasks.size());
+    for (int32_t r = 0; r < n_rows; ++r)
+      if (task_of_row[r] >= 0) chain_rows[task_of_row[r]].push_back(r);
+    std::vector<Task> cut;
+    const int32_t g = std::max(1, cf_group);
+    for (size_t t = 0; t < tasks.size(); ++t) {
+      int32_t left = tasks[t].n_chunks;
+      const std::vector<int32_t>& rows = chain_rows[t];
+      for (size_t i = 0; i < rows.size();) {
+        const int32_t runs_left = (left + g - 1) / g, cap = (left + runs_left - 1) / runs_left;
+        const int32_t id = static_cast<int32_t>(cut.size());
+        cut.push_back({tasks[t].b, tasks[t].e, -1, 0, -1});
+        do {
+          cut[id].n_chunks += tiles_of(R(rows[i], 3));
+          cut[id].last_row = rows[i];
+          task_of_row[rows[i]] = id;
+          ++i;
+        } while (i < rows.size() && cut[id].n_chunks + tiles_of(R(rows[i], 3)) <= cap);
+        left -= cut[id].n_chunks;
+      }
+    }
+    tasks.swap(cut);
   }
   // chunk refs of each run, in row order; its 32-row units (partial ids later)
   std::vector<int32_t> unit_task;

@@ -530,6 +530,25 @@ def test_sequence_first_fallback_three_without_single_chunk_tasks(private, want)
     assert st["sf_tasks"] == 32 * -(-n // want)
 
 
+@pytest.mark.parametrize("chunk,shared,group,want", [
+    (64, 1766, 16, [14, 14]), (64, 4096, 16, [16, 16, 16, 16]), (64, 1024, 16, [16]),
+    (64, 2112, 16, [11, 11, 11]), (128, 1766, 16, [14, 14]), (64, 1766, 5, [5, 5, 5, 5, 4, 4])])
+def test_chunk_first_runs_cut_evenly(chunk, shared, group, want):
+    """A chain of shared chunks longer than the chunk-first group is cut into
+    as few runs as the group allows, of equal length to within one chunk:
+    28 tiles (1,766 tokens at chunk 64) in two runs of 14, not 16 + 12; 33 in
+    three of 11; a 128-token chunk's two tiles stay in one run."""
+    ca = ChunkAttention(8, 10_000, device=None, chunk_size=chunk)
+    ca.set_option(_capi.CA_OPT_CF_CHUNKS_PER_TASK, group)
+    for i in range(32):
+        ca.insert(i, list(range(shared)) + [100_000 + 1000 * i + j for j in range(200)])
+    st = ca.stats()
+    img = np.frombuffer(ca.export_plan(), dtype=np.int32)
+    units = img[:32 * int(st["cf_units"])].reshape(-1, 32)
+    assert sorted(units[:, 1].tolist(), reverse=True) == want
+    assert sum(want) == -(-shared // 64)
+
+
 @pytest.mark.parametrize("shared,want", [(1024, 8), (0, 16)])
 def test_sequence_first_group_with_chunk_first_units(shared, want):
     """The automatic sequence-first group asks for 8/5 as many tasks when
